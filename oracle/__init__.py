@@ -1,0 +1,161 @@
+"""CPU oracle for the depthwise-convolution path (test infrastructure only).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark use
+this package; the library and its Python binding never import it.  It shares
+no code with the HIP path: the arithmetic lives in ``oracle.c`` (plain
+single-threaded C, fp64 accumulation), loaded here through ctypes.  Inputs
+are float32 numpy arrays (or anything ``numpy.asarray`` accepts), outputs
+are float64 numpy arrays.
+
+Parity pins for every function here live in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_F = ctypes.POINTER(ctypes.c_float)
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int32)
+_L = ctypes.c_long
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (plain IEEE arithmetic)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call([
+            "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c99",
+            "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        lib.oracle_dwconv1d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, ctypes.c_int]
+        lib.oracle_dwconv2d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, _L, _L, _L, _L]
+        lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L, _L]
+        lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L]
+        for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd,
+                  lib.oracle_dwconv2d_bwd, lib.oracle_dwsub_front_fwd):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(a, shape=None):
+    if a is None:
+        return None, None
+    if hasattr(a, "detach"):  # a torch tensor: take its float32 values on the host
+        a = a.detach().float().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a, a.ctypes.data_as(_F)
+
+
+def _lens(lengths, B):
+    if lengths is None:
+        return None, None
+    if hasattr(lengths, "detach"):
+        lengths = lengths.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+    if a.shape != (B,):
+        raise ValueError(f"lengths must have shape ({B},), got {a.shape}")
+    return a, a.ctypes.data_as(_I)
+
+
+def _ptr_d(a):
+    return a.ctypes.data_as(_D) if a is not None else None
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: invalid arguments")
+
+
+def conv_out_len(n: int, k: int, s: int, p: int) -> int:
+    """floor((n + 2p - k) / s) + 1, never below zero (the convolution output length)."""
+    return max(0, (n + 2 * p - k) // s + 1)
+
+
+def dwconv1d_fwd(x, w, b, lengths, causal: bool):
+    """y [B,T,C] of the masked, padded 1-D depthwise conv; x [B,T,C], w [K,C]."""
+    xa, xp = _f32(x)
+    B, T, C = xa.shape
+    wa, wp = _f32(w)
+    K = wa.shape[0]
+    if wa.shape != (K, C):
+        raise ValueError("w must be [K, C]")
+    ba, bp = _f32(b, (C,))
+    la, lp = _lens(lengths, B)
+    y = np.empty((B, T, C), dtype=np.float64)
+    _check(_load().oracle_dwconv1d_fwd(xp, wp, bp, lp, _ptr_d(y), B, T, C, K, int(bool(causal))),
+           "oracle_dwconv1d_fwd")
+    return y
+
+
+def dwconv2d_fwd(x, w, b, lengths, stride: int = 2, pad: int = 1):
+    """y [B,T',F',C] of the masked depthwise conv2d; x [B,T,F,C], w [KH,KW,C]."""
+    xa, xp = _f32(x)
+    B, T, F, C = xa.shape
+    wa, wp = _f32(w)
+    KH, KW = wa.shape[0], wa.shape[1]
+    if wa.shape != (KH, KW, C):
+        raise ValueError("w must be [KH, KW, C]")
+    ba, bp = _f32(b, (C,))
+    la, lp = _lens(lengths, B)
+    To, Fo = conv_out_len(T, KH, stride, pad), conv_out_len(F, KW, stride, pad)
+    y = np.empty((B, To, Fo, C), dtype=np.float64)
+    _check(_load().oracle_dwconv2d_fwd(xp, wp, bp, lp, _ptr_d(y), B, T, F, C, KH, KW, stride, pad),
+           "oracle_dwconv2d_fwd")
+    return y
+
+
+def dwconv2d_bwd(x, w, lengths, dy, stride: int = 2, pad: int = 1, want=("dx", "dw", "db")):
+    """(dx, dw, db) of the masked depthwise conv2d given dy; entries not in `want` are None."""
+    xa, xp = _f32(x)
+    B, T, F, C = xa.shape
+    wa, wp = _f32(w)
+    KH, KW = wa.shape[0], wa.shape[1]
+    la, lp = _lens(lengths, B)
+    To, Fo = conv_out_len(T, KH, stride, pad), conv_out_len(F, KW, stride, pad)
+    da, dp = _f32(dy, (B, To, Fo, C))
+    dx = np.empty((B, T, F, C), dtype=np.float64) if "dx" in want else None
+    dw = np.empty((KH, KW, C), dtype=np.float64) if "dw" in want else None
+    db = np.empty((C,), dtype=np.float64) if "db" in want else None
+    _check(_load().oracle_dwconv2d_bwd(xp, wp, lp, dp, _ptr_d(dx), _ptr_d(dw), _ptr_d(db),
+                                       B, T, F, C, KH, KW, stride, pad), "oracle_dwconv2d_bwd")
+    return dx, dw, db
+
+
+def dwsub_front_fwd(x, w0, b0, w1, b1, lengths):
+    """y [B,T2,F2,C] of the subsampler front; x [B,T,F] (one mel channel)."""
+    xa, xp = _f32(x)
+    B, T, F = xa.shape
+    w0a, w0p = _f32(w0)
+    C = w0a.shape[2]
+    if w0a.shape != (3, 3, C):
+        raise ValueError("w0 must be [3, 3, C]")
+    b0a, b0p = _f32(b0, (C,))
+    w1a, w1p = _f32(w1, (3, 3, C))
+    b1a, b1p = _f32(b1, (C,))
+    la, lp = _lens(lengths, B)
+    T1, F1 = conv_out_len(T, 3, 2, 1), conv_out_len(F, 3, 2, 1)
+    T2, F2 = conv_out_len(T1, 3, 2, 1), conv_out_len(F1, 3, 2, 1)
+    y = np.empty((B, T2, F2, C), dtype=np.float64)
+    _check(_load().oracle_dwsub_front_fwd(xp, w0p, b0p, w1p, b1p, lp, _ptr_d(y), B, T, F, C),
+           "oracle_dwsub_front_fwd")
+    return y
