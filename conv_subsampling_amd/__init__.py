@@ -1,0 +1,214 @@
+"""Depthwise-convolution path for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libdwconv.so``, whose C ABI is declared in
+``include/dwconv.h``.  Every step of every operation runs in the library's
+HIP kernels; this module only checks tensor dtypes, devices and layouts,
+allocates outputs with torch when the caller gives none, and passes raw
+device pointers plus torch's current HIP stream.  It fails loudly when the
+library has not been built: there is no other implementation to fall back on.
+
+Layouts are channel-last and contiguous: x [B,T,C] (1-D), [B,T,F,C] (2-D),
+[B,T,F] (mel); weights tap-major w [K,C] / [3,3,C]; lengths int32 [B] on the
+same device (or None for full length).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "DwconvError", "abi_version",
+    "dwconv1d_fwd", "dwsub_fused_fwd", "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
+    "out_len",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdwconv.so")
+
+DW_OK, DW_ERR_INVALID_ARG, DW_ERR_UNSUPPORTED, DW_ERR_WORKSPACE, DW_ERR_HIP = 0, -1, -2, -3, -4
+DW_F32, DW_BF16 = 0, 1
+DW_PAD_SYMMETRIC, DW_PAD_CAUSAL = 0, 1
+
+
+class DwconvError(RuntimeError):
+    """A call into libdwconv.so returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[status {status}] {message}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first "
+        "(python -m conv_subsampling_amd.build, or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+_lib.dw_abi_version.restype = _int
+_lib.dw_abi_version.argtypes = []
+_lib.dw_last_error.restype = ctypes.c_char_p
+_lib.dw_last_error.argtypes = []
+_lib.dwconv1d_fwd.restype = _int
+_lib.dwconv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp]
+_lib.dwsub_fused_fwd.restype = _int
+_lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
+_lib.dwconv2d_fwd.restype = _int
+_lib.dwconv2d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i64] * 8 + [_vp]
+_lib.dwconv2d_bwd_workspace_bytes.restype = _sz
+_lib.dwconv2d_bwd_workspace_bytes.argtypes = [_i64] * 8
+_lib.dwconv2d_bwd.restype = _int
+_lib.dwconv2d_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz] + [_i64] * 8 + [_vp]
+
+
+def abi_version() -> int:
+    return _lib.dw_abi_version()
+
+
+def _check(status: int) -> None:
+    if status != DW_OK:
+        raise DwconvError(status, _lib.dw_last_error().decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(name, t, dtype, device, shape=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def out_len(n: int) -> int:
+    """Output length of a 3x3 / stride 2 / pad 1 convolution along one axis."""
+    return (n + 1) // 2
+
+
+def dwconv1d_fwd(x, w, bias=None, lengths=None, y=None, causal: bool = False):
+    """Depthwise Conv1d in SSM_CONV form; x [B,T,C], w [K,C] (float32 or bfloat16)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
+    dev, dt = x.device, x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError("dwconv1d_fwd takes float32 or bfloat16 tensors")
+    B, T, C = x.shape
+    _dev_tensor("x", x, dt, dev)
+    if w.dim() != 2 or w.shape[1] != C:
+        raise ValueError("w must be [K, C]")
+    _dev_tensor("w", w, dt, dev)
+    K = w.shape[0]
+    _dev_tensor("bias", bias, dt, dev, (C,), allow_none=True)
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    if y is None:
+        y = torch.empty_like(x)
+    _dev_tensor("y", y, dt, dev, (B, T, C))
+    _check(_lib.dwconv1d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(lengths), _ptr(y), B, T, C, K,
+                             DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC,
+                             DW_BF16 if dt == torch.bfloat16 else DW_F32, _stream(dev)))
+    return y
+
+
+def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None):
+    """Fused subsampler front; x [B,T,F] float32 mel -> y [B,T2,F2,C]."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, F]")
+    dev, f32 = x.device, torch.float32
+    B, T, F = x.shape
+    _dev_tensor("x", x, f32, dev)
+    if w0.dim() != 3 or w0.shape[:2] != (3, 3):
+        raise ValueError("w0 must be [3, 3, C]")
+    C = w0.shape[2]
+    _dev_tensor("w0", w0, f32, dev)
+    _dev_tensor("b0", b0, f32, dev, (C,), allow_none=True)
+    _dev_tensor("w1", w1, f32, dev, (3, 3, C))
+    _dev_tensor("b1", b1, f32, dev, (C,), allow_none=True)
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    T2, F2 = out_len(out_len(T)), out_len(out_len(F))
+    if y is None:
+        y = torch.empty((B, T2, F2, C), dtype=f32, device=dev)
+    _dev_tensor("y", y, f32, dev, (B, T2, F2, C))
+    _check(_lib.dwsub_fused_fwd(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(b1), _ptr(lengths), _ptr(y),
+                                B, T, F, C, _stream(dev)))
+    return y
+
+
+def _conv2d_dims(x, w):
+    if x.dim() != 4:
+        raise ValueError("x must be [B, T, F, C]")
+    B, T, F, C = x.shape
+    if w.dim() != 3 or w.shape[2] != C:
+        raise ValueError("w must be [KH, KW, C]")
+    return B, T, F, C, w.shape[0], w.shape[1]
+
+
+def dwconv2d_fwd(x, w, bias=None, lengths=None, y=None, stride: int = 2, pad: int = 1):
+    """Masked depthwise conv2d; x [B,T,F,C], w [3,3,C] -> y [B,T',F',C] (float32)."""
+    dev, f32 = x.device, torch.float32
+    B, T, F, C, KH, KW = _conv2d_dims(x, w)
+    _dev_tensor("x", x, f32, dev)
+    _dev_tensor("w", w, f32, dev)
+    _dev_tensor("bias", bias, f32, dev, (C,), allow_none=True)
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    To = max(0, (T + 2 * pad - KH) // stride + 1)
+    Fo = max(0, (F + 2 * pad - KW) // stride + 1)
+    if y is None:
+        y = torch.empty((B, To, Fo, C), dtype=f32, device=dev)
+    _dev_tensor("y", y, f32, dev, (B, To, Fo, C))
+    _check(_lib.dwconv2d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(lengths), _ptr(y),
+                             B, T, F, C, KH, KW, stride, pad, _stream(dev)))
+    return y
+
+
+def dwconv2d_bwd_workspace_bytes(B, T, F, C, KH=3, KW=3, stride=2, pad=1) -> int:
+    return int(_lib.dwconv2d_bwd_workspace_bytes(B, T, F, C, KH, KW, stride, pad))
+
+
+def dwconv2d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None,
+                 need=("dx", "dw", "db"), stride: int = 2, pad: int = 1):
+    """Gradients (dx, dw, db) of dwconv2d_fwd given dy; outputs not in `need` are skipped (None)."""
+    dev, f32 = x.device, torch.float32
+    B, T, F, C, KH, KW = _conv2d_dims(x, w)
+    _dev_tensor("x", x, f32, dev)
+    _dev_tensor("w", w, f32, dev)
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    To = max(0, (T + 2 * pad - KH) // stride + 1)
+    Fo = max(0, (F + 2 * pad - KW) // stride + 1)
+    _dev_tensor("dy", dy, f32, dev, (B, To, Fo, C))
+    if dx is None and "dx" in need:
+        dx = torch.empty_like(x)
+    if dw is None and "dw" in need:
+        dw = torch.empty((KH, KW, C), dtype=f32, device=dev)
+    if db is None and "db" in need:
+        db = torch.empty((C,), dtype=f32, device=dev)
+    _dev_tensor("dx", dx, f32, dev, (B, T, F, C), allow_none=True)
+    _dev_tensor("dw", dw, f32, dev, (KH, KW, C), allow_none=True)
+    _dev_tensor("db", db, f32, dev, (C,), allow_none=True)
+    ws_bytes = 0
+    if dw is not None or db is not None:
+        need_ws = dwconv2d_bwd_workspace_bytes(B, T, F, C, KH, KW, stride, pad)
+        if workspace is None:
+            workspace = torch.empty((max(need_ws, 1),), dtype=torch.uint8, device=dev)
+        _dev_tensor("workspace", workspace, torch.uint8, dev)
+        ws_bytes = workspace.numel()
+    _check(_lib.dwconv2d_bwd(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
+                             _ptr(workspace), ws_bytes, B, T, F, C, KH, KW, stride, pad, _stream(dev)))
+    return dx, dw, db

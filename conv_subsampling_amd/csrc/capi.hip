@@ -1,0 +1,131 @@
+// The library's C ABI (declared in include/dwconv.h): host-side argument
+// validation, the thread-local error message, and dispatch to the kernel
+// launchers.  Nothing here allocates, frees or synchronises.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/dwconv.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+dw_status fail(dw_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dw_status ok() {
+    g_err[0] = '\0';
+    return DW_OK;
+}
+
+dw_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DW_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+bool geometry_3x3_s2_p1(int64_t KH, int64_t KW, int64_t stride, int64_t pad) {
+    return KH == 3 && KW == 3 && stride == 2 && pad == 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dw_abi_version(void) { return DW_ABI_VERSION; }
+
+const char* dw_last_error(void) { return g_err; }
+
+dw_status dwconv1d_fwd(const void* x, const void* w, const void* bias, const int32_t* lengths,
+                       void* y, int64_t B, int64_t T, int64_t C, int64_t K,
+                       dw_pad pad, dw_dtype dtype, void* stream) {
+    const char* fn = "dwconv1d_fwd";
+    if (B < 0 || T < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size (B=%lld T=%lld C=%lld)", fn, (long long)B, (long long)T, (long long)C);
+    if (K < 1) return fail(DW_ERR_INVALID_ARG, "%s: kernel width K=%lld must be >= 1", fn, (long long)K);
+    if (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL) return fail(DW_ERR_INVALID_ARG, "%s: unknown pad mode %d", fn, (int)pad);
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    if (B == 0 || T == 0 || C == 0) return ok();
+    if (!x || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
+    if (x == y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    const void* ptrs[4] = {x, w, bias, y};
+    const int vec = dw::pick_vec(C, es, ptrs, 4, dtype == DW_BF16 ? 4 : 4);
+    if (!dw::dwconv1d_fwd_fits(B, T, C, K, es, vec))
+        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch (B=%lld T=%lld C=%lld K=%lld)", fn, (long long)B, (long long)T, (long long)C, (long long)K);
+    const int64_t pL = pad == DW_PAD_CAUSAL ? K - 1 : (K - 1) / 2;
+    return from_hip(dw::launch_dwconv1d_fwd(x, w, bias, lengths, y, B, T, C, K, pL, dtype == DW_BF16, vec,
+                                            (hipStream_t)stream), fn);
+}
+
+dw_status dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,
+                          const int32_t* lengths, float* y, int64_t B, int64_t T, int64_t F, int64_t C,
+                          void* stream) {
+    const char* fn = "dwsub_fused_fwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (B == 0 || T == 0 || F == 0 || C == 0) return ok();
+    if (!x || !w0 || !w1 || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and y must not be NULL", fn);
+    if ((const void*)x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    if (!dw::dwsub_fused_fwd_fits(B, T, F, C))
+        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, (hipStream_t)stream), fn);
+}
+
+dw_status dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths, float* y,
+                       int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride,
+                       int64_t pad, void* stream) {
+    const char* fn = "dwconv2d_fwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (!geometry_3x3_s2_p1(KH, KW, stride, pad))
+        return fail(DW_ERR_UNSUPPORTED, "%s: only a 3x3 kernel with stride 2 and pad 1 is implemented (got %lldx%lld, stride %lld, pad %lld)", fn, (long long)KH, (long long)KW, (long long)stride, (long long)pad);
+    if (B == 0 || T == 0 || F == 0 || C == 0) return ok();
+    if (!x || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
+    if ((const void*)x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    const void* ptrs[4] = {x, w, bias, y};
+    const int vec = dw::pick_vec(C, 4, ptrs, 4, 4);
+    if (!dw::dwconv2d_fits(B, T, F, C, vec)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwconv2d_fwd(x, w, bias, lengths, y, B, T, F, C, vec, (hipStream_t)stream), fn);
+}
+
+size_t dwconv2d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW,
+                                    int64_t stride, int64_t pad) {
+    if (B < 0 || T < 0 || F < 0 || C < 0 || !geometry_3x3_s2_p1(KH, KW, stride, pad)) return 0;
+    return dw::dwconv2d_bwd_workspace(B, T, F, C);
+}
+
+dw_status dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+                       float* dw_, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                       int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad,
+                       void* stream) {
+    const char* fn = "dwconv2d_bwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    const int64_t To = (T + 1) / 2, Fo = (F + 1) / 2;
+    if ((!x && B * T * F * C > 0) || (!dy && B * To * Fo * C > 0) || (!w && C > 0))
+        return fail(DW_ERR_INVALID_ARG, "%s: x, w and dy must not be NULL (unless empty)", fn);
+    if (dx && ((const void*)dx == (const void*)x || (const void*)dx == (const void*)dy))
+        return fail(DW_ERR_INVALID_ARG, "%s: dx must not alias x or dy", fn);
+    if (!geometry_3x3_s2_p1(KH, KW, stride, pad))
+        return fail(DW_ERR_UNSUPPORTED, "%s: only a 3x3 kernel with stride 2 and pad 1 is implemented (got %lldx%lld, stride %lld, pad %lld)", fn, (long long)KH, (long long)KW, (long long)stride, (long long)pad);
+    const bool want_wb = dw_ || db;
+    if (want_wb) {
+        const size_t need = dw::dwconv2d_bwd_workspace(B, T, F, C);
+        if (!workspace || workspace_bytes < need)
+            return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
+    }
+    if (!dx && !want_wb) return ok();
+    if (C == 0) return ok();
+    // An empty batch or item still defines dw = 0 and db = 0; the launcher
+    // writes those zeros when there is nothing to reduce.
+    const void* ptrs[6] = {x, w, dy, dx, dw_, db};
+    const int vec = dw::pick_vec(C, 4, ptrs, 6, 4);
+    if (!dw::dwconv2d_fits(B, T, F, C, vec)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwconv2d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, T, F, C, vec,
+                                            (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// Depthwise Conv1d in SSM_CONV form for gfx950 (parakeet.cpp PR #102,
+// "What changes": y[t, c] = sum_k x[t + k, c] * w[k, c] over the input
+// padded to T + K - 1 frames, with per-item length masking).
+//
+// Mapping.  Each workgroup serves one batch item; within it, one thread owns
+// V consecutive channels (one vector access) of TT consecutive output frames.
+// Thread ids run channel-group fastest, so a wavefront's loads of one frame
+// are contiguous in memory, and neighbouring time tiles of the same channels
+// sit in the same or the next workgroup; blocks are renumbered so those land
+// on one XCD and the K - 1 halo frames they share are served from its L2.
+//
+// Masking and padding cost nothing: the item's input is read through a
+// buffer resource that ends at the item's valid length, so frames at or past
+// the length, and the left padding (negative offsets), load as zero with no
+// branch and no memory traffic; the output resource ends at T, so stores of
+// a ragged last tile are dropped.  Per thread, the TT + K - 1 input frames
+// the tile needs are loaded into a register window with back-to-back
+// independent loads, the K taps slide over it with fp32 FMAs (the bias seeds
+// each sum), and frames at or past the length are stored as exact zeros.  A
+// tile that lies wholly past the length stores zeros without loading.
+// Output uses non-temporal stores: nothing here reads it back.
+#include "common.h"
+#include "launch.h"
+
+namespace dw {
+
+constexpr int kBlock1d = 256;
+
+struct Tile1d {
+    uint32_t b, tile, cg;
+    bool valid;
+};
+
+// Decode (item, time tile, channel group) from the block and thread index;
+// the item depends on the block alone, so it is uniform across the wave.
+__device__ __forceinline__ Tile1d decode_1d(uint32_t n_tiles, uint32_t CG, uint32_t blocks_per_item) {
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    Tile1d d;
+    d.b = blk / blocks_per_item;
+    const uint32_t local = (blk - d.b * blocks_per_item) * kBlock1d + threadIdx.x;
+    d.tile = local / CG;
+    d.cg = local - d.tile * CG;
+    d.valid = d.tile < n_tiles;
+    return d;
+}
+
+template <typename S, int V, int K, int TT>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_kernel(
+    const S* __restrict__ x, const S* __restrict__ w, const S* __restrict__ bias,
+    const int32_t* __restrict__ lengths, S* __restrict__ y,
+    int32_t T, int32_t C, int32_t pL, uint32_t n_tiles, uint32_t CG, uint32_t blocks_per_item) {
+    const Tile1d d = decode_1d(n_tiles, CG, blocks_per_item);
+    if (!d.valid) return;
+    const int32_t len = (int32_t)item_length(lengths, d.b, T);
+    const uint32_t row = (uint32_t)C * sizeof(S);
+    const int64_t item = (int64_t)d.b * T * C;
+    const rsrc_t xr = make_rsrc(x + item, (uint32_t)len * row);
+    const rsrc_t yr = make_rsrc(y + item, (uint32_t)T * row);
+    const int32_t c0 = (int32_t)d.cg * V;
+    const uint32_t coff = (uint32_t)c0 * sizeof(S);
+    const int32_t t0 = (int32_t)d.tile * TT;
+
+    if (t0 >= len) {
+        const Vf<V> z = vzero<V>();
+#pragma unroll
+        for (int i = 0; i < TT; ++i) Buf<S, V>::store(yr, (uint32_t)(t0 + i) * row + coff, z);
+        return;
+    }
+
+    Vf<V> win[TT + K - 1];
+#pragma unroll
+    for (int r = 0; r < TT + K - 1; ++r)
+        win[r] = Buf<S, V>::load(xr, (uint32_t)((t0 - pL + r) * (int32_t)row) + coff);
+    Vf<V> wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
+    const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
+
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        Vf<V> acc = bv;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc.v[e] = __builtin_fmaf(win[i + k].v[e], wk[k].v[e], acc.v[e]);
+        const bool keep = t0 + i < len;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc.v[e] = keep ? acc.v[e] : 0.0f;
+        Buf<S, V>::store(yr, (uint32_t)(t0 + i) * row + coff, acc);
+    }
+}
+
+// Any K: the same tiling, with the taps read through the cache instead of a
+// register window whose size would have to be known at compile time.
+template <typename S, int V, int TT>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_anyk_kernel(
+    const S* __restrict__ x, const S* __restrict__ w, const S* __restrict__ bias,
+    const int32_t* __restrict__ lengths, S* __restrict__ y,
+    int32_t T, int32_t C, int32_t K, int32_t pL, uint32_t n_tiles, uint32_t CG, uint32_t blocks_per_item) {
+    const Tile1d d = decode_1d(n_tiles, CG, blocks_per_item);
+    if (!d.valid) return;
+    const int32_t len = (int32_t)item_length(lengths, d.b, T);
+    const uint32_t row = (uint32_t)C * sizeof(S);
+    const int64_t item = (int64_t)d.b * T * C;
+    const rsrc_t xr = make_rsrc(x + item, (uint32_t)len * row);
+    const rsrc_t yr = make_rsrc(y + item, (uint32_t)T * row);
+    const int32_t c0 = (int32_t)d.cg * V;
+    const uint32_t coff = (uint32_t)c0 * sizeof(S);
+    const int32_t t0 = (int32_t)d.tile * TT;
+    const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
+
+    for (int i = 0; i < TT; ++i) {
+        const int32_t t = t0 + i;
+        Vf<V> acc = bv;
+        if (t < len) {
+            for (int k = 0; k < K; ++k) {
+                const Vf<V> xv = Buf<S, V>::load(xr, (uint32_t)((t - pL + k) * (int32_t)row) + coff);
+                const Vf<V> wv = load_param<S, V>(w + (int64_t)k * C + c0);
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc.v[e] = __builtin_fmaf(xv.v[e], wv.v[e], acc.v[e]);
+            }
+        } else {
+            acc = vzero<V>();
+        }
+        Buf<S, V>::store(yr, (uint32_t)t * row + coff, acc);
+    }
+}
+
+// Time-tile length per thread for each specialised width (register window of
+// TT + K - 1 channel vectors).
+template <int K>
+constexpr int tile_1d() { return 16; }
+constexpr int kTileAnyK = 8;
+
+static int tile_for(int64_t K) {
+    switch (K) {
+        case 3: return tile_1d<3>();
+        case 4: return tile_1d<4>();
+        case 5: return tile_1d<5>();
+        case 9: return tile_1d<9>();
+        case 15: return tile_1d<15>();
+        default: return kTileAnyK;
+    }
+}
+
+bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec) {
+    // Per-item byte offsets, including the left padding as a negative
+    // offset, must stay within a signed 32-bit range.
+    if ((T + K) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    const int64_t tt = tile_for(K);
+    const int64_t per_item = ((T + tt - 1) / tt) * (C / vec);
+    const int64_t blocks = B * ((per_item + kBlock1d - 1) / kBlock1d);
+    return blocks < ((int64_t)1 << 31);
+}
+
+template <typename S, int V>
+static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int32_t* lengths, S* y,
+                               int64_t B, int64_t T, int64_t C, int64_t K, int64_t pL, hipStream_t st) {
+    const int tt = tile_for(K);
+    const uint32_t n_tiles = (uint32_t)((T + tt - 1) / tt);
+    const uint32_t CG = (uint32_t)(C / V);
+    const uint32_t bpi = (uint32_t)(((uint64_t)n_tiles * CG + kBlock1d - 1) / kBlock1d);
+    const dim3 grid((uint32_t)(B * bpi)), block(kBlock1d);
+    const int32_t T32 = (int32_t)T, C32 = (int32_t)C, p32 = (int32_t)pL;
+#define DW1D_CASE(KK)                                                                            \
+    case KK:                                                                                     \
+        hipLaunchKernelGGL((dwconv1d_fwd_kernel<S, V, KK, tile_1d<KK>()>), grid, block, 0, st, x, \
+                           w, bias, lengths, y, T32, C32, p32, n_tiles, CG, bpi);                  \
+        break;
+    switch (K) {
+        DW1D_CASE(3)
+        DW1D_CASE(4)
+        DW1D_CASE(5)
+        DW1D_CASE(9)
+        DW1D_CASE(15)
+        default:
+            hipLaunchKernelGGL((dwconv1d_fwd_anyk_kernel<S, V, kTileAnyK>), grid, block, 0, st, x, w,
+                               bias, lengths, y, T32, C32, (int32_t)K, p32, n_tiles, CG, bpi);
+    }
+#undef DW1D_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_dwconv1d_fwd(const void* x, const void* w, const void* bias, const int32_t* lengths,
+                               void* y, int64_t B, int64_t T, int64_t C, int64_t K, int64_t pad_left,
+                               bool bf16, int vec, hipStream_t st) {
+    if (bf16) {
+        auto X = (const uint16_t*)x; auto W = (const uint16_t*)w; auto Bi = (const uint16_t*)bias;
+        auto Y = (uint16_t*)y;
+        switch (vec) {
+            case 4: return launch_typed<uint16_t, 4>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
+            case 2: return launch_typed<uint16_t, 2>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
+            default: return launch_typed<uint16_t, 1>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
+        }
+    }
+    auto X = (const float*)x; auto W = (const float*)w; auto Bi = (const float*)bias;
+    auto Y = (float*)y;
+    switch (vec) {
+        case 4: return launch_typed<float, 4>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
+        case 2: return launch_typed<float, 2>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
+        default: return launch_typed<float, 1>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
+    }
+}
+
+int pick_vec(int64_t C, int elem_bytes, const void* const* ptrs, int nptrs, int max_vec) {
+    for (int v = max_vec; v > 1; v /= 2) {
+        if (C % v) continue;
+        bool ok = true;
+        for (int i = 0; i < nptrs; ++i)
+            if (ptrs[i] && ((uintptr_t)ptrs[i] % (uintptr_t)(v * elem_bytes))) ok = false;
+        if (ok) return v;
+    }
+    return 1;
+}
+
+}  // namespace dw

@@ -1,0 +1,43 @@
+// Host-side launchers of the gfx950 kernels.  The C ABI in capi.hip
+// validates every argument and then calls exactly one of these; they assume
+// valid, non-empty sizes and only compute launch geometry and enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dw {
+
+// Largest vector width V <= max_vec (channels per access, a power of two)
+// such that C is a multiple of V and every pointer given is aligned to V
+// elements.
+int pick_vec(int64_t C, int elem_bytes, const void* const* ptrs, int nptrs, int max_vec);
+
+// Whether launch_dwconv1d_fwd can address these sizes (32-bit per-item byte
+// offsets, 32-bit grid).
+bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec);
+
+hipError_t launch_dwconv1d_fwd(const void* x, const void* w, const void* bias, const int32_t* lengths,
+                               void* y, int64_t B, int64_t T, int64_t C, int64_t K, int64_t pad_left,
+                               bool bf16, int vec, hipStream_t stream);
+
+bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C);
+
+hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1,
+                                  const float* b1, const int32_t* lengths, float* y,
+                                  int64_t B, int64_t T, int64_t F, int64_t C, hipStream_t stream);
+
+bool dwconv2d_fits(int64_t B, int64_t T, int64_t F, int64_t C, int vec);
+
+hipError_t launch_dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths,
+                               float* y, int64_t B, int64_t T, int64_t F, int64_t C, int vec,
+                               hipStream_t stream);
+
+size_t dwconv2d_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C);
+
+hipError_t launch_dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy,
+                               float* dx, float* dw, float* db, void* workspace,
+                               int64_t B, int64_t T, int64_t F, int64_t C, int vec, hipStream_t stream);
+
+}  // namespace dw

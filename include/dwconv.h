@@ -1,0 +1,180 @@
+/*
+ * dwconv.h -- C ABI of the depthwise-convolution library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * What it computes (the pages cited are parakeet.cpp PR #102, "one SSM_CONV
+ * for the depthwise conv, less host work per step", and NVIDIA NeMo PR
+ * #16114, "Use Fused Kernels for Depthwise Striding Subsampler"):
+ *   dwconv1d_fwd     the Conformer conv module's depthwise Conv1d in SSM_CONV
+ *                    form (PR #102, "What changes")
+ *   dwsub_fused_fwd  the depthwise-striding subsampler front: conv0, bias,
+ *                    ReLU, time mask and depthwise conv, fused (PR #16114,
+ *                    "What does this PR do", first kernel)
+ *   dwconv2d_fwd     the general depthwise conv2d with pre/post masking
+ *                    (PR #16114, "What does this PR do", second kernel)
+ *   dwconv2d_bwd     its backward: dx, dw, db (same section)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, contiguous and channel-last (channel index fastest):
+ *     [B][T][C] for 1-D, [B][T][F][C] for 2-D, [B][T][F] for the one-channel
+ *     mel input.  Weights are tap-major: w[K][C] (1-D), w[KH][KW][C] (2-D).
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises; all work is enqueued
+ *     on `stream` (a hipStream_t; NULL means the default stream) and is
+ *     asynchronous with respect to the host.
+ *   - lengths[B] (int32, device memory) holds each item's valid number of
+ *     input frames; it is read on the device and clamped to [0, T].  NULL
+ *     means every item is T frames long.  Frames t >= length are treated as
+ *     zero on input (pre-mask) and written as exact zeros on output
+ *     (post-mask), where the operation masks.
+ *   - A NULL bias means a zero bias.
+ *   - Sizes are int64_t.  A forward call with no output elements enqueues
+ *     nothing and returns DW_OK without looking at its pointers; a tensor
+ *     with no elements may be NULL.
+ *   - Errors: every argument is validated on the host before anything is
+ *     enqueued.  A failing call returns a negative dw_status, enqueues
+ *     nothing (except DW_ERR_HIP, raised when a launch is rejected) and sets
+ *     a thread-local message readable with dw_last_error().  No entry point
+ *     aborts, and none falls back to another algorithm.
+ *   - The library keeps no mutable global state other than that message, so
+ *     calls from several host threads are safe.  Two calls whose output
+ *     buffers overlap race, as any two kernels writing the same memory do.
+ */
+#ifndef DWCONV_H
+#define DWCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DW_ABI_VERSION 1
+
+typedef enum {
+    DW_OK = 0,
+    DW_ERR_INVALID_ARG = -1,  /* null required pointer, negative size, aliasing, bad enum */
+    DW_ERR_UNSUPPORTED = -2,  /* a geometry this library does not implement */
+    DW_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+    DW_ERR_HIP = -4           /* the HIP runtime rejected a launch */
+} dw_status;
+
+typedef enum { DW_F32 = 0, DW_BF16 = 1 } dw_dtype;
+
+typedef enum { DW_PAD_SYMMETRIC = 0, DW_PAD_CAUSAL = 1 } dw_pad;
+
+/* DW_ABI_VERSION of the built library. */
+int dw_abi_version(void);
+
+/* Message describing the last failing call on this host thread ("" if none). */
+const char *dw_last_error(void);
+
+/*
+ * dwconv1d_fwd -- depthwise Conv1d (groups = C) in SSM_CONV form
+ * (parakeet.cpp PR #102, "What changes": one SSM_CONV over the input padded
+ * to T + K - 1 frames, summing x[t+k, c] * w[k, c] over k).
+ *
+ *   pL = K - 1                for DW_PAD_CAUSAL (all padding on the left)
+ *   pL = (K - 1) / 2          for DW_PAD_SYMMETRIC (an even K puts the extra
+ *                             frame of padding on the right)
+ *   xs[b, s, c] = x[b, s - pL, c] if 0 <= s - pL < len_b, else 0
+ *   y[b, t, c]  = sum_{k<K} xs[b, t + k, c] * w[k, c] + bias[c]   (t < len_b)
+ *   y[b, t, c]  = 0                                               (t >= len_b)
+ *
+ * x, y: [B][T][C]; w: [K][C]; bias: [C] or NULL; lengths: [B] or NULL.
+ * dtype DW_F32: all of x, w, bias, y are float.  DW_BF16: all are bf16
+ * (uint16 bit patterns); products and sums are carried in float32 and y is
+ * rounded to nearest-even.  Any C >= 1 and any K >= 1 are accepted.
+ * Errors: DW_ERR_INVALID_ARG for a null x, w or y, a negative size, K < 1, a
+ * bad pad or dtype, or x == y.
+ */
+dw_status dwconv1d_fwd(const void *x, const void *w, const void *bias, const int32_t *lengths,
+                       void *y, int64_t B, int64_t T, int64_t C, int64_t K,
+                       dw_pad pad, dw_dtype dtype, void *stream);
+
+/*
+ * dwsub_fused_fwd -- the depthwise-striding subsampler front, fused (NeMo PR
+ * #16114, "What does this PR do": mel [B,T,F,1] -> conv0 3x3 stride 2
+ * [B,T/2,F/2,C] -> ReLU -> masking -> depthwise 3x3 stride 2 conv
+ * [B,T/4,F/4,C]).  The intermediate h is never written to memory.
+ *
+ *   T1 = (T+1)/2, F1 = (F+1)/2, L1_b = (len_b+1)/2, T2 = (T1+1)/2, F2 = (F1+1)/2
+ *   h[b,t1,f1,c] = max(0, sum_{i,j<3} x[b, 2t1+i-1, 2f1+j-1] * w0[i,j,c] + b0[c])
+ *                  for t1 < L1_b, else 0
+ *   y[b,t2,f2,c] = sum_{i,j<3} h[b, 2t2+i-1, 2f2+j-1, c] * w1[i,j,c] + b1[c]
+ * with zero padding of one on each side of both stages.  The mel input is
+ * not length-masked and y is not masked; the one mask is the one on h.
+ *
+ * x: [B][T][F] float; w0, w1: [3][3][C] float; b0, b1: [C] float or NULL;
+ * lengths: [B] or NULL; y: [B][T2][F2][C] float.  Arithmetic is IEEE fp32
+ * fused multiply-add (no reduced-precision products).
+ * Errors: DW_ERR_INVALID_ARG for a null x, w0, w1 or y, a negative size or
+ * x == y.
+ */
+dw_status dwsub_fused_fwd(const float *x, const float *w0, const float *b0,
+                          const float *w1, const float *b1, const int32_t *lengths,
+                          float *y, int64_t B, int64_t T, int64_t F, int64_t C, void *stream);
+
+/*
+ * dwconv2d_fwd -- depthwise conv2d with pre- and post-masking (NeMo PR
+ * #16114, "What does this PR do", the general depthwise conv2d kernel).
+ *
+ *   T' = (T + 2p - KH)/s + 1,  F' = (F + 2p - KW)/s + 1  (floor division)
+ *   len'_b = (len_b + 2p - KH)/s + 1 clamped to [0, T'], and 0 if len_b = 0
+ *   y[b,t',f',c] = sum_{i,j} xm[b, s t'+i-p, s f'+j-p, c] * w[i,j,c] + bias[c]
+ *                  for t' < len'_b, else 0
+ * where xm is x with frames t >= len_b zeroed and indices outside the tensor
+ * read zero.  For the 3x3, stride 2, pad 1 geometry len' = ceil(len / 2).
+ *
+ * x: [B][T][F][C] float; w: [KH][KW][C] float; bias: [C] or NULL; y:
+ * [B][T'][F'][C] float.  Implemented geometry: KH = KW = 3, stride 2, pad 1;
+ * anything else returns DW_ERR_UNSUPPORTED.
+ * Errors: DW_ERR_INVALID_ARG for a null x, w or y, a negative size or x == y.
+ */
+dw_status dwconv2d_fwd(const float *x, const float *w, const float *bias, const int32_t *lengths,
+                       float *y, int64_t B, int64_t T, int64_t F, int64_t C,
+                       int64_t KH, int64_t KW, int64_t stride, int64_t pad, void *stream);
+
+/*
+ * Bytes of device workspace dwconv2d_bwd needs for these sizes when it
+ * computes dw or db (a call that requests neither needs none).  Returns 0
+ * for an unsupported geometry or invalid sizes.
+ */
+size_t dwconv2d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C,
+                                    int64_t KH, int64_t KW, int64_t stride, int64_t pad);
+
+/*
+ * dwconv2d_bwd -- gradients of dwconv2d_fwd (NeMo PR #16114, "What does this
+ * PR do": the general depthwise conv2d backward).  With g = dy at unmasked
+ * output rows (t' < len'_b) and 0 elsewhere:
+ *   dx[b,t,f,c] = sum over the (t',f',i,j) with t = s t'+i-p, f = s f'+j-p of
+ *                 g[b,t',f',c] * w[i,j,c]          for t < len_b, else 0
+ *   dw[i,j,c]   = sum_{b,t',f'} g[b,t',f',c] * xm[b, s t'+i-p, s f'+j-p, c]
+ *   db[c]       = sum_{b,t',f'} g[b,t',f',c]
+ * dx is written in gather form (no atomics); dw and db are accumulated in
+ * fp64 (the fp32 products are exact in fp64) and reduced in a fixed order,
+ * so repeated calls give bitwise-identical results.
+ *
+ * x: [B][T][F][C]; w: [KH][KW][C]; dy: [B][T'][F'][C]; dx: [B][T][F][C] or
+ * NULL (not computed); dw: [KH][KW][C] or NULL; db: [C] or NULL (all float).
+ * workspace: device memory of at least dwconv2d_bwd_workspace_bytes(...)
+ * bytes when dw or db is requested (may be NULL otherwise); its contents on
+ * entry are ignored and on return are unspecified.
+ * Implemented geometry: KH = KW = 3, stride 2, pad 1 (else DW_ERR_UNSUPPORTED).
+ * An empty batch (B, T or F zero) still writes dw = 0 and db = 0; x and dy
+ * may then be NULL.
+ * Errors: DW_ERR_INVALID_ARG for a null x, w or dy that holds elements, a
+ * negative size, dx aliasing x or dy; DW_ERR_WORKSPACE for a missing or
+ * short workspace.
+ */
+dw_status dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths, const float *dy,
+                       float *dx, float *dw, float *db, void *workspace, size_t workspace_bytes,
+                       int64_t B, int64_t T, int64_t F, int64_t C,
+                       int64_t KH, int64_t KW, int64_t stride, int64_t pad, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DWCONV_H */

@@ -1,0 +1,51 @@
+"""Helpers shared by the GPU parity tests (comparison rules and printing)."""
+import sys
+
+import numpy as np
+import torch
+
+# Tolerances, elementwise, in the form |gpu - ref| <= tol * (1 + |ref|):
+# fp32 storage 1e-5; bf16 storage with fp32 accumulation 2e-2.
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def say(*a):
+    """Name the case before each GPU step, flushed, so a failing run shows where it was."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host64(t):
+    if isinstance(t, torch.Tensor):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+    return np.asarray(t, dtype=np.float64)
+
+
+def assert_parity(gpu, ref, tol, what=""):
+    g = host64(gpu)
+    r = np.asarray(ref, dtype=np.float64)
+    assert g.shape == r.shape, f"{what}: shape {g.shape} vs {r.shape}"
+    if g.size == 0:
+        return 0.0
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    e = np.abs(g - r) / (1.0 + np.abs(r))
+    worst = float(e.max())
+    if worst > tol:
+        idx = np.unravel_index(int(e.argmax()), e.shape)
+        raise AssertionError(f"{what}: max err {worst:.3e} > {tol:.1e} at {idx}: gpu {g[idx]!r} ref {r[idx]!r}")
+    return worst
+
+
+def assert_exact_zero(gpu, mask, what=""):
+    g = host64(gpu)
+    m = np.broadcast_to(np.asarray(mask, dtype=bool), g.shape)
+    bad = np.count_nonzero(g[m] != 0.0)
+    assert bad == 0, f"{what}: {bad} masked outputs are not exactly zero"
+
+
+def time_mask(lengths, B, T, clamp=True):
+    """[B, T] boolean: True where the frame index is at or beyond the item's length."""
+    L = np.asarray(lengths.cpu() if isinstance(lengths, torch.Tensor) else lengths, dtype=np.int64)
+    L = np.clip(L, 0, T) if clamp else L
+    return np.arange(T)[None, :] >= L[:, None]

@@ -1,0 +1,135 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, and rejects bad arguments before touching the GPU.
+
+Argument validation happens on the host before anything is enqueued, so these
+calls pass dummy non-null addresses that are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dwconv.h")
+LIB = os.path.join(ROOT, "conv_subsampling_amd", "libdwconv.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, -1, -2, -3, -4
+P = ctypes.c_void_p(0x1000)      # dummy device addresses, never dereferenced
+Q = ctypes.c_void_p(0x2000)
+N = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert os.path.exists(LIB), "libdwconv.so is not built"
+    lib = ctypes.CDLL(LIB)
+    i64, vp, sz, i = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.dw_last_error.restype = ctypes.c_char_p
+    lib.dwconv1d_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i, i, vp]
+    lib.dwsub_fused_fwd.argtypes = [vp] * 7 + [i64] * 4 + [vp]
+    lib.dwconv2d_fwd.argtypes = [vp] * 5 + [i64] * 8 + [vp]
+    lib.dwconv2d_bwd_workspace_bytes.argtypes = [i64] * 8
+    lib.dwconv2d_bwd_workspace_bytes.restype = sz
+    lib.dwconv2d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 8 + [vp]
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for f in ("dwconv1d_fwd", "dwsub_fused_fwd", "dwconv2d_fwd", "dwconv2d_bwd",
+              "dwconv2d_bwd_workspace_bytes", "dw_abi_version", "dw_last_error"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libdwconv.so does not export {name}"
+
+
+def test_abi_version(lib):
+    assert lib.dw_abi_version() == 1
+
+
+def err(lib):
+    return lib.dw_last_error().decode()
+
+
+def test_dwconv1d_validation(lib):
+    f = lib.dwconv1d_fwd
+    assert f(P, P, N, N, Q, 2, 8, 4, 0, 0, 0, N) == INVALID and "K=0" in err(lib)
+    assert f(N, P, N, N, Q, 2, 8, 4, 3, 0, 0, N) == INVALID and "NULL" in err(lib)
+    assert f(P, N, N, N, Q, 2, 8, 4, 3, 0, 0, N) == INVALID
+    assert f(P, P, N, N, N, 2, 8, 4, 3, 0, 0, N) == INVALID
+    assert f(P, P, N, N, P, 2, 8, 4, 3, 0, 0, N) == INVALID and "alias" in err(lib)
+    assert f(P, P, N, N, Q, -1, 8, 4, 3, 0, 0, N) == INVALID and "negative" in err(lib)
+    assert f(P, P, N, N, Q, 2, -8, 4, 3, 0, 0, N) == INVALID
+    assert f(P, P, N, N, Q, 2, 8, 4, 3, 7, 0, N) == INVALID and "pad" in err(lib)
+    assert f(P, P, N, N, Q, 2, 8, 4, 3, 0, 9, N) == INVALID and "dtype" in err(lib)
+    # empty problems enqueue nothing and succeed
+    assert f(P, P, N, N, Q, 0, 8, 4, 3, 0, 0, N) == OK and err(lib) == ""
+    assert f(N, N, N, N, N, 0, 8, 4, 3, 0, 0, N) == OK
+    assert f(P, P, N, N, Q, 2, 0, 4, 3, 1, 1, N) == OK
+    assert f(P, P, N, N, Q, 2, 8, 0, 3, 1, 1, N) == OK
+
+
+def test_dwsub_fused_validation(lib):
+    f = lib.dwsub_fused_fwd
+    assert f(N, P, N, P, N, N, Q, 4, 100, 80, 256, N) == INVALID
+    assert f(P, N, N, P, N, N, Q, 4, 100, 80, 256, N) == INVALID
+    assert f(P, P, N, N, N, N, Q, 4, 100, 80, 256, N) == INVALID
+    assert f(P, P, N, P, N, N, P, 4, 100, 80, 256, N) == INVALID and "alias" in err(lib)
+    assert f(P, P, N, P, N, N, Q, 4, -1, 80, 256, N) == INVALID
+    assert f(P, P, N, P, N, N, Q, 0, 100, 80, 256, N) == OK
+
+
+def test_dwconv2d_fwd_validation(lib):
+    f = lib.dwconv2d_fwd
+    assert f(P, P, N, N, Q, 2, 8, 8, 4, 3, 3, 1, 1, N) == UNSUPPORTED and "stride" in err(lib)
+    assert f(P, P, N, N, Q, 2, 8, 8, 4, 5, 5, 2, 1, N) == UNSUPPORTED
+    assert f(P, P, N, N, Q, 2, 8, 8, 4, 3, 3, 2, 0, N) == UNSUPPORTED
+    assert f(N, P, N, N, Q, 2, 8, 8, 4, 3, 3, 2, 1, N) == INVALID
+    assert f(P, P, N, N, P, 2, 8, 8, 4, 3, 3, 2, 1, N) == INVALID
+    assert f(P, P, N, N, Q, 2, 8, -8, 4, 3, 3, 2, 1, N) == INVALID
+    assert f(P, P, N, N, Q, 2, 0, 8, 4, 3, 3, 2, 1, N) == OK
+    assert f(N, N, N, N, N, 0, 8, 8, 4, 3, 3, 2, 1, N) == OK  # empty: pointers unused
+
+
+def test_dwconv2d_bwd_validation(lib):
+    ws = lib.dwconv2d_bwd_workspace_bytes
+    need = ws(32, 1500, 64, 256, 3, 3, 2, 1)
+    assert need > 0
+    assert ws(32, 1500, 64, 256, 3, 3, 1, 1) == 0
+    assert ws(-1, 1500, 64, 256, 3, 3, 2, 1) == 0
+    f = lib.dwconv2d_bwd
+    R = ctypes.c_void_p(0x3000)
+    W = ctypes.c_void_p(0x4000)
+    args = (32, 1500, 64, 256, 3, 3, 2, 1, N)
+    assert f(P, P, N, Q, R, W, N, N, 0, *args) == WORKSPACE and "workspace" in err(lib)
+    assert f(P, P, N, Q, R, W, N, W, need - 1, *args) == WORKSPACE
+    assert f(P, P, N, Q, P, W, N, W, need, *args) == INVALID and "alias" in err(lib)
+    assert f(P, P, N, Q, Q, W, N, W, need, *args) == INVALID
+    assert f(N, P, N, Q, R, W, N, W, need, *args) == INVALID
+    assert f(P, P, N, Q, R, W, N, W, need, 32, 1500, 64, 256, 3, 3, 1, 1, N) == UNSUPPORTED
+    # nothing requested: nothing to do
+    assert f(P, P, N, Q, N, N, N, N, 0, *args) == OK
+
+
+def test_last_error_is_per_thread(lib):
+    import threading
+    assert lib.dwconv1d_fwd(P, P, N, N, Q, 2, 8, 4, 0, 0, 0, N) == INVALID
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.dw_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "K=0" in err(lib)

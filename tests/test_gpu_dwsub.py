@@ -1,0 +1,89 @@
+"""GPU parity of dwsub_fused_fwd (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_util import TOL_F32, assert_parity, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def lib():
+    import conv_subsampling_amd as dw
+    return dw
+
+
+def make(B, T, F, C, lens=None, seed=0):
+    f = datagen.fused_front(device=DEV, B=B, T=T, F=F, C=C, seed=seed)
+    if lens is not None:
+        f["lengths"] = torch.as_tensor(lens, dtype=torch.int32)
+    f["L"] = f["lengths"].to(DEV)
+    return f
+
+
+def run(f, x=None, b0="b0", b1="b1", L="L"):
+    y = lib().dwsub_fused_fwd(f["x"] if x is None else x, f["w0"], f[b0] if b0 else None, f["w1"],
+                              f[b1] if b1 else None, f[L] if L else None)
+    torch.cuda.synchronize()
+    return y
+
+
+def ref(f, b0=True, b1=True, L=True):
+    C = f["w0"].shape[2]
+    z = torch.zeros(C)
+    return oracle.dwsub_front_fwd(f["x"], f["w0"], f["b0"] if b0 else z, f["w1"], f["b1"] if b1 else z,
+                                  f["lengths"] if L else None)
+
+
+SHAPES = [
+    # (B, T, F, C)
+    (1, 1, 1, 4), (2, 5, 3, 2), (2, 16, 12, 8), (3, 13, 9, 5), (2, 37, 80, 64), (1, 64, 80, 256),
+    (2, 50, 17, 300), (2, 8, 80, 1), (3, 41, 23, 33),
+]
+
+
+@pytest.mark.parametrize("B,T,F,C", SHAPES)
+def test_grid(B, T, F, C):
+    f = make(B, T, F, C, lens=datagen.int_uniform(B, 0, T + 2, f"gs/{B}/{T}/{F}/{C}"))
+    say(f"dwsub_fused_fwd B={B} T={T} F={F} C={C} lengths={f['lengths'].tolist()}")
+    assert_parity(run(f), ref(f), TOL_F32, "front")
+    assert_parity(run(f, b0=None, b1=None), ref(f, b0=False, b1=False), TOL_F32, "front, null biases")
+    assert_parity(run(f, L=None), ref(f, L=False), TOL_F32, "front, null lengths")
+
+
+def test_odd_lengths_read_one_frame_past_the_length():
+    B, T, F, C = 4, 30, 16, 32
+    f = make(B, T, F, C, lens=[29, 9, 1, 0])
+    y = run(f)
+    assert_parity(y, ref(f), TOL_F32, "odd lengths")
+    # mel rows at or past 2*ceil(len/2) feed no unmasked h row: poison them
+    xp = f["x"].clone()
+    for bi, l in enumerate([29, 9, 1, 0]):
+        xp[bi, 2 * ((l + 1) // 2):] = float("nan")
+    assert torch.equal(run(f, x=xp), y)
+
+
+def test_fully_masked_rows_equal_output_bias_exactly():
+    B, T, F, C = 2, 60, 20, 16
+    f = make(B, T, F, C, lens=[25, 60])
+    y = run(f).cpu()
+    L1 = (25 + 1) // 2
+    b1 = f["b1"].cpu()
+    for t2 in range(y.shape[1]):
+        if 2 * t2 - 1 >= L1:
+            assert torch.equal(y[0, t2], b1[None, :].expand(y.shape[2], C))
+
+
+def test_repeatable_bitwise():
+    f = make(2, 100, 80, 256)
+    assert torch.equal(run(f), run(f))
+
+
+def test_front_full_size():
+    f = datagen.fused_front(device=DEV)
+    f["L"] = f["lengths"].to(DEV)
+    say("dwsub_fused_fwd full [4,1000,80] -> [4,250,20,256]")
+    assert_parity(run(f), ref(f), TOL_F32, "front full")
