@@ -1,0 +1,461 @@
+#!/usr/bin/env python3
+"""Throughput of the depthwise-convolution path on one MI355X.
+
+One step runs every operation of the path once, each at its workload's full
+size, on synthetic inputs resident in HBM:
+
+  front   dwsub_fused_fwd   mel [4,1000,80] -> [4,250,20,256]           fp32
+  conv1d  dwconv1d_fwd      [16,750,1024] K=9 symmetric                 bf16 storage
+  sweep   dwconv1d_fwd      [32,1500,512] causal, K = 3, 4, 5, 9, 15    fp32
+          dwconv1d_fwd      [32,1500,200] causal, K = 9                 fp32
+  stage   dwconv2d_fwd      [32,1500,64,256] -> [32,750,32,256]         fp32
+          dwconv2d_bwd      dx, dw, db of the same                      fp32
+
+The timed region is exactly --steps steps, bracketed by device
+synchronisation.  Per-operation times come from HIP events recorded on the
+stream the kernels run on.  The working set (about 10 GB) is far larger than
+the 256 MB Infinity Cache, and the stage rows stream several GB between
+consecutive uses of any other row's inputs, so every row reads cold data.
+
+Prints one JSON line on stdout (progress goes to stderr):
+  value        frames per second over the whole step (sum over operations of
+               the input frames B*T each processes, divided by step time)
+  hbm          algorithmic bytes per step / step time, and its fraction of
+               the 8 TB/s HBM peak
+  roofline     the dominant kernel's achieved algorithmic GB/s against 8 TB/s
+  rows         the same figures for every operation
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+`python bench.py --summarize-profile DIR` turns rocprofv3 output under DIR
+into the text summaries kept in profiles/.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E peak
+VALU_F32_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz, unpacked fp32
+DOMINANT = "dwconv2d_bwd"          # the operation with the largest share of the step
+DOMINANT_KERNEL = "dwconv2d_bwd_kernel"
+DOMINANT_SOURCES = ["conv_subsampling_amd/csrc/dwconv2d.hip", "conv_subsampling_amd/csrc/common.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dwconv2d_bwd_stage_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+# Algorithmic work per call: valid input rows, every output element, the
+# parameters and the lengths.  Masked input frames are never needed.
+# --------------------------------------------------------------------------
+
+def clamp_lengths(L, T):
+    return [min(max(int(v), 0), T) for v in L]
+
+
+def work_conv1d(c, es):
+    B, T, C, K = c["B"], c["T"], c["C"], c["K"]
+    L = clamp_lengths(c["lengths"].tolist(), T)
+    rd = sum(L) * C * es + (K * C + C) * es + 4 * B
+    wr = B * T * C * es
+    flops = 2 * K * C * sum(L)
+    return rd, wr, flops
+
+
+def work_front(c):
+    B, T, F, C = c["B"], c["T"], c["F"], c["C"]
+    T1, F1 = (T + 1) // 2, (F + 1) // 2
+    T2, F2 = (T1 + 1) // 2, (F1 + 1) // 2
+    L = clamp_lengths(c["lengths"].tolist(), T)
+    L1 = [(l + 1) // 2 for l in L]
+    rows_read = sum(min(T, 2 * l1) for l1 in L1)  # mel rows some unmasked h row reads
+    rd = rows_read * F * 4 + 20 * C * 4 + 4 * B
+    wr = B * T2 * F2 * C * 4
+    flops = 2 * 9 * C * F1 * sum(min(l1, T1) for l1 in L1) + 2 * 9 * B * T2 * F2 * C
+    return rd, wr, flops
+
+
+def work_stage_fwd(c):
+    B, T, F, C = c["B"], c["T"], c["F"], c["C"]
+    To, Fo = (T + 1) // 2, (F + 1) // 2
+    L = clamp_lengths(c["lengths"].tolist(), T)
+    Lo = [(l + 1) // 2 for l in L]
+    rd = sum(L) * F * C * 4 + 10 * C * 4 + 4 * B
+    wr = B * To * Fo * C * 4
+    flops = 2 * 9 * C * Fo * sum(Lo)
+    return rd, wr, flops
+
+
+def work_stage_bwd(c):
+    B, T, F, C = c["B"], c["T"], c["F"], c["C"]
+    To, Fo = (T + 1) // 2, (F + 1) // 2
+    L = clamp_lengths(c["lengths"].tolist(), T)
+    Lo = [(l + 1) // 2 for l in L]
+    rd = sum(L) * F * C * 4 + sum(Lo) * Fo * C * 4 + 9 * C * 4 + 4 * B
+    wr = B * T * F * C * 4 + 10 * C * 4
+    flops = 2 * 2 * 9 * C * Fo * sum(Lo) + C * Fo * sum(Lo)
+    return rd, wr, flops
+
+
+# --------------------------------------------------------------------------
+
+def build_rows(dev):
+    import torch
+
+    import conv_subsampling_amd as dw
+    import datagen
+
+    rows = []
+
+    def add(name, op, cfg, frames, rd, wr, flops, fn, bound="hbm"):
+        rows.append(dict(name=name, op=op, cfg=cfg, frames=frames, read=rd, write=wr, flops=flops, fn=fn,
+                         bound=bound))
+
+    f = datagen.fused_front(device=dev)
+    fL = f["lengths"].to(dev)
+    fy = torch.empty((f["B"], 250, 20, f["C"]), device=dev)
+    add("front", "dwsub_fused_fwd", "mel [4,1000,80] -> [4,250,20,256] fp32", f["B"] * f["T"], *work_front(f),
+        lambda: dw.dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], fL, y=fy), bound="alu")
+
+    e = datagen.conv1d_encoder_bf16(device=dev)
+    eL = e["lengths"].to(dev)
+    ey = torch.empty_like(e["x"])
+    add("conv1d_bf16", "dwconv1d_fwd", "[16,750,1024] K9 symmetric bf16", e["B"] * e["T"], *work_conv1d(e, 2),
+        lambda: dw.dwconv1d_fwd(e["x"], e["w"], e["b"], eL, y=ey, causal=False))
+
+    sweep = []
+    for K, C in [(3, 512), (4, 512), (5, 512), (9, 512), (15, 512), (9, 200)]:
+        s = datagen.conv1d_causal_sweep(K, device=dev, C=C)
+        sweep.append(s)
+        sL = s["lengths"].to(dev)
+        sy = torch.empty_like(s["x"])
+        add(f"conv1d_causal_K{K}_C{C}", "dwconv1d_fwd", f"[32,1500,{C}] K{K} causal fp32", s["B"] * s["T"],
+            *work_conv1d(s, 4),
+            (lambda s=s, sL=sL, sy=sy: dw.dwconv1d_fwd(s["x"], s["w"], s["b"], sL, y=sy, causal=True)))
+
+    g = datagen.conv2d_stage(device=dev)
+    gL = g["lengths"].to(dev)
+    gy = torch.empty((g["B"], 750, 32, g["C"]), device=dev)
+    gdx = torch.empty_like(g["x"])
+    gdw = torch.empty((3, 3, g["C"]), device=dev)
+    gdb = torch.empty((g["C"],), device=dev)
+    ws = torch.empty((dw.dwconv2d_bwd_workspace_bytes(g["B"], g["T"], g["F"], g["C"]),), dtype=torch.uint8,
+                     device=dev)
+    add("stage_fwd", "dwconv2d_fwd", "[32,1500,64,256] -> [32,750,32,256] fp32", g["B"] * g["T"],
+        *work_stage_fwd(g), lambda: dw.dwconv2d_fwd(g["x"], g["w"], g["b"], gL, y=gy))
+    add("stage_bwd", "dwconv2d_bwd", "dx,dw,db of [32,1500,64,256] fp32", g["B"] * g["T"], *work_stage_bwd(g),
+        lambda: dw.dwconv2d_bwd(g["x"], g["w"], gL, g["dy"], dx=gdx, dw=gdw, db=gdb, workspace=ws))
+    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g)
+    return rows, data
+
+
+def cpu_baseline(data, target_s: float):
+    """Time the CPU oracle on whole items of each workload (same shapes and
+    lengths), single-threaded, and scale to frames per second."""
+    import oracle
+
+    host = lambda t, n: t[:n].detach().float().cpu()
+    # parameters copied to the host once, outside the timed calls
+    hp = lambda d: {k: (v.detach().float().cpu() if hasattr(v, "detach") and k != "x" and k != "dy" else v)
+                    for k, v in d.items()}
+    f, e, g = hp(data["front"]), hp(data["conv1d_bf16"]), hp(data["stage"])
+    f["x"], e["x"], g["x"], g["dy"] = data["front"]["x"], data["conv1d_bf16"]["x"], data["stage"]["x"], \
+        data["stage"]["dy"]
+    sweep = []
+    for s in data["sweep"]:
+        hs = hp(s)
+        hs["x"] = s["x"]
+        sweep.append(hs)
+
+    def one_pass(n):
+        """The oracle on the first min(n, B) items of every operation's batch."""
+        secs, frames = 0.0, 0
+        m = min(n, f["B"])
+        xs = host(f["x"], m)
+        t = time.perf_counter()
+        oracle.dwsub_front_fwd(xs, f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"][:m])
+        secs += time.perf_counter() - t
+        frames += m * f["T"]
+        m = min(n, e["B"])
+        xs = host(e["x"], m)
+        t = time.perf_counter()
+        oracle.dwconv1d_fwd(xs, e["w"], e["b"], e["lengths"][:m], False)
+        secs += time.perf_counter() - t
+        frames += m * e["T"]
+        for s in sweep:
+            m = min(n, s["B"])
+            xs = host(s["x"], m)
+            t = time.perf_counter()
+            oracle.dwconv1d_fwd(xs, s["w"], s["b"], s["lengths"][:m], True)
+            secs += time.perf_counter() - t
+            frames += m * s["T"]
+        m = min(n, g["B"])
+        xs, dys = host(g["x"], m), host(g["dy"], m)
+        t = time.perf_counter()
+        oracle.dwconv2d_fwd(xs, g["w"], g["b"], g["lengths"][:m])
+        oracle.dwconv2d_bwd(xs, g["w"], g["lengths"][:m], dys)
+        secs += time.perf_counter() - t
+        frames += 2 * m * g["T"]
+        return secs, frames
+
+    s1, _ = one_pass(1)
+    n = int(max(1, min(g["B"], math.floor(target_s / max(s1, 1e-3)))))
+    secs, frames, reps = 0.0, 0, 0
+    while reps == 0 or secs < 0.5 * target_s:
+        ds, df = one_pass(n)
+        secs, frames, reps = secs + ds, frames + df, reps + 1
+    return dict(value=round(frames / secs, 1), unit="frames/s", cores=1, kind="oracle",
+                sample=(f"every operation of the step on the first {n} items of its batch (at most its batch "
+                        f"size), same shapes and lengths, {reps} pass(es): {frames} frames in {secs:.2f} s; "
+                        f"the oracle is single-threaded C with fp64 accumulation"))
+
+
+def read_traffic():
+    """Counter-derived HBM bytes per launch of the dominant kernel, if the
+    counters were taken on the current source of that kernel."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("src_sha256") != sources_sha(DOMINANT_SOURCES):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 output under DIR and exit")
+    args = ap.parse_args()
+
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    dev = torch.device("cuda", 0)
+    log("building workloads ...")
+    rows, data = build_rows(dev)
+    torch.cuda.synchronize()
+    if args.calib_copy:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        bcopy = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        del a, bcopy
+
+    for i in range(args.warmup):
+        for r in rows:
+            r["fn"]()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in rows]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, r in enumerate(rows):
+            ev[s][j][0].record()
+            r["fn"]()
+            ev[s][j][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"timed {args.steps} steps in {wall:.3f} s")
+
+    ms_step = wall * 1e3 / args.steps
+    frames = sum(r["frames"] for r in rows)
+    alg = sum(r["read"] + r["write"] for r in rows)
+    out_rows = []
+    for j, r in enumerate(rows):
+        us = sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) * 1e3 / args.steps
+        b = r["read"] + r["write"]
+        row = dict(row=r["name"], op=r["op"], config=r["cfg"], us=round(us, 2),
+                   frames_per_s=round(r["frames"] / (us * 1e-6)), alg_bytes=b,
+                   gbps=round(b / (us * 1e-6) / 1e9, 1), hbm_frac=round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
+        if r["bound"] == "alu":
+            tf = r["flops"] / (us * 1e-6) / 1e12
+            row.update(bound="alu", alg_flops=r["flops"], tflops=round(tf, 2),
+                       alu_frac=round(tf / VALU_F32_PEAK_TFLOPS, 4))
+        else:
+            row.update(bound="hbm")
+        out_rows.append(row)
+        log(f"  {r['name']:<22} {us:9.2f} us  {row['gbps']:8.1f} GB/s  ({100 * row['hbm_frac']:.1f}% of 8 TB/s)")
+
+    dom = next(r for r in out_rows if r["op"] == DOMINANT)
+    roofline = dict(kernel=DOMINANT_KERNEL, bound="hbm", achieved=dom["gbps"], peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(dom["gbps"] / HBM_PEAK_GBPS, 4), traffic=read_traffic(),
+                    launch_us=dom["us"], alg_bytes_per_launch=dom["alg_bytes"])
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(data, args.cpu_seconds)
+        log(f"  oracle: {cpu['value']:.0f} frames/s ({cpu['sample']})")
+
+    line = {
+        "metric": "depthwise conv frames/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
+        "value": round(frames / (ms_step * 1e-3), 1),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; log-mel-shaped inputs, lengths ~U[T/2,T])",
+        "config": {
+            "workload": "encoder depthwise path: fused front [4,1000,80]; conv-module dwconv1d [16,750,1024] K9 "
+                        "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 and [32,1500,200] K9; depthwise conv2d "
+                        "stage [32,1500,64,256] fwd+bwd",
+            "frames_per_step": frames,
+            "alg_bytes_per_step": alg,
+            "parallelism": "single GPU",
+        },
+        "hbm": {"achieved_gbps": round(alg / (ms_step * 1e-3) / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
+                "frac": round(alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "roofline": roofline,
+        "rows": out_rows,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+# --------------------------------------------------------------------------
+# rocprofv3 summaries
+# --------------------------------------------------------------------------
+
+def _csv_rows(pattern):
+    out = []
+    for p in sorted(glob.glob(pattern, recursive=True)):
+        with open(p, newline="") as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def summarize_profile(d):
+    """Write profiles/ summaries from rocprofv3 output under d:
+    d/stats/**/*kernel_stats.csv, d/fetch/**/*counter_collection.csv,
+    d/write/**/*counter_collection.csv (any of them may be missing)."""
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    stats = _csv_rows(os.path.join(d, "stats", "**", "*kernel_stats.csv"))
+    if stats:
+        lines = ["# rocprofv3 --kernel-trace --stats, one bench.py run on one MI355X",
+                 "# command: " + open(os.path.join(d, "stats", "command.txt")).read().strip()
+                 if os.path.exists(os.path.join(d, "stats", "command.txt")) else "#",
+                 f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
+        for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
+            name = r.get("Name", r.get("KernelName", "?"))
+            short = name.split("(")[0][:60]
+            lines.append(f"{short:<60} {int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
+                         f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} {float(r.get('MaxNs', 0)) / 1e3:>10.2f} "
+                         f"{float(r.get('Percentage', 0)):>6.2f}")
+        with open(os.path.join(ROOT, "profiles", "kernel_stats_bench_step.txt"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+
+    def counter(kind, cname):
+        """{dispatch id: (kernel name, value)} summed over the counter's instances."""
+        per = {}
+        for r in _csv_rows(os.path.join(d, kind, "**", "*counter_collection.csv")):
+            if r.get("Counter_Name") != cname:
+                continue
+            key = r.get("Dispatch_Id")
+            name, v = r.get("Kernel_Name", ""), float(r.get("Counter_Value", 0))
+            per[key] = (name, per.get(key, (name, 0.0))[1] + v)
+        return per
+
+    fetch = counter("fetch", "FETCH_SIZE")
+    write = counter("write", "WRITE_SIZE")
+    if not (fetch and write):
+        return
+    copy_bytes = float(1 << 30)
+
+    def calib(tab):
+        # the 1 GiB device copy is the largest copy-engine-kernel dispatch
+        vals = [v for (n, v) in tab.values() if "copyBuffer" in n]
+        return max(vals) if vals else None
+
+    def mean_of(tab, pat):
+        vals = [v for (n, v) in tab.values() if pat in n]
+        return sum(vals) / len(vals) if vals else None
+
+    cf, cw = calib(fetch), calib(write)
+    # copy-size reference: the copy reads and writes 1 GiB
+    by_kernel = {}
+    for tab, idx in ((fetch, 0), (write, 1)):
+        for n, v in tab.values():
+            short = n.split("(")[0] if not n.startswith("void ") else n[5:].split("(")[0]
+            by_kernel.setdefault(short[:64], [[], []])[idx].append(v)
+    kf, kw = mean_of(fetch, DOMINANT_KERNEL + "<"), mean_of(write, DOMINANT_KERNEL + "<")
+    cmd = lambda k: (open(os.path.join(d, k, "command.txt")).read().strip()
+                     if os.path.exists(os.path.join(d, k, "command.txt")) else "?")
+    lines = ["# HBM traffic per launch of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE and",
+             "# WRITE_SIZE (KiB per dispatch, separate runs), each scaled by the same counter's reading",
+             "# for a 1 GiB device copy (the copy reads 1 GiB and writes 1 GiB).",
+             "# fetch run: " + cmd("fetch"),
+             "# write run: " + cmd("write"),
+             f"kernel={DOMINANT_KERNEL}",
+             f"src_sha256={sources_sha(DOMINANT_SOURCES)}",
+             f"copy_fetch_kib={cf}", f"copy_write_kib={cw}",
+             f"kernel_fetch_kib={kf}", f"kernel_write_kib={kw}"]
+    if cf and cw and kf is not None and kw is not None:
+        sf, swr = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+        fb, wb = kf * 1024.0 * sf, kw * 1024.0 * swr
+        lines += [f"scale_fetch={sf:.4f}", f"scale_write={swr:.4f}", f"fetch_bytes_per_launch={fb:.0f}",
+                  f"write_bytes_per_launch={wb:.0f}", f"hbm_bytes_per_launch={fb + wb:.0f}"]
+        lines.append("# every kernel of the run, mean KiB per dispatch (raw counters): fetch, write")
+        for k in sorted(by_kernel):
+            fv, wv = by_kernel[k]
+            mf = sum(fv) / len(fv) if fv else float("nan")
+            mw = sum(wv) / len(wv) if wv else float("nan")
+            lines.append(f"#   {k:<64} {mf:>14.1f} {mw:>14.1f}")
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

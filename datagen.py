@@ -110,9 +110,11 @@ def conv1d_encoder_bf16(device="cpu", seed=DEFAULT_SEED, B=16, T=750, C=1024, K=
 
 
 def conv1d_causal_sweep(K, device="cpu", seed=DEFAULT_SEED, B=32, T=1500, C=512):
-    """Causal 1-D depthwise conv, fp32, w ~ N(0, 1/K), zero bias; lengths ~U[T/2, T]."""
+    """Causal 1-D depthwise conv, fp32, w ~ N(0, 1/K), zero bias; lengths ~U[T/2, T].
+    Each width gets its own input draw, so that back-to-back runs of the sweep
+    never find another width's input in a cache."""
     return dict(
-        x=normal((B, T, C), 1.0, f"c4/x/C{C}", seed, device),
+        x=normal((B, T, C), 1.0, f"c4/x/K{K}/C{C}", seed, device),
         w=normal((K, C), 1.0 / K, f"c4/w/K{K}/C{C}", seed, device),
         b=torch.zeros((C,), dtype=torch.float32, device=device),
         lengths=int_uniform(B, T // 2, T, f"c4/len/C{C}", seed),
