@@ -221,7 +221,7 @@ def cpu_baseline(data, target_s: float):
     s1, _ = one_pass(1)
     n = int(max(1, min(g["B"], math.floor(target_s / max(s1, 1e-3)))))
     secs, frames, reps = 0.0, 0, 0
-    while reps == 0 or secs < 0.5 * target_s:
+    while reps == 0 or secs < target_s:
         ds, df = one_pass(n)
         secs, frames, reps = secs + ds, frames + df, reps + 1
     return dict(value=round(frames / secs, 1), unit="frames/s", cores=1, kind="oracle",

@@ -44,23 +44,30 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build the HIP library first "
         "(python -m conv_subsampling_amd.build, or __graft_entry__.build())")
 
-_lib = ctypes.CDLL(LIB_PATH)
-
 _vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
-_lib.dw_abi_version.restype = _int
-_lib.dw_abi_version.argtypes = []
-_lib.dw_last_error.restype = ctypes.c_char_p
-_lib.dw_last_error.argtypes = []
-_lib.dwconv1d_fwd.restype = _int
-_lib.dwconv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp]
-_lib.dwsub_fused_fwd.restype = _int
-_lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
-_lib.dwconv2d_fwd.restype = _int
-_lib.dwconv2d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i64] * 8 + [_vp]
-_lib.dwconv2d_bwd_workspace_bytes.restype = _sz
-_lib.dwconv2d_bwd_workspace_bytes.argtypes = [_i64] * 8
-_lib.dwconv2d_bwd.restype = _int
-_lib.dwconv2d_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz] + [_i64] * 8 + [_vp]
+
+
+def _bind(path: str) -> ctypes.CDLL:
+    """Load a build of the library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    lib.dw_abi_version.restype = _int
+    lib.dw_abi_version.argtypes = []
+    lib.dw_last_error.restype = ctypes.c_char_p
+    lib.dw_last_error.argtypes = []
+    lib.dwconv1d_fwd.restype = _int
+    lib.dwconv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp]
+    lib.dwsub_fused_fwd.restype = _int
+    lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
+    lib.dwconv2d_fwd.restype = _int
+    lib.dwconv2d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i64] * 8 + [_vp]
+    lib.dwconv2d_bwd_workspace_bytes.restype = _sz
+    lib.dwconv2d_bwd_workspace_bytes.argtypes = [_i64] * 8
+    lib.dwconv2d_bwd.restype = _int
+    lib.dwconv2d_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz] + [_i64] * 8 + [_vp]
+    return lib
+
+
+_lib = _bind(LIB_PATH)
 
 
 def abi_version() -> int:

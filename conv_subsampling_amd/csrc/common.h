@@ -19,7 +19,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // of logical tiles, and the shared rows are found in that XCD's L2.
 constexpr int kNumXcd = 8;
 
+#ifndef DW_XCD_REMAP
+#define DW_XCD_REMAP 1
+#endif
 __device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t bid, uint32_t nblocks) {
+    if (!DW_XCD_REMAP) return bid;
     uint32_t q = nblocks / kNumXcd, r = nblocks % kNumXcd;
     uint32_t x = bid % kNumXcd, j = bid / kNumXcd;
     return x * q + (x < r ? x : r) + j;
@@ -63,7 +67,10 @@ struct Vf {
 // with no branch and no memory traffic.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kBufferFlags = 0x00020000;  // dword 3 of a raw (untyped) gfx9 buffer resource
-constexpr int kNonTemporal = 2;           // cache-policy bit: no reuse expected
+#ifndef DW_STORE_NT
+#define DW_STORE_NT 1
+#endif
+constexpr int kNonTemporal = DW_STORE_NT ? 2 : 0;  // store cache policy: 2 = no reuse expected
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);

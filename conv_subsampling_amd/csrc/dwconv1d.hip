@@ -128,8 +128,11 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_anyk_kernel(
 
 // Time-tile length per thread for each specialised width (register window of
 // TT + K - 1 channel vectors).
+#ifndef DW1D_TILE
+#define DW1D_TILE 8
+#endif
 template <int K>
-constexpr int tile_1d() { return 16; }
+constexpr int tile_1d() { return DW1D_TILE; }
 constexpr int kTileAnyK = 8;
 
 static int tile_for(int64_t K) {

@@ -13,7 +13,8 @@
 // column F when F is odd) needs an explicit zero.
 //
 // Forward mapping.  A thread owns V channels of TO consecutive output rows of
-// one item and walks left to right over all F' output columns.  At output
+// one item and walks left to right over the F' output columns (or a chunk of
+// them).  At output
 // column f' it needs input columns 2f'-1, 2f', 2f'+1 of the 2*TO+1 input rows
 // 2t0-1 .. 2t0+2*TO-1; column 2f'+1 is carried to the next step as its
 // column 2(f'+1)-1, so every input element is loaded once per thread, and
@@ -34,8 +35,8 @@
 // fp64, and fp64 FMA runs at the fp32 rate here), because a sum of ~10^6
 // terms can cancel to a value far smaller than its terms.  They are summed
 // per thread, then across the workgroup's row blocks in a fixed order,
-// written as one fp64 partial per workgroup to the workspace, and a second
-// kernel adds the partials in a fixed order: the result is bitwise
+// written as one fp64 partial per workgroup to the workspace, and two small
+// kernels add the partials in a fixed order: the result is bitwise
 // repeatable.
 #include "common.h"
 #include "launch.h"
@@ -47,12 +48,19 @@ constexpr int kLanes2d = 64;                      // channel groups per workgrou
 constexpr int kRowsPerBlock = kBlock2d / kLanes2d;  // row blocks per workgroup
 
 #ifndef DW2D_FWD_ROWS
-#define DW2D_FWD_ROWS 4
+#define DW2D_FWD_ROWS 1
+#endif
+#ifndef DW2D_FWD_PERSIST
+#define DW2D_FWD_PERSIST 512  // workgroups of a persistent forward grid; 0 = one workgroup per tile
+#endif
+#ifndef DW2D_FWD_COLS
+#define DW2D_FWD_COLS 8  // output columns per thread in the forward; 0 = all of them
 #endif
 #ifndef DW2D_BWD_ROWS
-#define DW2D_BWD_ROWS 2
+#define DW2D_BWD_ROWS 1
 #endif
 constexpr int kFwdRows = DW2D_FWD_ROWS;   // output rows per thread (forward)
+constexpr int kFwdCols = DW2D_FWD_COLS;   // output columns per thread (forward), 0 = all
 constexpr int kBwdRows = DW2D_BWD_ROWS;   // quad rows per thread (backward)
 
 template <int V>
@@ -100,11 +108,26 @@ __device__ __forceinline__ Tile2d decode_2d(uint32_t n_rb, uint32_t CG, uint32_t
 template <int V, int TO>
 __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
-    const int32_t* __restrict__ lengths, float* __restrict__ y,
+    const int32_t* __restrict__ lengths, float* __restrict__ y, int32_t B_items,
     int32_t T, int32_t F, int32_t C, int32_t To, int32_t Fo,
     uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t wg_per_item) {
+#if DW2D_FWD_PERSIST
+    // wg_per_item here is the number of row groups per item; the batch's row
+    // groups are dealt round-robin to the workgroups of a channel block.
+    const uint32_t blk0 = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t G = gridDim.x / n_cblk;
+    const uint32_t g0 = blk0 / n_cblk, cb0 = blk0 - g0 * n_cblk;
+    for (uint32_t j = g0; j < (uint32_t)B_items * wg_per_item; j += G) {
+    Tile2d d;
+    d.b = j / wg_per_item;
+    d.rb = (j - d.b * wg_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
+    d.cg = cb0 * kLanes2d + threadIdx.x % kLanes2d;
+    d.valid = d.rb < n_rb && d.cg < CG;
+    if (!d.valid) continue;
+#else
     const Tile2d d = decode_2d(n_rb, CG, n_cblk, wg_per_item);
     if (!d.valid) return;
+#endif
     const int32_t len = (int32_t)item_length(lengths, d.b, T);
     const int32_t leno = (len + 1) / 2;
     const uint32_t xrow = (uint32_t)F * C * 4, yrow = (uint32_t)Fo * C * 4, pix = (uint32_t)C * 4;
@@ -112,14 +135,22 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
     const rsrc_t yr = make_rsrc(y + (int64_t)d.b * To * Fo * C, (uint32_t)To * yrow);
     const int32_t c0 = (int32_t)d.cg * V;
     const uint32_t coff = (uint32_t)c0 * 4;
-    const int32_t t0 = (int32_t)d.rb * TO;
+    // row-block index = row block * column chunks + column chunk
+    const int32_t fch = kFwdCols > 0 ? kFwdCols : Fo;
+    const int32_t nfc = (Fo + fch - 1) / fch;
+    const int32_t t0 = (int32_t)(d.rb / nfc) * TO;
+    const int32_t fa = (int32_t)(d.rb % nfc) * fch, fb = min(Fo, fa + fch);
 
     if (t0 >= leno) {
         const Vf<V> z = vzero<V>();
-        for (int32_t f = 0; f < Fo; ++f)
+        for (int32_t f = fa; f < fb; ++f)
 #pragma unroll
             for (int i = 0; i < TO; ++i) Buf<float, V>::store(yr, (uint32_t)(t0 + i) * yrow + f * pix + coff, z);
+#if DW2D_FWD_PERSIST
+        continue;
+#else
         return;
+#endif
     }
 
     Vf<V> wk[9];
@@ -133,11 +164,12 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
 #pragma unroll
     for (int r = 0; r < 2 * TO + 1; ++r) roff[r] = (uint32_t)((2 * t0 - 1 + r) * (int32_t)xrow) + coff;
 
-    Vf<V> carry[2 * TO + 1];  // input column 2f'-1
+    Vf<V> carry[2 * TO + 1];  // input column 2f'-1 (zero left of the first column)
 #pragma unroll
-    for (int r = 0; r < 2 * TO + 1; ++r) carry[r] = vzero<V>();
+    for (int r = 0; r < 2 * TO + 1; ++r)
+        carry[r] = fa > 0 ? Buf<float, V>::load(xr, roff[r] + (uint32_t)(2 * fa - 1) * pix) : vzero<V>();
 
-    for (int32_t f = 0; f < Fo; ++f) {
+    for (int32_t f = fa; f < fb; ++f) {
         const uint32_t c_even = (uint32_t)(2 * f) * pix;
         const bool odd_ok = 2 * f + 1 < F;  // column 2f'+1 exists
         Vf<V> ce[2 * TO + 1], co[2 * TO + 1];
@@ -163,7 +195,48 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 2 * TO + 1; ++r) carry[r] = co[r];
     }
+#if DW2D_FWD_PERSIST
+    }  // row groups
+#endif
 }
+
+#ifdef DW2D_FWD_PIXEL
+// Experimental: one output pixel (V channels) per thread, 9 loads through L2.
+template <int V>
+__global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_pixel_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    const int32_t* __restrict__ lengths, float* __restrict__ y,
+    int32_t T, int32_t F, int32_t C, int32_t To, int32_t Fo, uint32_t CG, uint32_t blocks_per_item) {
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t b = blk / blocks_per_item;
+    const uint32_t local = (blk - b * blocks_per_item) * kBlock2d + threadIdx.x;
+    const uint32_t pixel = local / CG, cg = local - pixel * CG;
+    if (pixel >= (uint32_t)(To * Fo)) return;
+    const int32_t to = (int32_t)(pixel / Fo), fo = (int32_t)(pixel % Fo);
+    const int32_t len = (int32_t)item_length(lengths, b, T);
+    const int32_t leno = (len + 1) / 2;
+    const uint32_t xrow = (uint32_t)F * C * 4, pix = (uint32_t)C * 4;
+    const rsrc_t xr = make_rsrc(x + (int64_t)b * T * F * C, (uint32_t)len * xrow);
+    const rsrc_t yr = make_rsrc(y + (int64_t)b * To * Fo * C, (uint32_t)To * Fo * pix);
+    const int32_t c0 = (int32_t)cg * V;
+    const uint32_t coff = (uint32_t)c0 * 4;
+    const uint32_t yo = (uint32_t)pixel * pix + coff;
+    if (to >= leno) { Buf<float, V>::store(yr, yo, vzero<V>()); return; }
+    Vf<V> xv[9];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const int32_t f = 2 * fo + j - 1;
+            xv[3 * i + j] = Buf<float, V>::load(xr, (uint32_t)((2 * to + i - 1) * (int32_t)xrow + f * (int32_t)pix) + coff);
+            if (f < 0 || f >= F) xv[3 * i + j] = vzero<V>();
+        }
+    Vf<V> acc = bias ? load_param<float, V>(bias + c0) : vzero<V>();
+#pragma unroll
+    for (int k = 0; k < 9; ++k) fma_v<V>(acc, xv[k], load_param<float, V>(w + (int64_t)k * C + c0));
+    Buf<float, V>::store(yr, yo, acc);
+}
+#endif
 
 // ------------------------------------------------------------------ bwd ----
 
@@ -172,10 +245,20 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
     const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial,
     int32_t T, int32_t F, int32_t C, int32_t To, int32_t Fo,
-    uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t wg_per_item) {
+    uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
     __shared__ double red[kRowsPerBlock - 1][10][kLanes2d * V];
-    const Tile2d d = decode_2d(n_rb, CG, n_cblk, wg_per_item);
-    const int32_t c0 = (int32_t)d.cg * V;
+    // Workgroup = kRowsPerBlock waves x kLanes2d channel groups.  The batch's
+    // row groups (kRowsPerBlock row blocks each, items one after the other)
+    // are dealt round-robin to the G = gridDim.x / n_cblk workgroups of a
+    // channel block: group j goes to workgroup j mod G, so every workgroup
+    // gets a like mix of long and short (masked) items, and neighbouring
+    // workgroups work on neighbouring rows at the same time.  A workgroup
+    // keeps one dw/db sum for all of its groups.
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t G = gridDim.x / n_cblk;
+    const uint32_t g = blk / n_cblk, cblk = blk - g * n_cblk;
+    const uint32_t cg = cblk * kLanes2d + threadIdx.x % kLanes2d;
+    const int32_t c0 = (int32_t)cg * V;
 
     double gw[9][V], gb[V];
 #pragma unroll
@@ -185,6 +268,12 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
         for (int k = 0; k < 9; ++k) gw[k][e] = 0.0;
     }
 
+    for (uint32_t j = g; j < n_groups; j += G) {
+    Tile2d d;
+    d.b = j / groups_per_item;
+    d.cg = cg;
+    d.rb = (j - d.b * groups_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
+    d.valid = d.rb < n_rb && d.cg < CG;
     if (d.valid) {
         const int32_t len = (int32_t)item_length(lengths, d.b, T);
         const int32_t leno = (len + 1) / 2;
@@ -273,6 +362,8 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
         }
     }
 
+    }  // row groups
+
     if (!partial) return;  // uniform: dw and db not requested
     // Sum the row blocks of this workgroup in a fixed order (row block 0
     // first), then write one partial per workgroup: partial[p][k][c], k = 0..8
@@ -288,11 +379,7 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     }
     __syncthreads();
     if (rsub > 0) return;
-    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
-    const uint32_t b = blk / wg_per_item;
-    const uint32_t r = blk - b * wg_per_item;
-    const uint32_t rgroup = r / n_cblk, cblk = r - rgroup * n_cblk;
-    const uint32_t p = b * (wg_per_item / n_cblk) + rgroup;
+    const uint32_t p = g;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
         const int32_t c = ((int32_t)cblk * kLanes2d + (int32_t)lane) * V + e;
@@ -307,32 +394,52 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     }
 }
 
-// Fixed-order fp64 sum of the P workgroup partials: one output per thread
-// column, kSumSplit threads per column, combined through LDS in order.
-constexpr int kSumCols = 64, kSumSplit = 16;
+// Fixed-order fp64 sum of the P workgroup partials, in two levels so that
+// enough workgroups share the reading.  Each level sums chunks of up to
+// kSumChunk rows of a [rows][ncol] fp64 matrix: a workgroup of kSumRows
+// sub-rows x kSumCols columns adds its chunk's rows (sub-row q takes rows
+// q, q + kSumRows, ...), then the sub-rows are added in order through LDS.
+// Level 1 writes one fp64 row per chunk; level 2 (one chunk) writes dw, db.
+constexpr int kSumCols = 64, kSumRows = 4, kSumChunk = 64;
 
-__global__ __launch_bounds__(kSumCols* kSumSplit) void dwconv2d_bwd_reduce_kernel(
-    const double* __restrict__ partial, float* __restrict__ dw, float* __restrict__ db, int32_t C, int32_t P) {
-    __shared__ double acc[kSumSplit][kSumCols];
-    const int32_t col = blockIdx.x * kSumCols + threadIdx.x % kSumCols;  // column = k * C + c
-    const int32_t part = threadIdx.x / kSumCols;
-    const int32_t ncol = 10 * C;
+__device__ __forceinline__ double sum_chunk(const double* __restrict__ in, int32_t ncol, int32_t r0, int32_t r1,
+                                            int32_t col, double (*acc)[kSumCols]) {
+    const int32_t sub = threadIdx.x / kSumCols, lane = threadIdx.x % kSumCols;
     double s = 0.0;
     if (col < ncol) {
-        for (int32_t p = part; p < P; p += kSumSplit) s += partial[(int64_t)p * ncol + col];
+#pragma unroll 4
+        for (int32_t r = r0 + sub; r < r1; r += kSumRows) s += in[(int64_t)r * ncol + col];
     }
-    acc[part][threadIdx.x % kSumCols] = s;
+    acc[sub][lane] = s;
     __syncthreads();
-    if (part == 0 && col < ncol) {
-        double t = 0.0;
+    double t = acc[0][lane];
 #pragma unroll
-        for (int q = 0; q < kSumSplit; ++q) t += acc[q][threadIdx.x % kSumCols];
-        const int32_t k = col / C, c = col % C;
-        if (k < 9) {
-            if (dw) dw[(int64_t)k * C + c] = (float)t;
-        } else if (db) {
-            db[c] = (float)t;
-        }
+    for (int q = 1; q < kSumRows; ++q) t += acc[q][lane];
+    return t;
+}
+
+__global__ __launch_bounds__(kSumCols* kSumRows) void dwconv2d_bwd_reduce1_kernel(
+    const double* __restrict__ partial, double* __restrict__ chunk_sum, int32_t ncol, int32_t P) {
+    __shared__ double acc[kSumRows][kSumCols];
+    const int32_t col = blockIdx.x * kSumCols + threadIdx.x % kSumCols;  // column = k * C + c
+    const int32_t p0 = blockIdx.y * kSumChunk, p1 = min(P, p0 + kSumChunk);
+    const double t = sum_chunk(partial, ncol, p0, p1, col, acc);
+    if (threadIdx.x < kSumCols && col < ncol) chunk_sum[(int64_t)blockIdx.y * ncol + col] = t;
+}
+
+__global__ __launch_bounds__(kSumCols* kSumRows) void dwconv2d_bwd_reduce2_kernel(
+    const double* __restrict__ chunk_sum, float* __restrict__ dw, float* __restrict__ db, int32_t C,
+    int32_t nchunk) {
+    __shared__ double acc[kSumRows][kSumCols];
+    const int32_t ncol = 10 * C;
+    const int32_t col = blockIdx.x * kSumCols + threadIdx.x % kSumCols;
+    const double t = sum_chunk(chunk_sum, ncol, 0, nchunk, col, acc);
+    if (threadIdx.x >= kSumCols || col >= ncol) return;
+    const int32_t k = col / C, c = col % C;
+    if (k < 9) {
+        if (dw) dw[(int64_t)k * C + c] = (float)t;
+    } else if (db) {
+        db[c] = (float)t;
     }
 }
 
@@ -367,10 +474,27 @@ template <int V>
 static hipError_t launch_fwd_typed(const float* x, const float* w, const float* bias, const int32_t* lengths,
                                    float* y, int64_t B, int64_t T, int64_t F, int64_t C, hipStream_t st) {
     const int64_t To = (T + 1) / 2, Fo = (F + 1) / 2;
-    const Grid2d g = grid_2d(B, To, kFwdRows, C, V);
+#ifdef DW2D_FWD_PIXEL
+    {
+        const uint32_t CG = (uint32_t)(C / V);
+        const uint32_t bpi = (uint32_t)(((uint64_t)To * Fo * CG + kBlock2d - 1) / kBlock2d);
+        hipLaunchKernelGGL((dwconv2d_fwd_pixel_kernel<V>), dim3((uint32_t)(B * bpi)), dim3(kBlock2d), 0, st, x, w,
+                           bias, lengths, y, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To, (int32_t)Fo, CG, bpi);
+        return hipGetLastError();
+    }
+#endif
+    const int64_t nfc = kFwdCols > 0 ? (Fo + kFwdCols - 1) / kFwdCols : 1;
+    Grid2d g = grid_2d(B, To, kFwdRows, C, V);
+    if (nfc > 1) g = grid_2d(B, ((To + kFwdRows - 1) / kFwdRows) * nfc * kFwdRows, kFwdRows, C, V);
+#if DW2D_FWD_PERSIST
+    const uint32_t gpi = g.wg_per_item / g.n_cblk;  // row groups per item
+    const uint64_t ng = (uint64_t)B * gpi;
+    g.blocks = (ng < DW2D_FWD_PERSIST ? ng : DW2D_FWD_PERSIST) * g.n_cblk;
+    g.wg_per_item = gpi;
+#endif
     hipLaunchKernelGGL((dwconv2d_fwd_kernel<V, kFwdRows>), dim3((uint32_t)g.blocks), dim3(kBlock2d), 0, st, x, w,
-                       bias, lengths, y, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To, (int32_t)Fo, g.n_rb,
-                       g.CG, g.n_cblk, g.wg_per_item);
+                       bias, lengths, y, (int32_t)B, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To, (int32_t)Fo,
+                       g.n_rb, g.CG, g.n_cblk, g.wg_per_item);
     return hipGetLastError();
 }
 
@@ -383,19 +507,41 @@ hipError_t launch_dwconv2d_fwd(const float* x, const float* w, const float* bias
     }
 }
 
-static int64_t bwd_partials(int64_t B, int64_t T, int64_t C) {
-    // One partial per (item, workgroup row group); independent of the
-    // vector width, whose channel blocks share a partial row.
+#ifndef DW2D_BWD_TARGET_WGS
+#define DW2D_BWD_TARGET_WGS 256
+#endif
+
+// Backward grid: G workgroups per channel block share the batch's row groups
+// round-robin.  G is about the number of workgroups the chip holds at once
+// (2 per CU at this kernel's register use), so every workgroup runs for the
+// whole kernel, and there are G dw/db partials to add up afterwards.  G does
+// not depend on the vector width: the channel blocks of one workgroup index
+// share a partial row.
+struct BwdGrid {
+    uint32_t n_rb, groups_per_item, n_groups, G;
+    int64_t P;
+};
+
+static BwdGrid bwd_grid(int64_t B, int64_t T) {
+    BwdGrid g;
     const int64_t To = (T + 1) / 2;
-    const int64_t n_rb = (To + kBwdRows - 1) / kBwdRows;
-    return B * ((n_rb + kRowsPerBlock - 1) / kRowsPerBlock);
-    (void)C;
+    g.n_rb = (uint32_t)((To + kBwdRows - 1) / kBwdRows);
+    g.groups_per_item = (g.n_rb + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t n = B * (int64_t)g.groups_per_item;
+    g.n_groups = (uint32_t)n;
+    g.G = (uint32_t)(n < DW2D_BWD_TARGET_WGS ? n : DW2D_BWD_TARGET_WGS);
+    g.P = g.G;
+    return g;
 }
+
+static int64_t bwd_chunks(int64_t P) { return (P + kSumChunk - 1) / kSumChunk; }
 
 size_t dwconv2d_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C) {
     (void)F;
-    const int64_t P = bwd_partials(B, T, C);
-    return (size_t)((P > 0 ? P : 1) * 10 * C * (int64_t)sizeof(double));
+    // [P][10][C] workgroup partials, then [chunks][10][C] chunk sums, fp64.
+    const int64_t P = bwd_grid(B, T).P;
+    const int64_t rows = P + (bwd_chunks(P) > 0 ? bwd_chunks(P) : 1);
+    return (size_t)(rows * 10 * C * (int64_t)sizeof(double));
 }
 
 template <int V>
@@ -403,28 +549,45 @@ static hipError_t launch_bwd_typed(const float* x, const float* w, const int32_t
                                    float* dx, float* dw, float* db, double* partial, int64_t B, int64_t T,
                                    int64_t F, int64_t C, hipStream_t st) {
     const int64_t To = (T + 1) / 2, Fo = (F + 1) / 2;
-    const Grid2d g = grid_2d(B, To, kBwdRows, C, V);
-    if (g.blocks > 0 && (dx || partial)) {
-        hipLaunchKernelGGL((dwconv2d_bwd_kernel<V, kBwdRows>), dim3((uint32_t)g.blocks), dim3(kBlock2d), 0, st, x,
+    const BwdGrid g = bwd_grid(B, T);
+    const uint32_t CG = (uint32_t)(C / V);
+    const uint32_t n_cblk = (CG + kLanes2d - 1) / kLanes2d;
+    const uint64_t blocks = (uint64_t)g.G * n_cblk;
+    if (blocks > 0 && (dx || partial)) {
+        hipLaunchKernelGGL((dwconv2d_bwd_kernel<V, kBwdRows>), dim3((uint32_t)blocks), dim3(kBlock2d), 0, st, x,
                            w, lengths, dy, dx, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To,
-                           (int32_t)Fo, g.n_rb, g.CG, g.n_cblk, g.wg_per_item);
+                           (int32_t)Fo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (dw || db) {
-        const int32_t P = (int32_t)(g.blocks / (g.n_cblk ? g.n_cblk : 1));
-        const uint32_t nblk = (uint32_t)((10 * C + kSumCols - 1) / kSumCols);
-        hipLaunchKernelGGL(dwconv2d_bwd_reduce_kernel, dim3(nblk), dim3(kSumCols * kSumSplit), 0, st, partial, dw,
-                           db, (int32_t)C, P);
+        const int32_t P = (int32_t)g.P;
+        const int32_t ncol = (int32_t)(10 * C);
+        const int32_t nchunk = (int32_t)bwd_chunks(P);
+        const uint32_t ncblk = (uint32_t)((ncol + kSumCols - 1) / kSumCols);
+        double* chunk_sum = partial + (int64_t)P * ncol;
+        if (nchunk > 0) {
+            hipLaunchKernelGGL(dwconv2d_bwd_reduce1_kernel, dim3(ncblk, (uint32_t)nchunk), dim3(kSumCols * kSumRows),
+                               0, st, partial, chunk_sum, ncol, P);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(dwconv2d_bwd_reduce2_kernel, dim3(ncblk), dim3(kSumCols * kSumRows), 0, st, chunk_sum, dw,
+                           db, (int32_t)C, nchunk);
         return hipGetLastError();
     }
     return hipSuccess;
 }
 
+#ifndef DW2D_BWD_VEC
+#define DW2D_BWD_VEC 4
+#endif
+
 hipError_t launch_dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy,
                                float* dx, float* dw, float* db, void* workspace, int64_t B, int64_t T,
                                int64_t F, int64_t C, int vec, hipStream_t st) {
     double* partial = (dw || db) ? (double*)workspace : nullptr;
+    if (vec > DW2D_BWD_VEC) vec = DW2D_BWD_VEC;
     switch (vec) {
         case 4: return launch_bwd_typed<4>(x, w, lengths, dy, dx, dw, db, partial, B, T, F, C, st);
         case 2: return launch_bwd_typed<2>(x, w, lengths, dy, dx, dw, db, partial, B, T, F, C, st);

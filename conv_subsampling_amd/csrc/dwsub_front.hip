@@ -14,11 +14,13 @@
 // thread walks its columns left to right; at output column f2 it computes the
 // 2*TY+1 h rows it needs at h columns 2f2 and 2f2+1 and carries column 2f2+1
 // to the next step (as its column 2f2-1).  h rows past the item's time mask,
-// and h positions in the padding, are zero, and their conv0 is skipped (the
-// conditions are uniform across the workgroup).  Only the one h row and
+// and h positions in the padding, are zero; a tile whose h rows are all
+// masked stores the output bias without computing.  Only the one h row and
 // column shared with neighbouring tiles is computed twice.
 //
 // Arithmetic is IEEE fp32 FMA throughout, the bias seeding each sum.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -83,39 +85,57 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     // h rows 2*t0-1+l, l = 0..2*TY, read mel patch rows 2l .. 2l+2.
     // h row validity: inside [0, T1) and before the time mask.
     bool hrow_ok[2 * kSubRows + 1];
+    bool any_ok = false;
 #pragma unroll
     for (int l = 0; l < 2 * kSubRows + 1; ++l) {
         const int32_t r = 2 * t0 - 1 + l;
         hrow_ok[l] = r >= 0 && r < T1 && r < L1;
+        any_ok |= hrow_ok[l];
+    }
+
+    const int32_t ncols = min(kSubCols, F2 - f0);
+    const uint32_t yrow = (uint32_t)F2 * C * 4;
+    const rsrc_t yr = make_rsrc(y + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * yrow);
+    if (!any_ok) {
+        // Every h row this tile reads is masked or padding: y is the bias.
+        for (int s = 0; s < ncols; ++s)
+#pragma unroll
+            for (int i = 0; i < kSubRows; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bb), yr,
+                                                      (uint32_t)(t0 + i) * yrow + ((uint32_t)(f0 + s) * C + c) * 4, 0,
+                                                      kNonTemporal);
+        return;
     }
 
     // conv0 + bias + ReLU at h row l, for the h column whose three mel
-    // columns start at patch column q.
+    // columns start at patch column q; zero where the row is masked.  The
+    // sum is computed for every row and then selected, so the loads and FMAs
+    // of all rows can be scheduled together.
     auto conv0 = [&](int l, int q) -> float {
         float a = ba;
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j) a = __builtin_fmaf(patch[2 * l + i][q + j], wa[3 * i + j], a);
-        return fmaxf(a, 0.0f);
+        return hrow_ok[l] ? fmaxf(a, 0.0f) : 0.0f;
     };
 
     // Carried h column 2*f0-1 (zero at the left edge).
     float hc[2 * kSubRows + 1];
 #pragma unroll
-    for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = (f0 > 0 && hrow_ok[l]) ? conv0(l, 2) : 0.0f;
+    for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = f0 > 0 ? conv0(l, 2) : 0.0f;
 
-    const int32_t ncols = min(kSubCols, F2 - f0);
-    const uint32_t yrow = (uint32_t)F2 * C * 4;
-    const rsrc_t yr = make_rsrc(y + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * yrow);
-    for (int s = 0; s < ncols; ++s) {
+    // One output column: h columns 2f2 and 2f2+1 for every h row, then the
+    // depthwise taps.  h column 2f2+1 lies in the padding only at the last
+    // output column of an odd-width h, which is peeled off the loop so that
+    // the loop body has no condition around its LDS reads.
+    auto step = [&](int s, auto odd_valid) {
         const int32_t f2 = f0 + s;
-        const bool odd_ok = 2 * f2 + 1 < F1;  // h column 2f2+1 inside [0, F1)
         float he[2 * kSubRows + 1], ho[2 * kSubRows + 1];
 #pragma unroll
         for (int l = 0; l < 2 * kSubRows + 1; ++l) {
-            he[l] = hrow_ok[l] ? conv0(l, 4 * s + 4) : 0.0f;
-            ho[l] = (hrow_ok[l] && odd_ok) ? conv0(l, 4 * s + 6) : 0.0f;
+            he[l] = conv0(l, 4 * s + 4);
+            ho[l] = decltype(odd_valid)::value ? conv0(l, 4 * s + 6) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < kSubRows; ++i) {
@@ -131,7 +151,11 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
         }
 #pragma unroll
         for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = ho[l];
-    }
+    };
+    const bool last_odd_pad = 2 * (f0 + ncols - 1) + 1 >= F1;
+    const int full = last_odd_pad ? ncols - 1 : ncols;
+    for (int s = 0; s < full; ++s) step(s, std::true_type{});
+    if (last_odd_pad) step(full, std::false_type{});
 }
 
 bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C) {
