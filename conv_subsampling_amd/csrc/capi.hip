@@ -8,6 +8,10 @@
 #include "../../include/dwconv.h"
 #include "launch.h"
 
+#ifndef DW1D_BF16_VEC
+#define DW1D_BF16_VEC 4  // bf16 channels per lane access in the 1-D kernel
+#endif
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -55,7 +59,7 @@ dw_status dwconv1d_fwd(const void* x, const void* w, const void* bias, const int
     if (x == y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
     const int es = dtype == DW_BF16 ? 2 : 4;
     const void* ptrs[4] = {x, w, bias, y};
-    const int vec = dw::pick_vec(C, es, ptrs, 4, dtype == DW_BF16 ? 4 : 4);
+    const int vec = dw::pick_vec(C, es, ptrs, 4, dtype == DW_BF16 ? DW1D_BF16_VEC : 4);
     if (!dw::dwconv1d_fwd_fits(B, T, C, K, es, vec))
         return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch (B=%lld T=%lld C=%lld K=%lld)", fn, (long long)B, (long long)T, (long long)C, (long long)K);
     const int64_t pL = pad == DW_PAD_CAUSAL ? K - 1 : (K - 1) / 2;

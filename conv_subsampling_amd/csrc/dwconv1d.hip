@@ -131,17 +131,17 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_anyk_kernel(
 #ifndef DW1D_TILE
 #define DW1D_TILE 8
 #endif
-template <int K>
-constexpr int tile_1d() { return DW1D_TILE; }
+#ifndef DW1D_TILE_WIDE
+#define DW1D_TILE_WIDE 4  // time tile for 8-wide (16-byte bf16) channel vectors
+#endif
+template <int K, int V = 4>
+constexpr int tile_1d() { return V >= 8 ? DW1D_TILE_WIDE : DW1D_TILE; }
 constexpr int kTileAnyK = 8;
 
-static int tile_for(int64_t K) {
+static int tile_for(int64_t K, int vec) {
+    const bool wide = vec >= 8;
     switch (K) {
-        case 3: return tile_1d<3>();
-        case 4: return tile_1d<4>();
-        case 5: return tile_1d<5>();
-        case 9: return tile_1d<9>();
-        case 15: return tile_1d<15>();
+        case 3: case 4: case 5: case 9: case 15: return wide ? tile_1d<3, 8>() : tile_1d<3, 4>();
         default: return kTileAnyK;
     }
 }
@@ -150,7 +150,7 @@ bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
     // Per-item byte offsets, including the left padding as a negative
     // offset, must stay within a signed 32-bit range.
     if ((T + K) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
-    const int64_t tt = tile_for(K);
+    const int64_t tt = tile_for(K, vec);
     const int64_t per_item = ((T + tt - 1) / tt) * (C / vec);
     const int64_t blocks = B * ((per_item + kBlock1d - 1) / kBlock1d);
     return blocks < ((int64_t)1 << 31);
@@ -159,7 +159,7 @@ bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
 template <typename S, int V>
 static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int32_t* lengths, S* y,
                                int64_t B, int64_t T, int64_t C, int64_t K, int64_t pL, hipStream_t st) {
-    const int tt = tile_for(K);
+    const int tt = tile_for(K, V);
     const uint32_t n_tiles = (uint32_t)((T + tt - 1) / tt);
     const uint32_t CG = (uint32_t)(C / V);
     const uint32_t bpi = (uint32_t)(((uint64_t)n_tiles * CG + kBlock1d - 1) / kBlock1d);
@@ -167,7 +167,7 @@ static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int3
     const int32_t T32 = (int32_t)T, C32 = (int32_t)C, p32 = (int32_t)pL;
 #define DW1D_CASE(KK)                                                                            \
     case KK:                                                                                     \
-        hipLaunchKernelGGL((dwconv1d_fwd_kernel<S, V, KK, tile_1d<KK>()>), grid, block, 0, st, x, \
+        hipLaunchKernelGGL((dwconv1d_fwd_kernel<S, V, KK, tile_1d<KK, V>()>), grid, block, 0, st, x, \
                            w, bias, lengths, y, T32, C32, p32, n_tiles, CG, bpi);                  \
         break;
     switch (K) {
@@ -191,6 +191,7 @@ hipError_t launch_dwconv1d_fwd(const void* x, const void* w, const void* bias, c
         auto X = (const uint16_t*)x; auto W = (const uint16_t*)w; auto Bi = (const uint16_t*)bias;
         auto Y = (uint16_t*)y;
         switch (vec) {
+            case 8: return launch_typed<uint16_t, 8>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
             case 4: return launch_typed<uint16_t, 4>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
             case 2: return launch_typed<uint16_t, 2>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);
             default: return launch_typed<uint16_t, 1>(X, W, Bi, lengths, Y, B, T, C, K, pad_left, st);

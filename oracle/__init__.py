@@ -28,30 +28,41 @@ _I = ctypes.POINTER(ctypes.c_int32)
 _L = ctypes.c_long
 
 
+def compile_c(src: str, out: str) -> str:
+    """gcc, plain IEEE arithmetic: no fast-math, no FMA contraction."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call([
+        "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c99",
+        "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, src, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (plain IEEE arithmetic)."""
+    """Compile oracle.c into liboracle.so."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + f".tmp{os.getpid()}"
-        subprocess.check_call([
-            "gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-std=c99",
-            "-shared", "-fPIC", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
+        compile_c(_SRC, _LIB)
     return _LIB
+
+
+def _bind(path: str):
+    """Load a build of oracle.c and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    lib.oracle_dwconv1d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, ctypes.c_int]
+    lib.oracle_dwconv2d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, _L, _L, _L, _L]
+    lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L, _L]
+    lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L]
+    for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd,
+              lib.oracle_dwconv2d_bwd, lib.oracle_dwsub_front_fwd):
+        f.restype = ctypes.c_int
+    return lib
 
 
 def _load():
     global _lib
     if _lib is None:
         build(force=False)
-        lib = ctypes.CDLL(_LIB)
-        lib.oracle_dwconv1d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, ctypes.c_int]
-        lib.oracle_dwconv2d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, _L, _L, _L, _L]
-        lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L, _L]
-        lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L]
-        for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd,
-                  lib.oracle_dwconv2d_bwd, lib.oracle_dwsub_front_fwd):
-            f.restype = ctypes.c_int
-        _lib = lib
+        _lib = _bind(_LIB)
     return _lib
 
 
