@@ -52,8 +52,9 @@ def _bind(path: str):
     lib.oracle_dwconv2d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, _L, _L, _L, _L]
     lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L, _L]
     lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L]
-    for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd,
-              lib.oracle_dwconv2d_bwd, lib.oracle_dwsub_front_fwd):
+    lib.oracle_dwsub_front_bwd.argtypes = [_F, _F, _F, _F, _I, _F, _D, _D, _D, _D, _L, _L, _L, _L]
+    for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd, lib.oracle_dwconv2d_bwd,
+              lib.oracle_dwsub_front_fwd, lib.oracle_dwsub_front_bwd):
         f.restype = ctypes.c_int
     return lib
 
@@ -170,3 +171,24 @@ def dwsub_front_fwd(x, w0, b0, w1, b1, lengths):
     _check(_load().oracle_dwsub_front_fwd(xp, w0p, b0p, w1p, b1p, lp, _ptr_d(y), B, T, F, C),
            "oracle_dwsub_front_fwd")
     return y
+
+
+def dwsub_front_bwd(x, w0, b0, w1, lengths, dy):
+    """(dw0, db0, dw1, db1) of the subsampler front given dy [B,T2,F2,C]."""
+    xa, xp = _f32(x)
+    B, T, F = xa.shape
+    w0a, w0p = _f32(w0)
+    C = w0a.shape[2]
+    if w0a.shape != (3, 3, C):
+        raise ValueError("w0 must be [3, 3, C]")
+    b0a, b0p = _f32(b0, (C,))
+    w1a, w1p = _f32(w1, (3, 3, C))
+    la, lp = _lens(lengths, B)
+    T1, F1 = conv_out_len(T, 3, 2, 1), conv_out_len(F, 3, 2, 1)
+    T2, F2 = conv_out_len(T1, 3, 2, 1), conv_out_len(F1, 3, 2, 1)
+    da, dp = _f32(dy, (B, T2, F2, C))
+    dw0, db0 = np.empty((3, 3, C)), np.empty((C,))
+    dw1, db1 = np.empty((3, 3, C)), np.empty((C,))
+    _check(_load().oracle_dwsub_front_bwd(xp, w0p, b0p, w1p, lp, dp, _ptr_d(dw0), _ptr_d(db0), _ptr_d(dw1),
+                                          _ptr_d(db1), B, T, F, C), "oracle_dwsub_front_bwd")
+    return dw0, db0, dw1, db1

@@ -259,3 +259,103 @@ int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
     free(h);
     return 0;
 }
+
+/*
+ * Backward of the subsampler front with respect to its parameters (the
+ * training step of NeMo PR #16114, "What does this PR do": the fused kernels
+ * speed up the encoder's forward and backward).  The mel input needs no
+ * gradient.  With z = conv0(x) + b0 (before the ReLU) and h as in
+ * oracle_dwsub_front_fwd, given dy [B][T2][F2][C]:
+ *   db1[c]      = sum dy[b,t2,f2,c]
+ *   dw1[i,j,c]  = sum dy[b,t2,f2,c] * hz[b, 2t2+i-1, 2f2+j-1, c]
+ *   dh[b,t1,f1,c] = sum over (t2,i,f2,j) with t1 = 2t2+i-1, f1 = 2f2+j-1 of
+ *                   dy[b,t2,f2,c] * w1[i,j,c]
+ *   dz          = dh where t1 < L1_b and z > 0, else 0 (ReLU and mask)
+ *   db0[c]      = sum dz
+ *   dw0[i,j,c]  = sum dz[b,t1,f1,c] * xz[b, 2t1+i-1, 2f1+j-1]
+ * Computed unfused: z, h and dh are materialised per item, dh in scatter
+ * order.  Any output pointer may be NULL.
+ */
+int oracle_dwsub_front_bwd(const float *x, const float *w0, const float *b0,
+                           const float *w1, const int32_t *lengths, const float *dy,
+                           double *dw0, double *db0, double *dw1, double *db1,
+                           long B, long T, long F, long C)
+{
+    if (B < 0 || T < 0 || F < 0 || C < 0) return -1;
+    long T1 = conv_out_len(T, 3, 2, 1), F1 = conv_out_len(F, 3, 2, 1);
+    long T2 = conv_out_len(T1, 3, 2, 1), F2 = conv_out_len(F1, 3, 2, 1);
+    size_t hn = (size_t)(T1 * F1 * C);
+    double *z = (double *)malloc(sizeof(double) * (hn ? hn : 1));
+    double *h = (double *)malloc(sizeof(double) * (hn ? hn : 1));
+    double *dh = (double *)malloc(sizeof(double) * (hn ? hn : 1));
+    if (!z || !h || !dh) { free(z); free(h); free(dh); return -1; }
+    if (dw0) memset(dw0, 0, sizeof(double) * (size_t)(9 * C));
+    if (db0) memset(db0, 0, sizeof(double) * (size_t)C);
+    if (dw1) memset(dw1, 0, sizeof(double) * (size_t)(9 * C));
+    if (db1) memset(db1, 0, sizeof(double) * (size_t)C);
+    for (long b = 0; b < B; ++b) {
+        long len = clamp_len(lengths, b, T);
+        long L1 = (len + 1) / 2;
+        /* forward again: z = conv0(x) + b0, h = mask * ReLU(z) */
+        for (long t1 = 0; t1 < T1; ++t1)
+            for (long f1 = 0; f1 < F1; ++f1)
+                for (long c = 0; c < C; ++c) {
+                    double acc = 0.0;
+                    for (long i = 0; i < 3; ++i) {
+                        long t = 2 * t1 + i - 1;
+                        if (t < 0 || t >= T) continue;
+                        for (long j = 0; j < 3; ++j) {
+                            long f = 2 * f1 + j - 1;
+                            if (f < 0 || f >= F) continue;
+                            acc += (double)x[(b * T + t) * F + f] * (double)w0[(i * 3 + j) * C + c];
+                        }
+                    }
+                    acc += b0 ? (double)b0[c] : 0.0;
+                    size_t q = (size_t)((t1 * F1 + f1) * C + c);
+                    z[q] = acc;
+                    h[q] = (t1 < L1 && acc > 0.0) ? acc : 0.0;
+                    dh[q] = 0.0;
+                }
+        /* stage 2 backward, scatter order */
+        for (long t2 = 0; t2 < T2; ++t2)
+            for (long f2 = 0; f2 < F2; ++f2)
+                for (long c = 0; c < C; ++c) {
+                    double g = (double)dy[((b * T2 + t2) * F2 + f2) * C + c];
+                    if (db1) db1[c] += g;
+                    for (long i = 0; i < 3; ++i) {
+                        long t1 = 2 * t2 + i - 1;
+                        if (t1 < 0 || t1 >= T1) continue;
+                        for (long j = 0; j < 3; ++j) {
+                            long f1 = 2 * f2 + j - 1;
+                            if (f1 < 0 || f1 >= F1) continue;
+                            size_t q = (size_t)((t1 * F1 + f1) * C + c);
+                            if (dw1) dw1[(i * 3 + j) * C + c] += g * h[q];
+                            dh[q] += g * (double)w1[(i * 3 + j) * C + c];
+                        }
+                    }
+                }
+        /* through the mask and the ReLU, then conv0's parameters */
+        for (long t1 = 0; t1 < T1; ++t1)
+            for (long f1 = 0; f1 < F1; ++f1)
+                for (long c = 0; c < C; ++c) {
+                    size_t q = (size_t)((t1 * F1 + f1) * C + c);
+                    if (t1 >= L1) continue; /* masked: contributes nothing (and is never read) */
+                    double dz = z[q] > 0.0 ? dh[q] : 0.0;
+                    if (db0) db0[c] += dz;
+                    if (!dw0) continue;
+                    for (long i = 0; i < 3; ++i) {
+                        long t = 2 * t1 + i - 1;
+                        if (t < 0 || t >= T) continue;
+                        for (long j = 0; j < 3; ++j) {
+                            long f = 2 * f1 + j - 1;
+                            if (f < 0 || f >= F) continue;
+                            dw0[(i * 3 + j) * C + c] += dz * (double)x[(b * T + t) * F + f];
+                        }
+                    }
+                }
+    }
+    free(z);
+    free(h);
+    free(dh);
+    return 0;
+}

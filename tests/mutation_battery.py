@@ -41,6 +41,10 @@ BATTERY = [
     (P.test_front_center_delta_closed_form, ()),
     (P.test_front_fully_masked_rows_equal_output_bias, ()),
     (P.test_front_input_is_not_length_masked, ()),
+    (P.test_front_bwd_matches_torch_autograd, (2, 16, 12, 4)),
+    (P.test_front_bwd_matches_torch_autograd, (3, 13, 9, 3)),
+    (P.test_front_bwd_closed_forms_and_linearity, ()),
+    (P.test_front_bwd_masked_input_rows_never_read, ()),
 ]
 
 

@@ -55,6 +55,16 @@ MUTANTS = [
     ("front conv0 bias after ReLU", "                        acc += (double)b0[c];\n                        v = acc > 0.0 ? acc : 0.0;",
      "                        v = acc > 0.0 ? acc : 0.0;\n                        v += (double)b0[c];"),
     ("front stage-2 stride 1", "long t1 = 2 * t2 + i - 1;", "long t1 = t2 + i - 1;"),
+    ("front bwd ReLU derivative ignored", "double dz = z[q] > 0.0 ? dh[q] : 0.0;", "double dz = dh[q];"),
+    ("front bwd time mask ignored", "if (t1 >= L1) continue; /* masked", "if (0) continue; /* masked"),
+    ("front bwd dh with flipped taps", "dh[q] += g * (double)w1[(i * 3 + j) * C + c];",
+     "dh[q] += g * (double)w1[((2 - i) * 3 + (2 - j)) * C + c];"),
+    ("front bwd dw1 from pre-ReLU z", "if (dw1) dw1[(i * 3 + j) * C + c] += g * h[q];",
+     "if (dw1) dw1[(i * 3 + j) * C + c] += g * z[q];"),
+    ("front bwd dw0 taps transposed", "dw0[(i * 3 + j) * C + c] += dz * (double)x[(b * T + t) * F + f];",
+     "dw0[(j * 3 + i) * C + c] += dz * (double)x[(b * T + t) * F + f];"),
+    ("front bwd b0 left out of the recompute", "acc += b0 ? (double)b0[c] : 0.0;\n                    size_t q",
+     "size_t q"),
 ]
 
 

@@ -457,3 +457,78 @@ def test_front_positive_homogeneity():
     y = oracle.dwsub_front_fwd(x, w0, b0, w1, b1, lengths) - b1.astype(np.float64)
     y2 = oracle.dwsub_front_fwd(f32(2 * x), w0, f32(2 * b0), w1, b1, lengths) - b1.astype(np.float64)
     close(y2, 2 * y, 1e-13)
+
+
+# ------------------------------------------------- fused front backward -----
+
+def torch_front_grads(x, w0, b0, w1, b1, lengths, dy):
+    B, T, F = x.shape
+    C = w0.shape[2]
+    L = eff_len(lengths, B, T)
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64)).requires_grad_(True)
+    tw0, tb0, tw1, tb1 = t(w0), t(b0), t(w1), t(b1)
+    xt = torch.from_numpy(x.astype(np.float64))[:, None]
+    h = Fn.conv2d(xt, tw0.permute(2, 0, 1)[:, None], tb0, stride=2, padding=1)
+    h = torch.relu(h)
+    L1 = (L + 1) // 2
+    m = (torch.arange(h.shape[2])[None, :] < torch.as_tensor(L1)[:, None])[:, None, :, None]
+    h = torch.where(m, h, torch.zeros(()))
+    y = Fn.conv2d(h, tw1.permute(2, 0, 1)[:, None], tb1, stride=2, padding=1, groups=C).permute(0, 2, 3, 1)
+    (y * torch.from_numpy(dy.astype(np.float64))).sum().backward()
+    return tw0.grad.numpy(), tb0.grad.numpy(), tw1.grad.numpy(), tb1.grad.numpy()
+
+
+@pytest.mark.parametrize("B,T,F,C", [(2, 16, 12, 4), (3, 13, 9, 3), (1, 1, 1, 2), (2, 30, 20, 5), (1, 7, 80, 2)])
+def test_front_bwd_matches_torch_autograd(B, T, F, C):
+    r = rng(40 + B + T + F + C)
+    x = f32(r.standard_normal((B, T, F)))
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0, b1 = f32(r.standard_normal(C)), f32(r.standard_normal(C))
+    T2, F2 = (((T + 1) // 2) + 1) // 2, (((F + 1) // 2) + 1) // 2
+    dy = f32(r.standard_normal((B, T2, F2, C)))
+    for lengths in (None, r.integers(-1, T + 2, B).astype(np.int32)):
+        got = oracle.dwsub_front_bwd(x, w0, b0, w1, lengths, dy)
+        ref = torch_front_grads(x, w0, b0, w1, b1, lengths, dy)
+        for g, rf in zip(got, ref):
+            close(g, rf)
+
+
+def test_front_bwd_closed_forms_and_linearity():
+    r = rng(45)
+    B, T, F, C = 2, 20, 14, 3
+    x = f32(r.standard_normal((B, T, F)))
+    w0 = f32(r.standard_normal((3, 3, C)))
+    w1 = f32(r.integers(-4, 5, (3, 3, C)) / 4.0)  # quarter-integers: w1 +- 0.5 is exact in float32
+    b0 = f32(r.standard_normal(C))
+    lengths = np.array([20, 9], np.int32)
+    dy1 = f32(r.integers(-4, 5, (B, 5, 4, C)))
+    dy2 = f32(r.integers(-4, 5, (B, 5, 4, C)))
+    g1 = oracle.dwsub_front_bwd(x, w0, b0, w1, lengths, dy1)
+    g2 = oracle.dwsub_front_bwd(x, w0, b0, w1, lengths, dy2)
+    g12 = oracle.dwsub_front_bwd(x, w0, b0, w1, lengths, f32(dy1 + dy2))
+    for a, b_, c in zip(g1, g2, g12):
+        close(c, a + b_, 1e-12)                                   # linear in dy
+    close(g1[3], dy1.astype(np.float64).sum(axis=(0, 1, 2)))     # db1 = sum of dy
+    # dw1 is the loss's exact derivative in w1: y is linear in w1
+    loss = lambda ww1: float(np.sum((oracle.dwsub_front_fwd(x, w0, b0, ww1, np.zeros(C, np.float32), lengths))
+                                    * dy1.astype(np.float64)))
+    for idx in [(0, 0, 0), (1, 1, 2), (2, 1, 1)]:
+        e = np.zeros_like(w1)
+        e[idx] = 0.5
+        fd = (loss(w1 + e) - loss(w1 - e)) / 1.0
+        assert abs(fd - g1[2][idx]) <= 1e-9 * (1 + abs(fd))
+
+
+def test_front_bwd_masked_input_rows_never_read():
+    r = rng(46)
+    B, T, F, C = 2, 24, 10, 3
+    x = f32(r.standard_normal((B, T, F)))
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0 = f32(r.standard_normal(C))
+    lengths = np.array([24, 9], np.int32)  # L1 = 5 for item 1: mel rows >= 10 feed no unmasked h row
+    dy = f32(r.standard_normal((B, 6, 3, C)))
+    g = oracle.dwsub_front_bwd(x, w0, b0, w1, lengths, dy)
+    xp = x.copy()
+    xp[1, 10:] = np.nan
+    for a, b_ in zip(g, oracle.dwsub_front_bwd(xp, w0, b0, w1, lengths, dy)):
+        assert np.array_equal(a, b_)
