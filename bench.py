@@ -5,6 +5,7 @@ One step runs every operation of the path once, each at its workload's full
 size, on synthetic inputs resident in HBM:
 
   front   dwsub_fused_fwd   mel [4,1000,80] -> [4,250,20,256]           fp32
+          dwsub_fused_bwd   dw0, db0, dw1, db1 of the same, dy given     fp64 sums
   conv1d  dwconv1d_fwd      [16,750,1024] K=9 symmetric                 bf16 storage
   sweep   dwconv1d_fwd      [32,1500,512] causal, K = 3, 4, 5, 9, 15    fp32
           dwconv1d_fwd      [32,1500,200] causal, K = 9                 fp32
@@ -95,6 +96,20 @@ def work_front(c):
     return rd, wr, flops
 
 
+def work_front_bwd(c):
+    B, T, F, C = c["B"], c["T"], c["F"], c["C"]
+    T1, F1 = (T + 1) // 2, (F + 1) // 2
+    T2, F2 = (T1 + 1) // 2, (F1 + 1) // 2
+    L = clamp_lengths(c["lengths"].tolist(), T)
+    L1 = [min((l + 1) // 2, T1) for l in L]
+    rows_read = sum(min(T, 2 * l1) for l1 in L1)
+    rd = rows_read * F * 4 + B * T2 * F2 * C * 4 + 19 * C * 4 + 4 * B
+    wr = 20 * C * 4
+    hpos = sum(L1) * F1 * C                       # unmasked h positions
+    flops = hpos * (18 + 18 + 1) + B * T2 * F2 * C * (18 + 18 + 1)
+    return rd, wr, flops
+
+
 def work_stage_fwd(c):
     B, T, F, C = c["B"], c["T"], c["F"], c["C"]
     To, Fo = (T + 1) // 2, (F + 1) // 2
@@ -136,6 +151,15 @@ def build_rows(dev):
     fy = torch.empty((f["B"], 250, 20, f["C"]), device=dev)
     add("front", "dwsub_fused_fwd", "mel [4,1000,80] -> [4,250,20,256] fp32", f["B"] * f["T"], *work_front(f),
         lambda: dw.dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], fL, y=fy), bound="alu")
+
+    fdy = datagen.normal((f["B"], 250, 20, f["C"]), 1.0, "c2/dy", device=dev)
+    fg = [torch.empty(sh, device=dev) for sh in ((3, 3, f["C"]), (f["C"],), (3, 3, f["C"]), (f["C"],))]
+    fws = torch.empty((dw.dwsub_fused_bwd_workspace_bytes(f["B"], f["T"], f["F"], f["C"]),), dtype=torch.uint8,
+                      device=dev)
+    add("front_bwd", "dwsub_fused_bwd", "dw0,db0,dw1,db1 of the front, dy [4,250,20,256] fp64 accumulation",
+        f["B"] * f["T"], *work_front_bwd(f),
+        lambda: dw.dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], fL, fdy, *fg, workspace=fws), bound="alu")
+    f["dy"] = fdy
 
     e = datagen.conv1d_encoder_bf16(device=dev)
     eL = e["lengths"].to(dev)
@@ -179,8 +203,8 @@ def cpu_baseline(data, target_s: float):
     hp = lambda d: {k: (v.detach().float().cpu() if hasattr(v, "detach") and k != "x" and k != "dy" else v)
                     for k, v in d.items()}
     f, e, g = hp(data["front"]), hp(data["conv1d_bf16"]), hp(data["stage"])
-    f["x"], e["x"], g["x"], g["dy"] = data["front"]["x"], data["conv1d_bf16"]["x"], data["stage"]["x"], \
-        data["stage"]["dy"]
+    f["x"], f["dy"] = data["front"]["x"], data["front"]["dy"]
+    e["x"], g["x"], g["dy"] = data["conv1d_bf16"]["x"], data["stage"]["x"], data["stage"]["dy"]
     sweep = []
     for s in data["sweep"]:
         hs = hp(s)
@@ -194,6 +218,12 @@ def cpu_baseline(data, target_s: float):
         xs = host(f["x"], m)
         t = time.perf_counter()
         oracle.dwsub_front_fwd(xs, f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"][:m])
+        secs += time.perf_counter() - t
+        frames += m * f["T"]
+        m = min(n, f["B"])
+        xs, dys = host(f["x"], m), host(f["dy"], m)
+        t = time.perf_counter()
+        oracle.dwsub_front_bwd(xs, f["w0"], f["b0"], f["w1"], f["lengths"][:m], dys)
         secs += time.perf_counter() - t
         frames += m * f["T"]
         m = min(n, e["B"])
@@ -346,7 +376,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; log-mel-shaped inputs, lengths ~U[T/2,T])",
         "config": {
-            "workload": "encoder depthwise path: fused front [4,1000,80]; conv-module dwconv1d [16,750,1024] K9 "
+            "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd; conv-module dwconv1d [16,750,1024] K9 "
                         "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 and [32,1500,200] K9; depthwise conv2d "
                         "stage [32,1500,64,256] fwd+bwd",
             "frames_per_step": frames,

@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "DwconvError", "abi_version",
-    "dwconv1d_fwd", "dwsub_fused_fwd", "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
+    "dwconv1d_fwd", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
+    "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
     "out_len",
 ]
 
@@ -42,7 +43,7 @@ class DwconvError(RuntimeError):
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m conv_subsampling_amd.build, or __graft_entry__.build())")
+        "(python conv_subsampling_amd/build.py, or __graft_entry__.build())")
 
 _vp, _i64, _sz, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
 
@@ -58,6 +59,10 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dwconv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp]
     lib.dwsub_fused_fwd.restype = _int
     lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
+    lib.dwsub_fused_bwd_workspace_bytes.restype = _sz
+    lib.dwsub_fused_bwd_workspace_bytes.argtypes = [_i64] * 4
+    lib.dwsub_fused_bwd.restype = _int
+    lib.dwsub_fused_bwd.argtypes = [_vp] * 11 + [_sz] + [_i64] * 4 + [_vp]
     lib.dwconv2d_fwd.restype = _int
     lib.dwconv2d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp] + [_i64] * 8 + [_vp]
     lib.dwconv2d_bwd_workspace_bytes.restype = _sz
@@ -156,6 +161,42 @@ def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None):
     _check(_lib.dwsub_fused_fwd(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(b1), _ptr(lengths), _ptr(y),
                                 B, T, F, C, _stream(dev)))
     return y
+
+
+def dwsub_fused_bwd_workspace_bytes(B, T, F, C) -> int:
+    return int(_lib.dwsub_fused_bwd_workspace_bytes(B, T, F, C))
+
+
+def dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0=None, db0=None, dw1=None, db1=None, workspace=None,
+                    need=("dw0", "db0", "dw1", "db1")):
+    """Parameter gradients (dw0, db0, dw1, db1) of dwsub_fused_fwd given dy [B,T2,F2,C]."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, F]")
+    dev, f32 = x.device, torch.float32
+    B, T, F = x.shape
+    _dev_tensor("x", x, f32, dev)
+    if w0.dim() != 3 or w0.shape[:2] != (3, 3):
+        raise ValueError("w0 must be [3, 3, C]")
+    C = w0.shape[2]
+    _dev_tensor("w0", w0, f32, dev)
+    _dev_tensor("b0", b0, f32, dev, (C,), allow_none=True)
+    _dev_tensor("w1", w1, f32, dev, (3, 3, C))
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    T2, F2 = out_len(out_len(T)), out_len(out_len(F))
+    _dev_tensor("dy", dy, f32, dev, (B, T2, F2, C))
+    outs = {}
+    for name, t, shape in (("dw0", dw0, (3, 3, C)), ("db0", db0, (C,)), ("dw1", dw1, (3, 3, C)), ("db1", db1, (C,))):
+        if t is None and name in need:
+            t = torch.empty(shape, dtype=f32, device=dev)
+        outs[name] = _dev_tensor(name, t, f32, dev, shape, allow_none=True)
+    need_ws = dwsub_fused_bwd_workspace_bytes(B, T, F, C)
+    if workspace is None:
+        workspace = torch.empty((max(need_ws, 1),), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, torch.uint8, dev)
+    _check(_lib.dwsub_fused_bwd(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(lengths), _ptr(dy),
+                                _ptr(outs["dw0"]), _ptr(outs["db0"]), _ptr(outs["dw1"]), _ptr(outs["db1"]),
+                                _ptr(workspace), workspace.numel(), B, T, F, C, _stream(dev)))
+    return outs["dw0"], outs["db0"], outs["dw1"], outs["db1"]
 
 
 def _conv2d_dims(x, w):

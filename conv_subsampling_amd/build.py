@@ -1,6 +1,9 @@
 """Build libdwconv.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-    python -m conv_subsampling_amd.build
+    python conv_subsampling_amd/build.py
+
+(Run it by path, or through __graft_entry__.build(): importing it as a
+submodule would first import the package, which loads the library.)
 
 Each source is compiled to an object in parallel, then linked into one
 shared library next to this file.  Packed-FP32 instructions are disabled
@@ -20,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdwconv.so")
-SOURCES = ["capi.hip", "dwconv1d.hip", "dwsub_front.hip", "dwconv2d.hip"]
+SOURCES = ["capi.hip", "dwconv1d.hip", "dwsub_front.hip", "dwconv2d.hip", "reduce.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

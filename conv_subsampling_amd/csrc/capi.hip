@@ -80,6 +80,31 @@ dw_status dwsub_fused_fwd(const float* x, const float* w0, const float* b0, cons
     return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, (hipStream_t)stream), fn);
 }
 
+size_t dwsub_fused_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C) {
+    if (B < 0 || T < 0 || F < 0 || C < 0) return 0;
+    return dw::dwsub_fused_bwd_workspace(B, T, F, C);
+}
+
+dw_status dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
+                          const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1, float* db1,
+                          void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
+                          void* stream) {
+    const char* fn = "dwsub_fused_bwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (!dw0 && !db0 && !dw1 && !db1) return ok();
+    if (C == 0) return ok();
+    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
+    if ((!x && B * T * F > 0) || (!dy && B * T2 * F2 * C > 0) || !w0 || !w1)
+        return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and dy must not be NULL (unless empty)", fn);
+    const size_t need = dw::dwsub_fused_bwd_workspace(B, T, F, C);
+    if (!workspace || workspace_bytes < need)
+        return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (!dw::dwsub_fused_bwd_fits(B, T, F, C)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, B, T, F, C,
+                                               (hipStream_t)stream), fn);
+}
+
 dw_status dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths, float* y,
                        int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride,
                        int64_t pad, void* stream) {

@@ -35,8 +35,8 @@
 // fp64, and fp64 FMA runs at the fp32 rate here), because a sum of ~10^6
 // terms can cancel to a value far smaller than its terms.  They are summed
 // per thread, then across the workgroup's row blocks in a fixed order,
-// written as one fp64 partial per workgroup to the workspace, and two small
-// kernels add the partials in a fixed order: the result is bitwise
+// written as one fp64 partial per workgroup to the workspace, and the
+// partials are added in a fixed order (reduce.hip): the result is bitwise
 // repeatable.
 #include "common.h"
 #include "launch.h"
@@ -394,55 +394,6 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     }
 }
 
-// Fixed-order fp64 sum of the P workgroup partials, in two levels so that
-// enough workgroups share the reading.  Each level sums chunks of up to
-// kSumChunk rows of a [rows][ncol] fp64 matrix: a workgroup of kSumRows
-// sub-rows x kSumCols columns adds its chunk's rows (sub-row q takes rows
-// q, q + kSumRows, ...), then the sub-rows are added in order through LDS.
-// Level 1 writes one fp64 row per chunk; level 2 (one chunk) writes dw, db.
-constexpr int kSumCols = 64, kSumRows = 4, kSumChunk = 64;
-
-__device__ __forceinline__ double sum_chunk(const double* __restrict__ in, int32_t ncol, int32_t r0, int32_t r1,
-                                            int32_t col, double (*acc)[kSumCols]) {
-    const int32_t sub = threadIdx.x / kSumCols, lane = threadIdx.x % kSumCols;
-    double s = 0.0;
-    if (col < ncol) {
-#pragma unroll 4
-        for (int32_t r = r0 + sub; r < r1; r += kSumRows) s += in[(int64_t)r * ncol + col];
-    }
-    acc[sub][lane] = s;
-    __syncthreads();
-    double t = acc[0][lane];
-#pragma unroll
-    for (int q = 1; q < kSumRows; ++q) t += acc[q][lane];
-    return t;
-}
-
-__global__ __launch_bounds__(kSumCols* kSumRows) void dwconv2d_bwd_reduce1_kernel(
-    const double* __restrict__ partial, double* __restrict__ chunk_sum, int32_t ncol, int32_t P) {
-    __shared__ double acc[kSumRows][kSumCols];
-    const int32_t col = blockIdx.x * kSumCols + threadIdx.x % kSumCols;  // column = k * C + c
-    const int32_t p0 = blockIdx.y * kSumChunk, p1 = min(P, p0 + kSumChunk);
-    const double t = sum_chunk(partial, ncol, p0, p1, col, acc);
-    if (threadIdx.x < kSumCols && col < ncol) chunk_sum[(int64_t)blockIdx.y * ncol + col] = t;
-}
-
-__global__ __launch_bounds__(kSumCols* kSumRows) void dwconv2d_bwd_reduce2_kernel(
-    const double* __restrict__ chunk_sum, float* __restrict__ dw, float* __restrict__ db, int32_t C,
-    int32_t nchunk) {
-    __shared__ double acc[kSumRows][kSumCols];
-    const int32_t ncol = 10 * C;
-    const int32_t col = blockIdx.x * kSumCols + threadIdx.x % kSumCols;
-    const double t = sum_chunk(chunk_sum, ncol, 0, nchunk, col, acc);
-    if (threadIdx.x >= kSumCols || col >= ncol) return;
-    const int32_t k = col / C, c = col % C;
-    if (k < 9) {
-        if (dw) dw[(int64_t)k * C + c] = (float)t;
-    } else if (db) {
-        db[c] = (float)t;
-    }
-}
-
 // ------------------------------------------------------------- launchers ----
 
 struct Grid2d {
@@ -534,13 +485,11 @@ static BwdGrid bwd_grid(int64_t B, int64_t T) {
     return g;
 }
 
-static int64_t bwd_chunks(int64_t P) { return (P + kSumChunk - 1) / kSumChunk; }
-
 size_t dwconv2d_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C) {
     (void)F;
     // [P][10][C] workgroup partials, then [chunks][10][C] chunk sums, fp64.
     const int64_t P = bwd_grid(B, T).P;
-    const int64_t rows = P + (bwd_chunks(P) > 0 ? bwd_chunks(P) : 1);
+    const int64_t rows = P + (partial_reduce_chunks(P) > 0 ? partial_reduce_chunks(P) : 1);
     return (size_t)(rows * 10 * C * (int64_t)sizeof(double));
 }
 
@@ -561,20 +510,11 @@ static hipError_t launch_bwd_typed(const float* x, const float* w, const int32_t
         if (e != hipSuccess) return e;
     }
     if (dw || db) {
-        const int32_t P = (int32_t)g.P;
-        const int32_t ncol = (int32_t)(10 * C);
-        const int32_t nchunk = (int32_t)bwd_chunks(P);
-        const uint32_t ncblk = (uint32_t)((ncol + kSumCols - 1) / kSumCols);
-        double* chunk_sum = partial + (int64_t)P * ncol;
-        if (nchunk > 0) {
-            hipLaunchKernelGGL(dwconv2d_bwd_reduce1_kernel, dim3(ncblk, (uint32_t)nchunk), dim3(kSumCols * kSumRows),
-                               0, st, partial, chunk_sum, ncol, P);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL(dwconv2d_bwd_reduce2_kernel, dim3(ncblk), dim3(kSumCols * kSumRows), 0, st, chunk_sum, dw,
-                           db, (int32_t)C, nchunk);
-        return hipGetLastError();
+        RowOutputs out = {};
+        out.n = 2;
+        out.p[0] = dw; out.first[0] = 0; out.count[0] = 9;
+        out.p[1] = db; out.first[1] = 9; out.count[1] = 1;
+        return launch_partial_reduce(partial, g.P, 10, C, partial + g.P * 10 * C, out, st);
     }
     return hipSuccess;
 }

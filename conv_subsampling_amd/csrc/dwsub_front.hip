@@ -181,4 +181,251 @@ hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* 
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward of the front with respect to its parameters: dw0, db0, dw1, db1
+// (NeMo PR #16114, "What does this PR do": the fused kernels serve the
+// encoder's training step).  The mel input needs no gradient.
+//
+// h is recomputed on chip from the mel patch, never read from memory.  The
+// h positions are taken in "quads" (h rows 2t', 2t'+1 x columns 2f', 2f'+1),
+// each with the four gradients dy[t'..t'+1, f'..f'+1] it meets, exactly as
+// in the conv2d backward:
+//   dh[2t',  2f'  ] = g00 w1[1,1]
+//   dh[2t',  2f'+1] = g00 w1[1,2] + g01 w1[1,0]
+//   dh[2t'+1,2f'  ] = g00 w1[2,1] + g10 w1[0,1]
+//   dh[2t'+1,2f'+1] = g00 w1[2,2] + g01 w1[2,0] + g10 w1[0,2] + g11 w1[0,0]
+// and each (h, dy) pair above adds h * dy to the dw1 tap it multiplies; every
+// pair of the depthwise stage belongs to exactly one quad, and db1 adds g00
+// once per quad.  Then dz = dh where the h row is unmasked and z > 0, and
+// dw0[i,j] += dz * mel[2r+i-1, 2q+j-1], db0 += dz.
+//
+// Precision.  Everything from z on is fp64: the ReLU's derivative is a
+// decision on the sign of z, and an fp32 z would take it differently from a
+// full-precision reference for the few z that sit within an fp32 rounding of
+// zero, each such flip moving dw0 by a whole term.  fp64 FMA runs at the
+// fp32 vector rate here.  The sums are kept per thread in fp64, written as
+// one partial per workgroup and added in a fixed order (reduce.hip).
+//
+// Mapping.  One thread per channel; a tile is QR quad rows x QC quad columns
+// of one item, with its zero-padded mel patch staged in LDS as fp64.  G
+// persistent workgroups per channel block take the batch's tiles
+// round-robin and keep their sums across tiles.
+// ---------------------------------------------------------------------------
+
+#ifndef DWSUB_BWD_QROWS
+#define DWSUB_BWD_QROWS 2
+#endif
+#ifndef DWSUB_BWD_QCOLS
+#define DWSUB_BWD_QCOLS 5
+#endif
+#ifndef DWSUB_BWD_WGS
+#define DWSUB_BWD_WGS 512
+#endif
+constexpr int kBQR = DWSUB_BWD_QROWS;          // quad rows per tile
+constexpr int kBQC = DWSUB_BWD_QCOLS;          // quad columns per tile
+constexpr int kBPatchRows = 4 * kBQR + 1;      // mel rows 4*t0-1 .. 4*t0+4*QR-1
+constexpr int kBPatchCols = 4 * kBQC + 1;      // mel columns 4*f0-1 .. 4*f0+4*QC-1
+constexpr int kFrontGrads = 20;                // dw0 (9), db0, dw1 (9), db1
+
+__global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
+    const float* __restrict__ x, const float* __restrict__ w0, const float* __restrict__ b0,
+    const float* __restrict__ w1, const int32_t* __restrict__ lengths, const float* __restrict__ dy,
+    double* __restrict__ partial, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2,
+    int32_t F2, uint32_t n_rt, uint32_t n_ft, uint32_t n_tiles, uint32_t n_cblk) {
+    __shared__ double patch[kBPatchRows][kBPatchCols];
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t G = gridDim.x / n_cblk;
+    const uint32_t g = blk / n_cblk, cblk = blk - g * n_cblk;
+    const int32_t c = (int32_t)cblk * kSubBlock + (int32_t)threadIdx.x;
+    const bool active = c < C;
+
+    double wa[9], wb[9], ba = 0.0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        wa[k] = active ? (double)w0[(int64_t)k * C + c] : 0.0;
+        wb[k] = active ? (double)w1[(int64_t)k * C + c] : 0.0;
+    }
+    if (active && b0) ba = (double)b0[c];
+
+    double gw0[9], gw1[9], gb0 = 0.0, gb1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) gw0[k] = gw1[k] = 0.0;
+
+    const uint32_t grow = (uint32_t)F2 * C * 4;
+    for (uint32_t j = g; j < n_tiles; j += G) {
+        const uint32_t ft = j % n_ft, rest = j / n_ft;
+        const uint32_t rt = rest % n_rt, b = rest / n_rt;
+        const int32_t t0 = (int32_t)rt * kBQR, f0 = (int32_t)ft * kBQC;  // first quad row / column
+        const int32_t len = (int32_t)item_length(lengths, b, T);
+        const int32_t hvalid = min(T1, (len + 1) / 2);  // h rows below this are unmasked
+
+        __syncthreads();  // every thread is done with the previous tile's patch
+        const float* xb = x + (int64_t)b * T * F;
+        for (int i = threadIdx.x; i < kBPatchRows * kBPatchCols; i += kSubBlock) {
+            const int r = i / kBPatchCols, q = i % kBPatchCols;
+            const int32_t t = 4 * t0 - 1 + r, f = 4 * f0 - 1 + q;
+            patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? (double)xb[(int64_t)t * F + f] : 0.0;
+        }
+        __syncthreads();
+        if (!active) continue;
+
+        const rsrc_t gr = make_rsrc(dy + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * grow);
+        const uint32_t coff = (uint32_t)c * 4;
+        double gc[kBQR + 1];  // dy column f' for quad rows t0 .. t0+QR
+#pragma unroll
+        for (int q = 0; q <= kBQR; ++q)
+            gc[q] = (double)__uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(gr, (uint32_t)(t0 + q) * grow + (uint32_t)f0 * C * 4 + coff, 0, 0));
+        const int32_t ncols = min(kBQC, F2 - f0);
+        for (int s = 0; s < ncols; ++s) {
+            const int32_t f = f0 + s;
+            const bool next_ok = f + 1 < F2;     // dy column f'+1 exists
+            const bool cok = 2 * f + 1 < F1;     // h column 2f'+1 exists
+            double gn[kBQR + 1];
+#pragma unroll
+            for (int q = 0; q <= kBQR; ++q) {
+                const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    gr, (uint32_t)(t0 + q) * grow + (uint32_t)(f + 1) * C * 4 + coff, 0, 0));
+                gn[q] = next_ok ? (double)v : 0.0;
+            }
+#pragma unroll
+            for (int q = 0; q < kBQR; ++q) {
+                const double g00 = gc[q], g01 = gn[q], g10 = gc[q + 1], g11 = gn[q + 1];
+                gb1 += g00;
+                const int32_t r0 = 2 * (t0 + q);  // h rows r0, r0 + 1
+                if (r0 >= hvalid) continue;       // both h rows masked: no other term
+                const bool v1 = r0 + 1 < hvalid;
+                double P[5][5];
+#pragma unroll
+                for (int a = 0; a < 5; ++a)
+#pragma unroll
+                    for (int e = 0; e < 5; ++e) P[a][e] = patch[4 * q + a][4 * s + e];
+                // h row r0 is unmasked here; row r0 + 1 may not be, and then
+                // none of its terms is formed (its mel rows may be anything).
+                double z00 = ba, z01 = ba, z10 = 0.0, z11 = 0.0;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        z00 = __builtin_fma(P[i][k], wa[3 * i + k], z00);
+                        z01 = __builtin_fma(P[i][2 + k], wa[3 * i + k], z01);
+                    }
+                if (v1) {
+                    z10 = ba;
+                    z11 = ba;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int k = 0; k < 3; ++k) {
+                            z10 = __builtin_fma(P[2 + i][k], wa[3 * i + k], z10);
+                            z11 = __builtin_fma(P[2 + i][2 + k], wa[3 * i + k], z11);
+                        }
+                }
+                const bool m00 = z00 > 0.0, m01 = cok && z01 > 0.0;
+                const bool m10 = v1 && z10 > 0.0, m11 = v1 && cok && z11 > 0.0;
+                const double h00 = m00 ? z00 : 0.0, h01 = m01 ? z01 : 0.0;
+                const double h10 = m10 ? z10 : 0.0, h11 = m11 ? z11 : 0.0;
+                // depthwise stage: weight gradient from the (h, dy) pairs of this quad
+                gw1[4] = __builtin_fma(g00, h00, gw1[4]);
+                gw1[5] = __builtin_fma(g00, h01, gw1[5]);
+                gw1[3] = __builtin_fma(g01, h01, gw1[3]);
+                gw1[7] = __builtin_fma(g00, h10, gw1[7]);
+                gw1[1] = __builtin_fma(g10, h10, gw1[1]);
+                gw1[8] = __builtin_fma(g00, h11, gw1[8]);
+                gw1[6] = __builtin_fma(g01, h11, gw1[6]);
+                gw1[2] = __builtin_fma(g10, h11, gw1[2]);
+                gw1[0] = __builtin_fma(g11, h11, gw1[0]);
+                // gradient at h, then through the ReLU and the mask
+                const double dh00 = g00 * wb[4];
+                const double dh01 = __builtin_fma(g01, wb[3], g00 * wb[5]);
+                const double dz00 = m00 ? dh00 : 0.0, dz01 = m01 ? dh01 : 0.0;
+                gb0 += dz00 + dz01;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        gw0[3 * i + k] =
+                            __builtin_fma(dz01, P[i][2 + k], __builtin_fma(dz00, P[i][k], gw0[3 * i + k]));
+                if (v1) {
+                    const double dh10 = __builtin_fma(g10, wb[1], g00 * wb[7]);
+                    const double dh11 =
+                        __builtin_fma(g11, wb[0], __builtin_fma(g10, wb[2], __builtin_fma(g01, wb[6], g00 * wb[8])));
+                    const double dz10 = m10 ? dh10 : 0.0, dz11 = m11 ? dh11 : 0.0;
+                    gb0 += dz10 + dz11;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int k = 0; k < 3; ++k)
+                            gw0[3 * i + k] = __builtin_fma(dz11, P[2 + i][2 + k],
+                                                           __builtin_fma(dz10, P[2 + i][k], gw0[3 * i + k]));
+                }
+            }
+#pragma unroll
+            for (int q = 0; q <= kBQR; ++q) gc[q] = gn[q];
+        }
+    }
+    if (!active) return;
+    double* out = partial + (int64_t)g * kFrontGrads * C + c;
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        out[(int64_t)k * C] = gw0[k];
+        out[(int64_t)(10 + k) * C] = gw1[k];
+    }
+    out[(int64_t)9 * C] = gb0;
+    out[(int64_t)19 * C] = gb1;
+}
+
+struct FrontBwdGrid {
+    uint32_t n_rt, n_ft, n_tiles, G;
+};
+
+static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F) {
+    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
+    FrontBwdGrid g;
+    g.n_rt = (uint32_t)((T2 + kBQR - 1) / kBQR);
+    g.n_ft = (uint32_t)((F2 + kBQC - 1) / kBQC);
+    const uint64_t n = (uint64_t)B * g.n_rt * g.n_ft;
+    g.n_tiles = (uint32_t)n;
+    g.G = (uint32_t)(n < DWSUB_BWD_WGS ? n : DWSUB_BWD_WGS);
+    return g;
+}
+
+bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C) {
+    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
+    if ((T2 + kBQR + 1) * F2 * C * 4 >= ((int64_t)1 << 31)) return false;
+    if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28) || C >= ((int64_t)1 << 24)) return false;
+    return (uint64_t)B * ((T2 + kBQR - 1) / kBQR) * ((F2 + kBQC - 1) / kBQC) < ((uint64_t)1 << 31);
+}
+
+size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C) {
+    const int64_t P = front_bwd_grid(B, T, F).G;
+    const int64_t ch = partial_reduce_chunks(P);
+    return (size_t)((P + (ch > 0 ? ch : 1)) * kFrontGrads * C * (int64_t)sizeof(double));
+}
+
+hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
+                                  const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1,
+                                  float* db1, void* workspace, int64_t B, int64_t T, int64_t F, int64_t C,
+                                  hipStream_t st) {
+    const int64_t T1 = (T + 1) / 2, F1 = (F + 1) / 2, T2 = (T1 + 1) / 2, F2 = (F1 + 1) / 2;
+    const FrontBwdGrid g = front_bwd_grid(B, T, F);
+    const uint32_t n_cblk = (uint32_t)((C + kSubBlock - 1) / kSubBlock);
+    double* partial = (double*)workspace;
+    if (g.G > 0) {
+        hipLaunchKernelGGL(dwsub_fused_bwd_kernel, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st, x, w0, b0, w1,
+                           lengths, dy, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1,
+                           (int32_t)T2, (int32_t)F2, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    RowOutputs out = {};
+    out.n = 4;
+    out.p[0] = dw0; out.first[0] = 0; out.count[0] = 9;
+    out.p[1] = db0; out.first[1] = 9; out.count[1] = 1;
+    out.p[2] = dw1; out.first[2] = 10; out.count[2] = 9;
+    out.p[3] = db1; out.first[3] = 19; out.count[3] = 1;
+    return launch_partial_reduce(partial, g.G, kFrontGrads, C, partial + (int64_t)g.G * kFrontGrads * C, out, st);
+}
+
 }  // namespace dw

@@ -9,6 +9,16 @@
 
 namespace dw {
 
+// Outputs of a partial reduction: output s receives rows
+// [first[s], first[s] + count[s]) of the K rows, as [count[s]][C] floats.
+struct RowOutputs {
+    float* p[4];
+    int32_t first[4];
+    int32_t count[4];
+    int32_t n;
+};
+
+
 // Largest vector width V <= max_vec (channels per access, a power of two)
 // such that C is a multiple of V and every pointer given is aligned to V
 // elements.
@@ -28,6 +38,15 @@ hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* 
                                   const float* b1, const int32_t* lengths, float* y,
                                   int64_t B, int64_t T, int64_t F, int64_t C, hipStream_t stream);
 
+bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C);
+
+size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C);
+
+hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
+                                  const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1,
+                                  float* db1, void* workspace, int64_t B, int64_t T, int64_t F, int64_t C,
+                                  hipStream_t stream);
+
 bool dwconv2d_fits(int64_t B, int64_t T, int64_t F, int64_t C, int vec);
 
 hipError_t launch_dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths,
@@ -35,6 +54,15 @@ hipError_t launch_dwconv2d_fwd(const float* x, const float* w, const float* bias
                                hipStream_t stream);
 
 size_t dwconv2d_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C);
+
+// Number of fp64 [K][C] rows of scratch launch_partial_reduce needs after the
+// P partial rows (at least one).
+int64_t partial_reduce_chunks(int64_t P);
+
+// Sum a [P][K][C] fp64 partial matrix over P in a fixed order; chunk_sum is
+// scratch of max(1, partial_reduce_chunks(P)) rows of K*C doubles.
+hipError_t launch_partial_reduce(const double* partial, int64_t P, int32_t K, int64_t C, double* chunk_sum,
+                                 RowOutputs out, hipStream_t stream);
 
 hipError_t launch_dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy,
                                float* dx, float* dw, float* db, void* workspace,

@@ -12,6 +12,8 @@
  *                    "What does this PR do", first kernel)
  *   dwconv2d_fwd     the general depthwise conv2d with pre/post masking
  *                    (PR #16114, "What does this PR do", second kernel)
+ *   dwsub_fused_bwd  the front's parameter gradients dw0, db0, dw1, db1
+ *                    (same section: the kernels serve the training step)
  *   dwconv2d_bwd     its backward: dx, dw, db (same section)
  *
  * Conventions shared by every entry point
@@ -115,6 +117,41 @@ dw_status dwconv1d_fwd(const void *x, const void *w, const void *bias, const int
 dw_status dwsub_fused_fwd(const float *x, const float *w0, const float *b0,
                           const float *w1, const float *b1, const int32_t *lengths,
                           float *y, int64_t B, int64_t T, int64_t F, int64_t C, void *stream);
+
+/*
+ * Bytes of device workspace dwsub_fused_bwd needs for these sizes (0 for
+ * invalid sizes).
+ */
+size_t dwsub_fused_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C);
+
+/*
+ * dwsub_fused_bwd -- gradients of dwsub_fused_fwd with respect to its
+ * parameters, for the training step (NeMo PR #16114, "What does this PR
+ * do": the fused kernels speed up the encoder's forward and backward).  The
+ * mel input needs no gradient.  With z = conv0(x) + b0 before the ReLU, h
+ * and y as in dwsub_fused_fwd, and dy [B][T2][F2][C]:
+ *   db1[c]     = sum dy
+ *   dw1[i,j,c] = sum_{b,t2,f2} dy[b,t2,f2,c] * h[b, 2t2+i-1, 2f2+j-1, c]
+ *   dh         = the depthwise stage's input gradient (dy gathered through w1)
+ *   dz         = dh where t1 < ceil(len_b/2) and z > 0, else 0
+ *   db0[c]     = sum dz
+ *   dw0[i,j,c] = sum_{b,t1,f1} dz[b,t1,f1,c] * x[b, 2t1+i-1, 2f1+j-1]
+ * h is recomputed on chip and never written.  z, h, dh, dz and every sum are
+ * carried in fp64 (the ReLU derivative's decision on the sign of z is then
+ * taken as a full-precision reference takes it), and the sums are added in a
+ * fixed order, so repeated calls give bitwise-identical results.
+ *
+ * x: [B][T][F] float; w0, w1: [3][3][C]; b0: [C] or NULL; lengths: [B] or
+ * NULL; dy: [B][T2][F2][C]; dw0, dw1: [3][3][C]; db0, db1: [C] (float, any of
+ * the four may be NULL).  workspace: device memory of at least
+ * dwsub_fused_bwd_workspace_bytes(...) bytes, contents ignored on entry.
+ * Errors: DW_ERR_INVALID_ARG for a null x, w0, w1 or dy that holds elements
+ * or a negative size; DW_ERR_WORKSPACE for a missing or short workspace.
+ */
+dw_status dwsub_fused_bwd(const float *x, const float *w0, const float *b0, const float *w1,
+                          const int32_t *lengths, const float *dy, float *dw0, float *db0, float *dw1,
+                          float *db1, void *workspace, size_t workspace_bytes,
+                          int64_t B, int64_t T, int64_t F, int64_t C, void *stream);
 
 /*
  * dwconv2d_fwd -- depthwise conv2d with pre- and post-masking (NeMo PR

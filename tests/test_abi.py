@@ -31,6 +31,9 @@ def lib():
     lib.dwconv2d_bwd_workspace_bytes.argtypes = [i64] * 8
     lib.dwconv2d_bwd_workspace_bytes.restype = sz
     lib.dwconv2d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 8 + [vp]
+    lib.dwsub_fused_bwd_workspace_bytes.argtypes = [i64] * 4
+    lib.dwsub_fused_bwd_workspace_bytes.restype = sz
+    lib.dwsub_fused_bwd.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [vp]
     return lib
 
 
@@ -42,8 +45,8 @@ def declared_functions():
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
-    for f in ("dwconv1d_fwd", "dwsub_fused_fwd", "dwconv2d_fwd", "dwconv2d_bwd",
-              "dwconv2d_bwd_workspace_bytes", "dw_abi_version", "dw_last_error"):
+    for f in ("dwconv1d_fwd", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
+              "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dw_abi_version", "dw_last_error"):
         assert f in names
 
 
@@ -86,6 +89,22 @@ def test_dwsub_fused_validation(lib):
     assert f(P, P, N, P, N, N, P, 4, 100, 80, 256, N) == INVALID and "alias" in err(lib)
     assert f(P, P, N, P, N, N, Q, 4, -1, 80, 256, N) == INVALID
     assert f(P, P, N, P, N, N, Q, 0, 100, 80, 256, N) == OK
+
+
+def test_dwsub_fused_bwd_validation(lib):
+    ws = lib.dwsub_fused_bwd_workspace_bytes
+    need = ws(4, 1000, 80, 256)
+    assert need > 0 and ws(-1, 10, 10, 4) == 0
+    f = lib.dwsub_fused_bwd
+    R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    args = (4, 1000, 80, 256, N)
+    assert f(P, P, N, P, N, Q, R, N, N, N, W, need - 1, *args) == WORKSPACE and "workspace" in err(lib)
+    assert f(P, P, N, P, N, Q, R, N, N, N, N, need, *args) == WORKSPACE
+    assert f(N, P, N, P, N, Q, R, N, N, N, W, need, *args) == INVALID
+    assert f(P, P, N, P, N, N, R, N, N, N, W, need, *args) == INVALID
+    assert f(P, N, N, P, N, Q, R, N, N, N, W, need, *args) == INVALID
+    assert f(P, P, N, P, N, Q, R, N, N, N, W, need, 4, -1, 80, 256, N) == INVALID
+    assert f(P, P, N, P, N, Q, N, N, N, N, N, 0, *args) == OK  # nothing requested
 
 
 def test_dwconv2d_fwd_validation(lib):

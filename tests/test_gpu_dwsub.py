@@ -87,3 +87,73 @@ def test_front_full_size():
     f["L"] = f["lengths"].to(DEV)
     say("dwsub_fused_fwd full [4,1000,80] -> [4,250,20,256]")
     assert_parity(run(f), ref(f), TOL_F32, "front full")
+
+
+# ------------------------------------------------------------- backward -----
+
+def make_bwd(B, T, F, C, lens=None, seed=0):
+    f = make(B, T, F, C, lens=lens, seed=seed)
+    T2, F2 = lib().out_len(lib().out_len(T)), lib().out_len(lib().out_len(F))
+    f["dy"] = datagen.normal((B, T2, F2, C), 1.0, f"gsb/dy/{B}/{T}/{F}/{C}/{seed}", device=DEV)
+    return f
+
+
+def run_bwd(f, x=None, need=("dw0", "db0", "dw1", "db1"), b0="b0", L="L", workspace=None):
+    g = lib().dwsub_fused_bwd(f["x"] if x is None else x, f["w0"], f[b0] if b0 else None, f["w1"],
+                              f[L] if L else None, f["dy"], need=need, workspace=workspace)
+    torch.cuda.synchronize()
+    return g
+
+
+def ref_bwd(f, b0=True, L=True):
+    C = f["w0"].shape[2]
+    return oracle.dwsub_front_bwd(f["x"], f["w0"], f["b0"] if b0 else torch.zeros(C), f["w1"],
+                                  f["lengths"] if L else None, f["dy"])
+
+
+def check_bwd(got, ref, what):
+    for name, g, r in zip(("dw0", "db0", "dw1", "db1"), got, ref):
+        assert_parity(g, r, TOL_F32, f"{what} {name}")
+
+
+@pytest.mark.parametrize("B,T,F,C", SHAPES)
+def test_bwd_grid(B, T, F, C):
+    f = make_bwd(B, T, F, C, lens=datagen.int_uniform(B, 0, T + 2, f"gsb/{B}/{T}/{F}/{C}"))
+    say(f"dwsub_fused_bwd B={B} T={T} F={F} C={C} lengths={f['lengths'].tolist()}")
+    check_bwd(run_bwd(f), ref_bwd(f), "front bwd")
+    check_bwd(run_bwd(f, b0=None, L=None), ref_bwd(f, b0=False, L=False), "front bwd, null b0 and lengths")
+
+
+def test_bwd_subsets_repeatable_and_masked_rows_never_read():
+    B, T, F, C = 3, 40, 24, 64
+    f = make_bwd(B, T, F, C, lens=[40, 13, 0])
+    full = run_bwd(f)
+    again = run_bwd(f)
+    for a, b in zip(full, again):
+        assert torch.equal(a, b)
+    only = run_bwd(f, need=("dw1",))
+    assert only[0] is None and only[1] is None and only[3] is None and torch.equal(only[2], full[2])
+    xp = f["x"].clone()
+    xp[1, 14:] = float("nan")  # ceil(13/2) = 7 unmasked h rows read mel rows < 14
+    xp[2] = float("nan")
+    for a, b in zip(full, run_bwd(f, x=xp)):
+        assert torch.equal(a, b)
+
+
+def test_bwd_short_workspace_raises_and_empty_batch_is_zero():
+    f = make_bwd(2, 16, 12, 8)
+    need = lib().dwsub_fused_bwd_workspace_bytes(2, 16, 12, 8)
+    with pytest.raises(lib().DwconvError, match="workspace"):
+        run_bwd(f, workspace=torch.empty(need - 8, dtype=torch.uint8, device=DEV))
+    outs = [torch.full(s, 3.0, device=DEV) for s in ((3, 3, 8), (8,), (3, 3, 8), (8,))]
+    lib().dwsub_fused_bwd(f["x"][:0], f["w0"], f["b0"], f["w1"], f["L"][:0], f["dy"][:0], *outs)
+    torch.cuda.synchronize()
+    assert all(torch.all(o == 0) for o in outs)
+
+
+def test_bwd_front_full_size():
+    f = datagen.fused_front(device=DEV)
+    f["L"] = f["lengths"].to(DEV)
+    f["dy"] = datagen.normal((4, 250, 20, 256), 1.0, "c2/dy", device=DEV)
+    say("dwsub_fused_bwd full [4,1000,80], dy [4,250,20,256]")
+    check_bwd(run_bwd(f), ref_bwd(f), "front bwd full")
