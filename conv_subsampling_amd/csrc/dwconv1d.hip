@@ -128,20 +128,30 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_anyk_kernel(
 
 // Time-tile length per thread for each specialised width (register window of
 // TT + K - 1 channel vectors).
+// Time-tile length per thread (outputs per thread; the register window holds
+// TT + K - 1 channel vectors).  Chosen per width from measurements on MI355X:
+// short tiles re-read more halo through L2, long tiles hold more registers.
 #ifndef DW1D_TILE
-#define DW1D_TILE 8
+#define DW1D_TILE 0  // 0: the per-width choice below; otherwise one tile for every width
 #endif
-#ifndef DW1D_TILE_WIDE
-#define DW1D_TILE_WIDE 4  // time tile for 8-wide (16-byte bf16) channel vectors
-#endif
-template <int K, int V = 4>
-constexpr int tile_1d() { return V >= 8 ? DW1D_TILE_WIDE : DW1D_TILE; }
+template <int K>
+constexpr int tile_1d_f32() { return DW1D_TILE > 0 ? DW1D_TILE : (K <= 3 ? 4 : K == 4 ? 6 : K <= 9 ? 8 : 12); }
+template <int K>
+constexpr int tile_1d_bf16() { return DW1D_TILE > 0 ? DW1D_TILE : (K <= 4 ? 8 : 12); }
 constexpr int kTileAnyK = 8;
 
-static int tile_for(int64_t K, int vec) {
-    const bool wide = vec >= 8;
+// (The tile depends on the storage type and K only, so host and device agree
+// for every vector width.)
+template <typename S, int K, int V>
+constexpr int tile_of() { return sizeof(S) == 2 ? tile_1d_bf16<K>() : tile_1d_f32<K>(); }
+
+static int tile_for(int64_t K, bool bf16) {
     switch (K) {
-        case 3: case 4: case 5: case 9: case 15: return wide ? tile_1d<3, 8>() : tile_1d<3, 4>();
+        case 3: return bf16 ? tile_of<uint16_t, 3, 4>() : tile_of<float, 3, 4>();
+        case 4: return bf16 ? tile_of<uint16_t, 4, 4>() : tile_of<float, 4, 4>();
+        case 5: return bf16 ? tile_of<uint16_t, 5, 4>() : tile_of<float, 5, 4>();
+        case 9: return bf16 ? tile_of<uint16_t, 9, 4>() : tile_of<float, 9, 4>();
+        case 15: return bf16 ? tile_of<uint16_t, 15, 4>() : tile_of<float, 15, 4>();
         default: return kTileAnyK;
     }
 }
@@ -149,8 +159,8 @@ static int tile_for(int64_t K, int vec) {
 bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec) {
     // Per-item byte offsets, including the left padding as a negative
     // offset, must stay within a signed 32-bit range.
-    if ((T + K) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
-    const int64_t tt = tile_for(K, vec);
+    if ((T + K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    const int64_t tt = tile_for(K, elem_bytes == 2);
     const int64_t per_item = ((T + tt - 1) / tt) * (C / vec);
     const int64_t blocks = B * ((per_item + kBlock1d - 1) / kBlock1d);
     return blocks < ((int64_t)1 << 31);
@@ -159,7 +169,7 @@ bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
 template <typename S, int V>
 static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int32_t* lengths, S* y,
                                int64_t B, int64_t T, int64_t C, int64_t K, int64_t pL, hipStream_t st) {
-    const int tt = tile_for(K, V);
+    const int tt = tile_for(K, sizeof(S) == 2);
     const uint32_t n_tiles = (uint32_t)((T + tt - 1) / tt);
     const uint32_t CG = (uint32_t)(C / V);
     const uint32_t bpi = (uint32_t)(((uint64_t)n_tiles * CG + kBlock1d - 1) / kBlock1d);
@@ -167,7 +177,7 @@ static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int3
     const int32_t T32 = (int32_t)T, C32 = (int32_t)C, p32 = (int32_t)pL;
 #define DW1D_CASE(KK)                                                                            \
     case KK:                                                                                     \
-        hipLaunchKernelGGL((dwconv1d_fwd_kernel<S, V, KK, tile_1d<KK, V>()>), grid, block, 0, st, x, \
+        hipLaunchKernelGGL((dwconv1d_fwd_kernel<S, V, KK, tile_of<S, KK, V>()>), grid, block, 0, st, x, \
                            w, bias, lengths, y, T32, C32, p32, n_tiles, CG, bpi);                  \
         break;
     switch (K) {

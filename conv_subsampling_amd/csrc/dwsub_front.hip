@@ -260,6 +260,19 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
         const int32_t len = (int32_t)item_length(lengths, b, T);
         const int32_t hvalid = min(T1, (len + 1) / 2);  // h rows below this are unmasked
 
+        // The tile's gradients dy[t0 .. t0+QR, f0 .. f0+QC], all loaded at once
+        // (rows past T2 read zero through the buffer; column f0+QC past F2 is
+        // zeroed below), so their latency overlaps the patch staging.
+        const rsrc_t gr = make_rsrc(dy + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * grow);
+        const uint32_t coff = (uint32_t)(active ? c : 0) * 4;
+        float gt[kBQR + 1][kBQC + 1];
+#pragma unroll
+        for (int q = 0; q <= kBQR; ++q)
+#pragma unroll
+            for (int e = 0; e <= kBQC; ++e)
+                gt[q][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    gr, (uint32_t)(t0 + q) * grow + (uint32_t)(f0 + e) * C * 4 + coff, 0, 0));
+
         __syncthreads();  // every thread is done with the previous tile's patch
         const float* xb = x + (int64_t)b * T * F;
         for (int i = threadIdx.x; i < kBPatchRows * kBPatchCols; i += kSubBlock) {
@@ -270,25 +283,19 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
         __syncthreads();
         if (!active) continue;
 
-        const rsrc_t gr = make_rsrc(dy + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * grow);
-        const uint32_t coff = (uint32_t)c * 4;
         double gc[kBQR + 1];  // dy column f' for quad rows t0 .. t0+QR
 #pragma unroll
-        for (int q = 0; q <= kBQR; ++q)
-            gc[q] = (double)__uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(gr, (uint32_t)(t0 + q) * grow + (uint32_t)f0 * C * 4 + coff, 0, 0));
+        for (int q = 0; q <= kBQR; ++q) gc[q] = (double)gt[q][0];
         const int32_t ncols = min(kBQC, F2 - f0);
-        for (int s = 0; s < ncols; ++s) {
+#pragma unroll
+        for (int s = 0; s < kBQC; ++s) {
+            if (s >= ncols) break;
             const int32_t f = f0 + s;
             const bool next_ok = f + 1 < F2;     // dy column f'+1 exists
             const bool cok = 2 * f + 1 < F1;     // h column 2f'+1 exists
             double gn[kBQR + 1];
 #pragma unroll
-            for (int q = 0; q <= kBQR; ++q) {
-                const float v = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    gr, (uint32_t)(t0 + q) * grow + (uint32_t)(f + 1) * C * 4 + coff, 0, 0));
-                gn[q] = next_ok ? (double)v : 0.0;
-            }
+            for (int q = 0; q <= kBQR; ++q) gn[q] = next_ok ? (double)gt[q][s + 1] : 0.0;
 #pragma unroll
             for (int q = 0; q < kBQR; ++q) {
                 const double g00 = gc[q], g01 = gn[q], g10 = gc[q + 1], g11 = gn[q + 1];

@@ -3,7 +3,8 @@
 // K*C sums per workgroup); the result is its sum over P, rounded to float and
 // written to up to four outputs, each taking a range of the K rows.
 //
-// Two levels, so that enough workgroups share the reading: level 1 sums
+// Up to 2048 partials are summed in one pass (16 sub-rows per column).
+// Beyond that, two levels, so that enough workgroups share the reading: level 1 sums
 // chunks of up to kSumChunk partial rows and writes one fp64 row per chunk;
 // level 2 sums the chunk rows.  Each level's workgroup is kSumRows sub-rows x
 // kSumCols columns: sub-row q adds rows q, q + kSumRows, ... of its chunk,
@@ -56,6 +57,35 @@ __global__ __launch_bounds__(kSumCols* kSumRows) void partial_reduce2_kernel(
     }
 }
 
+// One pass for up to kOnePassMax partials: kOnePassRows sub-rows x kSumCols
+// columns per workgroup, sub-row q adding rows q, q + kOnePassRows, ...
+constexpr int kOnePassRows = 16, kOnePassMax = 2048;
+
+__global__ __launch_bounds__(kSumCols* kOnePassRows) void partial_reduce_onepass_kernel(
+    const double* __restrict__ partial, RowOutputs out, int32_t K, int32_t C, int32_t P) {
+    __shared__ double acc[kOnePassRows][kSumCols];
+    const int32_t ncol = K * C;
+    const int32_t lane = threadIdx.x % kSumCols, sub = threadIdx.x / kSumCols;
+    const int32_t col = blockIdx.x * kSumCols + lane;
+    double s = 0.0;
+    if (col < ncol) {
+#pragma unroll 4
+        for (int32_t r = sub; r < P; r += kOnePassRows) s += partial[(int64_t)r * ncol + col];
+    }
+    acc[sub][lane] = s;
+    __syncthreads();
+    if (sub != 0 || col >= ncol) return;
+    double t = acc[0][lane];
+#pragma unroll
+    for (int q = 1; q < kOnePassRows; ++q) t += acc[q][lane];
+    const int32_t k = col / C, c = col % C;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        if (o < out.n && out.p[o] && k >= out.first[o] && k < out.first[o] + out.count[o])
+            out.p[o][(int64_t)(k - out.first[o]) * C + c] = (float)t;
+    }
+}
+
 int64_t partial_reduce_chunks(int64_t P) { return (P + kSumChunk - 1) / kSumChunk; }
 
 hipError_t launch_partial_reduce(const double* partial, int64_t P, int32_t K, int64_t C, double* chunk_sum,
@@ -63,6 +93,11 @@ hipError_t launch_partial_reduce(const double* partial, int64_t P, int32_t K, in
     const int32_t ncol = (int32_t)(K * C);
     const int32_t nchunk = (int32_t)partial_reduce_chunks(P);
     const uint32_t ncblk = (uint32_t)((ncol + kSumCols - 1) / kSumCols);
+    if (P <= kOnePassMax) {
+        hipLaunchKernelGGL(partial_reduce_onepass_kernel, dim3(ncblk), dim3(kSumCols * kOnePassRows), 0, st, partial,
+                           out, K, (int32_t)C, (int32_t)P);
+        return hipGetLastError();
+    }
     if (nchunk > 0) {
         hipLaunchKernelGGL(partial_reduce1_kernel, dim3(ncblk, (uint32_t)nchunk), dim3(kSumCols * kSumRows), 0, st,
                            partial, chunk_sum, ncol, (int32_t)P);
