@@ -53,8 +53,9 @@ def _bind(path: str):
     lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L, _L]
     lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L]
     lib.oracle_dwsub_front_bwd.argtypes = [_F, _F, _F, _F, _I, _F, _D, _D, _D, _D, _L, _L, _L, _L]
+    lib.oracle_dwconv1d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, ctypes.c_int]
     for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd, lib.oracle_dwconv2d_bwd,
-              lib.oracle_dwsub_front_fwd, lib.oracle_dwsub_front_bwd):
+              lib.oracle_dwsub_front_fwd, lib.oracle_dwsub_front_bwd, lib.oracle_dwconv1d_bwd):
         f.restype = ctypes.c_int
     return lib
 
@@ -117,6 +118,24 @@ def dwconv1d_fwd(x, w, b, lengths, causal: bool):
     _check(_load().oracle_dwconv1d_fwd(xp, wp, bp, lp, _ptr_d(y), B, T, C, K, int(bool(causal))),
            "oracle_dwconv1d_fwd")
     return y
+
+
+def dwconv1d_bwd(x, w, lengths, dy, causal: bool, want=("dx", "dw", "db")):
+    """(dx, dw, db) of the masked, padded 1-D depthwise conv given dy [B,T,C]."""
+    xa, xp = _f32(x)
+    B, T, C = xa.shape
+    wa, wp = _f32(w)
+    K = wa.shape[0]
+    if wa.shape != (K, C):
+        raise ValueError("w must be [K, C]")
+    la, lp = _lens(lengths, B)
+    da, dp = _f32(dy, (B, T, C))
+    dx = np.empty((B, T, C), dtype=np.float64) if "dx" in want else None
+    dw = np.empty((K, C), dtype=np.float64) if "dw" in want else None
+    db = np.empty((C,), dtype=np.float64) if "db" in want else None
+    _check(_load().oracle_dwconv1d_bwd(xp, wp, lp, dp, _ptr_d(dx), _ptr_d(dw), _ptr_d(db), B, T, C, K,
+                                       int(bool(causal))), "oracle_dwconv1d_bwd")
+    return dx, dw, db
 
 
 def dwconv2d_fwd(x, w, b, lengths, stride: int = 2, pad: int = 1):

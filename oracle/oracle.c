@@ -359,3 +359,40 @@ int oracle_dwsub_front_bwd(const float *x, const float *w0, const float *b0,
     free(dh);
     return 0;
 }
+
+/*
+ * Backward of oracle_dwconv1d_fwd with respect to x, w and bias, given dy
+ * [B][T][C] (the conv module's depthwise Conv1d in training; the forward is
+ * parakeet.cpp PR #102, "What changes").  Only dy at unmasked output frames
+ * (t < len_b) flows back.  Scatter order: every unmasked dy element pushes
+ * its contribution to the K padded input frames it was computed from.
+ *   db[c]          += dy[b, t, c]
+ *   dx[b, u, c]    += dy[b, t, c] * w[k, c]      for u = t + k - pL, 0 <= u < len_b
+ *   dw[k, c]       += dy[b, t, c] * x[b, u, c]   (same u)
+ * pL as in the forward.  dx at u >= len_b stays 0 (the pre-mask's
+ * derivative).  Any of dx, dw, db may be NULL.
+ */
+int oracle_dwconv1d_bwd(const float *x, const float *w, const int32_t *lengths, const float *dy,
+                        double *dx, double *dw, double *db, long B, long T, long C, long K, int causal)
+{
+    if (B < 0 || T < 0 || C < 0 || K < 1) return -1;
+    long pL = causal ? K - 1 : (K - 1) / 2;
+    if (dx) memset(dx, 0, sizeof(double) * (size_t)(B * T * C));
+    if (dw) memset(dw, 0, sizeof(double) * (size_t)(K * C));
+    if (db) memset(db, 0, sizeof(double) * (size_t)C);
+    for (long b = 0; b < B; ++b) {
+        long len = clamp_len(lengths, b, T);
+        for (long t = 0; t < len; ++t)
+            for (long c = 0; c < C; ++c) {
+                double g = (double)dy[(b * T + t) * C + c];
+                if (db) db[c] += g;
+                for (long k = 0; k < K; ++k) {
+                    long u = t + k - pL;
+                    if (u < 0 || u >= len) continue;
+                    if (dx) dx[(b * T + u) * C + c] += g * (double)w[k * C + c];
+                    if (dw) dw[k * C + c] += g * (double)x[(b * T + u) * C + c];
+                }
+            }
+    }
+    return 0;
+}

@@ -45,6 +45,10 @@ BATTERY = [
     (P.test_front_bwd_matches_torch_autograd, (3, 13, 9, 3)),
     (P.test_front_bwd_closed_forms_and_linearity, ()),
     (P.test_front_bwd_masked_input_rows_never_read, ()),
+    (P.test_1d_bwd_matches_torch_autograd, (3, 7, 8, 4, True)),
+    (P.test_1d_bwd_matches_torch_autograd, (2, 50, 3, 15, False)),
+    (P.test_1d_bwd_adjoint_closed_forms_and_masks, ()),
+    (P.test_1d_bwd_finite_differences_in_w, ()),
 ]
 
 

@@ -63,6 +63,14 @@ MUTANTS = [
      "if (dw1) dw1[(i * 3 + j) * C + c] += g * z[q];"),
     ("front bwd dw0 taps transposed", "dw0[(i * 3 + j) * C + c] += dz * (double)x[(b * T + t) * F + f];",
      "dw0[(j * 3 + i) * C + c] += dz * (double)x[(b * T + t) * F + f];"),
+    ("1d bwd dx with unflipped taps", "if (dx) dx[(b * T + u) * C + c] += g * (double)w[k * C + c];",
+     "if (dx) dx[(b * T + u) * C + c] += g * (double)w[(K - 1 - k) * C + c];"),
+    ("1d bwd dy beyond the length used", "        for (long t = 0; t < len; ++t)\n            for (long c = 0; c < C; ++c) {\n                double g = (double)dy[(b * T + t) * C + c];",
+     "        for (long t = 0; t < T; ++t)\n            for (long c = 0; c < C; ++c) {\n                double g = (double)dy[(b * T + t) * C + c];"),
+    ("1d bwd x beyond the length used", "if (u < 0 || u >= len) continue;\n                    if (dx) dx[(b * T + u) * C + c]",
+     "if (u < 0 || u >= T) continue;\n                    if (dx) dx[(b * T + u) * C + c]"),
+    ("1d bwd pad side swapped", "    long pL = causal ? K - 1 : (K - 1) / 2;\n    if (dx) memset(dx, 0, sizeof(double) * (size_t)(B * T * C));",
+     "    long pL = causal ? 0 : (K - 1) / 2;\n    if (dx) memset(dx, 0, sizeof(double) * (size_t)(B * T * C));"),
     ("front bwd b0 left out of the recompute", "acc += b0 ? (double)b0[c] : 0.0;\n                    size_t q",
      "size_t q"),
 ]

@@ -532,3 +532,76 @@ def test_front_bwd_masked_input_rows_never_read():
     xp[1, 10:] = np.nan
     for a, b_ in zip(g, oracle.dwsub_front_bwd(xp, w0, b0, w1, lengths, dy)):
         assert np.array_equal(a, b_)
+
+
+# ------------------------------------------------------ 1-D backward -----
+
+def torch_dwconv1d_grads(x, w, b, lengths, dy, causal):
+    B, T, C = x.shape
+    K = w.shape[0]
+    L = eff_len(lengths, B, T)
+    tmask = (torch.arange(T)[None, :] < torch.as_tensor(L)[:, None])[:, :, None]
+    xt = torch.from_numpy(x.astype(np.float64)).requires_grad_(True)
+    wt = torch.from_numpy(w.astype(np.float64)).requires_grad_(True)
+    bt = torch.from_numpy(b.astype(np.float64)).requires_grad_(True)
+    xm = torch.where(tmask, xt, torch.zeros(())).permute(0, 2, 1)
+    pL = K - 1 if causal else (K - 1) // 2
+    xm = Fn.pad(xm, (pL, K - 1 - pL))
+    y = Fn.conv1d(xm, wt.t()[:, None, :], bt, groups=C).permute(0, 2, 1)
+    y = torch.where(tmask, y, torch.zeros(()))
+    (y * torch.from_numpy(dy.astype(np.float64))).sum().backward()
+    return xt.grad.numpy(), wt.grad.numpy(), bt.grad.numpy()
+
+
+@pytest.mark.parametrize("B,T,C,K,causal", GRID_1D)
+def test_1d_bwd_matches_torch_autograd(B, T, C, K, causal):
+    r = rng(50 + B * 100 + T + K)
+    x = f32(r.standard_normal((B, T, C)))
+    w = f32(r.standard_normal((K, C)))
+    b = f32(r.standard_normal(C))
+    dy = f32(r.standard_normal((B, T, C)))
+    for lengths in (None, r.integers(-2, T + 3, B).astype(np.int32)):
+        got = oracle.dwconv1d_bwd(x, w, lengths, dy, causal)
+        ref = torch_dwconv1d_grads(x, w, b, lengths, dy, causal)
+        for g_, r_ in zip(got, ref):
+            close(g_, r_)
+
+
+def test_1d_bwd_adjoint_closed_forms_and_masks():
+    r = rng(51)
+    B, T, C, K = 3, 30, 4, 9
+    x = f32(r.standard_normal((B, T, C)))
+    w = f32(r.standard_normal((K, C)))
+    dy = f32(r.standard_normal((B, T, C)))
+    lengths = np.array([30, 11, 0], np.int32)
+    for causal in (False, True):
+        dx, dw, db = oracle.dwconv1d_bwd(x, w, lengths, dy, causal)
+        y_nb = oracle.dwconv1d_fwd(x, w, None, lengths, causal)
+        mask = (np.arange(T)[None, :] < lengths[:, None])[:, :, None]
+        g = dy.astype(np.float64) * mask
+        inner = np.sum(g * y_nb)
+        close(np.sum(dx * x.astype(np.float64)), inner, 1e-10)      # adjoint in x
+        close(np.sum(dw * w.astype(np.float64)), inner, 1e-10)      # bilinear in (x, w)
+        close(db, g.sum(axis=(0, 1)))                               # db = masked sum of dy
+        assert np.all(dx[1, 11:] == 0) and np.all(dx[2] == 0)
+        xn, dyn = x.copy(), dy.copy()
+        xn[1, 11:] = np.nan
+        dyn[1, 11:] = np.nan
+        dyn[2] = np.nan
+        for a, b_ in zip((dx, dw, db), oracle.dwconv1d_bwd(xn, w, lengths, dyn, causal)):
+            assert np.array_equal(a, b_)
+
+
+def test_1d_bwd_finite_differences_in_w():
+    r = rng(52)
+    B, T, C, K = 2, 20, 3, 5
+    x = f32(r.standard_normal((B, T, C)))
+    w = f32(r.integers(-4, 5, (K, C)) / 4.0)
+    dy = f32(r.standard_normal((B, T, C)))
+    lengths = np.array([20, 13], np.int32)
+    _, dw, _ = oracle.dwconv1d_bwd(x, w, lengths, dy, True)
+    loss = lambda ww: float(np.sum(oracle.dwconv1d_fwd(x, ww, None, lengths, True) * dy.astype(np.float64)))
+    for idx in itertools.product(range(K), range(C)):
+        e = np.zeros_like(w)
+        e[idx] = 0.5
+        assert abs((loss(w + e) - loss(w - e)) - dw[idx]) <= 1e-9 * (1 + abs(dw[idx]))
