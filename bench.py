@@ -9,6 +9,7 @@ size, on synthetic inputs resident in HBM:
   conv1d  dwconv1d_fwd      [16,750,1024] K=9 symmetric                 bf16 storage
   sweep   dwconv1d_fwd      [32,1500,512] causal, K = 3, 4, 5, 9, 15    fp32
           dwconv1d_fwd      [32,1500,200] causal, K = 9                 fp32
+          dwconv1d_bwd      dx, dw, db of [32,1500,512] causal K = 9    fp32, fp64 sums
   stage   dwconv2d_fwd      [32,1500,64,256] -> [32,750,32,256]         fp32
           dwconv2d_bwd      dx, dw, db of the same                      fp32
 
@@ -80,6 +81,15 @@ def work_conv1d(c, es):
     rd = sum(L) * C * es + (K * C + C) * es + 4 * B
     wr = B * T * C * es
     flops = 2 * K * C * sum(L)
+    return rd, wr, flops
+
+
+def work_conv1d_bwd(c):
+    B, T, C, K = c["B"], c["T"], c["C"], c["K"]
+    L = clamp_lengths(c["lengths"].tolist(), T)
+    rd = 2 * sum(L) * C * 4 + K * C * 4 + 4 * B   # x and dy at unmasked frames, w, lengths
+    wr = B * T * C * 4 + (K + 1) * C * 4           # dx (zeros past the length), dw, db
+    flops = 2 * K * C * sum(L) * 2 + C * sum(L)
     return rd, wr, flops
 
 
@@ -177,6 +187,20 @@ def build_rows(dev):
             *work_conv1d(s, 4),
             (lambda s=s, sL=sL, sy=sy: dw.dwconv1d_fwd(s["x"], s["w"], s["b"], sL, y=sy, causal=True)))
 
+    s9 = sweep[3]
+    assert s9["K"] == 9 and s9["C"] == 512
+    s9["dy"] = datagen.normal((s9["B"], s9["T"], s9["C"]), 1.0, "c4/dy/K9/C512", device=dev)
+    s9L = s9["lengths"].to(dev)
+    bdx = torch.empty_like(s9["x"])
+    bdw = torch.empty((9, s9["C"]), device=dev)
+    bdb = torch.empty((s9["C"],), device=dev)
+    bws = torch.empty((dw.dwconv1d_bwd_workspace_bytes(s9["B"], s9["T"], s9["C"], 9),), dtype=torch.uint8,
+                      device=dev)
+    add("conv1d_bwd_K9_C512", "dwconv1d_bwd", "dx,dw,db of [32,1500,512] K9 causal fp32, fp64 sums",
+        s9["B"] * s9["T"], *work_conv1d_bwd(s9),
+        lambda: dw.dwconv1d_bwd(s9["x"], s9["w"], s9L, s9["dy"], dx=bdx, dw=bdw, db=bdb, workspace=bws,
+                                causal=True))
+
     g = datagen.conv2d_stage(device=dev)
     gL = g["lengths"].to(dev)
     gy = torch.empty((g["B"], 750, 32, g["C"]), device=dev)
@@ -209,6 +233,8 @@ def cpu_baseline(data, target_s: float):
     for s in data["sweep"]:
         hs = hp(s)
         hs["x"] = s["x"]
+        if "dy" in s:
+            hs["dy"] = s["dy"]
         sweep.append(hs)
 
     def one_pass(n):
@@ -239,6 +265,12 @@ def cpu_baseline(data, target_s: float):
             oracle.dwconv1d_fwd(xs, s["w"], s["b"], s["lengths"][:m], True)
             secs += time.perf_counter() - t
             frames += m * s["T"]
+            if "dy" in s:
+                dys = host(s["dy"], m)
+                t = time.perf_counter()
+                oracle.dwconv1d_bwd(xs, s["w"], s["lengths"][:m], dys, True)
+                secs += time.perf_counter() - t
+                frames += m * s["T"]
         m = min(n, g["B"])
         xs, dys = host(g["x"], m), host(g["dy"], m)
         t = time.perf_counter()
@@ -377,7 +409,7 @@ def main():
         "data": "synthetic (seeded; log-mel-shaped inputs, lengths ~U[T/2,T])",
         "config": {
             "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd; conv-module dwconv1d [16,750,1024] K9 "
-                        "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 and [32,1500,200] K9; depthwise conv2d "
+                        "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; depthwise conv2d "
                         "stage [32,1500,64,256] fwd+bwd",
             "frames_per_step": frames,
             "alg_bytes_per_step": alg,

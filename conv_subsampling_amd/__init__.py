@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "DwconvError", "abi_version",
-    "dwconv1d_fwd", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
+    "dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
     "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
     "out_len",
 ]
@@ -57,6 +57,10 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dw_last_error.argtypes = []
     lib.dwconv1d_fwd.restype = _int
     lib.dwconv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp]
+    lib.dwconv1d_bwd_workspace_bytes.restype = _sz
+    lib.dwconv1d_bwd_workspace_bytes.argtypes = [_i64] * 4
+    lib.dwconv1d_bwd.restype = _int
+    lib.dwconv1d_bwd.argtypes = [_vp] * 8 + [_sz] + [_i64] * 4 + [_int, _int, _vp]
     lib.dwsub_fused_fwd.restype = _int
     lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
     lib.dwsub_fused_bwd_workspace_bytes.restype = _sz
@@ -137,6 +141,46 @@ def dwconv1d_fwd(x, w, bias=None, lengths=None, y=None, causal: bool = False):
                              DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC,
                              DW_BF16 if dt == torch.bfloat16 else DW_F32, _stream(dev)))
     return y
+
+
+def dwconv1d_bwd_workspace_bytes(B, T, C, K) -> int:
+    return int(_lib.dwconv1d_bwd_workspace_bytes(B, T, C, K))
+
+
+def dwconv1d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None, causal: bool = False,
+                 need=("dx", "dw", "db")):
+    """Gradients (dx, dw, db) of dwconv1d_fwd given dy [B,T,C] (float32)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
+    dev, f32 = x.device, torch.float32
+    B, T, C = x.shape
+    _dev_tensor("x", x, f32, dev)
+    if w.dim() != 2 or w.shape[1] != C:
+        raise ValueError("w must be [K, C]")
+    _dev_tensor("w", w, f32, dev)
+    K = w.shape[0]
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    _dev_tensor("dy", dy, f32, dev, (B, T, C))
+    if dx is None and "dx" in need:
+        dx = torch.empty_like(x)
+    if dw is None and "dw" in need:
+        dw = torch.empty((K, C), dtype=f32, device=dev)
+    if db is None and "db" in need:
+        db = torch.empty((C,), dtype=f32, device=dev)
+    _dev_tensor("dx", dx, f32, dev, (B, T, C), allow_none=True)
+    _dev_tensor("dw", dw, f32, dev, (K, C), allow_none=True)
+    _dev_tensor("db", db, f32, dev, (C,), allow_none=True)
+    ws_bytes = 0
+    if dw is not None or db is not None:
+        need_ws = dwconv1d_bwd_workspace_bytes(B, T, C, K)
+        if workspace is None:
+            workspace = torch.empty((max(need_ws, 1),), dtype=torch.uint8, device=dev)
+        _dev_tensor("workspace", workspace, torch.uint8, dev)
+        ws_bytes = workspace.numel()
+    _check(_lib.dwconv1d_bwd(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
+                             _ptr(workspace), ws_bytes, B, T, C, K,
+                             DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, DW_F32, _stream(dev)))
+    return dx, dw, db
 
 
 def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None):

@@ -67,6 +67,41 @@ dw_status dwconv1d_fwd(const void* x, const void* w, const void* bias, const int
                                             (hipStream_t)stream), fn);
 }
 
+size_t dwconv1d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t K) {
+    if (B < 0 || T < 0 || C < 0 || !dw::dwconv1d_bwd_supported(K)) return 0;
+    return dw::dwconv1d_bwd_workspace(B, T, C, K);
+}
+
+dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx, float* dw_,
+                       float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t C,
+                       int64_t K, dw_pad pad, dw_dtype dtype, void* stream) {
+    const char* fn = "dwconv1d_bwd";
+    if (B < 0 || T < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (K < 1) return fail(DW_ERR_INVALID_ARG, "%s: kernel width K=%lld must be >= 1", fn, (long long)K);
+    if (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL) return fail(DW_ERR_INVALID_ARG, "%s: unknown pad mode %d", fn, (int)pad);
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    if (dtype != DW_F32) return fail(DW_ERR_UNSUPPORTED, "%s: only float32 storage is implemented", fn);
+    if (!dw::dwconv1d_bwd_supported(K))
+        return fail(DW_ERR_UNSUPPORTED, "%s: kernel width K=%lld has no backward kernel (3, 4, 5, 7, 9, 15, 31)", fn, (long long)K);
+    const bool want_wb = dw_ || db;
+    if (!dx && !want_wb) return ok();
+    if (C == 0) return ok();
+    if ((!x && B * T > 0) || (!dy && B * T > 0) || !w)
+        return fail(DW_ERR_INVALID_ARG, "%s: x, w and dy must not be NULL (unless empty)", fn);
+    if (dx && (dx == x || dx == dy)) return fail(DW_ERR_INVALID_ARG, "%s: dx must not alias x or dy", fn);
+    if (want_wb) {
+        const size_t need = dw::dwconv1d_bwd_workspace(B, T, C, K);
+        if (!workspace || workspace_bytes < need)
+            return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
+    }
+    if (!dw::dwconv1d_bwd_fits(B, T, C, K)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    const void* ptrs[5] = {x, w, dy, dx, dw_};
+    const int vec = dw::pick_vec(C, 4, ptrs, 5, dw::dwconv1d_bwd_max_vec(K));
+    return from_hip(dw::launch_dwconv1d_bwd((const float*)x, (const float*)w, lengths, (const float*)dy, (float*)dx,
+                                            dw_, db, workspace, B, T, C, K, pad == DW_PAD_CAUSAL, vec,
+                                            (hipStream_t)stream), fn);
+}
+
 dw_status dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,
                           const int32_t* lengths, float* y, int64_t B, int64_t T, int64_t F, int64_t C,
                           void* stream) {

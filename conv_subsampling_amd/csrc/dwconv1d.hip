@@ -227,4 +227,206 @@ int pick_vec(int64_t C, int elem_bytes, const void* const* ptrs, int nptrs, int 
     return 1;
 }
 
+
+// ---------------------------------------------------------------------------
+// Backward of the 1-D depthwise conv (the conv module in training): with
+// g = dy at unmasked frames (t < len) and 0 elsewhere,
+//   dx[u, c] = [u < len] sum_k g[u + pL - k, c] w[k, c]
+//   dw[k, c] = sum_{b,u} g[u + pL - k, c] x[u, c]      (x masked at u >= len)
+//   db[c]    = sum_{b,t} g[t, c]
+// Gather form, no atomics: the thread that owns input frame u forms dx[u]
+// and every (g, x[u]) pair of dw, so each pair is counted once.  One thread
+// owns V channels of TT input frames; a register window holds the TT + K - 1
+// gradient frames those need (through the same length-bounded buffer
+// resources as the forward, which give the masks and the padding).  dw and
+// db are accumulated in fp64 (the fp32 products are exact there), summed
+// across the workgroup's 4 time sub-blocks in a fixed order, and written as
+// one partial per persistent workgroup for the fixed-order reduction of
+// reduce.hip.
+// ---------------------------------------------------------------------------
+
+constexpr int kLanes1b = 64, kSubs1b = kBlock1d / kLanes1b;
+constexpr int kBwdTile1d = 8;
+#ifndef DW1D_BWD_WGS
+#define DW1D_BWD_WGS 256
+#endif
+
+template <int V, int K, bool CAUSAL, int TT>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
+    const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
+    uint32_t n_tb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
+    constexpr int pL = CAUSAL ? K - 1 : (K - 1) / 2;
+    __shared__ double red[kSubs1b - 1][K + 1][kLanes1b * V];
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t G = gridDim.x / n_cblk;
+    const uint32_t g = blk / n_cblk, cblk = blk - g * n_cblk;
+    const uint32_t lane = threadIdx.x % kLanes1b, sub = threadIdx.x / kLanes1b;
+    const uint32_t cg = cblk * kLanes1b + lane;
+    const bool cvalid = cg < CG;
+    const int32_t c0 = (int32_t)(cvalid ? cg : 0) * V;
+    const uint32_t row = (uint32_t)C * 4, coff = (uint32_t)c0 * 4;
+
+    Vf<V> wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
+    double gw[K][V], gb[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        gb[e] = 0.0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) gw[k][e] = 0.0;
+    }
+
+    for (uint32_t j = g; j < n_groups; j += G) {
+        const uint32_t b = j / groups_per_item;
+        const uint32_t tb = (j - b * groups_per_item) * kSubs1b + sub;
+        if (!cvalid || tb >= n_tb) continue;
+        const int32_t len = (int32_t)item_length(lengths, b, T);
+        const int32_t u0 = (int32_t)tb * TT;
+        const int64_t item = (int64_t)b * T * C;
+        const rsrc_t dxr = make_rsrc(dx ? dx + item : x, dx ? (uint32_t)T * row : 0u);
+        if (u0 >= len) {
+            // masked input frames: dx is zero, and there is nothing to add
+            if (dx) {
+#pragma unroll
+                for (int i = 0; i < TT; ++i) Buf<float, V>::store(dxr, (uint32_t)(u0 + i) * row + coff, vzero<V>());
+            }
+            continue;
+        }
+        const rsrc_t gr = make_rsrc(dy + item, (uint32_t)len * row);
+        const rsrc_t xr = make_rsrc(x + item, (uint32_t)len * row);
+        Vf<V> gwin[TT + K - 1], xv[TT];
+#pragma unroll
+        for (int r = 0; r < TT + K - 1; ++r)
+            gwin[r] = Buf<float, V>::load(gr, (uint32_t)((u0 + pL - (K - 1) + r) * (int32_t)row) + coff);
+#pragma unroll
+        for (int i = 0; i < TT; ++i) xv[i] = Buf<float, V>::load(xr, (uint32_t)(u0 + i) * row + coff);
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+            Vf<V> d = vzero<V>();
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    const float gv = gwin[i + K - 1 - k].v[e];
+                    d.v[e] = __builtin_fmaf(gv, wk[k].v[e], d.v[e]);
+                    gw[k][e] = __builtin_fma((double)gv, (double)xv[i].v[e], gw[k][e]);
+                }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                gb[e] += (double)gwin[i + K - 1 - pL].v[e];
+                d.v[e] = u0 + i < len ? d.v[e] : 0.0f;
+            }
+            if (dx) Buf<float, V>::store(dxr, (uint32_t)(u0 + i) * row + coff, d);
+        }
+    }
+
+    if (!partial) return;  // uniform: dw and db not requested
+    if (sub > 0) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) red[sub - 1][k][lane * V + e] = gw[k][e];
+            red[sub - 1][K][lane * V + e] = gb[e];
+        }
+    }
+    __syncthreads();
+    if (sub > 0 || !cvalid) return;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int32_t c = c0 + e;
+#pragma unroll
+        for (int k = 0; k <= K; ++k) {
+            double s = k < K ? gw[k][e] : gb[e];
+#pragma unroll
+            for (int q = 0; q < kSubs1b - 1; ++q) s += red[q][k][lane * V + e];
+            partial[((int64_t)g * (K + 1) + k) * C + c] = s;
+        }
+    }
+}
+
+struct Bwd1dGrid {
+    uint32_t n_tb, groups_per_item, n_groups, G;
+};
+
+static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T) {
+    Bwd1dGrid g;
+    g.n_tb = (uint32_t)((T + kBwdTile1d - 1) / kBwdTile1d);
+    g.groups_per_item = (g.n_tb + kSubs1b - 1) / kSubs1b;
+    const uint64_t n = (uint64_t)B * g.groups_per_item;
+    g.n_groups = (uint32_t)n;
+    g.G = (uint32_t)(n < DW1D_BWD_WGS ? n : DW1D_BWD_WGS);
+    return g;
+}
+
+bool dwconv1d_bwd_supported(int64_t K) {
+    return K == 3 || K == 4 || K == 5 || K == 7 || K == 9 || K == 15 || K == 31;
+}
+
+int dwconv1d_bwd_max_vec(int64_t K) { return K <= 5 ? 4 : (K <= 15 ? 2 : 1); }
+
+bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K) {
+    if ((T + K + 32) * C * 4 >= ((int64_t)1 << 31)) return false;
+    return (uint64_t)B * ((T + kBwdTile1d - 1) / kBwdTile1d) < ((uint64_t)1 << 31);
+}
+
+size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
+    const int64_t P = bwd1d_grid(B, T).G;
+    const int64_t ch = partial_reduce_chunks(P);
+    return (size_t)((P + (ch > 0 ? ch : 1)) * (K + 1) * C * (int64_t)sizeof(double));
+}
+
+template <int V, int K, bool CAUSAL>
+static hipError_t launch_bwd1d_typed(const float* x, const float* w, const int32_t* lengths, const float* dy,
+                                     float* dx, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+    const Bwd1dGrid g = bwd1d_grid(B, T);
+    const uint32_t CG = (uint32_t)(C / V);
+    const uint32_t n_cblk = (CG + kLanes1b - 1) / kLanes1b;
+    if (g.G == 0 || (!dx && !partial)) return hipSuccess;
+    hipLaunchKernelGGL((dwconv1d_bwd_kernel<V, K, CAUSAL, kBwdTile1d>), dim3(g.G * n_cblk), dim3(kBlock1d), 0, st, x,
+                       w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk, g.groups_per_item,
+                       g.n_groups);
+    return hipGetLastError();
+}
+
+template <int K, bool CAUSAL>
+static hipError_t launch_bwd1d_k(int vec, const float* x, const float* w, const int32_t* lengths, const float* dy,
+                                 float* dx, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+    constexpr int VMAX = K <= 5 ? 4 : (K <= 15 ? 2 : 1);
+    if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<(VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    if (vec >= 2 && VMAX >= 2) return launch_bwd1d_typed<(VMAX >= 2 ? 2 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    return launch_bwd1d_typed<1, K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+}
+
+hipError_t launch_dwconv1d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+                               float* dw, float* db, void* workspace, int64_t B, int64_t T, int64_t C, int64_t K,
+                               bool causal, int vec, hipStream_t st) {
+    double* partial = (dw || db) ? (double*)workspace : nullptr;
+    hipError_t e = hipSuccess;
+#define DW1B_CASE(KK)                                                                                        \
+    case KK:                                                                                                 \
+        e = causal ? launch_bwd1d_k<KK, true>(vec, x, w, lengths, dy, dx, partial, B, T, C, st)              \
+                   : launch_bwd1d_k<KK, false>(vec, x, w, lengths, dy, dx, partial, B, T, C, st);            \
+        break;
+    switch (K) {
+        DW1B_CASE(3)
+        DW1B_CASE(4)
+        DW1B_CASE(5)
+        DW1B_CASE(7)
+        DW1B_CASE(9)
+        DW1B_CASE(15)
+        DW1B_CASE(31)
+        default: return hipErrorInvalidValue;
+    }
+#undef DW1B_CASE
+    if (e != hipSuccess || !partial) return e;
+    const int64_t P = bwd1d_grid(B, T).G;
+    RowOutputs out = {};
+    out.n = 2;
+    out.p[0] = dw; out.first[0] = 0; out.count[0] = (int32_t)K;
+    out.p[1] = db; out.first[1] = (int32_t)K; out.count[1] = 1;
+    return launch_partial_reduce(partial, P, (int32_t)(K + 1), C, partial + P * (K + 1) * C, out, st);
+}
+
 }  // namespace dw

@@ -32,6 +32,16 @@ hipError_t launch_dwconv1d_fwd(const void* x, const void* w, const void* bias, c
                                void* y, int64_t B, int64_t T, int64_t C, int64_t K, int64_t pad_left,
                                bool bf16, int vec, hipStream_t stream);
 
+// 1-D backward: the widths with a kernel, the widest vector each takes, and
+// the workspace (fp64 partials) it needs.
+bool dwconv1d_bwd_supported(int64_t K);
+int dwconv1d_bwd_max_vec(int64_t K);
+bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K);
+size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K);
+hipError_t launch_dwconv1d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+                               float* dw, float* db, void* workspace, int64_t B, int64_t T, int64_t C, int64_t K,
+                               bool causal, int vec, hipStream_t stream);
+
 bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C);
 
 hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1,

@@ -7,6 +7,7 @@
  * #16114, "Use Fused Kernels for Depthwise Striding Subsampler"):
  *   dwconv1d_fwd     the Conformer conv module's depthwise Conv1d in SSM_CONV
  *                    form (PR #102, "What changes")
+ *   dwconv1d_bwd     its gradients dx, dw, db (the conv module in training)
  *   dwsub_fused_fwd  the depthwise-striding subsampler front: conv0, bias,
  *                    ReLU, time mask and depthwise conv, fused (PR #16114,
  *                    "What does this PR do", first kernel)
@@ -94,6 +95,36 @@ const char *dw_last_error(void);
 dw_status dwconv1d_fwd(const void *x, const void *w, const void *bias, const int32_t *lengths,
                        void *y, int64_t B, int64_t T, int64_t C, int64_t K,
                        dw_pad pad, dw_dtype dtype, void *stream);
+
+/*
+ * Bytes of device workspace dwconv1d_bwd needs when it computes dw or db (0
+ * for invalid sizes or a width without a backward kernel).
+ */
+size_t dwconv1d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t K);
+
+/*
+ * dwconv1d_bwd -- gradients of dwconv1d_fwd (the conv module's depthwise
+ * Conv1d in training; the forward is parakeet.cpp PR #102, "What changes").
+ * With pL as in the forward and g = dy at unmasked frames (t < len_b), 0
+ * elsewhere:
+ *   dx[b, u, c] = sum_k g[b, u + pL - k, c] * w[k, c]     for u < len_b, else 0
+ *   dw[k, c]    = sum_{b,u} g[b, u + pL - k, c] * x[b, u, c]   (x masked at u >= len_b)
+ *   db[c]       = sum_{b,t} g[b, t, c]
+ * dx is gathered (no atomics); dw and db are accumulated in fp64 and reduced
+ * in a fixed order, so repeated calls give bitwise-identical results.
+ *
+ * x, dy, dx: [B][T][C]; w: [K][C]; dx, dw ([K][C]) and db ([C], float) may be
+ * NULL (not computed).  dtype: DW_F32 only (DW_BF16 returns
+ * DW_ERR_UNSUPPORTED).  K must be one of 3, 4, 5, 7, 9, 15, 31, else
+ * DW_ERR_UNSUPPORTED.  workspace: at least dwconv1d_bwd_workspace_bytes(...)
+ * bytes of device memory when dw or db is requested.
+ * Errors: DW_ERR_INVALID_ARG for a null x, w or dy that holds elements, a
+ * negative size, K < 1, a bad enum, or dx aliasing x or dy;
+ * DW_ERR_WORKSPACE for a missing or short workspace.
+ */
+dw_status dwconv1d_bwd(const void *x, const void *w, const int32_t *lengths, const void *dy, void *dx,
+                       float *dw, float *db, void *workspace, size_t workspace_bytes,
+                       int64_t B, int64_t T, int64_t C, int64_t K, dw_pad pad, dw_dtype dtype, void *stream);
 
 /*
  * dwsub_fused_fwd -- the depthwise-striding subsampler front, fused (NeMo PR

@@ -52,7 +52,7 @@ BATTERY = [
 ]
 
 
-def main(path):
+def main(path, stop_at_first=True):
     oracle._lib = oracle._bind(path)
     failed = []
     for fn, args in BATTERY:
@@ -60,6 +60,8 @@ def main(path):
             fn(*args)
         except Exception:  # noqa: BLE001 - any failure counts as a catch
             failed.append(f"{fn.__name__}{args}: {traceback.format_exc(limit=1).splitlines()[-1]}")
+            if stop_at_first:
+                break
     for f in failed:
         print("caught by", f)
     return 1 if failed else 0

@@ -31,6 +31,9 @@ def lib():
     lib.dwconv2d_bwd_workspace_bytes.argtypes = [i64] * 8
     lib.dwconv2d_bwd_workspace_bytes.restype = sz
     lib.dwconv2d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 8 + [vp]
+    lib.dwconv1d_bwd_workspace_bytes.argtypes = [i64] * 4
+    lib.dwconv1d_bwd_workspace_bytes.restype = sz
+    lib.dwconv1d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 4 + [i, i, vp]
     lib.dwsub_fused_bwd_workspace_bytes.argtypes = [i64] * 4
     lib.dwsub_fused_bwd_workspace_bytes.restype = sz
     lib.dwsub_fused_bwd.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [vp]
@@ -45,7 +48,7 @@ def declared_functions():
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
-    for f in ("dwconv1d_fwd", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
+    for f in ("dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
               "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dw_abi_version", "dw_last_error"):
         assert f in names
 
@@ -79,6 +82,23 @@ def test_dwconv1d_validation(lib):
     assert f(N, N, N, N, N, 0, 8, 4, 3, 0, 0, N) == OK
     assert f(P, P, N, N, Q, 2, 0, 4, 3, 1, 1, N) == OK
     assert f(P, P, N, N, Q, 2, 8, 0, 3, 1, 1, N) == OK
+
+
+def test_dwconv1d_bwd_validation(lib):
+    ws = lib.dwconv1d_bwd_workspace_bytes
+    need = ws(32, 1500, 512, 9)
+    assert need > 0 and ws(32, 1500, 512, 6) == 0 and ws(-1, 10, 10, 9) == 0
+    f = lib.dwconv1d_bwd
+    R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    args = (32, 1500, 512)
+    assert f(P, P, N, Q, R, W, N, W, need, *args, 6, 1, 0, N) == UNSUPPORTED and "K=6" in err(lib)
+    assert f(P, P, N, Q, R, W, N, W, need, *args, 9, 1, 1, N) == UNSUPPORTED and "float32" in err(lib)
+    assert f(P, P, N, Q, R, W, N, W, need - 1, *args, 9, 1, 0, N) == WORKSPACE
+    assert f(P, P, N, Q, P, W, N, W, need, *args, 9, 1, 0, N) == INVALID and "alias" in err(lib)
+    assert f(N, P, N, Q, R, W, N, W, need, *args, 9, 1, 0, N) == INVALID
+    assert f(P, P, N, Q, R, W, N, W, need, *args, 0, 1, 0, N) == INVALID
+    assert f(P, P, N, Q, R, W, N, W, need, *args, 9, 5, 0, N) == INVALID
+    assert f(P, P, N, Q, N, N, N, N, 0, *args, 9, 1, 0, N) == OK  # nothing requested
 
 
 def test_dwsub_fused_validation(lib):

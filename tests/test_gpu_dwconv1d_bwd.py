@@ -1,0 +1,130 @@
+"""GPU parity of dwconv1d_bwd (through the C ABI) against the CPU oracle."""
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_util import TOL_F32, assert_exact_zero, assert_parity, say, time_mask
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda", 0)
+
+
+def lib():
+    import conv_subsampling_amd as dw
+    return dw
+
+
+def make(B, T, C, K, seed=0, lens=None):
+    tag = f"t1b/{B}/{T}/{C}/{K}/{seed}"
+    x = datagen.normal((B, T, C), 1.0, tag + "/x", device=DEV)
+    w = datagen.normal((K, C), 1.0 / K, tag + "/w", device=DEV)
+    dy = datagen.normal((B, T, C), 1.0, tag + "/dy", device=DEV)
+    if lens is None:
+        lens = datagen.int_uniform(B, 0, T, tag + "/len")
+    return x, w, dy, torch.as_tensor(lens, dtype=torch.int32).to(DEV)
+
+
+def run(x, w, L, dy, causal, need=("dx", "dw", "db"), workspace=None):
+    g = lib().dwconv1d_bwd(x, w, L, dy, causal=causal, need=need, workspace=workspace)
+    torch.cuda.synchronize()
+    return g
+
+
+def check(x, w, L, dy, causal, what):
+    B, T, C = x.shape
+    say(f"dwconv1d_bwd {what}: B={B} T={T} C={C} K={w.shape[0]} causal={causal}")
+    got = run(x, w, L, dy, causal)
+    ref = oracle.dwconv1d_bwd(x, w, L, dy, causal)
+    for name, g, r in zip(("dx", "dw", "db"), got, ref):
+        assert_parity(g, r, TOL_F32, f"{what} {name}")
+    Lh = L.cpu() if L is not None else torch.full((B,), T, dtype=torch.int32)
+    assert_exact_zero(got[0], time_mask(Lh, B, T)[:, :, None], f"{what} dx")
+    return got
+
+
+GRID = [
+    # (B, T, C, K, causal)
+    (1, 1, 4, 3, False), (3, 1, 8, 9, True), (1, 2, 4, 5, False), (3, 7, 3, 4, False), (3, 7, 3, 4, True),
+    (2, 50, 8, 15, False), (2, 50, 8, 15, True), (2, 13, 6, 7, True), (1, 33, 100, 9, False),
+    (3, 45, 200, 9, True), (2, 17, 256, 3, True), (1, 100, 1, 9, False), (2, 64, 128, 31, False),
+    (2, 70, 130, 31, True), (3, 49, 6, 9, False), (1, 300, 64, 5, False), (5, 97, 44, 5, True),
+    (2, 129, 512, 9, True),
+]
+
+
+@pytest.mark.parametrize("B,T,C,K,causal", GRID)
+def test_grid(B, T, C, K, causal):
+    x, w, dy, L = make(B, T, C, K)
+    check(x, w, L, dy, causal, "grid")
+
+
+def test_null_and_clamped_lengths():
+    B, T, C, K = 3, 40, 16, 9
+    x, w, dy, _ = make(B, T, C, K)
+    check(x, w, None, dy, False, "null lengths")
+    over = torch.tensor([T + 5, -3, 17], dtype=torch.int32, device=DEV)
+    got = run(x, w, over, dy, True)
+    ref = oracle.dwconv1d_bwd(x, w, torch.tensor([T, 0, 17], dtype=torch.int32), dy, True)
+    for g, r in zip(got, ref):
+        assert_parity(g, r, TOL_F32, "clamped lengths")
+
+
+def test_masked_frames_are_never_read():
+    B, T, C, K = 3, 60, 32, 9
+    x, w, dy, L = make(B, T, C, K, lens=[60, 21, 0])
+    full = run(x, w, L, dy, False)
+    xp, dyp = x.clone(), dy.clone()
+    xp[1, 21:] = float("nan")
+    dyp[1, 21:] = float("nan")
+    xp[2] = float("nan")
+    dyp[2] = float("nan")
+    for a, b in zip(full, run(xp, w, L, dyp, False)):
+        assert torch.equal(a, b)
+
+
+def test_subsets_and_repeatable_bitwise():
+    B, T, C, K = 4, 200, 64, 5
+    x, w, dy, L = make(B, T, C, K)
+    full = run(x, w, L, dy, True)
+    again = run(x, w, L, dy, True)
+    for a, b in zip(full, again):
+        assert torch.equal(a, b)
+    for need in (("dx",), ("dw",), ("db",), ("dw", "db")):
+        got = run(x, w, L, dy, True, need=need)
+        for name, a, b in zip(("dx", "dw", "db"), got, full):
+            assert (a is None) == (name not in need)
+            if a is not None:
+                assert torch.equal(a, b), name
+
+
+def test_unaligned_pointers_take_the_narrow_path():
+    B, T, C, K = 2, 30, 64, 5
+    x, wt, dy, L = make(B, T, C, K)
+    xs = torch.empty(B * T * C + 1, device=DEV)[1:].view(B, T, C)
+    xs.copy_(x)
+    check(xs, wt, L, dy, False, "unaligned x")
+
+
+def test_short_workspace_raises_and_empty_batch_is_zero():
+    x, w, dy, L = make(2, 16, 8, 9)
+    need = lib().dwconv1d_bwd_workspace_bytes(2, 16, 8, 9)
+    with pytest.raises(lib().DwconvError, match="workspace"):
+        run(x, w, L, dy, False, workspace=torch.empty(need - 8, dtype=torch.uint8, device=DEV))
+    dw_, db = torch.full((9, 8), 3.0, device=DEV), torch.full((8,), 3.0, device=DEV)
+    lib().dwconv1d_bwd(x[:0], w, L[:0], dy[:0], dw=dw_, db=db, need=("dw", "db"))
+    torch.cuda.synchronize()
+    assert torch.all(dw_ == 0) and torch.all(db == 0)
+
+
+def test_unsupported_width_raises():
+    x, w, dy, L = make(1, 8, 4, 6)
+    with pytest.raises(lib().DwconvError, match="K=6"):
+        run(x, w, L, dy, False)
+
+
+@pytest.mark.parametrize("K", [9, 31])
+def test_conv_module_full_size(K):
+    c = datagen.conv1d_causal_sweep(K, device=DEV)
+    dy = datagen.normal((c["B"], c["T"], c["C"]), 1.0, f"c4/dy/K{K}/C{c['C']}", device=DEV)
+    check(c["x"], c["w"], c["lengths"].to(DEV), dy, True, f"full [32,1500,512] K={K}")
