@@ -49,10 +49,10 @@ def _bind(path: str):
     """Load a build of oracle.c and declare its C signatures."""
     lib = ctypes.CDLL(path)
     lib.oracle_dwconv1d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, ctypes.c_int]
-    lib.oracle_dwconv2d_fwd.argtypes = [_F, _F, _F, _I, _D, _L, _L, _L, _L, _L, _L, _L, _L]
-    lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, _L, _L, _L, _L]
-    lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L]
-    lib.oracle_dwsub_front_bwd.argtypes = [_F, _F, _F, _F, _I, _F, _D, _D, _D, _D, _L, _L, _L, _L]
+    lib.oracle_dwconv2d_fwd.argtypes = [_F, _F, _F, _I, _D] + [_L] * 11
+    lib.oracle_dwconv2d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D] + [_L] * 11
+    lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L, ctypes.c_int]
+    lib.oracle_dwsub_front_bwd.argtypes = [_F, _F, _F, _F, _I, _F, _D, _D, _D, _D, _L, _L, _L, _L, ctypes.c_int]
     lib.oracle_dwconv1d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, ctypes.c_int]
     for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd, lib.oracle_dwconv2d_bwd,
               lib.oracle_dwsub_front_fwd, lib.oracle_dwsub_front_bwd, lib.oracle_dwconv1d_bwd):
@@ -99,9 +99,26 @@ def _check(rc, name):
         raise ValueError(f"{name}: invalid arguments")
 
 
-def conv_out_len(n: int, k: int, s: int, p: int) -> int:
-    """floor((n + 2p - k) / s) + 1, never below zero (the convolution output length)."""
-    return max(0, (n + 2 * p - k) // s + 1)
+def conv_out_len(n: int, k: int, s: int, p: int, p_hi=None) -> int:
+    """floor((n + p + p_hi - k) / s) + 1, never below zero: the convolution
+    output length with p zeros before the input and p_hi (default p) after."""
+    p_hi = p if p_hi is None else p_hi
+    return max(0, (n + p + p_hi - k) // s + 1)
+
+
+def pads_of(pad, pads):
+    """(pt0, pt1, pf0, pf1): `pads` if given, else the symmetric `pad`."""
+    if pads is None:
+        return (pad, pad, pad, pad)
+    pads = tuple(int(v) for v in pads)
+    if len(pads) != 4:
+        raise ValueError("pads must be (time before, time after, freq before, freq after)")
+    return pads
+
+
+def front_pads(causal: bool):
+    """The front's padding per axis: (before, after)."""
+    return (2, 1) if causal else (1, 1)
 
 
 def dwconv1d_fwd(x, w, b, lengths, causal: bool):
@@ -138,8 +155,9 @@ def dwconv1d_bwd(x, w, lengths, dy, causal: bool, want=("dx", "dw", "db")):
     return dx, dw, db
 
 
-def dwconv2d_fwd(x, w, b, lengths, stride: int = 2, pad: int = 1):
-    """y [B,T',F',C] of the masked depthwise conv2d; x [B,T,F,C], w [KH,KW,C]."""
+def dwconv2d_fwd(x, w, b, lengths, stride: int = 2, pad: int = 1, pads=None):
+    """y [B,T',F',C] of the masked depthwise conv2d; x [B,T,F,C], w [KH,KW,C].
+    pads = (time before, time after, freq before, freq after) overrides pad."""
     xa, xp = _f32(x)
     B, T, F, C = xa.shape
     wa, wp = _f32(w)
@@ -148,31 +166,33 @@ def dwconv2d_fwd(x, w, b, lengths, stride: int = 2, pad: int = 1):
         raise ValueError("w must be [KH, KW, C]")
     ba, bp = _f32(b, (C,))
     la, lp = _lens(lengths, B)
-    To, Fo = conv_out_len(T, KH, stride, pad), conv_out_len(F, KW, stride, pad)
+    pt0, pt1, pf0, pf1 = pads_of(pad, pads)
+    To, Fo = conv_out_len(T, KH, stride, pt0, pt1), conv_out_len(F, KW, stride, pf0, pf1)
     y = np.empty((B, To, Fo, C), dtype=np.float64)
-    _check(_load().oracle_dwconv2d_fwd(xp, wp, bp, lp, _ptr_d(y), B, T, F, C, KH, KW, stride, pad),
-           "oracle_dwconv2d_fwd")
+    _check(_load().oracle_dwconv2d_fwd(xp, wp, bp, lp, _ptr_d(y), B, T, F, C, KH, KW, stride,
+                                       pt0, pt1, pf0, pf1), "oracle_dwconv2d_fwd")
     return y
 
 
-def dwconv2d_bwd(x, w, lengths, dy, stride: int = 2, pad: int = 1, want=("dx", "dw", "db")):
+def dwconv2d_bwd(x, w, lengths, dy, stride: int = 2, pad: int = 1, want=("dx", "dw", "db"), pads=None):
     """(dx, dw, db) of the masked depthwise conv2d given dy; entries not in `want` are None."""
     xa, xp = _f32(x)
     B, T, F, C = xa.shape
     wa, wp = _f32(w)
     KH, KW = wa.shape[0], wa.shape[1]
     la, lp = _lens(lengths, B)
-    To, Fo = conv_out_len(T, KH, stride, pad), conv_out_len(F, KW, stride, pad)
+    pt0, pt1, pf0, pf1 = pads_of(pad, pads)
+    To, Fo = conv_out_len(T, KH, stride, pt0, pt1), conv_out_len(F, KW, stride, pf0, pf1)
     da, dp = _f32(dy, (B, To, Fo, C))
     dx = np.empty((B, T, F, C), dtype=np.float64) if "dx" in want else None
     dw = np.empty((KH, KW, C), dtype=np.float64) if "dw" in want else None
     db = np.empty((C,), dtype=np.float64) if "db" in want else None
     _check(_load().oracle_dwconv2d_bwd(xp, wp, lp, dp, _ptr_d(dx), _ptr_d(dw), _ptr_d(db),
-                                       B, T, F, C, KH, KW, stride, pad), "oracle_dwconv2d_bwd")
+                                       B, T, F, C, KH, KW, stride, pt0, pt1, pf0, pf1), "oracle_dwconv2d_bwd")
     return dx, dw, db
 
 
-def dwsub_front_fwd(x, w0, b0, w1, b1, lengths):
+def dwsub_front_fwd(x, w0, b0, w1, b1, lengths, causal: bool = False):
     """y [B,T2,F2,C] of the subsampler front; x [B,T,F] (one mel channel)."""
     xa, xp = _f32(x)
     B, T, F = xa.shape
@@ -184,15 +204,16 @@ def dwsub_front_fwd(x, w0, b0, w1, b1, lengths):
     w1a, w1p = _f32(w1, (3, 3, C))
     b1a, b1p = _f32(b1, (C,))
     la, lp = _lens(lengths, B)
-    T1, F1 = conv_out_len(T, 3, 2, 1), conv_out_len(F, 3, 2, 1)
-    T2, F2 = conv_out_len(T1, 3, 2, 1), conv_out_len(F1, 3, 2, 1)
+    pl, ph = front_pads(causal)
+    T1, F1 = conv_out_len(T, 3, 2, pl, ph), conv_out_len(F, 3, 2, pl, ph)
+    T2, F2 = conv_out_len(T1, 3, 2, pl, ph), conv_out_len(F1, 3, 2, pl, ph)
     y = np.empty((B, T2, F2, C), dtype=np.float64)
-    _check(_load().oracle_dwsub_front_fwd(xp, w0p, b0p, w1p, b1p, lp, _ptr_d(y), B, T, F, C),
+    _check(_load().oracle_dwsub_front_fwd(xp, w0p, b0p, w1p, b1p, lp, _ptr_d(y), B, T, F, C, int(bool(causal))),
            "oracle_dwsub_front_fwd")
     return y
 
 
-def dwsub_front_bwd(x, w0, b0, w1, lengths, dy):
+def dwsub_front_bwd(x, w0, b0, w1, lengths, dy, causal: bool = False):
     """(dw0, db0, dw1, db1) of the subsampler front given dy [B,T2,F2,C]."""
     xa, xp = _f32(x)
     B, T, F = xa.shape
@@ -203,11 +224,12 @@ def dwsub_front_bwd(x, w0, b0, w1, lengths, dy):
     b0a, b0p = _f32(b0, (C,))
     w1a, w1p = _f32(w1, (3, 3, C))
     la, lp = _lens(lengths, B)
-    T1, F1 = conv_out_len(T, 3, 2, 1), conv_out_len(F, 3, 2, 1)
-    T2, F2 = conv_out_len(T1, 3, 2, 1), conv_out_len(F1, 3, 2, 1)
+    pl, ph = front_pads(causal)
+    T1, F1 = conv_out_len(T, 3, 2, pl, ph), conv_out_len(F, 3, 2, pl, ph)
+    T2, F2 = conv_out_len(T1, 3, 2, pl, ph), conv_out_len(F1, 3, 2, pl, ph)
     da, dp = _f32(dy, (B, T2, F2, C))
     dw0, db0 = np.empty((3, 3, C)), np.empty((C,))
     dw1, db1 = np.empty((3, 3, C)), np.empty((C,))
     _check(_load().oracle_dwsub_front_bwd(xp, w0p, b0p, w1p, lp, dp, _ptr_d(dw0), _ptr_d(db0), _ptr_d(dw1),
-                                          _ptr_d(db1), B, T, F, C), "oracle_dwsub_front_bwd")
+                                          _ptr_d(db1), B, T, F, C, int(bool(causal))), "oracle_dwsub_front_bwd")
     return dw0, db0, dw1, db1

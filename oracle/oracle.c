@@ -41,11 +41,11 @@ static long floor_div(long a, long b)
     return q;
 }
 
-/* Output length of a convolution along one axis: floor((n + 2p - k)/s) + 1,
- * never below zero. */
-static long conv_out_len(long n, long k, long s, long p)
+/* Output length of a convolution along one axis with pl zeros before the
+ * input and ph after it: floor((n + pl + ph - k)/s) + 1, never below zero. */
+static long conv_out_len(long n, long k, long s, long pl, long ph)
 {
-    long o = floor_div(n + 2 * p - k, s) + 1;
+    long o = floor_div(n + pl + ph - k, s) + 1;
     return o < 0 ? 0 : o;
 }
 
@@ -97,11 +97,15 @@ int oracle_dwconv1d_fwd(const float *x, const float *w, const float *bias,
 /*
  * Depthwise 2-D convolution with length masking (NeMo PR #16114, "What does
  * this PR do": the general depthwise conv2d, with pre- and post-masking
- * fused).  For a KH x KW kernel, stride s and zero padding p on both axes:
- *   T' = floor((T + 2p - KH)/s) + 1,  F' = floor((F + 2p - KW)/s) + 1,
- *   len'_b = clamp(floor((len_b + 2p - KH)/s) + 1, 0, T')  (0 for an empty item),
+ * fused).  For a KH x KW kernel, stride s, and pt0 zero rows before the
+ * input and pt1 after it in time, pf0 and pf1 columns before and after it in
+ * frequency (pt0 = pt1 = pf0 = pf1 = p is the symmetric padding; the causal
+ * padding the same section names is read as pt0 = KH - 1, pt1 = s - 1, and
+ * likewise in frequency):
+ *   T' = floor((T + pt0 + pt1 - KH)/s) + 1,  F' = floor((F + pf0 + pf1 - KW)/s) + 1,
+ *   len'_b = clamp(floor((len_b + pt0 + pt1 - KH)/s) + 1, 0, T')  (0 for an empty item),
  *   xm[b, t, f, c] = x[b, t, f, c] if t < len_b, else 0 (pre-mask),
- *   y[b, t', f', c] = sum_{i,j} xm[b, s t' + i - p, s f' + j - p, c] * w[i, j, c]
+ *   y[b, t', f', c] = sum_{i,j} xm[b, s t' + i - pt0, s f' + j - pf0, c] * w[i, j, c]
  *                     + bias[c]                  for t' < len'_b,
  *   y[b, t', f', c] = 0                          for t' >= len'_b (post-mask),
  * where indices outside [0,T) x [0,F) read zero.
@@ -109,13 +113,14 @@ int oracle_dwconv1d_fwd(const float *x, const float *w, const float *bias,
 int oracle_dwconv2d_fwd(const float *x, const float *w, const float *bias,
                         const int32_t *lengths, double *y,
                         long B, long T, long F, long C,
-                        long KH, long KW, long s, long p)
+                        long KH, long KW, long s, long pt0, long pt1, long pf0, long pf1)
 {
-    if (B < 0 || T < 0 || F < 0 || C < 0 || KH < 1 || KW < 1 || s < 1 || p < 0) return -1;
-    long To = conv_out_len(T, KH, s, p), Fo = conv_out_len(F, KW, s, p);
+    if (B < 0 || T < 0 || F < 0 || C < 0 || KH < 1 || KW < 1 || s < 1) return -1;
+    if (pt0 < 0 || pt1 < 0 || pf0 < 0 || pf1 < 0) return -1;
+    long To = conv_out_len(T, KH, s, pt0, pt1), Fo = conv_out_len(F, KW, s, pf0, pf1);
     for (long b = 0; b < B; ++b) {
         long len = clamp_len(lengths, b, T);
-        long leno = conv_out_len(len, KH, s, p);
+        long leno = conv_out_len(len, KH, s, pt0, pt1);
         if (leno > To) leno = To;
         if (len == 0) leno = 0;
         for (long to = 0; to < To; ++to)
@@ -124,10 +129,10 @@ int oracle_dwconv2d_fwd(const float *x, const float *w, const float *bias,
                     double acc = 0.0;
                     if (to < leno) {
                         for (long i = 0; i < KH; ++i) {
-                            long t = s * to + i - p;
+                            long t = s * to + i - pt0;
                             if (t < 0 || t >= len) continue; /* padding or pre-masked */
                             for (long j = 0; j < KW; ++j) {
-                                long f = s * fo + j - p;
+                                long f = s * fo + j - pf0;
                                 if (f < 0 || f >= F) continue;
                                 acc += (double)x[((b * T + t) * F + f) * C + c] *
                                        (double)w[(i * KW + j) * C + c];
@@ -151,21 +156,23 @@ int oracle_dwconv2d_fwd(const float *x, const float *w, const float *bias,
  *                                                        the pre-mask's derivative)
  *   dw[i, j, c]    += dy[b, t', f', c] * xm[b, t, f, c]
  *   db[c]          += dy[b, t', f', c]
- * with t = s t' + i - p, f = s f' + j - p.  Any of dx, dw, db may be NULL.
+ * with t = s t' + i - pt0, f = s f' + j - pf0 (pads as in the forward).  Any
+ * of dx, dw, db may be NULL.
  */
 int oracle_dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths,
                         const float *dy, double *dx, double *dw, double *db,
                         long B, long T, long F, long C,
-                        long KH, long KW, long s, long p)
+                        long KH, long KW, long s, long pt0, long pt1, long pf0, long pf1)
 {
-    if (B < 0 || T < 0 || F < 0 || C < 0 || KH < 1 || KW < 1 || s < 1 || p < 0) return -1;
-    long To = conv_out_len(T, KH, s, p), Fo = conv_out_len(F, KW, s, p);
+    if (B < 0 || T < 0 || F < 0 || C < 0 || KH < 1 || KW < 1 || s < 1) return -1;
+    if (pt0 < 0 || pt1 < 0 || pf0 < 0 || pf1 < 0) return -1;
+    long To = conv_out_len(T, KH, s, pt0, pt1), Fo = conv_out_len(F, KW, s, pf0, pf1);
     if (dx) memset(dx, 0, sizeof(double) * (size_t)(B * T * F * C));
     if (dw) memset(dw, 0, sizeof(double) * (size_t)(KH * KW * C));
     if (db) memset(db, 0, sizeof(double) * (size_t)C);
     for (long b = 0; b < B; ++b) {
         long len = clamp_len(lengths, b, T);
-        long leno = conv_out_len(len, KH, s, p);
+        long leno = conv_out_len(len, KH, s, pt0, pt1);
         if (leno > To) leno = To;
         if (len == 0) leno = 0;
         for (long to = 0; to < leno; ++to)
@@ -174,10 +181,10 @@ int oracle_dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths,
                     double g = (double)dy[((b * To + to) * Fo + fo) * C + c];
                     if (db) db[c] += g;
                     for (long i = 0; i < KH; ++i) {
-                        long t = s * to + i - p;
+                        long t = s * to + i - pt0;
                         if (t < 0 || t >= len) continue;
                         for (long j = 0; j < KW; ++j) {
-                            long f = s * fo + j - p;
+                            long f = s * fo + j - pf0;
                             if (f < 0 || f >= F) continue;
                             size_t xi = (size_t)(((b * T + t) * F + f) * C + c);
                             size_t wi = (size_t)((i * KW + j) * C + c);
@@ -193,30 +200,36 @@ int oracle_dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths,
 /*
  * The depthwise-striding subsampler front (NeMo PR #16114, "What does this
  * PR do": mel input [B,T,F,1] -> conv0 [B,T/2,F/2,256] -> ReLU -> masking ->
- * conv_dw1 [B,T/4,F/4,256]).  Computed unfused, stage by stage, with the
- * intermediate h held in memory:
- *   T1 = floor((T-1)/2) + 1,  F1 = floor((F-1)/2) + 1,  L1_b = ceil(len_b / 2)
- *   h[b,t1,f1,c] = max(0, sum_{i,j<3} xz[b, 2t1+i-1, 2f1+j-1] * w0[i,j,c] + b0[c])
+ * conv_dw1 [B,T/4,F/4,256]).  Both convolutions pad every axis with pl zeros
+ * before and one after: pl = 1 is the symmetric padding, pl = 2 the causal
+ * mode (the section's "extra padding layer", read as K - 1 = 2 zeros before
+ * and stride - 1 = 1 after).  Computed unfused, stage by stage, with h held
+ * in memory:
+ *   T1 = floor((T+pl-2)/2) + 1,  F1 = floor((F+pl-2)/2) + 1,
+ *   L1_b = floor((len_b+pl-2)/2) + 1 (0 for an empty item): ceil(len_b/2)
+ *          for pl = 1, floor(len_b/2) + 1 for pl = 2
+ *   h[b,t1,f1,c] = max(0, sum_{i,j<3} xz[b, 2t1+i-pl, 2f1+j-pl] * w0[i,j,c] + b0[c])
  *                  for t1 < L1_b, and 0 for t1 >= L1_b (the time mask)
- *   T2 = floor((T1-1)/2) + 1,  F2 = floor((F1-1)/2) + 1
- *   y[b,t2,f2,c] = sum_{i,j<3} hz[b, 2t2+i-1, 2f2+j-1, c] * w1[i,j,c] + b1[c]
+ *   T2 = floor((T1+pl-2)/2) + 1,  F2 = floor((F1+pl-2)/2) + 1
+ *   y[b,t2,f2,c] = sum_{i,j<3} hz[b, 2t2+i-pl, 2f2+j-pl, c] * w1[i,j,c] + b1[c]
  * where xz and hz read zero outside their extents.  The mel input is not
  * length-masked and the output is not masked: the only mask in the chain is
  * the one after the ReLU.
  */
 int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
                            const float *w1, const float *b1, const int32_t *lengths,
-                           double *y, long B, long T, long F, long C)
+                           double *y, long B, long T, long F, long C, int causal)
 {
     if (B < 0 || T < 0 || F < 0 || C < 0) return -1;
-    long T1 = conv_out_len(T, 3, 2, 1), F1 = conv_out_len(F, 3, 2, 1);
-    long T2 = conv_out_len(T1, 3, 2, 1), F2 = conv_out_len(F1, 3, 2, 1);
+    long pl = causal ? 2 : 1;
+    long T1 = conv_out_len(T, 3, 2, pl, 1), F1 = conv_out_len(F, 3, 2, pl, 1);
+    long T2 = conv_out_len(T1, 3, 2, pl, 1), F2 = conv_out_len(F1, 3, 2, pl, 1);
     size_t hn = (size_t)(T1 * F1 * C);
     double *h = (double *)malloc(sizeof(double) * (hn ? hn : 1));
     if (!h) return -1;
     for (long b = 0; b < B; ++b) {
         long len = clamp_len(lengths, b, T);
-        long L1 = (len + 1) / 2;
+        long L1 = len > 0 ? conv_out_len(len, 3, 2, pl, 1) : 0;
         /* stage 1: conv0 (one input channel to C), bias, ReLU, time mask */
         for (long t1 = 0; t1 < T1; ++t1)
             for (long f1 = 0; f1 < F1; ++f1)
@@ -225,10 +238,10 @@ int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
                     if (t1 < L1) {
                         double acc = 0.0;
                         for (long i = 0; i < 3; ++i) {
-                            long t = 2 * t1 + i - 1;
+                            long t = 2 * t1 + i - pl;
                             if (t < 0 || t >= T) continue;
                             for (long j = 0; j < 3; ++j) {
-                                long f = 2 * f1 + j - 1;
+                                long f = 2 * f1 + j - pl;
                                 if (f < 0 || f >= F) continue;
                                 acc += (double)x[(b * T + t) * F + f] * (double)w0[(i * 3 + j) * C + c];
                             }
@@ -244,10 +257,10 @@ int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
                 for (long c = 0; c < C; ++c) {
                     double acc = 0.0;
                     for (long i = 0; i < 3; ++i) {
-                        long t1 = 2 * t2 + i - 1;
+                        long t1 = 2 * t2 + i - pl;
                         if (t1 < 0 || t1 >= T1) continue;
                         for (long j = 0; j < 3; ++j) {
-                            long f1 = 2 * f2 + j - 1;
+                            long f1 = 2 * f2 + j - pl;
                             if (f1 < 0 || f1 >= F1) continue;
                             acc += h[(t1 * F1 + f1) * C + c] * (double)w1[(i * 3 + j) * C + c];
                         }
@@ -267,23 +280,25 @@ int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
  * gradient.  With z = conv0(x) + b0 (before the ReLU) and h as in
  * oracle_dwsub_front_fwd, given dy [B][T2][F2][C]:
  *   db1[c]      = sum dy[b,t2,f2,c]
- *   dw1[i,j,c]  = sum dy[b,t2,f2,c] * hz[b, 2t2+i-1, 2f2+j-1, c]
- *   dh[b,t1,f1,c] = sum over (t2,i,f2,j) with t1 = 2t2+i-1, f1 = 2f2+j-1 of
+ *   dw1[i,j,c]  = sum dy[b,t2,f2,c] * hz[b, 2t2+i-pl, 2f2+j-pl, c]
+ *   dh[b,t1,f1,c] = sum over (t2,i,f2,j) with t1 = 2t2+i-pl, f1 = 2f2+j-pl of
  *                   dy[b,t2,f2,c] * w1[i,j,c]
  *   dz          = dh where t1 < L1_b and z > 0, else 0 (ReLU and mask)
  *   db0[c]      = sum dz
- *   dw0[i,j,c]  = sum dz[b,t1,f1,c] * xz[b, 2t1+i-1, 2f1+j-1]
- * Computed unfused: z, h and dh are materialised per item, dh in scatter
- * order.  Any output pointer may be NULL.
+ *   dw0[i,j,c]  = sum dz[b,t1,f1,c] * xz[b, 2t1+i-pl, 2f1+j-pl]
+ * (pl, T1 and L1 as in the forward).  Computed unfused: z, h and dh are
+ * materialised per item, dh in scatter order.  Any output pointer may be
+ * NULL.
  */
 int oracle_dwsub_front_bwd(const float *x, const float *w0, const float *b0,
                            const float *w1, const int32_t *lengths, const float *dy,
                            double *dw0, double *db0, double *dw1, double *db1,
-                           long B, long T, long F, long C)
+                           long B, long T, long F, long C, int causal)
 {
     if (B < 0 || T < 0 || F < 0 || C < 0) return -1;
-    long T1 = conv_out_len(T, 3, 2, 1), F1 = conv_out_len(F, 3, 2, 1);
-    long T2 = conv_out_len(T1, 3, 2, 1), F2 = conv_out_len(F1, 3, 2, 1);
+    long pl = causal ? 2 : 1;
+    long T1 = conv_out_len(T, 3, 2, pl, 1), F1 = conv_out_len(F, 3, 2, pl, 1);
+    long T2 = conv_out_len(T1, 3, 2, pl, 1), F2 = conv_out_len(F1, 3, 2, pl, 1);
     size_t hn = (size_t)(T1 * F1 * C);
     double *z = (double *)malloc(sizeof(double) * (hn ? hn : 1));
     double *h = (double *)malloc(sizeof(double) * (hn ? hn : 1));
@@ -295,17 +310,17 @@ int oracle_dwsub_front_bwd(const float *x, const float *w0, const float *b0,
     if (db1) memset(db1, 0, sizeof(double) * (size_t)C);
     for (long b = 0; b < B; ++b) {
         long len = clamp_len(lengths, b, T);
-        long L1 = (len + 1) / 2;
+        long L1 = len > 0 ? conv_out_len(len, 3, 2, pl, 1) : 0;
         /* forward again: z = conv0(x) + b0, h = mask * ReLU(z) */
         for (long t1 = 0; t1 < T1; ++t1)
             for (long f1 = 0; f1 < F1; ++f1)
                 for (long c = 0; c < C; ++c) {
                     double acc = 0.0;
                     for (long i = 0; i < 3; ++i) {
-                        long t = 2 * t1 + i - 1;
+                        long t = 2 * t1 + i - pl;
                         if (t < 0 || t >= T) continue;
                         for (long j = 0; j < 3; ++j) {
-                            long f = 2 * f1 + j - 1;
+                            long f = 2 * f1 + j - pl;
                             if (f < 0 || f >= F) continue;
                             acc += (double)x[(b * T + t) * F + f] * (double)w0[(i * 3 + j) * C + c];
                         }
@@ -323,10 +338,10 @@ int oracle_dwsub_front_bwd(const float *x, const float *w0, const float *b0,
                     double g = (double)dy[((b * T2 + t2) * F2 + f2) * C + c];
                     if (db1) db1[c] += g;
                     for (long i = 0; i < 3; ++i) {
-                        long t1 = 2 * t2 + i - 1;
+                        long t1 = 2 * t2 + i - pl;
                         if (t1 < 0 || t1 >= T1) continue;
                         for (long j = 0; j < 3; ++j) {
-                            long f1 = 2 * f2 + j - 1;
+                            long f1 = 2 * f2 + j - pl;
                             if (f1 < 0 || f1 >= F1) continue;
                             size_t q = (size_t)((t1 * F1 + f1) * C + c);
                             if (dw1) dw1[(i * 3 + j) * C + c] += g * h[q];
@@ -344,10 +359,10 @@ int oracle_dwsub_front_bwd(const float *x, const float *w0, const float *b0,
                     if (db0) db0[c] += dz;
                     if (!dw0) continue;
                     for (long i = 0; i < 3; ++i) {
-                        long t = 2 * t1 + i - 1;
+                        long t = 2 * t1 + i - pl;
                         if (t < 0 || t >= T) continue;
                         for (long j = 0; j < 3; ++j) {
-                            long f = 2 * f1 + j - 1;
+                            long f = 2 * f1 + j - pl;
                             if (f < 0 || f >= F) continue;
                             dw0[(i * 3 + j) * C + c] += dz * (double)x[(b * T + t) * F + f];
                         }

@@ -33,6 +33,12 @@ BATTERY = [
     (P.test_2d_matches_torch_grouped_conv, (1, 12, 4, 5, 5, 3, 3, 2)),
     (P.test_2d_center_delta_closed_form, ()),
     (P.test_2d_masked_rows_exact_zero_and_no_nan_leak, ()),
+    (P.test_2d_asymmetric_pads_match_torch, (2, 9, 8, 3, 3, 3, 2, (2, 1, 2, 1))),
+    (P.test_2d_asymmetric_pads_match_torch, (2, 12, 10, 2, 3, 3, 2, (1, 0, 0, 2))),
+    (P.test_2d_causal_pads_never_look_ahead, ()),
+    (P.test_2d_causal_present_tap_closed_form, ()),
+    (P.test_bwd_asymmetric_pads_match_torch_autograd, (2, 9, 8, 3, 3, 3, 2, (2, 1, 2, 1))),
+    (P.test_bwd_asymmetric_pads_match_torch_autograd, (2, 12, 10, 2, 3, 3, 2, (1, 0, 0, 2))),
     (P.test_bwd_matches_torch_autograd, (2, 9, 8, 3, 3, 3, 2, 1)),
     (P.test_bwd_matches_torch_autograd, (1, 12, 4, 5, 5, 3, 3, 2)),
     (P.test_bwd_adjoint_and_bilinear_identities, ()),
@@ -41,6 +47,10 @@ BATTERY = [
     (P.test_front_center_delta_closed_form, ()),
     (P.test_front_fully_masked_rows_equal_output_bias, ()),
     (P.test_front_input_is_not_length_masked, ()),
+    (P.test_front_causal_matches_torch_chain, (3, 13, 9, 3)),
+    (P.test_front_causal_present_tap_and_no_look_ahead, ()),
+    (P.test_front_causal_empty_item_is_output_bias, ()),
+    (P.test_front_causal_bwd_matches_torch_autograd, (3, 13, 9, 3)),
     (P.test_front_bwd_matches_torch_autograd, (2, 16, 12, 4)),
     (P.test_front_bwd_matches_torch_autograd, (3, 13, 9, 3)),
     (P.test_front_bwd_closed_forms_and_linearity, ()),

@@ -28,11 +28,26 @@ MUTANTS = [
     ("1d batch axis scrambled", "xp[s] = (t >= 0 && t < len) ? (double)x[(b * T + t) * C + c] : 0.0;",
      "xp[s] = (t >= 0 && t < len) ? (double)x[(((B - 1 - b)) * T + t) * C + c] : 0.0;"),
     ("length not clamped", "    if (l > T) l = T;\n", "\n"),
-    ("2d stride ignored in time", "long t = s * to + i - p;\n                            if (t < 0 || t >= len) continue; /* padding or pre-masked */",
-     "long t = to + i - p;\n                            if (t < 0 || t >= len) continue; /* padding or pre-masked */"),
+    ("2d stride ignored in time", "long t = s * to + i - pt0;\n                            if (t < 0 || t >= len) continue; /* padding or pre-masked */",
+     "long t = to + i - pt0;\n                            if (t < 0 || t >= len) continue; /* padding or pre-masked */"),
+    ("2d time pad taken from the wrong side", "long t = s * to + i - pt0;\n                            if (t < 0 || t >= len) continue; /* padding or pre-masked */",
+     "long t = s * to + i - pt1;\n                            if (t < 0 || t >= len) continue; /* padding or pre-masked */"),
+    ("2d frequency pad taken from time", "                                long f = s * fo + j - pf0;",
+     "                                long f = s * fo + j - pt0;"),
+    ("2d bwd frequency pad from the wrong side", "                            long f = s * fo + j - pf0;\n                            if (f < 0 || f >= F) continue;\n                            size_t xi",
+     "                            long f = s * fo + j - pf1;\n                            if (f < 0 || f >= F) continue;\n                            size_t xi"),
+    ("output length doubles the pad before", "long o = floor_div(n + pl + ph - k, s) + 1;", "long o = floor_div(n + 2 * pl - k, s) + 1;"),
+    ("2d empty item not masked", "        if (leno > To) leno = To;\n        if (len == 0) leno = 0;\n        for (long to = 0; to < To; ++to)",
+     "        if (leno > To) leno = To;\n        for (long to = 0; to < To; ++to)"),
+    ("front causal mode pads symmetrically", "    long pl = causal ? 2 : 1;\n    long T1 = conv_out_len(T, 3, 2, pl, 1), F1 = conv_out_len(F, 3, 2, pl, 1);\n    long T2 = conv_out_len(T1, 3, 2, pl, 1), F2 = conv_out_len(F1, 3, 2, pl, 1);\n    size_t hn = (size_t)(T1 * F1 * C);\n    double *h",
+     "    long pl = 1;\n    long T1 = conv_out_len(T, 3, 2, pl, 1), F1 = conv_out_len(F, 3, 2, pl, 1);\n    long T2 = conv_out_len(T1, 3, 2, pl, 1), F2 = conv_out_len(F1, 3, 2, pl, 1);\n    size_t hn = (size_t)(T1 * F1 * C);\n    double *h"),
+    ("front causal mask ceil(len/2)", "long L1 = len > 0 ? conv_out_len(len, 3, 2, pl, 1) : 0;", "long L1 = (len + 1) / 2;"),
+    ("front empty item not masked", "long L1 = len > 0 ? conv_out_len(len, 3, 2, pl, 1) : 0;", "long L1 = conv_out_len(len, 3, 2, pl, 1);"),
+    ("front bwd causal pads symmetric", "    long pl = causal ? 2 : 1;\n    long T1 = conv_out_len(T, 3, 2, pl, 1), F1 = conv_out_len(F, 3, 2, pl, 1);\n    long T2 = conv_out_len(T1, 3, 2, pl, 1), F2 = conv_out_len(F1, 3, 2, pl, 1);\n    size_t hn = (size_t)(T1 * F1 * C);\n    double *z",
+     "    long pl = 1;\n    long T1 = conv_out_len(T, 3, 2, pl, 1), F1 = conv_out_len(F, 3, 2, pl, 1);\n    long T2 = conv_out_len(T1, 3, 2, pl, 1), F2 = conv_out_len(F1, 3, 2, pl, 1);\n    size_t hn = (size_t)(T1 * F1 * C);\n    double *z"),
     ("2d pre-mask dropped", "if (t < 0 || t >= len) continue; /* padding or pre-masked */",
      "if (t < 0 || t >= T) continue; /* padding or pre-masked */"),
-    ("2d post-mask length floor", "        long leno = conv_out_len(len, KH, s, p);\n        if (leno > To) leno = To;\n        if (len == 0) leno = 0;\n        for (long to = 0; to < To; ++to)",
+    ("2d post-mask length floor", "        long leno = conv_out_len(len, KH, s, pt0, pt1);\n        if (leno > To) leno = To;\n        if (len == 0) leno = 0;\n        for (long to = 0; to < To; ++to)",
      "        long leno = len / 2;\n        if (leno > To) leno = To;\n        if (len == 0) leno = 0;\n        for (long to = 0; to < To; ++to)"),
     ("2d taps transposed", "                                       (double)w[(i * KW + j) * C + c];",
      "                                       (double)w[(j * KH + i) * C + c];"),
@@ -44,17 +59,17 @@ MUTANTS = [
      "if (dx) dx[xi] += g * (double)w[((KH - 1 - i) * KW + (KW - 1 - j)) * C + c];"),
     ("bwd db counted per tap", "                    if (db) db[c] += g;\n                    for (long i = 0; i < KH; ++i) {",
      "                    for (long i = 0; i < KH; ++i) {\n                        if (db) db[c] += g;"),
-    ("bwd dw misses the pre-mask", "                        long t = s * to + i - p;\n                        if (t < 0 || t >= len) continue;\n                        for (long j = 0; j < KW; ++j) {\n                            long f = s * fo + j - p;\n                            if (f < 0 || f >= F) continue;\n                            size_t xi",
-     "                        long t = s * to + i - p;\n                        if (t < 0 || t >= T) continue;\n                        for (long j = 0; j < KW; ++j) {\n                            long f = s * fo + j - p;\n                            if (f < 0 || f >= F) continue;\n                            size_t xi"),
+    ("bwd dw misses the pre-mask", "                        long t = s * to + i - pt0;\n                        if (t < 0 || t >= len) continue;\n                        for (long j = 0; j < KW; ++j) {\n                            long f = s * fo + j - pf0;\n                            if (f < 0 || f >= F) continue;\n                            size_t xi",
+     "                        long t = s * to + i - pt0;\n                        if (t < 0 || t >= T) continue;\n                        for (long j = 0; j < KW; ++j) {\n                            long f = s * fo + j - pf0;\n                            if (f < 0 || f >= F) continue;\n                            size_t xi"),
     ("front ReLU dropped", "v = acc > 0.0 ? acc : 0.0;", "v = acc;"),
-    ("front mask floor(len/2)", "long L1 = (len + 1) / 2;", "long L1 = len / 2;"),
+    ("front mask floor(len/2)", "long L1 = len > 0 ? conv_out_len(len, 3, 2, pl, 1) : 0;", "long L1 = len / 2;"),
     ("front mask dropped", "if (t1 < L1) {", "if (1) {"),
-    ("front input length-masked", "                            if (t < 0 || t >= T) continue;\n                            for (long j = 0; j < 3; ++j) {\n                                long f = 2 * f1 + j - 1;",
-     "                            if (t < 0 || t >= len) continue;\n                            for (long j = 0; j < 3; ++j) {\n                                long f = 2 * f1 + j - 1;"),
+    ("front input length-masked", "                            if (t < 0 || t >= T) continue;\n                            for (long j = 0; j < 3; ++j) {\n                                long f = 2 * f1 + j - pl;",
+     "                            if (t < 0 || t >= len) continue;\n                            for (long j = 0; j < 3; ++j) {\n                                long f = 2 * f1 + j - pl;"),
     ("front output bias dropped", "                    acc += (double)b1[c];\n", "\n"),
     ("front conv0 bias after ReLU", "                        acc += (double)b0[c];\n                        v = acc > 0.0 ? acc : 0.0;",
      "                        v = acc > 0.0 ? acc : 0.0;\n                        v += (double)b0[c];"),
-    ("front stage-2 stride 1", "long t1 = 2 * t2 + i - 1;", "long t1 = t2 + i - 1;"),
+    ("front stage-2 stride 1", "long t1 = 2 * t2 + i - pl;", "long t1 = t2 + i - pl;"),
     ("front bwd ReLU derivative ignored", "double dz = z[q] > 0.0 ? dh[q] : 0.0;", "double dz = dh[q];"),
     ("front bwd time mask ignored", "if (t1 >= L1) continue; /* masked", "if (0) continue; /* masked"),
     ("front bwd dh with flipped taps", "dh[q] += g * (double)w1[(i * 3 + j) * C + c];",

@@ -266,6 +266,114 @@ def test_2d_masked_rows_exact_zero_and_no_nan_leak():
     assert np.all(y[0, 4:] == 0) and np.all(y[1] == 0)
 
 
+# ----------------------------------------------- asymmetric (causal) pads -----
+# The causal padding the pages name for the conv2d and the front (NeMo PR
+# #16114, "What does this PR do") is read as kernel - 1 zeros before and
+# stride - 1 after, on each axis.  The reference here pads explicitly with
+# F.pad and convolves without padding, a different route from the oracle's
+# index arithmetic.
+
+def torch_dwconv2d_pads(x, w, b, lengths, stride, pads, dy=None):
+    B, T, F, C = x.shape
+    KH, KW = w.shape[:2]
+    pt0, pt1, pf0, pf1 = pads
+    L = eff_len(lengths, B, T)
+    xt = torch.from_numpy(x.astype(np.float64)).requires_grad_(dy is not None)
+    wt = torch.from_numpy(w.astype(np.float64)).requires_grad_(dy is not None)
+    bt = torch.from_numpy((b if b is not None else np.zeros(C, np.float32)).astype(np.float64))
+    bt.requires_grad_(dy is not None)
+    m = (torch.arange(T)[None, :] < torch.as_tensor(L)[:, None])[:, :, None, None]
+    xm = torch.where(m, xt, torch.zeros(())).permute(0, 3, 1, 2)
+    xm = Fn.pad(xm, (pf0, pf1, pt0, pt1))
+    y = Fn.conv2d(xm, wt.permute(2, 0, 1)[:, None], bt, stride=stride, groups=C).permute(0, 2, 3, 1)
+    To = y.shape[1]
+    Lo = np.array([min(max(0, (l + pt0 + pt1 - KH) // stride + 1), To) if l > 0 else 0 for l in L])
+    mo = (torch.arange(To)[None, :] < torch.as_tensor(Lo)[:, None])[:, :, None, None]
+    y = torch.where(mo, y, torch.zeros(()))
+    if dy is None:
+        return y.detach().numpy()
+    (y * torch.from_numpy(dy.astype(np.float64))).sum().backward()
+    return xt.grad.numpy(), wt.grad.numpy(), bt.grad.numpy()
+
+
+PADS_2D = [
+    # (B, T, F, C, KH, KW, stride, (pt0, pt1, pf0, pf1))
+    (2, 9, 8, 3, 3, 3, 2, (2, 1, 2, 1)), (3, 10, 7, 2, 3, 3, 2, (2, 1, 2, 1)), (1, 1, 1, 2, 3, 3, 2, (2, 1, 2, 1)),
+    (2, 11, 6, 2, 3, 3, 2, (2, 1, 1, 1)), (2, 8, 9, 3, 3, 3, 2, (1, 1, 2, 1)), (2, 12, 10, 2, 3, 3, 2, (1, 0, 0, 2)),
+    (2, 7, 5, 2, 3, 3, 2, (2, 2, 1, 0)), (2, 9, 8, 2, 3, 2, 1, (2, 0, 1, 0)), (1, 13, 7, 3, 5, 3, 3, (4, 2, 2, 0)),
+]
+
+
+@pytest.mark.parametrize("B,T,F,C,KH,KW,s,pads", PADS_2D)
+def test_2d_asymmetric_pads_match_torch(B, T, F, C, KH, KW, s, pads):
+    r = rng(B + T * 5 + F * 17 + sum(pads) * 3)
+    x = f32(r.standard_normal((B, T, F, C)))
+    w = f32(r.standard_normal((KH, KW, C)))
+    b = f32(r.standard_normal(C))
+    lengths = r.integers(-1, T + 2, B).astype(np.int32)
+    lengths[0] = 0  # an empty item: no output row is valid, whatever the padding
+    for L in (None, lengths):
+        for bias in (None, b):
+            close(oracle.dwconv2d_fwd(x, w, bias, L, s, pads=pads), torch_dwconv2d_pads(x, w, bias, L, s, pads))
+
+
+@pytest.mark.parametrize("B,T,F,C,KH,KW,s,pads", PADS_2D)
+def test_bwd_asymmetric_pads_match_torch_autograd(B, T, F, C, KH, KW, s, pads):
+    r = rng(7 * B + T + F * 11 + sum(pads))
+    x = f32(r.standard_normal((B, T, F, C)))
+    w = f32(r.standard_normal((KH, KW, C)))
+    b = f32(r.standard_normal(C))
+    To = oracle.conv_out_len(T, KH, s, pads[0], pads[1])
+    Fo = oracle.conv_out_len(F, KW, s, pads[2], pads[3])
+    dy = f32(r.standard_normal((B, To, Fo, C)))
+    lengths = r.integers(0, T + 2, B).astype(np.int32)
+    got = oracle.dwconv2d_bwd(x, w, lengths, dy, s, pads=pads)
+    for g, rf in zip(got, torch_dwconv2d_pads(x, w, b, lengths, s, pads, dy=dy)):
+        close(g, rf)
+
+
+def test_2d_causal_pads_never_look_ahead():
+    """With kernel - 1 rows of padding before and stride - 1 after, output row
+    t' reads input rows up to s t' only; symmetric padding reads s t' + 1."""
+    r = rng(13)
+    B, T, F, C = 2, 14, 6, 3
+    x = f32(r.standard_normal((B, T, F, C)))
+    w = f32(r.standard_normal((3, 3, C)))
+    b = f32(r.standard_normal(C))
+    causal = (2, 1, 2, 1)
+    y = oracle.dwconv2d_fwd(x, w, b, None, 2, pads=causal)
+    for t0 in (1, 5, 8):
+        x2 = x.copy()
+        x2[:, t0:] += 1.0 + r.standard_normal((B, T - t0, F, C)).astype(np.float32) ** 2
+        y2 = oracle.dwconv2d_fwd(x2, w, b, None, 2, pads=causal)
+        keep = (t0 + 1) // 2                            # rows t' with 2 t' < t0
+        assert np.array_equal(y[:, :keep], y2[:, :keep])
+        assert not np.array_equal(y[:, keep], y2[:, keep])
+        ys, ys2 = oracle.dwconv2d_fwd(x, w, b, None), oracle.dwconv2d_fwd(x2, w, b, None)
+        assert not np.array_equal(ys[:, :keep], ys2[:, :keep]) or t0 % 2 == 0
+
+
+def test_2d_causal_present_tap_closed_form():
+    """Causal pads and w = e_{2,2} (the tap on the present row and column):
+    y[t', f'] = x[2t', 2f'], masked at t' >= floor(len/2) + 1."""
+    r = rng(14)
+    B, T, F, C = 3, 11, 9, 2
+    x = f32(r.standard_normal((B, T, F, C)))
+    w = np.zeros((3, 3, C), np.float32)
+    w[2, 2] = 1.0
+    lengths = np.array([11, 6, 0], np.int32)
+    y = oracle.dwconv2d_fwd(x, w, None, lengths, 2, pads=(2, 1, 2, 1))
+    assert y.shape == (B, T // 2 + 1, F // 2 + 1, C)
+    xm = x.astype(np.float64).copy()
+    for bi, l in enumerate(lengths):
+        xm[bi, l:] = 0.0
+    ref = np.zeros_like(y)
+    ref[:, : (T + 1) // 2, : (F + 1) // 2] = xm[:, 0::2, 0::2]
+    for bi, l in enumerate(lengths):
+        ref[bi, (l // 2 + 1 if l > 0 else 0):] = 0.0
+    assert np.array_equal(y, ref)
+
+
 # ---------------------------------------------------------- backward -----
 
 def torch_dwconv2d_grads(x, w, b, lengths, dy, stride, pad):
@@ -457,6 +565,103 @@ def test_front_positive_homogeneity():
     y = oracle.dwsub_front_fwd(x, w0, b0, w1, b1, lengths) - b1.astype(np.float64)
     y2 = oracle.dwsub_front_fwd(f32(2 * x), w0, f32(2 * b0), w1, b1, lengths) - b1.astype(np.float64)
     close(y2, 2 * y, 1e-13)
+
+
+# ------------------------------------------------------ causal front -----
+
+def torch_front_causal(x, w0, b0, w1, b1, lengths, dy=None):
+    """The front in causal mode: each stride-2 conv pads 2 before and 1 after
+    on both axes (explicit F.pad), h masked at t1 >= floor(len/2) + 1."""
+    B, T, F = x.shape
+    C = w0.shape[2]
+    L = eff_len(lengths, B, T)
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64)).requires_grad_(dy is not None)
+    tw0, tb0, tw1, tb1 = t(w0), t(b0), t(w1), t(b1)
+    xt = Fn.pad(torch.from_numpy(x.astype(np.float64))[:, None], (2, 1, 2, 1))
+    h = torch.relu(Fn.conv2d(xt, tw0.permute(2, 0, 1)[:, None], tb0, stride=2))
+    L1 = np.where(L > 0, L // 2 + 1, 0)
+    m = (torch.arange(h.shape[2])[None, :] < torch.as_tensor(L1)[:, None])[:, None, :, None]
+    h = torch.where(m, h, torch.zeros(()))
+    y = Fn.conv2d(Fn.pad(h, (2, 1, 2, 1)), tw1.permute(2, 0, 1)[:, None], tb1, stride=2, groups=C)
+    y = y.permute(0, 2, 3, 1)
+    if dy is None:
+        return y.detach().numpy()
+    (y * torch.from_numpy(dy.astype(np.float64))).sum().backward()
+    return tw0.grad.numpy(), tb0.grad.numpy(), tw1.grad.numpy(), tb1.grad.numpy()
+
+
+FRONT_CAUSAL = [(2, 16, 12, 4), (3, 13, 9, 3), (1, 1, 1, 2), (2, 30, 20, 5), (1, 7, 80, 2), (2, 2, 3, 2)]
+
+
+@pytest.mark.parametrize("B,T,F,C", FRONT_CAUSAL)
+def test_front_causal_matches_torch_chain(B, T, F, C):
+    r = rng(50 + B + T + F + C)
+    x = f32(r.standard_normal((B, T, F)))
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0, b1 = f32(r.standard_normal(C)), f32(r.standard_normal(C))
+    lengths = r.integers(-1, T + 2, B).astype(np.int32)
+    lengths[0] = 0
+    for L in (None, lengths):
+        close(oracle.dwsub_front_fwd(x, w0, b0, w1, b1, L, causal=True), torch_front_causal(x, w0, b0, w1, b1, L))
+
+
+@pytest.mark.parametrize("B,T,F,C", FRONT_CAUSAL)
+def test_front_causal_bwd_matches_torch_autograd(B, T, F, C):
+    r = rng(60 + B + T + F + C)
+    x = f32(r.standard_normal((B, T, F)))
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0, b1 = f32(r.standard_normal(C)), f32(r.standard_normal(C))
+    T2 = (T // 2 + 1) // 2 + 1
+    F2 = (F // 2 + 1) // 2 + 1
+    dy = f32(r.standard_normal((B, T2, F2, C)))
+    lengths = r.integers(-1, T + 2, B).astype(np.int32)
+    lengths[-1] = 0
+    for L in (None, lengths):
+        got = oracle.dwsub_front_bwd(x, w0, b0, w1, L, dy, causal=True)
+        for g, rf in zip(got, torch_front_causal(x, w0, b0, w1, b1, L, dy=dy)):
+            close(g, rf)
+
+
+def test_front_causal_present_tap_and_no_look_ahead():
+    """Causal front with w0 = w1 = e_{2,2} and zero biases gives
+    y[t2, f2] = [2 t2 < L1] max(0, x[4 t2, 4 f2]); and output row t2 never
+    depends on mel rows after 4 t2."""
+    r = rng(61)
+    B, T, F, C = 3, 23, 17, 2
+    x = f32(r.standard_normal((B, T, F)))
+    e = np.zeros((3, 3, C), np.float32)
+    e[2, 2] = 1.0
+    z = np.zeros(C, np.float32)
+    lengths = np.array([23, 10, 0], np.int32)
+    y = oracle.dwsub_front_fwd(x, e, z, e, z, lengths, causal=True)
+    T2, F2 = y.shape[1], y.shape[2]
+    assert (T2, F2) == ((T // 2 + 1) // 2 + 1, (F // 2 + 1) // 2 + 1)
+    ref = np.zeros_like(y)
+    sub = np.maximum(x[:, 0::4, 0::4].astype(np.float64), 0.0)
+    ref[:, : sub.shape[1], : sub.shape[2]] = sub[..., None]
+    for bi, l in enumerate(lengths):
+        L1 = l // 2 + 1 if l > 0 else 0
+        ref[bi, (np.arange(T2) * 2) >= L1] = 0.0
+    assert np.array_equal(y, ref)
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0, b1 = f32(r.standard_normal(C)), f32(r.standard_normal(C))
+    y = oracle.dwsub_front_fwd(x, w0, b0, w1, b1, None, causal=True)
+    for t2 in (1, 3):
+        x2 = x.copy()
+        x2[:, 4 * t2 + 1:] += 2.0
+        y2 = oracle.dwsub_front_fwd(x2, w0, b0, w1, b1, None, causal=True)
+        assert np.array_equal(y[:, : t2 + 1], y2[:, : t2 + 1])
+        assert not np.array_equal(y[:, t2 + 1], y2[:, t2 + 1])
+
+
+def test_front_causal_empty_item_is_output_bias():
+    r = rng(62)
+    B, T, F, C = 2, 12, 10, 3
+    x = f32(r.standard_normal((B, T, F)))
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0, b1 = f32(np.abs(r.standard_normal(C)) + 1), f32(r.standard_normal(C))
+    y = oracle.dwsub_front_fwd(x, w0, b0, w1, b1, np.array([0, 12], np.int32), causal=True)
+    assert np.all(y[0] == b1.astype(np.float64)[None, None, :])
 
 
 # ------------------------------------------------- fused front backward -----
