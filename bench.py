@@ -12,6 +12,10 @@ size, on synthetic inputs resident in HBM:
           dwconv1d_bwd      dx, dw, db of [32,1500,512] causal K = 9    fp32, fp64 sums
   stage   dwconv2d_fwd      [32,1500,64,256] -> [32,750,32,256]         fp32
           dwconv2d_bwd      dx, dw, db of the same                      fp32
+          dwconv2d_fwd_ex   the same with causal padding -> [32,751,33,256]  fp32
+          dwconv2d_bwd_ex   its dx, dw, db                              fp32
+          dwconv2d_fwd_ex   the symmetric stage with bf16 storage       bf16
+          dwconv2d_bwd_ex   its dx, dw, db (dw, db in fp32)             bf16
 
 The timed region is exactly --steps steps, bracketed by device
 synchronisation.  Per-operation times come from HIP events recorded on the
@@ -120,24 +124,28 @@ def work_front_bwd(c):
     return rd, wr, flops
 
 
-def work_stage_fwd(c):
+def stage_out(n, pl, ph):
+    return max(0, (n + pl + ph - 3) // 2 + 1)
+
+
+def work_stage_fwd(c, pads=(1, 1, 1, 1), es=4):
     B, T, F, C = c["B"], c["T"], c["F"], c["C"]
-    To, Fo = (T + 1) // 2, (F + 1) // 2
+    To, Fo = stage_out(T, pads[0], pads[1]), stage_out(F, pads[2], pads[3])
     L = clamp_lengths(c["lengths"].tolist(), T)
-    Lo = [(l + 1) // 2 for l in L]
-    rd = sum(L) * F * C * 4 + 10 * C * 4 + 4 * B
-    wr = B * To * Fo * C * 4
+    Lo = [min(stage_out(l, pads[0], pads[1]), To) if l > 0 else 0 for l in L]
+    rd = sum(L) * F * C * es + 10 * C * es + 4 * B
+    wr = B * To * Fo * C * es
     flops = 2 * 9 * C * Fo * sum(Lo)
     return rd, wr, flops
 
 
-def work_stage_bwd(c):
+def work_stage_bwd(c, pads=(1, 1, 1, 1), es=4):
     B, T, F, C = c["B"], c["T"], c["F"], c["C"]
-    To, Fo = (T + 1) // 2, (F + 1) // 2
+    To, Fo = stage_out(T, pads[0], pads[1]), stage_out(F, pads[2], pads[3])
     L = clamp_lengths(c["lengths"].tolist(), T)
-    Lo = [(l + 1) // 2 for l in L]
-    rd = sum(L) * F * C * 4 + sum(Lo) * Fo * C * 4 + 9 * C * 4 + 4 * B
-    wr = B * T * F * C * 4 + 10 * C * 4
+    Lo = [min(stage_out(l, pads[0], pads[1]), To) if l > 0 else 0 for l in L]
+    rd = sum(L) * F * C * es + sum(Lo) * Fo * C * es + 9 * C * es + 4 * B
+    wr = B * T * F * C * es + 10 * C * 4
     flops = 2 * 2 * 9 * C * Fo * sum(Lo) + C * Fo * sum(Lo)
     return rd, wr, flops
 
@@ -213,7 +221,29 @@ def build_rows(dev):
         *work_stage_fwd(g), lambda: dw.dwconv2d_fwd(g["x"], g["w"], g["b"], gL, y=gy))
     add("stage_bwd", "dwconv2d_bwd", "dx,dw,db of [32,1500,64,256] fp32", g["B"] * g["T"], *work_stage_bwd(g),
         lambda: dw.dwconv2d_bwd(g["x"], g["w"], gL, g["dy"], dx=gdx, dw=gdw, db=gdb, workspace=ws))
-    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g)
+
+    # the same stage with causal padding (fp32), and with bf16 storage (symmetric)
+    causal = dw.CAUSAL_PADS_2D
+    To_c, Fo_c = dw.conv2d_out_shape(g["T"], g["F"], pads=causal)
+    gc = dict(g, dy=datagen.normal((g["B"], To_c, Fo_c, g["C"]), 1.0, "c5/dy", device=dev))
+    gcy = torch.empty((g["B"], To_c, Fo_c, g["C"]), device=dev)
+    wsc = torch.empty((dw.dwconv2d_bwd_workspace_bytes(g["B"], g["T"], g["F"], g["C"], pads=causal),),
+                      dtype=torch.uint8, device=dev)
+    add("stage_fwd_causal", "dwconv2d_fwd_ex", "[32,1500,64,256] -> [32,751,33,256] causal pads fp32",
+        g["B"] * g["T"], *work_stage_fwd(g, causal),
+        lambda: dw.dwconv2d_fwd(g["x"], g["w"], g["b"], gL, y=gcy, pads=causal))
+    add("stage_bwd_causal", "dwconv2d_bwd_ex", "dx,dw,db of [32,1500,64,256] causal pads fp32", g["B"] * g["T"],
+        *work_stage_bwd(g, causal),
+        lambda: dw.dwconv2d_bwd(g["x"], g["w"], gL, gc["dy"], dx=gdx, dw=gdw, db=gdb, workspace=wsc, pads=causal))
+    h = {k: (v.to(torch.bfloat16) if k in ("x", "w", "b", "dy") else v) for k, v in g.items()}
+    hy = torch.empty((g["B"], 750, 32, g["C"]), dtype=torch.bfloat16, device=dev)
+    hdx = torch.empty_like(h["x"])
+    add("stage_fwd_bf16", "dwconv2d_fwd_ex", "[32,1500,64,256] -> [32,750,32,256] bf16 storage", g["B"] * g["T"],
+        *work_stage_fwd(g, es=2), lambda: dw.dwconv2d_fwd(h["x"], h["w"], h["b"], gL, y=hy))
+    add("stage_bwd_bf16", "dwconv2d_bwd_ex", "dx,dw,db of [32,1500,64,256] bf16 storage, fp32 dw/db",
+        g["B"] * g["T"], *work_stage_bwd(g, es=2),
+        lambda: dw.dwconv2d_bwd(h["x"], h["w"], gL, h["dy"], dx=hdx, dw=gdw, db=gdb, workspace=ws))
+    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h)
     return rows, data
 
 
@@ -229,6 +259,9 @@ def cpu_baseline(data, target_s: float):
     f, e, g = hp(data["front"]), hp(data["conv1d_bf16"]), hp(data["stage"])
     f["x"], f["dy"] = data["front"]["x"], data["front"]["dy"]
     e["x"], g["x"], g["dy"] = data["conv1d_bf16"]["x"], data["stage"]["x"], data["stage"]["dy"]
+    gc = dict(g, dy=data["stage_causal"]["dy"])
+    gh = hp(data["stage_bf16"])                    # bf16 values, widened exactly on the host
+    gh["x"], gh["dy"] = data["stage_bf16"]["x"], data["stage_bf16"]["dy"]
     sweep = []
     for s in data["sweep"]:
         hs = hp(s)
@@ -272,12 +305,13 @@ def cpu_baseline(data, target_s: float):
                 secs += time.perf_counter() - t
                 frames += m * s["T"]
         m = min(n, g["B"])
-        xs, dys = host(g["x"], m), host(g["dy"], m)
-        t = time.perf_counter()
-        oracle.dwconv2d_fwd(xs, g["w"], g["b"], g["lengths"][:m])
-        oracle.dwconv2d_bwd(xs, g["w"], g["lengths"][:m], dys)
-        secs += time.perf_counter() - t
-        frames += 2 * m * g["T"]
+        for st, pads in ((g, None), (gc, (2, 1, 2, 1)), (gh, None)):
+            xs, dys = host(st["x"], m), host(st["dy"], m)
+            t = time.perf_counter()
+            oracle.dwconv2d_fwd(xs, st["w"], st["b"], st["lengths"][:m], pads=pads)
+            oracle.dwconv2d_bwd(xs, st["w"], st["lengths"][:m], dys, pads=pads)
+            secs += time.perf_counter() - t
+            frames += 2 * m * g["T"]
         return secs, frames
 
     s1, _ = one_pass(1)
@@ -410,7 +444,7 @@ def main():
         "config": {
             "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd; conv-module dwconv1d [16,750,1024] K9 "
                         "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; depthwise conv2d "
-                        "stage [32,1500,64,256] fwd+bwd",
+                        "stage [32,1500,64,256] fwd+bwd (symmetric fp32, causal fp32, symmetric bf16)",
             "frames_per_step": frames,
             "alg_bytes_per_step": alg,
             "parallelism": "single GPU",

@@ -22,7 +22,7 @@ __all__ = [
     "LIB_PATH", "DwconvError", "abi_version",
     "dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
     "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
-    "out_len",
+    "conv2d_out_shape", "CAUSAL_PADS_2D", "out_len",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdwconv.so")
@@ -73,6 +73,12 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dwconv2d_bwd_workspace_bytes.argtypes = [_i64] * 8
     lib.dwconv2d_bwd.restype = _int
     lib.dwconv2d_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz] + [_i64] * 8 + [_vp]
+    lib.dwconv2d_fwd_ex.restype = _int
+    lib.dwconv2d_fwd_ex.argtypes = [_vp] * 5 + [_i64] * 11 + [_int, _vp]
+    lib.dwconv2d_bwd_workspace_bytes_ex.restype = _sz
+    lib.dwconv2d_bwd_workspace_bytes_ex.argtypes = [_i64] * 11
+    lib.dwconv2d_bwd_ex.restype = _int
+    lib.dwconv2d_bwd_ex.argtypes = [_vp] * 8 + [_sz] + [_i64] * 11 + [_int, _vp]
     return lib
 
 
@@ -252,55 +258,90 @@ def _conv2d_dims(x, w):
     return B, T, F, C, w.shape[0], w.shape[1]
 
 
-def dwconv2d_fwd(x, w, bias=None, lengths=None, y=None, stride: int = 2, pad: int = 1):
-    """Masked depthwise conv2d; x [B,T,F,C], w [3,3,C] -> y [B,T',F',C] (float32)."""
-    dev, f32 = x.device, torch.float32
+CAUSAL_PADS_2D = (2, 1, 2, 1)   # kernel - 1 before, stride - 1 after, on each axis (3x3, stride 2)
+
+
+def _pads(pad, pads):
+    if pads is None:
+        return (pad, pad, pad, pad)
+    pads = tuple(int(v) for v in pads)
+    if len(pads) != 4:
+        raise ValueError("pads must be (time before, time after, freq before, freq after)")
+    return pads
+
+
+def conv2d_out_shape(T, F, KH=3, KW=3, stride=2, pad=1, pads=None):
+    """(T', F') of the conv2d for these sizes and pads."""
+    pt0, pt1, pf0, pf1 = _pads(pad, pads)
+    return max(0, (T + pt0 + pt1 - KH) // stride + 1), max(0, (F + pf0 + pf1 - KW) // stride + 1)
+
+
+def _storage(x):
+    if x.dtype == torch.float32:
+        return torch.float32, DW_F32
+    if x.dtype == torch.bfloat16:
+        return torch.bfloat16, DW_BF16
+    raise TypeError(f"x must be float32 or bfloat16, not {x.dtype}")
+
+
+def dwconv2d_fwd(x, w, bias=None, lengths=None, y=None, stride: int = 2, pad: int = 1, pads=None):
+    """Masked depthwise conv2d; x [B,T,F,C], w [3,3,C] -> y [B,T',F',C].
+    x, w, bias and y share one storage type (float32 or bfloat16); pads =
+    (time before, time after, freq before, freq after) overrides pad
+    (CAUSAL_PADS_2D is the causal padding)."""
+    dev = x.device
+    st, code = _storage(x)
     B, T, F, C, KH, KW = _conv2d_dims(x, w)
-    _dev_tensor("x", x, f32, dev)
-    _dev_tensor("w", w, f32, dev)
-    _dev_tensor("bias", bias, f32, dev, (C,), allow_none=True)
+    _dev_tensor("x", x, st, dev)
+    _dev_tensor("w", w, st, dev)
+    _dev_tensor("bias", bias, st, dev, (C,), allow_none=True)
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
-    To = max(0, (T + 2 * pad - KH) // stride + 1)
-    Fo = max(0, (F + 2 * pad - KW) // stride + 1)
+    pt0, pt1, pf0, pf1 = _pads(pad, pads)
+    To, Fo = conv2d_out_shape(T, F, KH, KW, stride, pads=(pt0, pt1, pf0, pf1))
     if y is None:
-        y = torch.empty((B, To, Fo, C), dtype=f32, device=dev)
-    _dev_tensor("y", y, f32, dev, (B, To, Fo, C))
-    _check(_lib.dwconv2d_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(lengths), _ptr(y),
-                             B, T, F, C, KH, KW, stride, pad, _stream(dev)))
+        y = torch.empty((B, To, Fo, C), dtype=st, device=dev)
+    _dev_tensor("y", y, st, dev, (B, To, Fo, C))
+    _check(_lib.dwconv2d_fwd_ex(_ptr(x), _ptr(w), _ptr(bias), _ptr(lengths), _ptr(y),
+                                B, T, F, C, KH, KW, stride, pt0, pt1, pf0, pf1, code, _stream(dev)))
     return y
 
 
-def dwconv2d_bwd_workspace_bytes(B, T, F, C, KH=3, KW=3, stride=2, pad=1) -> int:
-    return int(_lib.dwconv2d_bwd_workspace_bytes(B, T, F, C, KH, KW, stride, pad))
+def dwconv2d_bwd_workspace_bytes(B, T, F, C, KH=3, KW=3, stride=2, pad=1, pads=None) -> int:
+    pt0, pt1, pf0, pf1 = _pads(pad, pads)
+    return int(_lib.dwconv2d_bwd_workspace_bytes_ex(B, T, F, C, KH, KW, stride, pt0, pt1, pf0, pf1))
 
 
 def dwconv2d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None,
-                 need=("dx", "dw", "db"), stride: int = 2, pad: int = 1):
-    """Gradients (dx, dw, db) of dwconv2d_fwd given dy; outputs not in `need` are skipped (None)."""
+                 need=("dx", "dw", "db"), stride: int = 2, pad: int = 1, pads=None):
+    """Gradients (dx, dw, db) of dwconv2d_fwd given dy; outputs not in `need`
+    are skipped (None).  x, w, dy and dx share one storage type; dw and db
+    are float32."""
     dev, f32 = x.device, torch.float32
+    st, code = _storage(x)
     B, T, F, C, KH, KW = _conv2d_dims(x, w)
-    _dev_tensor("x", x, f32, dev)
-    _dev_tensor("w", w, f32, dev)
+    _dev_tensor("x", x, st, dev)
+    _dev_tensor("w", w, st, dev)
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
-    To = max(0, (T + 2 * pad - KH) // stride + 1)
-    Fo = max(0, (F + 2 * pad - KW) // stride + 1)
-    _dev_tensor("dy", dy, f32, dev, (B, To, Fo, C))
+    pt0, pt1, pf0, pf1 = _pads(pad, pads)
+    To, Fo = conv2d_out_shape(T, F, KH, KW, stride, pads=(pt0, pt1, pf0, pf1))
+    _dev_tensor("dy", dy, st, dev, (B, To, Fo, C))
     if dx is None and "dx" in need:
         dx = torch.empty_like(x)
     if dw is None and "dw" in need:
         dw = torch.empty((KH, KW, C), dtype=f32, device=dev)
     if db is None and "db" in need:
         db = torch.empty((C,), dtype=f32, device=dev)
-    _dev_tensor("dx", dx, f32, dev, (B, T, F, C), allow_none=True)
+    _dev_tensor("dx", dx, st, dev, (B, T, F, C), allow_none=True)
     _dev_tensor("dw", dw, f32, dev, (KH, KW, C), allow_none=True)
     _dev_tensor("db", db, f32, dev, (C,), allow_none=True)
     ws_bytes = 0
     if dw is not None or db is not None:
-        need_ws = dwconv2d_bwd_workspace_bytes(B, T, F, C, KH, KW, stride, pad)
+        need_ws = dwconv2d_bwd_workspace_bytes(B, T, F, C, KH, KW, stride, pads=(pt0, pt1, pf0, pf1))
         if workspace is None:
             workspace = torch.empty((max(need_ws, 1),), dtype=torch.uint8, device=dev)
         _dev_tensor("workspace", workspace, torch.uint8, dev)
         ws_bytes = workspace.numel()
-    _check(_lib.dwconv2d_bwd(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
-                             _ptr(workspace), ws_bytes, B, T, F, C, KH, KW, stride, pad, _stream(dev)))
+    _check(_lib.dwconv2d_bwd_ex(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
+                                _ptr(workspace), ws_bytes, B, T, F, C, KH, KW, stride, pt0, pt1, pf0, pf1, code,
+                                _stream(dev)))
     return dx, dw, db

@@ -34,8 +34,24 @@ dw_status from_hip(hipError_t e, const char* what) {
     return fail(DW_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
 }
 
-bool geometry_3x3_s2_p1(int64_t KH, int64_t KW, int64_t stride, int64_t pad) {
-    return KH == 3 && KW == 3 && stride == 2 && pad == 1;
+// The 2-D kernels: a 3x3 kernel, stride 2, and the paddings
+// dwconv2d_pads_supported accepts.
+dw_status check_geometry_2d(const char* fn, int64_t KH, int64_t KW, int64_t stride, int64_t pt0, int64_t pt1,
+                            int64_t pf0, int64_t pf1) {
+    if (KH < 1 || KW < 1 || stride < 1 || pt0 < 0 || pt1 < 0 || pf0 < 0 || pf1 < 0)
+        return fail(DW_ERR_INVALID_ARG, "%s: kernel %lldx%lld, stride %lld, pads (%lld, %lld, %lld, %lld) are not a "
+                    "valid geometry", fn, (long long)KH, (long long)KW, (long long)stride, (long long)pt0,
+                    (long long)pt1, (long long)pf0, (long long)pf1);
+    if (KH != 3 || KW != 3 || stride != 2 || !dw::dwconv2d_pads_supported(pt0, pt1, pf0, pf1))
+        return fail(DW_ERR_UNSUPPORTED, "%s: implemented for a 3x3 kernel, stride 2, padding 1 or 2 before and 0 to 2 "
+                    "after on each axis (got %lldx%lld, stride %lld, pads (%lld, %lld, %lld, %lld))", fn,
+                    (long long)KH, (long long)KW, (long long)stride, (long long)pt0, (long long)pt1,
+                    (long long)pf0, (long long)pf1);
+    return DW_OK;
+}
+
+bool geometry_ok_2d(int64_t KH, int64_t KW, int64_t stride, int64_t pt0, int64_t pt1, int64_t pf0, int64_t pf1) {
+    return KH == 3 && KW == 3 && stride == 2 && dw::dwconv2d_pads_supported(pt0, pt1, pf0, pf1);
 }
 
 }  // namespace
@@ -140,44 +156,61 @@ dw_status dwsub_fused_bwd(const float* x, const float* w0, const float* b0, cons
                                                (hipStream_t)stream), fn);
 }
 
+dw_status dwconv2d_fwd_ex(const void* x, const void* w, const void* bias, const int32_t* lengths, void* y,
+                          int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride,
+                          int64_t pad_t0, int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype,
+                          void* stream) {
+    const char* fn = "dwconv2d_fwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    const dw_status gs = check_geometry_2d(fn, KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1);
+    if (gs != DW_OK) return gs;
+    const dw::Conv2dGeom g = dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1);
+    if (B == 0 || g.To == 0 || g.Fo == 0 || C == 0) return ok();
+    if ((!x && T * F > 0) || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
+    if (x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    const void* ptrs[4] = {x, w, bias, y};
+    const int vec = dw::pick_vec(C, es, ptrs, 4, dtype == DW_BF16 ? 8 : 4);
+    if (!dw::dwconv2d_fits(B, g, es)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwconv2d_fwd(x, w, bias, lengths, y, B, g, dtype == DW_BF16, vec,
+                                            (hipStream_t)stream), fn);
+}
+
 dw_status dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths, float* y,
                        int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride,
                        int64_t pad, void* stream) {
-    const char* fn = "dwconv2d_fwd";
-    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
-    if (!geometry_3x3_s2_p1(KH, KW, stride, pad))
-        return fail(DW_ERR_UNSUPPORTED, "%s: only a 3x3 kernel with stride 2 and pad 1 is implemented (got %lldx%lld, stride %lld, pad %lld)", fn, (long long)KH, (long long)KW, (long long)stride, (long long)pad);
-    if (B == 0 || T == 0 || F == 0 || C == 0) return ok();
-    if (!x || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
-    if ((const void*)x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
-    const void* ptrs[4] = {x, w, bias, y};
-    const int vec = dw::pick_vec(C, 4, ptrs, 4, 4);
-    if (!dw::dwconv2d_fits(B, T, F, C, vec)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
-    return from_hip(dw::launch_dwconv2d_fwd(x, w, bias, lengths, y, B, T, F, C, vec, (hipStream_t)stream), fn);
+    return dwconv2d_fwd_ex(x, w, bias, lengths, y, B, T, F, C, KH, KW, stride, pad, pad, pad, pad, DW_F32, stream);
+}
+
+size_t dwconv2d_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW,
+                                       int64_t stride, int64_t pad_t0, int64_t pad_t1, int64_t pad_f0,
+                                       int64_t pad_f1) {
+    if (B < 0 || T < 0 || F < 0 || C < 0 || !geometry_ok_2d(KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1)) return 0;
+    return dw::dwconv2d_bwd_workspace(B, dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1));
 }
 
 size_t dwconv2d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW,
                                     int64_t stride, int64_t pad) {
-    if (B < 0 || T < 0 || F < 0 || C < 0 || !geometry_3x3_s2_p1(KH, KW, stride, pad)) return 0;
-    return dw::dwconv2d_bwd_workspace(B, T, F, C);
+    return dwconv2d_bwd_workspace_bytes_ex(B, T, F, C, KH, KW, stride, pad, pad, pad, pad);
 }
 
-dw_status dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
-                       float* dw_, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
-                       int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad,
-                       void* stream) {
+dw_status dwconv2d_bwd_ex(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
+                          float* dw_, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                          int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad_t0,
+                          int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype, void* stream) {
     const char* fn = "dwconv2d_bwd";
     if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
-    const int64_t To = (T + 1) / 2, Fo = (F + 1) / 2;
-    if ((!x && B * T * F * C > 0) || (!dy && B * To * Fo * C > 0) || (!w && C > 0))
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    const dw_status gs = check_geometry_2d(fn, KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1);
+    if (gs != DW_OK) return gs;
+    const dw::Conv2dGeom g = dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1);
+    if ((!x && B * T * F * C > 0) || (!dy && B * g.To * g.Fo * C > 0) || (!w && C > 0))
         return fail(DW_ERR_INVALID_ARG, "%s: x, w and dy must not be NULL (unless empty)", fn);
-    if (dx && ((const void*)dx == (const void*)x || (const void*)dx == (const void*)dy))
-        return fail(DW_ERR_INVALID_ARG, "%s: dx must not alias x or dy", fn);
-    if (!geometry_3x3_s2_p1(KH, KW, stride, pad))
-        return fail(DW_ERR_UNSUPPORTED, "%s: only a 3x3 kernel with stride 2 and pad 1 is implemented (got %lldx%lld, stride %lld, pad %lld)", fn, (long long)KH, (long long)KW, (long long)stride, (long long)pad);
+    if (dx && (dx == x || dx == dy)) return fail(DW_ERR_INVALID_ARG, "%s: dx must not alias x or dy", fn);
     const bool want_wb = dw_ || db;
     if (want_wb) {
-        const size_t need = dw::dwconv2d_bwd_workspace(B, T, F, C);
+        const size_t need = dw::dwconv2d_bwd_workspace(B, g);
         if (!workspace || workspace_bytes < need)
             return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
     }
@@ -185,11 +218,20 @@ dw_status dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, c
     if (C == 0) return ok();
     // An empty batch or item still defines dw = 0 and db = 0; the launcher
     // writes those zeros when there is nothing to reduce.
-    const void* ptrs[6] = {x, w, dy, dx, dw_, db};
-    const int vec = dw::pick_vec(C, 4, ptrs, 6, 4);
-    if (!dw::dwconv2d_fits(B, T, F, C, vec)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
-    return from_hip(dw::launch_dwconv2d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, T, F, C, vec,
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    const void* ptrs[4] = {x, w, dy, dx};
+    const int vec = dw::pick_vec(C, es, ptrs, 4, 4);
+    if (!dw::dwconv2d_fits(B, g, es)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwconv2d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, g, dtype == DW_BF16, vec,
                                             (hipStream_t)stream), fn);
+}
+
+dw_status dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+                       float* dw_, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                       int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad,
+                       void* stream) {
+    return dwconv2d_bwd_ex(x, w, lengths, dy, dx, dw_, db, workspace, workspace_bytes, B, T, F, C, KH, KW, stride,
+                           pad, pad, pad, pad, DW_F32, stream);
 }
 
 }  // extern "C"

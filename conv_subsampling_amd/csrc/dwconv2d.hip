@@ -1,27 +1,35 @@
-// Depthwise conv2d, 3x3, stride 2, pad 1, forward and backward, for gfx950
-// (NeMo PR #16114, "What does this PR do": the general depthwise conv2d with
-// the pre- and post-masking fused into the kernel, and its backward).
+// Depthwise conv2d, 3x3, stride 2, forward and backward, for gfx950 (NeMo PR
+// #16114, "What does this PR do": the general depthwise conv2d with the pre-
+// and post-masking and the causal padding fused into the kernel, and its
+// backward).  fp32 or bf16 storage; arithmetic in fp32, weight gradients in
+// fp64.
 //
-// Layout: x, dx [B][T][F][C], y, dy [B][T'][F'][C] with T' = ceil(T/2),
-// F' = ceil(F/2); w [3][3][C]; channel fastest.
+// Layout: x, dx [B][T][F][C], y, dy [B][T'][F'][C]; w [3][3][C]; channel
+// fastest.  Padding: pt0 (1 or 2) zero rows before the input and pt1 (0..2)
+// after it in time, pf0 and pf1 likewise in frequency; pads of 1 everywhere
+// are the symmetric convolution, (2, 1) on an axis its causal padding.  With
+// dt = pt0 - 1 and df = pf0 - 1 (0 or 1), output (t', f') reads input rows
+// 2t'-1-dt .. 2t'+1-dt and columns 2f'-1-df .. 2f'+1-df;
+// T' = floor((T + pt0 + pt1 - 3)/2) + 1, and likewise F'.
 //
 // Masks through buffer resources: each item's x is read through a resource
 // that ends at its valid length (rows t >= len read as zero: the pre-mask)
-// and dy through one that ends at len' = ceil(len/2) (masked gradient rows
-// read as zero), and a negative row offset is out of range as well, which
-// gives the top padding row.  Only the frequency padding (column -1, and
-// column F when F is odd) needs an explicit zero.
+// and dy through one that ends at len' = floor((len + pt0 + pt1 - 3)/2) + 1
+// (masked gradient rows read as zero), and a negative row offset is out of
+// range as well, which gives the top padding rows.  Only the frequency
+// padding needs an explicit zero, since a column offset past either edge
+// lands in a neighbouring row.
 //
 // Forward mapping.  A thread owns V channels of TO consecutive output rows of
-// one item and walks left to right over the F' output columns (or a chunk of
-// them).  At output
-// column f' it needs input columns 2f'-1, 2f', 2f'+1 of the 2*TO+1 input rows
-// 2t0-1 .. 2t0+2*TO-1; column 2f'+1 is carried to the next step as its
-// column 2(f'+1)-1, so every input element is loaded once per thread, and
-// the one input row shared with the next row block comes from L2.
+// one item and walks left to right over a chunk of the F' output columns.  At
+// output column f' it needs input columns 2f'-1-df, 2f'-df, 2f'+1-df; the
+// last is carried to the next step as its first, so every input element is
+// loaded once per thread, and the one input row shared with the next row
+// block comes from L2.
 //
 // Backward mapping.  dx is gathered, not scattered: output-parity phases.
-// With x rows 2t', 2t'+1 and columns 2f', 2f'+1 as one "quad" (t', f'):
+// With x rows 2m-dt, 2m+1-dt and columns 2n-df, 2n+1-df as one "quad" (m, n),
+// and writing t' = m, f' = n:
 //   dx[2t',  2f'  ] = g[t',f'] w11
 //   dx[2t',  2f'+1] = g[t',f'] w12 + g[t',f'+1] w10
 //   dx[2t'+1,2f'  ] = g[t',f'] w21 + g[t'+1,f'] w01
@@ -29,7 +37,11 @@
 // and the same (g, x) pairs give the weight gradient: each pair above adds
 // g * x(quad element) to the tap it multiplies.  Every (input, output) pair
 // of the convolution belongs to exactly one quad, so dw is complete and no
-// pair is counted twice; db adds g[t',f'] once per quad.  A thread walks one
+// pair is counted twice; db adds g[t',f'] once per quad.  (The top pad only
+// shifts which x rows a quad holds: x row t is hit by the taps i with
+// t = 2t' + i - pt0, one tap when t + dt is even and two when it is odd.)
+// The quad grid spans max(ceil((T+dt)/2), T') rows and max(ceil((F+df)/2), F')
+// columns, so it covers every x element and every g element.  A thread walks one
 // row block of quads left to right, carrying the g column f'+1.  dw and db
 // are accumulated in fp64 from the start (an fp32 x fp32 product is exact in
 // fp64, and fp64 FMA runs at the fp32 rate here), because a sum of ~10^6
@@ -51,17 +63,26 @@ constexpr int kRowsPerBlock = kBlock2d / kLanes2d;  // row blocks per workgroup
 #define DW2D_FWD_ROWS 1
 #endif
 #ifndef DW2D_FWD_PERSIST
-#define DW2D_FWD_PERSIST 512  // workgroups of a persistent forward grid; 0 = one workgroup per tile
+#define DW2D_FWD_PERSIST 512  // workgroups of the persistent forward grid
 #endif
 #ifndef DW2D_FWD_COLS
-#define DW2D_FWD_COLS 8  // output columns per thread in the forward; 0 = all of them
+#define DW2D_FWD_COLS 8  // output columns per thread in the forward
 #endif
 #ifndef DW2D_BWD_ROWS
 #define DW2D_BWD_ROWS 1
 #endif
 constexpr int kFwdRows = DW2D_FWD_ROWS;   // output rows per thread (forward)
-constexpr int kFwdCols = DW2D_FWD_COLS;   // output columns per thread (forward), 0 = all
+constexpr int kFwdCols = DW2D_FWD_COLS;   // output columns per thread (forward)
 constexpr int kBwdRows = DW2D_BWD_ROWS;   // quad rows per thread (backward)
+#ifndef DW2D_BWD_ROWS_BF16
+#define DW2D_BWD_ROWS_BF16 2
+#endif
+#ifndef DW2D_FWD_BF16_VEC
+#define DW2D_FWD_BF16_VEC 8  // widest bf16 forward access: 8 channels, 16 bytes
+#endif
+// quad rows per thread of the backward, per storage type
+template <typename S>
+constexpr int bwd_rows() { return sizeof(S) == 2 ? DW2D_BWD_ROWS_BF16 : kBwdRows; }
 
 template <int V>
 __device__ __forceinline__ void fma_v(Vf<V>& acc, const Vf<V>& a, const Vf<V>& b) {
@@ -84,168 +105,128 @@ __device__ __forceinline__ Vf<V> select_v(bool keep, const Vf<V>& a) {
     return r;
 }
 
-// Block decode shared by the forward and backward kernels: the workgroup is
-// kRowsPerBlock row blocks x kLanes2d channel groups of one item.
-struct Tile2d {
-    uint32_t b, rb, cg;
-    bool valid;
+// A column offset past either edge of a row would land in a neighbouring row,
+// so such a column is addressed at this offset instead: added to any row
+// offset the kernels form (below 2^31 - 2 rows, or a row -1 that wrapped),
+// it is at or past every resource's size, and the load returns zero.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Geometry handed to the kernels (all sizes fit in 32 bits: dwconv2d_fits).
+struct Geo2d {
+    int32_t T, F, C, To, Fo;
+    int32_t dt, df;     // pad before - 1, per axis (0 or 1)
+    int32_t len_add;    // pt0 + pt1 - 3: len' = floor((len + len_add) / 2) + 1
+    int32_t NQt, NQf;   // quad rows and columns of the backward
+    int32_t fcols;      // output columns per forward thread
 };
 
-__device__ __forceinline__ Tile2d decode_2d(uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t wg_per_item) {
-    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
-    Tile2d d;
-    d.b = blk / wg_per_item;
-    const uint32_t r = blk - d.b * wg_per_item;
-    const uint32_t rgroup = r / n_cblk, cblk = r - rgroup * n_cblk;
-    d.rb = rgroup * kRowsPerBlock + threadIdx.x / kLanes2d;
-    d.cg = cblk * kLanes2d + threadIdx.x % kLanes2d;
-    d.valid = d.rb < n_rb && d.cg < CG;
-    return d;
+// Valid output rows of an item with len valid input rows.
+__device__ __forceinline__ int32_t out_rows(int32_t len, const Geo2d& g) {
+    if (len <= 0) return 0;
+    const int32_t o = ((len + g.len_add) >> 1) + 1;  // arithmetic shift: floor division
+    return o < 0 ? 0 : (o > g.To ? g.To : o);
 }
 
 // ------------------------------------------------------------------ fwd ----
 
-template <int V, int TO>
+template <typename S, int V, int TO, int LANES>
 __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
-    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
-    const int32_t* __restrict__ lengths, float* __restrict__ y, int32_t B_items,
-    int32_t T, int32_t F, int32_t C, int32_t To, int32_t Fo,
-    uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t wg_per_item) {
-#if DW2D_FWD_PERSIST
-    // wg_per_item here is the number of row groups per item; the batch's row
-    // groups are dealt round-robin to the workgroups of a channel block.
+    const S* __restrict__ x, const S* __restrict__ w, const S* __restrict__ bias,
+    const int32_t* __restrict__ lengths, S* __restrict__ y, Geo2d geo, int32_t B_items,
+    uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item) {
+    // A workgroup is kBlock2d / LANES row blocks of LANES channel groups
+    // (LANES = 32 when there are at most 32 groups: two row blocks a wave).
+    constexpr int32_t es = (int32_t)sizeof(S);
+    constexpr uint32_t kRB = kBlock2d / LANES;
+    const int32_t T = geo.T, F = geo.F, C = geo.C, To = geo.To, Fo = geo.Fo;
+    // The batch's row groups are dealt round-robin to the workgroups of a
+    // channel block, so every workgroup gets a like mix of long and short
+    // (masked) items.
     const uint32_t blk0 = xcd_contiguous_block(blockIdx.x, gridDim.x);
     const uint32_t G = gridDim.x / n_cblk;
     const uint32_t g0 = blk0 / n_cblk, cb0 = blk0 - g0 * n_cblk;
-    for (uint32_t j = g0; j < (uint32_t)B_items * wg_per_item; j += G) {
-    Tile2d d;
-    d.b = j / wg_per_item;
-    d.rb = (j - d.b * wg_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
-    d.cg = cb0 * kLanes2d + threadIdx.x % kLanes2d;
-    d.valid = d.rb < n_rb && d.cg < CG;
-    if (!d.valid) continue;
-#else
-    const Tile2d d = decode_2d(n_rb, CG, n_cblk, wg_per_item);
-    if (!d.valid) return;
-#endif
-    const int32_t len = (int32_t)item_length(lengths, d.b, T);
-    const int32_t leno = (len + 1) / 2;
-    const uint32_t xrow = (uint32_t)F * C * 4, yrow = (uint32_t)Fo * C * 4, pix = (uint32_t)C * 4;
-    const rsrc_t xr = make_rsrc(x + (int64_t)d.b * T * F * C, (uint32_t)len * xrow);
-    const rsrc_t yr = make_rsrc(y + (int64_t)d.b * To * Fo * C, (uint32_t)To * yrow);
-    const int32_t c0 = (int32_t)d.cg * V;
-    const uint32_t coff = (uint32_t)c0 * 4;
-    // row-block index = row block * column chunks + column chunk
-    const int32_t fch = kFwdCols > 0 ? kFwdCols : Fo;
-    const int32_t nfc = (Fo + fch - 1) / fch;
-    const int32_t t0 = (int32_t)(d.rb / nfc) * TO;
-    const int32_t fa = (int32_t)(d.rb % nfc) * fch, fb = min(Fo, fa + fch);
+    const uint32_t cg = cb0 * LANES + threadIdx.x % LANES;
+    for (uint32_t j = g0; j < (uint32_t)B_items * groups_per_item; j += G) {
+        const uint32_t b = j / groups_per_item;
+        const uint32_t rb = (j - b * groups_per_item) * kRB + threadIdx.x / LANES;
+        if (rb >= n_rb || cg >= CG) continue;
+        const int32_t len = (int32_t)item_length(lengths, b, T);
+        const int32_t leno = out_rows(len, geo);
+        const uint32_t xrow = (uint32_t)(F * C * es), yrow = (uint32_t)(Fo * C * es);
+        const int32_t pix = C * es;
+        const rsrc_t xr = make_rsrc(x + (int64_t)b * T * F * C, (uint32_t)len * xrow);
+        const rsrc_t yr = make_rsrc(y + (int64_t)b * To * Fo * C, (uint32_t)To * yrow);
+        const int32_t c0 = (int32_t)cg * V;
+        const uint32_t coff = (uint32_t)(c0 * es);
+        // row-block index = row block * column chunks + column chunk
+        const int32_t nfc = (Fo + geo.fcols - 1) / geo.fcols;
+        const int32_t t0 = (int32_t)(rb / nfc) * TO;
+        const int32_t fa = (int32_t)(rb % nfc) * geo.fcols, fb = min(Fo, fa + geo.fcols);
 
-    if (t0 >= leno) {
-        const Vf<V> z = vzero<V>();
-        for (int32_t f = fa; f < fb; ++f)
+        if (t0 >= leno) {
+            const Vf<V> z = vzero<V>();
+            for (int32_t f = fa; f < fb; ++f)
 #pragma unroll
-            for (int i = 0; i < TO; ++i) Buf<float, V>::store(yr, (uint32_t)(t0 + i) * yrow + f * pix + coff, z);
-#if DW2D_FWD_PERSIST
-        continue;
-#else
-        return;
-#endif
-    }
-
-    Vf<V> wk[9];
-#pragma unroll
-    for (int k = 0; k < 9; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
-    const Vf<V> bv = bias ? load_param<float, V>(bias + c0) : vzero<V>();
-
-    // Input rows 2t0-1+r, r = 0 .. 2*TO; byte offset of each row start (a
-    // negative row wraps out of range and reads zero).
-    uint32_t roff[2 * TO + 1];
-#pragma unroll
-    for (int r = 0; r < 2 * TO + 1; ++r) roff[r] = (uint32_t)((2 * t0 - 1 + r) * (int32_t)xrow) + coff;
-
-    Vf<V> carry[2 * TO + 1];  // input column 2f'-1 (zero left of the first column)
-#pragma unroll
-    for (int r = 0; r < 2 * TO + 1; ++r)
-        carry[r] = fa > 0 ? Buf<float, V>::load(xr, roff[r] + (uint32_t)(2 * fa - 1) * pix) : vzero<V>();
-
-    for (int32_t f = fa; f < fb; ++f) {
-        const uint32_t c_even = (uint32_t)(2 * f) * pix;
-        const bool odd_ok = 2 * f + 1 < F;  // column 2f'+1 exists
-        Vf<V> ce[2 * TO + 1], co[2 * TO + 1];
-#pragma unroll
-        for (int r = 0; r < 2 * TO + 1; ++r) {
-            ce[r] = Buf<float, V>::load(xr, roff[r] + c_even);
-            co[r] = Buf<float, V>::load(xr, roff[r] + c_even + pix);
+                for (int i = 0; i < TO; ++i)
+                    Buf<S, V>::store(yr, (uint32_t)(t0 + i) * yrow + (uint32_t)(f * pix) + coff, z);
+            continue;
         }
+
+        Vf<V> wk[9];
 #pragma unroll
-        for (int r = 0; r < 2 * TO + 1; ++r) co[r] = select_v<V>(odd_ok, co[r]);
+        for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
+        const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
+
+        // Input rows 2t0-1-dt+r, r = 0 .. 2*TO; byte offset of each row start
+        // (a negative row wraps out of range and reads zero).
+        uint32_t roff[2 * TO + 1];
 #pragma unroll
-        for (int i = 0; i < TO; ++i) {
-            Vf<V> acc = bv;
+        for (int r = 0; r < 2 * TO + 1; ++r) roff[r] = (uint32_t)((2 * t0 - 1 - geo.dt + r) * (int32_t)xrow) + coff;
+
+        // Input column 2f'-1-df, carried; zero left of the first column.
+        const int32_t c_first = 2 * fa - 1 - geo.df;
+        Vf<V> carry[2 * TO + 1];
 #pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                fma_v<V>(acc, carry[2 * i + a], wk[3 * a + 0]);
-                fma_v<V>(acc, ce[2 * i + a], wk[3 * a + 1]);
-                fma_v<V>(acc, co[2 * i + a], wk[3 * a + 2]);
+        for (int r = 0; r < 2 * TO + 1; ++r)
+            carry[r] = c_first >= 0 ? Buf<S, V>::load(xr, roff[r] + (uint32_t)(c_first * pix)) : vzero<V>();
+
+        for (int32_t f = fa; f < fb; ++f) {
+            const int32_t ce = 2 * f - geo.df;           // input columns ce, ce + 1
+            const uint32_t eo = ce >= 0 && ce < F ? (uint32_t)(ce * pix) : kOutOfRange;
+            const uint32_t oo = ce + 1 < F ? (uint32_t)((ce + 1) * pix) : kOutOfRange;
+            Vf<V> xe[2 * TO + 1], xo[2 * TO + 1];
+#pragma unroll
+            for (int r = 0; r < 2 * TO + 1; ++r) {
+                xe[r] = Buf<S, V>::load(xr, roff[r] + eo);
+                xo[r] = Buf<S, V>::load(xr, roff[r] + oo);
             }
-            acc = select_v<V>(t0 + i < leno, acc);
-            Buf<float, V>::store(yr, (uint32_t)(t0 + i) * yrow + f * pix + coff, acc);
-        }
 #pragma unroll
-        for (int r = 0; r < 2 * TO + 1; ++r) carry[r] = co[r];
+            for (int i = 0; i < TO; ++i) {
+                Vf<V> acc = bv;
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    fma_v<V>(acc, carry[2 * i + a], wk[3 * a + 0]);
+                    fma_v<V>(acc, xe[2 * i + a], wk[3 * a + 1]);
+                    fma_v<V>(acc, xo[2 * i + a], wk[3 * a + 2]);
+                }
+                acc = select_v<V>(t0 + i < leno, acc);
+                Buf<S, V>::store(yr, (uint32_t)(t0 + i) * yrow + (uint32_t)(f * pix) + coff, acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 2 * TO + 1; ++r) carry[r] = xo[r];
+        }
     }
-#if DW2D_FWD_PERSIST
-    }  // row groups
-#endif
 }
-
-#ifdef DW2D_FWD_PIXEL
-// Experimental: one output pixel (V channels) per thread, 9 loads through L2.
-template <int V>
-__global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_pixel_kernel(
-    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
-    const int32_t* __restrict__ lengths, float* __restrict__ y,
-    int32_t T, int32_t F, int32_t C, int32_t To, int32_t Fo, uint32_t CG, uint32_t blocks_per_item) {
-    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
-    const uint32_t b = blk / blocks_per_item;
-    const uint32_t local = (blk - b * blocks_per_item) * kBlock2d + threadIdx.x;
-    const uint32_t pixel = local / CG, cg = local - pixel * CG;
-    if (pixel >= (uint32_t)(To * Fo)) return;
-    const int32_t to = (int32_t)(pixel / Fo), fo = (int32_t)(pixel % Fo);
-    const int32_t len = (int32_t)item_length(lengths, b, T);
-    const int32_t leno = (len + 1) / 2;
-    const uint32_t xrow = (uint32_t)F * C * 4, pix = (uint32_t)C * 4;
-    const rsrc_t xr = make_rsrc(x + (int64_t)b * T * F * C, (uint32_t)len * xrow);
-    const rsrc_t yr = make_rsrc(y + (int64_t)b * To * Fo * C, (uint32_t)To * Fo * pix);
-    const int32_t c0 = (int32_t)cg * V;
-    const uint32_t coff = (uint32_t)c0 * 4;
-    const uint32_t yo = (uint32_t)pixel * pix + coff;
-    if (to >= leno) { Buf<float, V>::store(yr, yo, vzero<V>()); return; }
-    Vf<V> xv[9];
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            const int32_t f = 2 * fo + j - 1;
-            xv[3 * i + j] = Buf<float, V>::load(xr, (uint32_t)((2 * to + i - 1) * (int32_t)xrow + f * (int32_t)pix) + coff);
-            if (f < 0 || f >= F) xv[3 * i + j] = vzero<V>();
-        }
-    Vf<V> acc = bias ? load_param<float, V>(bias + c0) : vzero<V>();
-#pragma unroll
-    for (int k = 0; k < 9; ++k) fma_v<V>(acc, xv[k], load_param<float, V>(w + (int64_t)k * C + c0));
-    Buf<float, V>::store(yr, yo, acc);
-}
-#endif
 
 // ------------------------------------------------------------------ bwd ----
 
-template <int V, int TQ>
+template <typename S, int V, int TQ>
 __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
-    const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
-    const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial,
-    int32_t T, int32_t F, int32_t C, int32_t To, int32_t Fo,
+    const S* __restrict__ x, const S* __restrict__ w, const int32_t* __restrict__ lengths,
+    const S* __restrict__ dy, S* __restrict__ dx, double* __restrict__ partial, Geo2d geo,
     uint32_t n_rb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
+    constexpr int32_t es = (int32_t)sizeof(S);
+    const int32_t T = geo.T, F = geo.F, C = geo.C, To = geo.To, Fo = geo.Fo;
     __shared__ double red[kRowsPerBlock - 1][10][kLanes2d * V];
     // Workgroup = kRowsPerBlock waves x kLanes2d channel groups.  The batch's
     // row groups (kRowsPerBlock row blocks each, items one after the other)
@@ -269,100 +250,119 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     }
 
     for (uint32_t j = g; j < n_groups; j += G) {
-    Tile2d d;
-    d.b = j / groups_per_item;
-    d.cg = cg;
-    d.rb = (j - d.b * groups_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
-    d.valid = d.rb < n_rb && d.cg < CG;
-    if (d.valid) {
-        const int32_t len = (int32_t)item_length(lengths, d.b, T);
-        const int32_t leno = (len + 1) / 2;
-        const uint32_t xrow = (uint32_t)F * C * 4, grow = (uint32_t)Fo * C * 4, pix = (uint32_t)C * 4;
-        const int64_t xitem = (int64_t)d.b * T * F * C;
+        const uint32_t b = j / groups_per_item;
+        const uint32_t rb = (j - b * groups_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
+        if (rb >= n_rb || cg >= CG) continue;
+        const int32_t len = (int32_t)item_length(lengths, b, T);
+        const int32_t leno = out_rows(len, geo);
+        const uint32_t xrow = (uint32_t)(F * C * es), grow = (uint32_t)(Fo * C * es);
+        const int32_t pix = C * es;
+        const int64_t xitem = (int64_t)b * T * F * C;
         const rsrc_t xr = make_rsrc(x + xitem, (uint32_t)len * xrow);
-        const rsrc_t gr = make_rsrc(dy + (int64_t)d.b * To * Fo * C, (uint32_t)leno * grow);
+        const rsrc_t gr = make_rsrc(dy + (int64_t)b * To * Fo * C, (uint32_t)leno * grow);
         const rsrc_t dxr = make_rsrc(dx ? dx + xitem : x, dx ? (uint32_t)T * xrow : 0u);
-        const uint32_t coff = (uint32_t)c0 * 4;
-        const int32_t t0 = (int32_t)d.rb * TQ;  // first quad row
+        const uint32_t coff = (uint32_t)(c0 * es);
+        const int32_t t0 = (int32_t)rb * TQ;       // first quad row
+        const int32_t xr0 = 2 * t0 - geo.dt;       // its first x row
 
-        if (2 * t0 >= len) {
-            // Every x row of this block is masked, so is every g row it
-            // touches: dx is zero and nothing adds to dw or db.
+        if (xr0 >= len && t0 >= leno) {
+            // Every x row of this block is masked, and so is every g row it
+            // adds to db: dx is zero and nothing adds to dw or db.
             if (dx) {
                 const Vf<V> z = vzero<V>();
                 for (int32_t f = 0; f < F; ++f)
 #pragma unroll
                     for (int r = 0; r < 2 * TQ; ++r)
-                        Buf<float, V>::store(dxr, (uint32_t)(2 * t0 + r) * xrow + f * pix + coff, z);
+                        Buf<S, V>::store(dxr, (uint32_t)(xr0 + r) * xrow + (uint32_t)(f * pix) + coff, z);
             }
-        } else {
-            Vf<V> wk[9];
+            continue;
+        }
+        Vf<V> wk[9];
 #pragma unroll
-            for (int k = 0; k < 9; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
-            // g rows t0 .. t0+TQ (the last one belongs to the next block).
-            Vf<V> gcur[TQ + 1];
+        for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
+        // g rows t0 .. t0+TQ (the last one belongs to the next block), column 0.
+        Vf<V> gcur[TQ + 1];
+        const uint32_t no0 = Fo > 0 ? 0u : kOutOfRange;
+#pragma unroll
+        for (int q = 0; q <= TQ; ++q) gcur[q] = Buf<S, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow) + coff + no0);
+
+        // Loads for quad column n: g column n+1, and x columns 2n-df and
+        // 2n-df+1, each replaced by an out-of-range offset (which reads zero
+        // with no memory traffic) where it does not exist.
+        auto load_col = [&](int32_t n, Vf<V>(&gn)[TQ + 1], Vf<V>(&xe)[2 * TQ], Vf<V>(&xo)[2 * TQ]) {
+            const int32_t ce = 2 * n - geo.df;
+            // g column n+1 (past the last column it is loaded from the next
+            // row, or read as zero past the valid rows, and then discarded)
 #pragma unroll
             for (int q = 0; q <= TQ; ++q)
-                gcur[q] = Buf<float, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow) + coff);
-            for (int32_t f = 0; f < Fo; ++f) {
-                const bool next_ok = f + 1 < Fo;      // g column f'+1 exists
-                const bool odd_ok = 2 * f + 1 < F;    // x column 2f'+1 exists
-                Vf<V> gnext[TQ + 1], xe[2 * TQ], xo[2 * TQ];
+                gn[q] = select_v<V>(n + 1 < Fo,
+                                    Buf<S, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow + (n + 1) * pix) + coff));
+            const uint32_t eo = ce >= 0 && ce < F ? (uint32_t)(ce * pix) : kOutOfRange;
+            const uint32_t oo = ce + 1 < F ? (uint32_t)((ce + 1) * pix) : kOutOfRange;
 #pragma unroll
-                for (int q = 0; q <= TQ; ++q)
-                    gnext[q] = Buf<float, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow) + (f + 1) * pix + coff);
+            for (int r = 0; r < 2 * TQ; ++r) {
+                const uint32_t ro = (uint32_t)((xr0 + r) * (int32_t)xrow) + coff;
+                xe[r] = Buf<S, V>::load(xr, ro + eo);
+                xo[r] = Buf<S, V>::load(xr, ro + oo);
+            }
+        };
+        // The quads of column n, given its loads; g column n+1 becomes the
+        // current column afterwards.
+        auto quads = [&](int32_t n, const Vf<V>(&gnext)[TQ + 1], const Vf<V>(&xe)[2 * TQ],
+                         const Vf<V>(&xo)[2 * TQ]) {
+            const int32_t ce = 2 * n - geo.df;
+            const bool ce_ok = ce >= 0 && ce < F, co_ok = ce + 1 < F;
 #pragma unroll
-                for (int r = 0; r < 2 * TQ; ++r) {
-                    const uint32_t ro = (uint32_t)(2 * t0 + r) * xrow + (uint32_t)(2 * f) * pix + coff;
-                    xe[r] = Buf<float, V>::load(xr, ro);
-                    xo[r] = Buf<float, V>::load(xr, ro + pix);
-                }
+            for (int q = 0; q < TQ; ++q) {
+                const Vf<V>& g00 = gcur[q];       // g[t', f']
+                const Vf<V>& g01 = gnext[q];      // g[t', f'+1]
+                const Vf<V>& g10 = gcur[q + 1];   // g[t'+1, f']
+                const Vf<V>& g11 = gnext[q + 1];  // g[t'+1, f'+1]
+                const Vf<V>& x00 = xe[2 * q];
+                const Vf<V>& x01 = xo[2 * q];
+                const Vf<V>& x10 = xe[2 * q + 1];
+                const Vf<V>& x11 = xo[2 * q + 1];
+                // tap index k = 3*i + j of w[i][j]
+                Vf<V> d00 = vzero<V>(), d01 = vzero<V>(), d10 = vzero<V>(), d11 = vzero<V>();
+                fma_v<V>(d00, g00, wk[4]);
+                fma_v<V>(d01, g00, wk[5]); fma_v<V>(d01, g01, wk[3]);
+                fma_v<V>(d10, g00, wk[7]); fma_v<V>(d10, g10, wk[1]);
+                fma_v<V>(d11, g00, wk[8]); fma_v<V>(d11, g01, wk[6]);
+                fma_v<V>(d11, g10, wk[2]); fma_v<V>(d11, g11, wk[0]);
+                fma_d<V>(gw[4], g00, x00);
+                fma_d<V>(gw[5], g00, x01); fma_d<V>(gw[3], g01, x01);
+                fma_d<V>(gw[7], g00, x10); fma_d<V>(gw[1], g10, x10);
+                fma_d<V>(gw[8], g00, x11); fma_d<V>(gw[6], g01, x11);
+                fma_d<V>(gw[2], g10, x11); fma_d<V>(gw[0], g11, x11);
 #pragma unroll
-                for (int q = 0; q <= TQ; ++q) gnext[q] = select_v<V>(next_ok, gnext[q]);
-#pragma unroll
-                for (int r = 0; r < 2 * TQ; ++r) xo[r] = select_v<V>(odd_ok, xo[r]);
-#pragma unroll
-                for (int q = 0; q < TQ; ++q) {
-                    const Vf<V>& g00 = gcur[q];       // g[t', f']
-                    const Vf<V>& g01 = gnext[q];      // g[t', f'+1]
-                    const Vf<V>& g10 = gcur[q + 1];   // g[t'+1, f']
-                    const Vf<V>& g11 = gnext[q + 1];  // g[t'+1, f'+1]
-                    const Vf<V>& x00 = xe[2 * q];
-                    const Vf<V>& x01 = xo[2 * q];
-                    const Vf<V>& x10 = xe[2 * q + 1];
-                    const Vf<V>& x11 = xo[2 * q + 1];
-                    // tap index k = 3*i + j of w[i][j]
-                    Vf<V> d00 = vzero<V>(), d01 = vzero<V>(), d10 = vzero<V>(), d11 = vzero<V>();
-                    fma_v<V>(d00, g00, wk[4]);
-                    fma_v<V>(d01, g00, wk[5]); fma_v<V>(d01, g01, wk[3]);
-                    fma_v<V>(d10, g00, wk[7]); fma_v<V>(d10, g10, wk[1]);
-                    fma_v<V>(d11, g00, wk[8]); fma_v<V>(d11, g01, wk[6]);
-                    fma_v<V>(d11, g10, wk[2]); fma_v<V>(d11, g11, wk[0]);
-                    fma_d<V>(gw[4], g00, x00);
-                    fma_d<V>(gw[5], g00, x01); fma_d<V>(gw[3], g01, x01);
-                    fma_d<V>(gw[7], g00, x10); fma_d<V>(gw[1], g10, x10);
-                    fma_d<V>(gw[8], g00, x11); fma_d<V>(gw[6], g01, x11);
-                    fma_d<V>(gw[2], g10, x11); fma_d<V>(gw[0], g11, x11);
-#pragma unroll
-                    for (int e = 0; e < V; ++e) gb[e] += (double)g00.v[e];
-                    if (dx) {
-                        const int32_t te = 2 * (t0 + q);
-                        const uint32_t o = (uint32_t)te * xrow + (uint32_t)(2 * f) * pix + coff;
-                        Buf<float, V>::store(dxr, o, select_v<V>(te < len, d00));
-                        Buf<float, V>::store(dxr, o + xrow, select_v<V>(te + 1 < len, d10));
-                        if (odd_ok) {
-                            Buf<float, V>::store(dxr, o + pix, select_v<V>(te < len, d01));
-                            Buf<float, V>::store(dxr, o + xrow + pix, select_v<V>(te + 1 < len, d11));
-                        }
+                for (int e = 0; e < V; ++e) gb[e] += (double)g00.v[e];
+                if (dx) {
+                    // Row xr0 + 2q may be -1 (top padding): its offset is
+                    // negative, out of range, and the store is dropped.  A
+                    // column outside [0, F) would land in a neighbouring
+                    // row, so those stores are skipped.
+                    const int32_t te = xr0 + 2 * q;
+                    const uint32_t o = (uint32_t)(te * (int32_t)xrow + ce * pix) + coff;  // used where ce_ok
+                    if (ce_ok) {
+                        Buf<S, V>::store(dxr, o, select_v<V>(te < len, d00));
+                        Buf<S, V>::store(dxr, o + xrow, select_v<V>(te + 1 < len, d10));
+                    }
+                    if (co_ok) {
+                        Buf<S, V>::store(dxr, o + (uint32_t)pix, select_v<V>(te < len, d01));
+                        Buf<S, V>::store(dxr, o + xrow + (uint32_t)pix, select_v<V>(te + 1 < len, d11));
                     }
                 }
-#pragma unroll
-                for (int q = 0; q <= TQ; ++q) gcur[q] = gnext[q];
             }
+#pragma unroll
+            for (int q = 0; q <= TQ; ++q) gcur[q] = gnext[q];
+        };
+
+        for (int32_t n = 0; n < geo.NQf; ++n) {
+            Vf<V> gn[TQ + 1], xe[2 * TQ], xo[2 * TQ];
+            load_col(n, gn, xe, xo);
+            quads(n, gn, xe, xo);
         }
     }
-
-    }  // row groups
 
     if (!partial) return;  // uniform: dw and db not requested
     // Sum the row blocks of this workgroup in a fixed order (row block 0
@@ -396,66 +396,93 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
 
 // ------------------------------------------------------------- launchers ----
 
-struct Grid2d {
-    uint32_t n_rb, CG, n_cblk, wg_per_item;
-    uint64_t blocks;
-};
+static int64_t floor_half(int64_t n) { return n >= 0 ? n / 2 : (n - 1) / 2; }
 
-static Grid2d grid_2d(int64_t B, int64_t rows, int rows_per_thread, int64_t C, int vec) {
-    Grid2d g;
-    g.n_rb = (uint32_t)((rows + rows_per_thread - 1) / rows_per_thread);
-    g.CG = (uint32_t)(C / vec);
-    g.n_cblk = (g.CG + kLanes2d - 1) / kLanes2d;
-    const uint32_t rgroups = (g.n_rb + kRowsPerBlock - 1) / kRowsPerBlock;
-    g.wg_per_item = rgroups * g.n_cblk;
-    g.blocks = (uint64_t)B * g.wg_per_item;
+Conv2dGeom conv2d_geom(int64_t T, int64_t F, int64_t C, int64_t pt0, int64_t pt1, int64_t pf0, int64_t pf1) {
+    Conv2dGeom g;
+    g.T = T; g.F = F; g.C = C;
+    g.pt0 = pt0; g.pt1 = pt1; g.pf0 = pf0; g.pf1 = pf1;
+    const int64_t to = floor_half(T + pt0 + pt1 - 3) + 1, fo = floor_half(F + pf0 + pf1 - 3) + 1;
+    g.To = to < 0 ? 0 : to;
+    g.Fo = fo < 0 ? 0 : fo;
     return g;
 }
 
-bool dwconv2d_fits(int64_t B, int64_t T, int64_t F, int64_t C, int vec) {
-    // Per-item byte offsets (with one row of slack on each side) must stay
-    // within a signed 32-bit range.
-    if ((T + 2) * F * C * 4 >= ((int64_t)1 << 31)) return false;
-    const int64_t To = (T + 1) / 2;
-    const Grid2d g = grid_2d(B, To, 1, C, vec);
-    return g.blocks < ((uint64_t)1 << 31);
+bool dwconv2d_pads_supported(int64_t pt0, int64_t pt1, int64_t pf0, int64_t pf1) {
+    return pt0 >= 1 && pt0 <= 2 && pf0 >= 1 && pf0 <= 2 && pt1 >= 0 && pt1 <= 2 && pf1 >= 0 && pf1 <= 2;
 }
 
-template <int V>
-static hipError_t launch_fwd_typed(const float* x, const float* w, const float* bias, const int32_t* lengths,
-                                   float* y, int64_t B, int64_t T, int64_t F, int64_t C, hipStream_t st) {
-    const int64_t To = (T + 1) / 2, Fo = (F + 1) / 2;
-#ifdef DW2D_FWD_PIXEL
-    {
-        const uint32_t CG = (uint32_t)(C / V);
-        const uint32_t bpi = (uint32_t)(((uint64_t)To * Fo * CG + kBlock2d - 1) / kBlock2d);
-        hipLaunchKernelGGL((dwconv2d_fwd_pixel_kernel<V>), dim3((uint32_t)(B * bpi)), dim3(kBlock2d), 0, st, x, w,
-                           bias, lengths, y, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To, (int32_t)Fo, CG, bpi);
-        return hipGetLastError();
-    }
-#endif
-    const int64_t nfc = kFwdCols > 0 ? (Fo + kFwdCols - 1) / kFwdCols : 1;
-    Grid2d g = grid_2d(B, To, kFwdRows, C, V);
-    if (nfc > 1) g = grid_2d(B, ((To + kFwdRows - 1) / kFwdRows) * nfc * kFwdRows, kFwdRows, C, V);
-#if DW2D_FWD_PERSIST
-    const uint32_t gpi = g.wg_per_item / g.n_cblk;  // row groups per item
+static Geo2d device_geo(const Conv2dGeom& c) {
+    Geo2d g;
+    g.T = (int32_t)c.T; g.F = (int32_t)c.F; g.C = (int32_t)c.C;
+    g.To = (int32_t)c.To; g.Fo = (int32_t)c.Fo;
+    g.dt = (int32_t)(c.pt0 - 1); g.df = (int32_t)(c.pf0 - 1);
+    g.len_add = (int32_t)(c.pt0 + c.pt1 - 3);
+    const int64_t nqt = (c.T + g.dt + 1) / 2, nqf = (c.F + g.df + 1) / 2;
+    g.NQt = (int32_t)(nqt > c.To ? nqt : c.To);
+    g.NQf = (int32_t)(nqf > c.Fo ? nqf : c.Fo);
+    // kFwdCols columns per chunk, evened out over the chunks F' needs
+    const int64_t nfc = c.Fo > 0 ? (c.Fo + kFwdCols - 1) / kFwdCols : 1;
+    g.fcols = (int32_t)(c.Fo > 0 ? (c.Fo + nfc - 1) / nfc : 1);
+    return g;
+}
+
+bool dwconv2d_fits(int64_t B, const Conv2dGeom& g, int elem_bytes) {
+    // Per-item byte offsets (with two rows of slack on each side) must stay
+    // within a signed 32-bit range, and the row groups within 32 bits.
+    if ((g.T + 4) * g.F * g.C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    if ((g.To + 4) * (g.Fo + 2) * g.C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    if ((g.F + 4) * g.C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    return (uint64_t)B * (uint64_t)(g.T / 2 + 2) * (uint64_t)(g.F / 2 + 2) < ((uint64_t)1 << 31);
+}
+
+template <typename S, int V, int LANES>
+static hipError_t launch_fwd_lanes(const S* x, const S* w, const S* bias, const int32_t* lengths, S* y, int64_t B,
+                                   const Conv2dGeom& c, hipStream_t st) {
+    constexpr uint32_t kRB = kBlock2d / LANES;
+    const Geo2d geo = device_geo(c);
+    const int64_t nfc = (c.Fo + geo.fcols - 1) / geo.fcols;
+    const uint32_t n_rb = (uint32_t)(((c.To + kFwdRows - 1) / kFwdRows) * nfc);
+    const uint32_t CG = (uint32_t)(c.C / V);
+    const uint32_t n_cblk = (CG + LANES - 1) / LANES;
+    const uint32_t gpi = (n_rb + kRB - 1) / kRB;  // row groups per item
     const uint64_t ng = (uint64_t)B * gpi;
-    g.blocks = (ng < DW2D_FWD_PERSIST ? ng : DW2D_FWD_PERSIST) * g.n_cblk;
-    g.wg_per_item = gpi;
-#endif
-    hipLaunchKernelGGL((dwconv2d_fwd_kernel<V, kFwdRows>), dim3((uint32_t)g.blocks), dim3(kBlock2d), 0, st, x, w,
-                       bias, lengths, y, (int32_t)B, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To, (int32_t)Fo,
-                       g.n_rb, g.CG, g.n_cblk, g.wg_per_item);
+    if (ng == 0 || n_cblk == 0) return hipSuccess;
+    const uint64_t blocks = (ng < DW2D_FWD_PERSIST ? ng : DW2D_FWD_PERSIST) * n_cblk;
+    hipLaunchKernelGGL((dwconv2d_fwd_kernel<S, V, kFwdRows, LANES>), dim3((uint32_t)blocks), dim3(kBlock2d), 0, st,
+                       x, w, bias, lengths, y, geo, (int32_t)B, n_rb, CG, n_cblk, gpi);
     return hipGetLastError();
 }
 
-hipError_t launch_dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths,
-                               float* y, int64_t B, int64_t T, int64_t F, int64_t C, int vec, hipStream_t st) {
+template <typename S, int V>
+static hipError_t launch_fwd_typed(const S* x, const S* w, const S* bias, const int32_t* lengths, S* y, int64_t B,
+                                   const Conv2dGeom& c, hipStream_t st) {
+    if (c.C / V <= 32) return launch_fwd_lanes<S, V, 32>(x, w, bias, lengths, y, B, c, st);
+    return launch_fwd_lanes<S, V, 64>(x, w, bias, lengths, y, B, c, st);
+}
+
+template <typename S>
+static hipError_t launch_fwd_s(const void* x, const void* w, const void* bias, const int32_t* lengths, void* y,
+                               int64_t B, const Conv2dGeom& c, int vec, hipStream_t st) {
+    const S* xs = (const S*)x;
+    const S* ws = (const S*)w;
+    const S* bs = (const S*)bias;
+    S* ys = (S*)y;
     switch (vec) {
-        case 4: return launch_fwd_typed<4>(x, w, bias, lengths, y, B, T, F, C, st);
-        case 2: return launch_fwd_typed<2>(x, w, bias, lengths, y, B, T, F, C, st);
-        default: return launch_fwd_typed<1>(x, w, bias, lengths, y, B, T, F, C, st);
+        case 8:
+            if constexpr (sizeof(S) == 2 && DW2D_FWD_BF16_VEC >= 8)
+                return launch_fwd_typed<S, 8>(xs, ws, bs, lengths, ys, B, c, st);
+            return launch_fwd_typed<S, 4>(xs, ws, bs, lengths, ys, B, c, st);
+        case 4: return launch_fwd_typed<S, 4>(xs, ws, bs, lengths, ys, B, c, st);
+        case 2: return launch_fwd_typed<S, 2>(xs, ws, bs, lengths, ys, B, c, st);
+        default: return launch_fwd_typed<S, 1>(xs, ws, bs, lengths, ys, B, c, st);
     }
+}
+
+hipError_t launch_dwconv2d_fwd(const void* x, const void* w, const void* bias, const int32_t* lengths, void* y,
+                               int64_t B, const Conv2dGeom& c, bool bf16, int vec, hipStream_t st) {
+    return bf16 ? launch_fwd_s<uint16_t>(x, w, bias, lengths, y, B, c, vec, st)
+                : launch_fwd_s<float>(x, w, bias, lengths, y, B, c, vec, st);
 }
 
 #ifndef DW2D_BWD_TARGET_WGS
@@ -473,10 +500,9 @@ struct BwdGrid {
     int64_t P;
 };
 
-static BwdGrid bwd_grid(int64_t B, int64_t T) {
+static BwdGrid bwd_grid(int64_t B, const Geo2d& geo, int rows) {
     BwdGrid g;
-    const int64_t To = (T + 1) / 2;
-    g.n_rb = (uint32_t)((To + kBwdRows - 1) / kBwdRows);
+    g.n_rb = (uint32_t)((geo.NQt + rows - 1) / rows);
     g.groups_per_item = (g.n_rb + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t n = B * (int64_t)g.groups_per_item;
     g.n_groups = (uint32_t)n;
@@ -485,27 +511,28 @@ static BwdGrid bwd_grid(int64_t B, int64_t T) {
     return g;
 }
 
-size_t dwconv2d_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C) {
-    (void)F;
-    // [P][10][C] workgroup partials, then [chunks][10][C] chunk sums, fp64.
-    const int64_t P = bwd_grid(B, T).P;
+size_t dwconv2d_bwd_workspace(int64_t B, const Conv2dGeom& c) {
+    // [P][10][C] workgroup partials, then [chunks][10][C] chunk sums, fp64
+    // (sized for either storage type's grid).
+    const Geo2d geo = device_geo(c);
+    const int64_t P1 = bwd_grid(B, geo, bwd_rows<float>()).P, P2 = bwd_grid(B, geo, bwd_rows<uint16_t>()).P;
+    const int64_t P = P1 > P2 ? P1 : P2;
     const int64_t rows = P + (partial_reduce_chunks(P) > 0 ? partial_reduce_chunks(P) : 1);
-    return (size_t)(rows * 10 * C * (int64_t)sizeof(double));
+    return (size_t)(rows * 10 * c.C * (int64_t)sizeof(double));
 }
 
-template <int V>
-static hipError_t launch_bwd_typed(const float* x, const float* w, const int32_t* lengths, const float* dy,
-                                   float* dx, float* dw, float* db, double* partial, int64_t B, int64_t T,
-                                   int64_t F, int64_t C, hipStream_t st) {
-    const int64_t To = (T + 1) / 2, Fo = (F + 1) / 2;
-    const BwdGrid g = bwd_grid(B, T);
-    const uint32_t CG = (uint32_t)(C / V);
+template <typename S, int V>
+static hipError_t launch_bwd_typed(const S* x, const S* w, const int32_t* lengths, const S* dy, S* dx, float* dw,
+                                   float* db, double* partial, int64_t B, const Conv2dGeom& c, hipStream_t st) {
+    const Geo2d geo = device_geo(c);
+    constexpr int TQ = bwd_rows<S>();
+    const BwdGrid g = bwd_grid(B, geo, TQ);
+    const uint32_t CG = (uint32_t)(c.C / V);
     const uint32_t n_cblk = (CG + kLanes2d - 1) / kLanes2d;
     const uint64_t blocks = (uint64_t)g.G * n_cblk;
     if (blocks > 0 && (dx || partial)) {
-        hipLaunchKernelGGL((dwconv2d_bwd_kernel<V, kBwdRows>), dim3((uint32_t)blocks), dim3(kBlock2d), 0, st, x,
-                           w, lengths, dy, dx, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)To,
-                           (int32_t)Fo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
+        hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ>), dim3((uint32_t)blocks), dim3(kBlock2d), 0, st, x,
+                           w, lengths, dy, dx, partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -514,7 +541,7 @@ static hipError_t launch_bwd_typed(const float* x, const float* w, const int32_t
         out.n = 2;
         out.p[0] = dw; out.first[0] = 0; out.count[0] = 9;
         out.p[1] = db; out.first[1] = 9; out.count[1] = 1;
-        return launch_partial_reduce(partial, g.P, 10, C, partial + g.P * 10 * C, out, st);
+        return launch_partial_reduce(partial, g.P, 10, c.C, partial + g.P * 10 * c.C, out, st);
     }
     return hipSuccess;
 }
@@ -523,16 +550,28 @@ static hipError_t launch_bwd_typed(const float* x, const float* w, const int32_t
 #define DW2D_BWD_VEC 4
 #endif
 
-hipError_t launch_dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy,
-                               float* dx, float* dw, float* db, void* workspace, int64_t B, int64_t T,
-                               int64_t F, int64_t C, int vec, hipStream_t st) {
-    double* partial = (dw || db) ? (double*)workspace : nullptr;
+template <typename S>
+static hipError_t launch_bwd_s(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
+                               float* dw, float* db, double* partial, int64_t B, const Conv2dGeom& c, int vec,
+                               hipStream_t st) {
+    const S* xs = (const S*)x;
+    const S* ws = (const S*)w;
+    const S* gs = (const S*)dy;
+    S* dxs = (S*)dx;
     if (vec > DW2D_BWD_VEC) vec = DW2D_BWD_VEC;
     switch (vec) {
-        case 4: return launch_bwd_typed<4>(x, w, lengths, dy, dx, dw, db, partial, B, T, F, C, st);
-        case 2: return launch_bwd_typed<2>(x, w, lengths, dy, dx, dw, db, partial, B, T, F, C, st);
-        default: return launch_bwd_typed<1>(x, w, lengths, dy, dx, dw, db, partial, B, T, F, C, st);
+        case 4: return launch_bwd_typed<S, 4>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
+        case 2: return launch_bwd_typed<S, 2>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
+        default: return launch_bwd_typed<S, 1>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
     }
+}
+
+hipError_t launch_dwconv2d_bwd(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
+                               float* dw, float* db, void* workspace, int64_t B, const Conv2dGeom& c, bool bf16,
+                               int vec, hipStream_t st) {
+    double* partial = (dw || db) ? (double*)workspace : nullptr;
+    return bf16 ? launch_bwd_s<uint16_t>(x, w, lengths, dy, dx, dw, db, partial, B, c, vec, st)
+                : launch_bwd_s<float>(x, w, lengths, dy, dx, dw, db, partial, B, c, vec, st);
 }
 
 }  // namespace dw

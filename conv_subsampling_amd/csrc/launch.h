@@ -57,13 +57,24 @@ hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* 
                                   float* db1, void* workspace, int64_t B, int64_t T, int64_t F, int64_t C,
                                   hipStream_t stream);
 
-bool dwconv2d_fits(int64_t B, int64_t T, int64_t F, int64_t C, int vec);
+// A 3x3, stride-2 depthwise conv2d with pt0 / pt1 zero rows before / after
+// the input in time and pf0 / pf1 columns in frequency, and its output extent.
+struct Conv2dGeom {
+    int64_t T, F, C;
+    int64_t pt0, pt1, pf0, pf1;
+    int64_t To, Fo;
+};
+Conv2dGeom conv2d_geom(int64_t T, int64_t F, int64_t C, int64_t pt0, int64_t pt1, int64_t pf0, int64_t pf1);
 
-hipError_t launch_dwconv2d_fwd(const float* x, const float* w, const float* bias, const int32_t* lengths,
-                               float* y, int64_t B, int64_t T, int64_t F, int64_t C, int vec,
-                               hipStream_t stream);
+// The paddings with a kernel: 1 or 2 before, 0 to 2 after, on each axis.
+bool dwconv2d_pads_supported(int64_t pt0, int64_t pt1, int64_t pf0, int64_t pf1);
 
-size_t dwconv2d_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C);
+bool dwconv2d_fits(int64_t B, const Conv2dGeom& g, int elem_bytes);
+
+hipError_t launch_dwconv2d_fwd(const void* x, const void* w, const void* bias, const int32_t* lengths, void* y,
+                               int64_t B, const Conv2dGeom& g, bool bf16, int vec, hipStream_t stream);
+
+size_t dwconv2d_bwd_workspace(int64_t B, const Conv2dGeom& g);
 
 // Number of fp64 [K][C] rows of scratch launch_partial_reduce needs after the
 // P partial rows (at least one).
@@ -74,8 +85,8 @@ int64_t partial_reduce_chunks(int64_t P);
 hipError_t launch_partial_reduce(const double* partial, int64_t P, int32_t K, int64_t C, double* chunk_sum,
                                  RowOutputs out, hipStream_t stream);
 
-hipError_t launch_dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy,
-                               float* dx, float* dw, float* db, void* workspace,
-                               int64_t B, int64_t T, int64_t F, int64_t C, int vec, hipStream_t stream);
+hipError_t launch_dwconv2d_bwd(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
+                               float* dw, float* db, void* workspace, int64_t B, const Conv2dGeom& g, bool bf16,
+                               int vec, hipStream_t stream);
 
 }  // namespace dw

@@ -122,12 +122,14 @@ def conv1d_causal_sweep(K, device="cpu", seed=DEFAULT_SEED, B=32, T=1500, C=512)
     )
 
 
-def conv2d_stage(device="cpu", seed=DEFAULT_SEED, B=32, T=1500, F=64, C=256):
+def conv2d_stage(device="cpu", seed=DEFAULT_SEED, B=32, T=1500, F=64, C=256, dy_rows_cols=None, bf16=False):
     """Depthwise 3x3 stride-2 conv2d fwd+bwd: x = max(N(0,1), 0) [B,T,F,C],
-    dy ~ N(0,1) [B,ceil(T/2),ceil(F/2),C]; lengths ~U[T/2, T] in input frames."""
-    T2, F2 = (T + 1) // 2, (F + 1) // 2
+    dy ~ N(0,1) [B,T',F',C] with (T', F') = dy_rows_cols, by default
+    (ceil(T/2), ceil(F/2)); lengths ~U[T/2, T] in input frames.  With bf16,
+    x, w, b and dy are the same draws rounded to bfloat16 (nearest even)."""
+    T2, F2 = dy_rows_cols if dy_rows_cols is not None else ((T + 1) // 2, (F + 1) // 2)
     x = normal((B, T, F, C), 1.0, "c5/x", seed, device).clamp_(min=0.0)
-    return dict(
+    d = dict(
         x=x,
         w=normal((3, 3, C), 1.0 / 9, "c5/w", seed, device),
         b=normal((C,), 0.1, "c5/b", seed, device),
@@ -135,3 +137,7 @@ def conv2d_stage(device="cpu", seed=DEFAULT_SEED, B=32, T=1500, F=64, C=256):
         lengths=int_uniform(B, T // 2, T, "c5/len", seed),
         B=B, T=T, F=F, C=C,
     )
+    if bf16:
+        for k in ("x", "w", "b", "dy"):
+            d[k] = d[k].to(torch.bfloat16)
+    return d

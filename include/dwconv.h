@@ -16,6 +16,9 @@
  *   dwsub_fused_bwd  the front's parameter gradients dw0, db0, dw1, db1
  *                    (same section: the kernels serve the training step)
  *   dwconv2d_bwd     its backward: dx, dw, db (same section)
+ *   dwconv2d_fwd_ex, dwconv2d_bwd_ex
+ *                    the same with per-side padding (the causal padding of
+ *                    the same section) and bf16 storage
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, contiguous and channel-last (channel index fastest):
@@ -196,8 +199,9 @@ dw_status dwsub_fused_bwd(const float *x, const float *w0, const float *b0, cons
  * read zero.  For the 3x3, stride 2, pad 1 geometry len' = ceil(len / 2).
  *
  * x: [B][T][F][C] float; w: [KH][KW][C] float; bias: [C] or NULL; y:
- * [B][T'][F'][C] float.  Implemented geometry: KH = KW = 3, stride 2, pad 1;
- * anything else returns DW_ERR_UNSUPPORTED.
+ * [B][T'][F'][C] float.  Implemented geometry: KH = KW = 3, stride 2, pad 1
+ * or 2; anything else returns DW_ERR_UNSUPPORTED.  Equal to dwconv2d_fwd_ex
+ * with the same pad on every side and DW_F32.
  * Errors: DW_ERR_INVALID_ARG for a null x, w or y, a negative size or x == y.
  */
 dw_status dwconv2d_fwd(const float *x, const float *w, const float *bias, const int32_t *lengths,
@@ -229,7 +233,8 @@ size_t dwconv2d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C,
  * workspace: device memory of at least dwconv2d_bwd_workspace_bytes(...)
  * bytes when dw or db is requested (may be NULL otherwise); its contents on
  * entry are ignored and on return are unspecified.
- * Implemented geometry: KH = KW = 3, stride 2, pad 1 (else DW_ERR_UNSUPPORTED).
+ * Implemented geometry: KH = KW = 3, stride 2, pad 1 or 2 (else
+ * DW_ERR_UNSUPPORTED).
  * An empty batch (B, T or F zero) still writes dw = 0 and db = 0; x and dy
  * may then be NULL.
  * Errors: DW_ERR_INVALID_ARG for a null x, w or dy that holds elements, a
@@ -240,6 +245,54 @@ dw_status dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths, c
                        float *dx, float *dw, float *db, void *workspace, size_t workspace_bytes,
                        int64_t B, int64_t T, int64_t F, int64_t C,
                        int64_t KH, int64_t KW, int64_t stride, int64_t pad, void *stream);
+
+/*
+ * dwconv2d_fwd_ex -- dwconv2d_fwd with its padding given per axis and side,
+ * and a storage type: the general depthwise conv2d of NeMo PR #16114 ("What
+ * does this PR do"), which fuses the masking and the causal padding.
+ *
+ *   pad_t0 / pad_t1: zero rows before / after the input in time
+ *   pad_f0 / pad_f1: zero columns before / after it in frequency
+ *   T' = floor((T + pad_t0 + pad_t1 - KH)/s) + 1, F' likewise,
+ *   len'_b = floor((len_b + pad_t0 + pad_t1 - KH)/s) + 1 clamped to [0, T'],
+ *            and 0 if len_b = 0
+ *   y[b,t',f',c] = sum_{i,j} xm[b, s t'+i-pad_t0, s f'+j-pad_f0, c] * w[i,j,c]
+ *                  + bias[c]  for t' < len'_b, else 0
+ * Symmetric padding is pad 1 everywhere (dwconv2d_fwd's pad = 1).  The causal
+ * padding is read as KH - 1 = 2 before and s - 1 = 1 after on each axis
+ * (2, 1, 2, 1): output row t' then reads input rows up to 2t' only.
+ *
+ * dtype DW_F32: x, w, bias, y are float.  DW_BF16: they are bf16 (uint16
+ * bit patterns), widened exactly to fp32, accumulated in fp32 and stored
+ * rounded to nearest even.
+ * Implemented: KH = KW = 3, stride 2, pad_t0 and pad_f0 in {1, 2}, pad_t1
+ * and pad_f1 in {0, 1, 2}; other valid geometries return DW_ERR_UNSUPPORTED,
+ * negative pads DW_ERR_INVALID_ARG.  Errors otherwise as dwconv2d_fwd.
+ */
+dw_status dwconv2d_fwd_ex(const void *x, const void *w, const void *bias, const int32_t *lengths, void *y,
+                          int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride,
+                          int64_t pad_t0, int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype,
+                          void *stream);
+
+/* Workspace of dwconv2d_bwd_ex for these sizes and pads (0 if unsupported). */
+size_t dwconv2d_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW,
+                                       int64_t stride, int64_t pad_t0, int64_t pad_t1, int64_t pad_f0,
+                                       int64_t pad_f1);
+
+/*
+ * dwconv2d_bwd_ex -- gradients of dwconv2d_fwd_ex: as dwconv2d_bwd with
+ * t = s t'+i-pad_t0, f = s f'+j-pad_f0 and len' as in dwconv2d_fwd_ex.
+ * dtype DW_BF16: x, w, dy and dx are bf16; dw and db are always float
+ * (accumulated in fp64 from the exactly widened values).  workspace: at
+ * least dwconv2d_bwd_workspace_bytes_ex(...) bytes when dw or db is
+ * requested.  Implemented geometries and errors as dwconv2d_fwd_ex and
+ * dwconv2d_bwd.
+ */
+dw_status dwconv2d_bwd_ex(const void *x, const void *w, const int32_t *lengths, const void *dy, void *dx,
+                          float *dw, float *db, void *workspace, size_t workspace_bytes,
+                          int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride,
+                          int64_t pad_t0, int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype,
+                          void *stream);
 
 #ifdef __cplusplus
 }

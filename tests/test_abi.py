@@ -31,6 +31,10 @@ def lib():
     lib.dwconv2d_bwd_workspace_bytes.argtypes = [i64] * 8
     lib.dwconv2d_bwd_workspace_bytes.restype = sz
     lib.dwconv2d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 8 + [vp]
+    lib.dwconv2d_fwd_ex.argtypes = [vp] * 5 + [i64] * 11 + [i, vp]
+    lib.dwconv2d_bwd_workspace_bytes_ex.argtypes = [i64] * 11
+    lib.dwconv2d_bwd_workspace_bytes_ex.restype = sz
+    lib.dwconv2d_bwd_ex.argtypes = [vp] * 8 + [sz] + [i64] * 11 + [i, vp]
     lib.dwconv1d_bwd_workspace_bytes.argtypes = [i64] * 4
     lib.dwconv1d_bwd_workspace_bytes.restype = sz
     lib.dwconv1d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 4 + [i, i, vp]
@@ -49,7 +53,8 @@ def declared_functions():
 def test_header_declares_the_four_operations():
     names = declared_functions()
     for f in ("dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
-              "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dw_abi_version", "dw_last_error"):
+              "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dwconv2d_fwd_ex", "dwconv2d_bwd_ex",
+              "dwconv2d_bwd_workspace_bytes_ex", "dw_abi_version", "dw_last_error"):
         assert f in names
 
 
@@ -132,6 +137,7 @@ def test_dwconv2d_fwd_validation(lib):
     assert f(P, P, N, N, Q, 2, 8, 8, 4, 3, 3, 1, 1, N) == UNSUPPORTED and "stride" in err(lib)
     assert f(P, P, N, N, Q, 2, 8, 8, 4, 5, 5, 2, 1, N) == UNSUPPORTED
     assert f(P, P, N, N, Q, 2, 8, 8, 4, 3, 3, 2, 0, N) == UNSUPPORTED
+    assert f(P, P, N, N, Q, 2, 8, 8, 4, 3, 3, 2, 3, N) == UNSUPPORTED
     assert f(N, P, N, N, Q, 2, 8, 8, 4, 3, 3, 2, 1, N) == INVALID
     assert f(P, P, N, N, P, 2, 8, 8, 4, 3, 3, 2, 1, N) == INVALID
     assert f(P, P, N, N, Q, 2, 8, -8, 4, 3, 3, 2, 1, N) == INVALID
@@ -157,6 +163,32 @@ def test_dwconv2d_bwd_validation(lib):
     assert f(P, P, N, Q, R, W, N, W, need, 32, 1500, 64, 256, 3, 3, 1, 1, N) == UNSUPPORTED
     # nothing requested: nothing to do
     assert f(P, P, N, Q, N, N, N, N, 0, *args) == OK
+
+
+def test_dwconv2d_ex_validation(lib):
+    f = lib.dwconv2d_fwd_ex
+    geo = (2, 8, 8, 4, 3, 3, 2)
+    for pads in ((1, 1, 1, 1), (2, 1, 2, 1), (2, 2, 1, 0), (1, 0, 2, 2)):
+        for dt in (0, 1):  # empty batch: validated, nothing enqueued
+            assert f(P, P, N, N, Q, 0, *geo[1:], *pads, dt, N) == OK
+    assert f(P, P, N, N, Q, *geo, 0, 1, 1, 1, 0, N) == UNSUPPORTED and "pads" in err(lib)
+    assert f(P, P, N, N, Q, *geo, 1, 3, 1, 1, 0, N) == UNSUPPORTED
+    assert f(P, P, N, N, Q, *geo, 1, 1, 3, 1, 0, N) == UNSUPPORTED
+    assert f(P, P, N, N, Q, *geo, 1, -1, 1, 1, 0, N) == INVALID
+    assert f(P, P, N, N, Q, *geo, 1, 1, 1, 1, 2, N) == INVALID and "dtype" in err(lib)
+    assert f(P, P, N, N, P, *geo, 2, 1, 2, 1, 1, N) == INVALID and "alias" in err(lib)
+    assert f(N, P, N, N, Q, *geo, 2, 1, 2, 1, 1, N) == INVALID
+    ws = lib.dwconv2d_bwd_workspace_bytes_ex
+    need = ws(32, 1500, 64, 256, 3, 3, 2, 2, 1, 2, 1)
+    assert need > 0 and ws(32, 1500, 64, 256, 3, 3, 2, 0, 1, 1, 1) == 0
+    assert ws(32, 1500, 64, 256, 3, 3, 2, 1, 1, 1, 1) == lib.dwconv2d_bwd_workspace_bytes(32, 1500, 64, 256, 3, 3, 2, 1)
+    g = lib.dwconv2d_bwd_ex
+    R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    args = (32, 1500, 64, 256, 3, 3, 2, 2, 1, 2, 1)
+    assert g(P, P, N, Q, R, W, N, W, need - 1, *args, 1, N) == WORKSPACE
+    assert g(P, P, N, Q, Q, W, N, W, need, *args, 1, N) == INVALID and "alias" in err(lib)
+    assert g(P, P, N, Q, R, W, N, W, need, *args, 7, N) == INVALID
+    assert g(P, P, N, Q, N, N, N, N, 0, *args, 1, N) == OK  # nothing requested
 
 
 def test_last_error_is_per_thread(lib):
