@@ -6,6 +6,7 @@ size, on synthetic inputs resident in HBM:
 
   front   dwsub_fused_fwd   mel [4,1000,80] -> [4,250,20,256]           fp32
           dwsub_fused_bwd   dw0, db0, dw1, db1 of the same, dy given     fp64 sums
+          dwsub_fused_*_ex  the same two in causal mode -> [4,251,21,256]
   conv1d  dwconv1d_fwd      [16,750,1024] K=9 symmetric                 bf16 storage
   sweep   dwconv1d_fwd      [32,1500,512] causal, K = 3, 4, 5, 9, 15    fp32
           dwconv1d_fwd      [32,1500,200] causal, K = 9                 fp32
@@ -97,12 +98,16 @@ def work_conv1d_bwd(c):
     return rd, wr, flops
 
 
-def work_front(c):
+def front_half(n, d):
+    return (n - 1 + d) // 2 + 1 if n > 0 else d
+
+
+def work_front(c, d=0):
     B, T, F, C = c["B"], c["T"], c["F"], c["C"]
-    T1, F1 = (T + 1) // 2, (F + 1) // 2
-    T2, F2 = (T1 + 1) // 2, (F1 + 1) // 2
+    T1, F1 = front_half(T, d), front_half(F, d)
+    T2, F2 = front_half(T1, d), front_half(F1, d)
     L = clamp_lengths(c["lengths"].tolist(), T)
-    L1 = [(l + 1) // 2 for l in L]
+    L1 = [min(front_half(l, d), T1) if l > 0 else 0 for l in L]
     rows_read = sum(min(T, 2 * l1) for l1 in L1)  # mel rows some unmasked h row reads
     rd = rows_read * F * 4 + 20 * C * 4 + 4 * B
     wr = B * T2 * F2 * C * 4
@@ -110,12 +115,12 @@ def work_front(c):
     return rd, wr, flops
 
 
-def work_front_bwd(c):
+def work_front_bwd(c, d=0):
     B, T, F, C = c["B"], c["T"], c["F"], c["C"]
-    T1, F1 = (T + 1) // 2, (F + 1) // 2
-    T2, F2 = (T1 + 1) // 2, (F1 + 1) // 2
+    T1, F1 = front_half(T, d), front_half(F, d)
+    T2, F2 = front_half(T1, d), front_half(F1, d)
     L = clamp_lengths(c["lengths"].tolist(), T)
-    L1 = [min((l + 1) // 2, T1) for l in L]
+    L1 = [min(front_half(l, d), T1) if l > 0 else 0 for l in L]
     rows_read = sum(min(T, 2 * l1) for l1 in L1)
     rd = rows_read * F * 4 + B * T2 * F2 * C * 4 + 19 * C * 4 + 4 * B
     wr = 20 * C * 4
@@ -178,6 +183,18 @@ def build_rows(dev):
         f["B"] * f["T"], *work_front_bwd(f),
         lambda: dw.dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], fL, fdy, *fg, workspace=fws), bound="alu")
     f["dy"] = fdy
+    fcy = torch.empty((f["B"], 251, 21, f["C"]), device=dev)
+    fcdy = datagen.normal((f["B"], 251, 21, f["C"]), 1.0, "c2/dy", device=dev)
+    fcws = torch.empty((dw.dwsub_fused_bwd_workspace_bytes(f["B"], f["T"], f["F"], f["C"], causal=True),),
+                       dtype=torch.uint8, device=dev)
+    add("front_causal", "dwsub_fused_fwd_ex", "mel [4,1000,80] -> [4,251,21,256] causal fp32", f["B"] * f["T"],
+        *work_front(f, 1),
+        lambda: dw.dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], fL, y=fcy, causal=True), bound="alu")
+    add("front_bwd_causal", "dwsub_fused_bwd_ex", "dw0,db0,dw1,db1 of the causal front, dy [4,251,21,256]",
+        f["B"] * f["T"], *work_front_bwd(f, 1),
+        lambda: dw.dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], fL, fcdy, *fg, workspace=fcws, causal=True),
+        bound="alu")
+    f["dy_causal"] = fcdy
 
     e = datagen.conv1d_encoder_bf16(device=dev)
     eL = e["lengths"].to(dev)
@@ -257,7 +274,7 @@ def cpu_baseline(data, target_s: float):
     hp = lambda d: {k: (v.detach().float().cpu() if hasattr(v, "detach") and k != "x" and k != "dy" else v)
                     for k, v in d.items()}
     f, e, g = hp(data["front"]), hp(data["conv1d_bf16"]), hp(data["stage"])
-    f["x"], f["dy"] = data["front"]["x"], data["front"]["dy"]
+    f["x"], f["dy"], f["dy_causal"] = data["front"]["x"], data["front"]["dy"], data["front"]["dy_causal"]
     e["x"], g["x"], g["dy"] = data["conv1d_bf16"]["x"], data["stage"]["x"], data["stage"]["dy"]
     gc = dict(g, dy=data["stage_causal"]["dy"])
     gh = hp(data["stage_bf16"])                    # bf16 values, widened exactly on the host
@@ -285,6 +302,12 @@ def cpu_baseline(data, target_s: float):
         oracle.dwsub_front_bwd(xs, f["w0"], f["b0"], f["w1"], f["lengths"][:m], dys)
         secs += time.perf_counter() - t
         frames += m * f["T"]
+        dys = host(f["dy_causal"], m)
+        t = time.perf_counter()
+        oracle.dwsub_front_fwd(xs, f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"][:m], causal=True)
+        oracle.dwsub_front_bwd(xs, f["w0"], f["b0"], f["w1"], f["lengths"][:m], dys, causal=True)
+        secs += time.perf_counter() - t
+        frames += 2 * m * f["T"]
         m = min(n, e["B"])
         xs = host(e["x"], m)
         t = time.perf_counter()
@@ -442,7 +465,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic (seeded; log-mel-shaped inputs, lengths ~U[T/2,T])",
         "config": {
-            "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd; conv-module dwconv1d [16,750,1024] K9 "
+            "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd (symmetric and causal); conv-module dwconv1d [16,750,1024] K9 "
                         "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; depthwise conv2d "
                         "stage [32,1500,64,256] fwd+bwd (symmetric fp32, causal fp32, symmetric bf16)",
             "frames_per_step": frames,

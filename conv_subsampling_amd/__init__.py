@@ -22,7 +22,7 @@ __all__ = [
     "LIB_PATH", "DwconvError", "abi_version",
     "dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
     "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
-    "conv2d_out_shape", "CAUSAL_PADS_2D", "out_len",
+    "conv2d_out_shape", "CAUSAL_PADS_2D", "front_out_shape", "out_len",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdwconv.so")
@@ -61,6 +61,12 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dwconv1d_bwd_workspace_bytes.argtypes = [_i64] * 4
     lib.dwconv1d_bwd.restype = _int
     lib.dwconv1d_bwd.argtypes = [_vp] * 8 + [_sz] + [_i64] * 4 + [_int, _int, _vp]
+    lib.dwsub_fused_fwd_ex.restype = _int
+    lib.dwsub_fused_fwd_ex.argtypes = [_vp] * 7 + [_i64] * 4 + [_int, _vp]
+    lib.dwsub_fused_bwd_workspace_bytes_ex.restype = _sz
+    lib.dwsub_fused_bwd_workspace_bytes_ex.argtypes = [_i64] * 4 + [_int]
+    lib.dwsub_fused_bwd_ex.restype = _int
+    lib.dwsub_fused_bwd_ex.argtypes = [_vp] * 11 + [_sz] + [_i64] * 4 + [_int, _vp]
     lib.dwsub_fused_fwd.restype = _int
     lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
     lib.dwsub_fused_bwd_workspace_bytes.restype = _sz
@@ -189,7 +195,15 @@ def dwconv1d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None, c
     return dx, dw, db
 
 
-def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None):
+def front_out_shape(T, F, causal: bool = False):
+    """(T2, F2) of the fused front: two stride-2 stages, each padding 1 before
+    and after (symmetric) or 2 before and 1 after (causal)."""
+    d = 1 if causal else 0
+    half = lambda n: (n - 1 + d) // 2 + 1 if n > 0 else d
+    return half(half(T)), half(half(F))
+
+
+def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None, causal: bool = False):
     """Fused subsampler front; x [B,T,F] float32 mel -> y [B,T2,F2,C]."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, F]")
@@ -204,21 +218,21 @@ def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None):
     _dev_tensor("w1", w1, f32, dev, (3, 3, C))
     _dev_tensor("b1", b1, f32, dev, (C,), allow_none=True)
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
-    T2, F2 = out_len(out_len(T)), out_len(out_len(F))
+    T2, F2 = front_out_shape(T, F, causal)
     if y is None:
         y = torch.empty((B, T2, F2, C), dtype=f32, device=dev)
     _dev_tensor("y", y, f32, dev, (B, T2, F2, C))
-    _check(_lib.dwsub_fused_fwd(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(b1), _ptr(lengths), _ptr(y),
-                                B, T, F, C, _stream(dev)))
+    _check(_lib.dwsub_fused_fwd_ex(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(b1), _ptr(lengths), _ptr(y),
+                                   B, T, F, C, DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, _stream(dev)))
     return y
 
 
-def dwsub_fused_bwd_workspace_bytes(B, T, F, C) -> int:
-    return int(_lib.dwsub_fused_bwd_workspace_bytes(B, T, F, C))
+def dwsub_fused_bwd_workspace_bytes(B, T, F, C, causal: bool = False) -> int:
+    return int(_lib.dwsub_fused_bwd_workspace_bytes_ex(B, T, F, C, DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC))
 
 
 def dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0=None, db0=None, dw1=None, db1=None, workspace=None,
-                    need=("dw0", "db0", "dw1", "db1")):
+                    need=("dw0", "db0", "dw1", "db1"), causal: bool = False):
     """Parameter gradients (dw0, db0, dw1, db1) of dwsub_fused_fwd given dy [B,T2,F2,C]."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, F]")
@@ -232,20 +246,21 @@ def dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0=None, db0=None, dw1=None, db
     _dev_tensor("b0", b0, f32, dev, (C,), allow_none=True)
     _dev_tensor("w1", w1, f32, dev, (3, 3, C))
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
-    T2, F2 = out_len(out_len(T)), out_len(out_len(F))
+    T2, F2 = front_out_shape(T, F, causal)
     _dev_tensor("dy", dy, f32, dev, (B, T2, F2, C))
     outs = {}
     for name, t, shape in (("dw0", dw0, (3, 3, C)), ("db0", db0, (C,)), ("dw1", dw1, (3, 3, C)), ("db1", db1, (C,))):
         if t is None and name in need:
             t = torch.empty(shape, dtype=f32, device=dev)
         outs[name] = _dev_tensor(name, t, f32, dev, shape, allow_none=True)
-    need_ws = dwsub_fused_bwd_workspace_bytes(B, T, F, C)
+    need_ws = dwsub_fused_bwd_workspace_bytes(B, T, F, C, causal)
     if workspace is None:
         workspace = torch.empty((max(need_ws, 1),), dtype=torch.uint8, device=dev)
     _dev_tensor("workspace", workspace, torch.uint8, dev)
-    _check(_lib.dwsub_fused_bwd(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(lengths), _ptr(dy),
-                                _ptr(outs["dw0"]), _ptr(outs["db0"]), _ptr(outs["dw1"]), _ptr(outs["db1"]),
-                                _ptr(workspace), workspace.numel(), B, T, F, C, _stream(dev)))
+    _check(_lib.dwsub_fused_bwd_ex(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(lengths), _ptr(dy),
+                                   _ptr(outs["dw0"]), _ptr(outs["db0"]), _ptr(outs["dw1"]), _ptr(outs["db1"]),
+                                   _ptr(workspace), workspace.numel(), B, T, F, C,
+                                   DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, _stream(dev)))
     return outs["dw0"], outs["db0"], outs["dw1"], outs["db1"]
 
 

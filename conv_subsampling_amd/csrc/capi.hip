@@ -54,6 +54,12 @@ bool geometry_ok_2d(int64_t KH, int64_t KW, int64_t stride, int64_t pt0, int64_t
     return KH == 3 && KW == 3 && stride == 2 && dw::dwconv2d_pads_supported(pt0, pt1, pf0, pf1);
 }
 
+dw_status check_pad(const char* fn, dw_pad pad) {
+    if (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL)
+        return fail(DW_ERR_INVALID_ARG, "%s: unknown pad mode %d", fn, (int)pad);
+    return DW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,42 +124,70 @@ dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, con
                                             (hipStream_t)stream), fn);
 }
 
+dw_status dwsub_fused_fwd_ex(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,
+                             const int32_t* lengths, float* y, int64_t B, int64_t T, int64_t F, int64_t C,
+                             dw_pad pad, void* stream) {
+    const char* fn = "dwsub_fused_fwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    const dw_status ps = check_pad(fn, pad);
+    if (ps != DW_OK) return ps;
+    const bool causal = pad == DW_PAD_CAUSAL;
+    const dw::FrontDims fd = dw::front_dims(T, F, causal ? 1 : 0);
+    if (B == 0 || fd.T2 == 0 || fd.F2 == 0 || C == 0) return ok();
+    if ((!x && T * F > 0) || !w0 || !w1 || !y)
+        return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and y must not be NULL", fn);
+    if ((const void*)x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    if (!dw::dwsub_fused_fwd_fits(B, T, F, C, causal))
+        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, causal,
+                                               (hipStream_t)stream), fn);
+}
+
 dw_status dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,
                           const int32_t* lengths, float* y, int64_t B, int64_t T, int64_t F, int64_t C,
                           void* stream) {
-    const char* fn = "dwsub_fused_fwd";
-    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
-    if (B == 0 || T == 0 || F == 0 || C == 0) return ok();
-    if (!x || !w0 || !w1 || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and y must not be NULL", fn);
-    if ((const void*)x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
-    if (!dw::dwsub_fused_fwd_fits(B, T, F, C))
-        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
-    return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, (hipStream_t)stream), fn);
+    return dwsub_fused_fwd_ex(x, w0, b0, w1, b1, lengths, y, B, T, F, C, DW_PAD_SYMMETRIC, stream);
+}
+
+size_t dwsub_fused_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, dw_pad pad) {
+    if (B < 0 || T < 0 || F < 0 || C < 0 || (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL)) return 0;
+    return dw::dwsub_fused_bwd_workspace(B, T, F, C, pad == DW_PAD_CAUSAL);
 }
 
 size_t dwsub_fused_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C) {
-    if (B < 0 || T < 0 || F < 0 || C < 0) return 0;
-    return dw::dwsub_fused_bwd_workspace(B, T, F, C);
+    return dwsub_fused_bwd_workspace_bytes_ex(B, T, F, C, DW_PAD_SYMMETRIC);
+}
+
+dw_status dwsub_fused_bwd_ex(const float* x, const float* w0, const float* b0, const float* w1,
+                             const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1, float* db1,
+                             void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
+                             dw_pad pad, void* stream) {
+    const char* fn = "dwsub_fused_bwd";
+    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    const dw_status ps = check_pad(fn, pad);
+    if (ps != DW_OK) return ps;
+    const bool causal = pad == DW_PAD_CAUSAL;
+    if (!dw0 && !db0 && !dw1 && !db1) return ok();
+    if (C == 0) return ok();
+    const dw::FrontDims fd = dw::front_dims(T, F, causal ? 1 : 0);
+    if ((!x && B * T * F > 0) || (!dy && B * fd.T2 * fd.F2 * C > 0) || !w0 || !w1)
+        return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and dy must not be NULL (unless empty)", fn);
+    const size_t need = dw::dwsub_fused_bwd_workspace(B, T, F, C, causal);
+    if (!workspace || workspace_bytes < need)
+        return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                    workspace ? workspace_bytes : (size_t)0, need);
+    if (!dw::dwsub_fused_bwd_fits(B, T, F, C, causal))
+        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, B, T, F, C,
+                                               causal, (hipStream_t)stream), fn);
 }
 
 dw_status dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
                           const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1, float* db1,
                           void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
                           void* stream) {
-    const char* fn = "dwsub_fused_bwd";
-    if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
-    if (!dw0 && !db0 && !dw1 && !db1) return ok();
-    if (C == 0) return ok();
-    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
-    if ((!x && B * T * F > 0) || (!dy && B * T2 * F2 * C > 0) || !w0 || !w1)
-        return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and dy must not be NULL (unless empty)", fn);
-    const size_t need = dw::dwsub_fused_bwd_workspace(B, T, F, C);
-    if (!workspace || workspace_bytes < need)
-        return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
-                    workspace ? workspace_bytes : (size_t)0, need);
-    if (!dw::dwsub_fused_bwd_fits(B, T, F, C)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
-    return from_hip(dw::launch_dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, B, T, F, C,
-                                               (hipStream_t)stream), fn);
+    return dwsub_fused_bwd_ex(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, workspace_bytes, B, T, F, C,
+                              DW_PAD_SYMMETRIC, stream);
 }
 
 dw_status dwconv2d_fwd_ex(const void* x, const void* w, const void* bias, const int32_t* lengths, void* y,

@@ -3,8 +3,16 @@
 // ReLU -> masking -> depthwise 3x3 stride 2 conv, with no intermediate
 // tensor in memory).
 //
-//   h[t1,f1,c] = max(0, sum_{i,j} x[2t1+i-1, 2f1+j-1] w0[i,j,c] + b0[c]), zero for t1 >= ceil(len/2)
-//   y[t2,f2,c] = sum_{i,j} h[2t2+i-1, 2f2+j-1, c] w1[i,j,c] + b1[c]
+//   h[t1,f1,c] = max(0, sum_{i,j} x[2t1+i-pl, 2f1+j-pl] w0[i,j,c] + b0[c]), zero for t1 >= L1
+//   y[t2,f2,c] = sum_{i,j} h[2t2+i-pl, 2f2+j-pl, c] w1[i,j,c] + b1[c]
+//
+// Both convolutions pad each axis with pl zeros before and one after: pl = 1
+// is the symmetric front, pl = 2 its causal mode (the page's extra padding
+// layer: kernel - 1 before, stride - 1 after).  With d = pl - 1,
+// T1 = floor((T - 1 + d)/2) + 1, likewise F1, T2, F2, and
+// L1 = floor((len - 1 + d)/2) + 1 (0 for an empty item).  The kernels take d
+// as a shift: the mel patch a tile stages starts 3d rows and columns earlier,
+// so every index into it is the same in both modes.
 //
 // Mapping.  The mel input has one channel, so its values are the same for
 // every output channel: a workgroup stages the mel patch its outputs need in
@@ -32,12 +40,19 @@ namespace dw {
 #ifndef DWSUB_COLS
 #define DWSUB_COLS 5
 #endif
+FrontDims front_dims(int64_t T, int64_t F, int d) {
+    auto half = [d](int64_t n) { return n > 0 ? (n - 1 + d) / 2 + 1 : (int64_t)d; };
+    FrontDims r;
+    r.T1 = half(T); r.F1 = half(F); r.T2 = half(r.T1); r.F2 = half(r.F1);
+    return r;
+}
+
 constexpr int kSubBlock = 256;       // channels per workgroup
 constexpr int kSubRows = DWSUB_ROWS;  // output rows per thread
 constexpr int kSubCols = DWSUB_COLS;  // output columns per thread
-// Staged mel patch: rows 4*t0-3 .. 4*t0+4*TY-1, columns 4*f0-5 .. 4*f0+4*FC-1
-// (column 4*f0-5 sits at LDS column 0 so that every step reads an aligned
-// 16-byte group).
+// Staged mel patch: rows 4*t0-3-3d .. 4*t0+4*TY-1-3d, columns
+// 4*f0-5-3d .. 4*f0+4*FC-1-3d (column 4*f0-5-3d sits at LDS column 0 so that
+// every step reads an aligned 16-byte group).
 constexpr int kPatchRows = 4 * kSubRows + 3;
 constexpr int kPatchCols = 4 * kSubCols + 8;
 
@@ -45,7 +60,7 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     const float* __restrict__ x, const float* __restrict__ w0, const float* __restrict__ b0,
     const float* __restrict__ w1, const float* __restrict__ b1, const int32_t* __restrict__ lengths,
     float* __restrict__ y, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2, int32_t F2,
-    uint32_t n_rt, uint32_t n_ft, uint32_t n_cblk) {
+    int32_t d, uint32_t n_rt, uint32_t n_ft, uint32_t n_cblk) {
     __shared__ __align__(16) float patch[kPatchRows][kPatchCols];
 
     // Block -> (item, row tile, column tile, channel block); all uniform.
@@ -59,13 +74,13 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     const int32_t t0 = (int32_t)rt * kSubRows;  // first output row
     const int32_t f0 = (int32_t)ft * kSubCols;  // first output column
     const int32_t len = (int32_t)item_length(lengths, b, T);
-    const int32_t L1 = (len + 1) / 2;
+    const int32_t L1 = len > 0 ? (len - 1 + d) / 2 + 1 : 0;
 
     // Stage the zero-padded mel patch.  The input is not length-masked.
     const float* xb = x + (int64_t)b * T * F;
     for (int i = threadIdx.x; i < kPatchRows * kPatchCols; i += kSubBlock) {
         const int r = i / kPatchCols, q = i % kPatchCols;
-        const int32_t t = 4 * t0 - 3 + r, f = 4 * f0 - 5 + q;
+        const int32_t t = 4 * t0 - 3 - 3 * d + r, f = 4 * f0 - 5 - 3 * d + q;
         patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? xb[(int64_t)t * F + f] : 0.0f;
     }
     __syncthreads();
@@ -82,13 +97,13 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     const float ba = b0 ? b0[c] : 0.0f;
     const float bb = b1 ? b1[c] : 0.0f;
 
-    // h rows 2*t0-1+l, l = 0..2*TY, read mel patch rows 2l .. 2l+2.
+    // h rows 2*t0-1-d+l, l = 0..2*TY, read mel patch rows 2l .. 2l+2.
     // h row validity: inside [0, T1) and before the time mask.
     bool hrow_ok[2 * kSubRows + 1];
     bool any_ok = false;
 #pragma unroll
     for (int l = 0; l < 2 * kSubRows + 1; ++l) {
-        const int32_t r = 2 * t0 - 1 + l;
+        const int32_t r = 2 * t0 - 1 - d + l;
         hrow_ok[l] = r >= 0 && r < T1 && r < L1;
         any_ok |= hrow_ok[l];
     }
@@ -120,21 +135,22 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
         return hrow_ok[l] ? fmaxf(a, 0.0f) : 0.0f;
     };
 
-    // Carried h column 2*f0-1 (zero at the left edge).
+    // Carried h column 2*f0-1-d (zero left of the first h column).
     float hc[2 * kSubRows + 1];
 #pragma unroll
-    for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = f0 > 0 ? conv0(l, 2) : 0.0f;
+    for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = 2 * f0 - 1 - d >= 0 ? conv0(l, 2) : 0.0f;
 
-    // One output column: h columns 2f2 and 2f2+1 for every h row, then the
-    // depthwise taps.  h column 2f2+1 lies in the padding only at the last
-    // output column of an odd-width h, which is peeled off the loop so that
-    // the loop body has no condition around its LDS reads.
-    auto step = [&](int s, auto odd_valid) {
+    // One output column: h columns 2f2-d and 2f2+1-d for every h row, then
+    // the depthwise taps.  The first lies in the padding only at output
+    // column 0 of the causal mode, the second only at the last output column
+    // when it passes F1; those steps are peeled off the loop so that the loop
+    // body has no condition around its LDS reads.
+    auto step = [&](int s, auto odd_valid, auto even_valid) {
         const int32_t f2 = f0 + s;
         float he[2 * kSubRows + 1], ho[2 * kSubRows + 1];
 #pragma unroll
         for (int l = 0; l < 2 * kSubRows + 1; ++l) {
-            he[l] = conv0(l, 4 * s + 4);
+            he[l] = decltype(even_valid)::value ? conv0(l, 4 * s + 4) : 0.0f;
             ho[l] = decltype(odd_valid)::value ? conv0(l, 4 * s + 6) : 0.0f;
         }
 #pragma unroll
@@ -152,14 +168,22 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
 #pragma unroll
         for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = ho[l];
     };
-    const bool last_odd_pad = 2 * (f0 + ncols - 1) + 1 >= F1;
+    const bool first_even_pad = 2 * f0 - d < 0;
+    const bool last_odd_pad = 2 * (f0 + ncols - 1) + 1 - d >= F1;
+    int s = 0;
+    if (first_even_pad) {
+        if (ncols == 1 && last_odd_pad) step(0, std::false_type{}, std::false_type{});
+        else step(0, std::true_type{}, std::false_type{});
+        s = 1;
+    }
     const int full = last_odd_pad ? ncols - 1 : ncols;
-    for (int s = 0; s < full; ++s) step(s, std::true_type{});
-    if (last_odd_pad) step(full, std::false_type{});
+    for (; s < full; ++s) step(s, std::true_type{}, std::true_type{});
+    if (last_odd_pad && s < ncols) step(s, std::false_type{}, std::true_type{});
 }
 
-bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C) {
-    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
+bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal) {
+    const FrontDims fd = front_dims(T, F, causal ? 1 : 0);
+    const int64_t T2 = fd.T2, F2 = fd.F2;
     if ((T2 + kSubRows) * F2 * C * 4 >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28)) return false;
     const int64_t blocks = B * ((T2 + kSubRows - 1) / kSubRows) * ((F2 + kSubCols - 1) / kSubCols) *
@@ -169,15 +193,17 @@ bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C) {
 
 hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1,
                                   const float* b1, const int32_t* lengths, float* y,
-                                  int64_t B, int64_t T, int64_t F, int64_t C, hipStream_t st) {
-    const int64_t T1 = (T + 1) / 2, F1 = (F + 1) / 2, T2 = (T1 + 1) / 2, F2 = (F1 + 1) / 2;
+                                  int64_t B, int64_t T, int64_t F, int64_t C, bool causal, hipStream_t st) {
+    const int d = causal ? 1 : 0;
+    const FrontDims fd = front_dims(T, F, d);
+    const int64_t T1 = fd.T1, F1 = fd.F1, T2 = fd.T2, F2 = fd.F2;
     const uint32_t n_rt = (uint32_t)((T2 + kSubRows - 1) / kSubRows);
     const uint32_t n_ft = (uint32_t)((F2 + kSubCols - 1) / kSubCols);
     const uint32_t n_cblk = (uint32_t)((C + kSubBlock - 1) / kSubBlock);
     const uint64_t blocks = (uint64_t)B * n_rt * n_ft * n_cblk;
     hipLaunchKernelGGL(dwsub_fused_fwd_kernel, dim3((uint32_t)blocks), dim3(kSubBlock), 0, st, x, w0, b0, w1, b1,
                        lengths, y, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1, (int32_t)T2,
-                       (int32_t)F2, n_rt, n_ft, n_cblk);
+                       (int32_t)F2, (int32_t)d, n_rt, n_ft, n_cblk);
     return hipGetLastError();
 }
 
@@ -188,7 +214,9 @@ hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* 
 // encoder's training step).  The mel input needs no gradient.
 //
 // h is recomputed on chip from the mel patch, never read from memory.  The
-// h positions are taken in "quads" (h rows 2t', 2t'+1 x columns 2f', 2f'+1),
+// h positions are taken in "quads" (h rows 2t'-d, 2t'+1-d x columns 2f'-d,
+// 2f'+1-d; the causal mode's shift d = 1 only moves which h rows a quad
+// holds, and quad row or column 0 then holds the padding row or column -1),
 // each with the four gradients dy[t'..t'+1, f'..f'+1] it meets, exactly as
 // in the conv2d backward:
 //   dh[2t',  2f'  ] = g00 w1[1,1]
@@ -224,15 +252,15 @@ hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* 
 #endif
 constexpr int kBQR = DWSUB_BWD_QROWS;          // quad rows per tile
 constexpr int kBQC = DWSUB_BWD_QCOLS;          // quad columns per tile
-constexpr int kBPatchRows = 4 * kBQR + 1;      // mel rows 4*t0-1 .. 4*t0+4*QR-1
-constexpr int kBPatchCols = 4 * kBQC + 1;      // mel columns 4*f0-1 .. 4*f0+4*QC-1
+constexpr int kBPatchRows = 4 * kBQR + 1;      // mel rows 4*t0-1-3d .. 4*t0+4*QR-1-3d
+constexpr int kBPatchCols = 4 * kBQC + 1;      // mel columns 4*f0-1-3d .. 4*f0+4*QC-1-3d
 constexpr int kFrontGrads = 20;                // dw0 (9), db0, dw1 (9), db1
 
 __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
     const float* __restrict__ x, const float* __restrict__ w0, const float* __restrict__ b0,
     const float* __restrict__ w1, const int32_t* __restrict__ lengths, const float* __restrict__ dy,
     double* __restrict__ partial, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2,
-    int32_t F2, uint32_t n_rt, uint32_t n_ft, uint32_t n_tiles, uint32_t n_cblk) {
+    int32_t F2, int32_t d, uint32_t n_rt, uint32_t n_ft, uint32_t n_tiles, uint32_t n_cblk) {
     __shared__ double patch[kBPatchRows][kBPatchCols];
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
     const uint32_t G = gridDim.x / n_cblk;
@@ -258,7 +286,7 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
         const uint32_t rt = rest % n_rt, b = rest / n_rt;
         const int32_t t0 = (int32_t)rt * kBQR, f0 = (int32_t)ft * kBQC;  // first quad row / column
         const int32_t len = (int32_t)item_length(lengths, b, T);
-        const int32_t hvalid = min(T1, (len + 1) / 2);  // h rows below this are unmasked
+        const int32_t hvalid = min(T1, len > 0 ? (len - 1 + d) / 2 + 1 : 0);  // h rows below this are unmasked
 
         // The tile's gradients dy[t0 .. t0+QR, f0 .. f0+QC], all loaded at once
         // (rows past T2 read zero through the buffer; column f0+QC past F2 is
@@ -277,7 +305,7 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
         const float* xb = x + (int64_t)b * T * F;
         for (int i = threadIdx.x; i < kBPatchRows * kBPatchCols; i += kSubBlock) {
             const int r = i / kBPatchCols, q = i % kBPatchCols;
-            const int32_t t = 4 * t0 - 1 + r, f = 4 * f0 - 1 + q;
+            const int32_t t = 4 * t0 - 1 - 3 * d + r, f = 4 * f0 - 1 - 3 * d + q;
             patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? (double)xb[(int64_t)t * F + f] : 0.0;
         }
         __syncthreads();
@@ -292,7 +320,8 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
             if (s >= ncols) break;
             const int32_t f = f0 + s;
             const bool next_ok = f + 1 < F2;     // dy column f'+1 exists
-            const bool cok = 2 * f + 1 < F1;     // h column 2f'+1 exists
+            const bool eok = 2 * f - d >= 0;     // h column 2f'-d exists
+            const bool cok = 2 * f + 1 - d < F1; // h column 2f'+1-d exists
             double gn[kBQR + 1];
 #pragma unroll
             for (int q = 0; q <= kBQR; ++q) gn[q] = next_ok ? (double)gt[q][s + 1] : 0.0;
@@ -300,16 +329,18 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
             for (int q = 0; q < kBQR; ++q) {
                 const double g00 = gc[q], g01 = gn[q], g10 = gc[q + 1], g11 = gn[q + 1];
                 gb1 += g00;
-                const int32_t r0 = 2 * (t0 + q);  // h rows r0, r0 + 1
-                if (r0 >= hvalid) continue;       // both h rows masked: no other term
-                const bool v1 = r0 + 1 < hvalid;
+                const int32_t r0 = 2 * (t0 + q) - d;  // h rows r0, r0 + 1
+                // A masked row's mel rows may be anything and are never
+                // combined.  Past this test row r0 is unmasked, or it is the
+                // padding row -1 of the causal mode, whose staged mel rows
+                // are zeros: its terms are then formed and add exact zeros.
+                const bool v0 = r0 >= 0 && r0 < hvalid, v1 = r0 + 1 >= 0 && r0 + 1 < hvalid;
+                if (r0 >= hvalid) continue;  // both rows masked: no other term
                 double P[5][5];
 #pragma unroll
                 for (int a = 0; a < 5; ++a)
 #pragma unroll
                     for (int e = 0; e < 5; ++e) P[a][e] = patch[4 * q + a][4 * s + e];
-                // h row r0 is unmasked here; row r0 + 1 may not be, and then
-                // none of its terms is formed (its mel rows may be anything).
                 double z00 = ba, z01 = ba, z10 = 0.0, z11 = 0.0;
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
@@ -329,8 +360,8 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
                             z11 = __builtin_fma(P[2 + i][2 + k], wa[3 * i + k], z11);
                         }
                 }
-                const bool m00 = z00 > 0.0, m01 = cok && z01 > 0.0;
-                const bool m10 = v1 && z10 > 0.0, m11 = v1 && cok && z11 > 0.0;
+                const bool m00 = v0 && eok && z00 > 0.0, m01 = v0 && cok && z01 > 0.0;
+                const bool m10 = v1 && eok && z10 > 0.0, m11 = v1 && cok && z11 > 0.0;
                 const double h00 = m00 ? z00 : 0.0, h01 = m01 ? z01 : 0.0;
                 const double h10 = m10 ? z10 : 0.0, h11 = m11 ? z11 : 0.0;
                 // depthwise stage: weight gradient from the (h, dy) pairs of this quad
@@ -387,8 +418,11 @@ struct FrontBwdGrid {
     uint32_t n_rt, n_ft, n_tiles, G;
 };
 
-static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F) {
-    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
+// The quad grid is T2 x F2 in both modes: ceil((T1 + d)/2) = T2 quad rows
+// cover the h rows, and every dy row is a quad row.
+static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F, int d) {
+    const FrontDims fd = front_dims(T, F, d);
+    const int64_t T2 = fd.T2, F2 = fd.F2;
     FrontBwdGrid g;
     g.n_rt = (uint32_t)((T2 + kBQR - 1) / kBQR);
     g.n_ft = (uint32_t)((F2 + kBQC - 1) / kBQC);
@@ -398,15 +432,16 @@ static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F) {
     return g;
 }
 
-bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C) {
-    const int64_t T2 = ((T + 1) / 2 + 1) / 2, F2 = ((F + 1) / 2 + 1) / 2;
+bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal) {
+    const FrontDims fd = front_dims(T, F, causal ? 1 : 0);
+    const int64_t T2 = fd.T2, F2 = fd.F2;
     if ((T2 + kBQR + 1) * F2 * C * 4 >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28) || C >= ((int64_t)1 << 24)) return false;
     return (uint64_t)B * ((T2 + kBQR - 1) / kBQR) * ((F2 + kBQC - 1) / kBQC) < ((uint64_t)1 << 31);
 }
 
-size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C) {
-    const int64_t P = front_bwd_grid(B, T, F).G;
+size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C, bool causal) {
+    const int64_t P = front_bwd_grid(B, T, F, causal ? 1 : 0).G;
     const int64_t ch = partial_reduce_chunks(P);
     return (size_t)((P + (ch > 0 ? ch : 1)) * kFrontGrads * C * (int64_t)sizeof(double));
 }
@@ -414,15 +449,17 @@ size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C) {
 hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
                                   const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1,
                                   float* db1, void* workspace, int64_t B, int64_t T, int64_t F, int64_t C,
-                                  hipStream_t st) {
-    const int64_t T1 = (T + 1) / 2, F1 = (F + 1) / 2, T2 = (T1 + 1) / 2, F2 = (F1 + 1) / 2;
-    const FrontBwdGrid g = front_bwd_grid(B, T, F);
+                                  bool causal, hipStream_t st) {
+    const int d = causal ? 1 : 0;
+    const FrontDims fd = front_dims(T, F, d);
+    const int64_t T1 = fd.T1, F1 = fd.F1, T2 = fd.T2, F2 = fd.F2;
+    const FrontBwdGrid g = front_bwd_grid(B, T, F, d);
     const uint32_t n_cblk = (uint32_t)((C + kSubBlock - 1) / kSubBlock);
     double* partial = (double*)workspace;
     if (g.G > 0) {
         hipLaunchKernelGGL(dwsub_fused_bwd_kernel, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st, x, w0, b0, w1,
                            lengths, dy, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1,
-                           (int32_t)T2, (int32_t)F2, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
+                           (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

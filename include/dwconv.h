@@ -19,6 +19,8 @@
  *   dwconv2d_fwd_ex, dwconv2d_bwd_ex
  *                    the same with per-side padding (the causal padding of
  *                    the same section) and bf16 storage
+ *   dwsub_fused_fwd_ex, dwsub_fused_bwd_ex
+ *                    the front with its causal mode (same section)
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, contiguous and channel-last (channel index fastest):
@@ -245,6 +247,37 @@ dw_status dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths, c
                        float *dx, float *dw, float *db, void *workspace, size_t workspace_bytes,
                        int64_t B, int64_t T, int64_t F, int64_t C,
                        int64_t KH, int64_t KW, int64_t stride, int64_t pad, void *stream);
+
+/*
+ * dwsub_fused_fwd_ex -- dwsub_fused_fwd with a padding mode: DW_PAD_SYMMETRIC
+ * is dwsub_fused_fwd; DW_PAD_CAUSAL is the front's causal mode (NeMo PR
+ * #16114, "What does this PR do": the extra padding layer of causal mode),
+ * read as both convolutions padding each axis with 2 zeros before and 1
+ * after.  With d = 0 (symmetric) or 1 (causal):
+ *   T1 = floor((T - 1 + d)/2) + 1, F1 likewise; T2, F2 the same from T1, F1
+ *        (0 for an empty axis when d = 0, 1 when d = 1)
+ *   L1_b = floor((len_b - 1 + d)/2) + 1, 0 for an empty item
+ *   h[b,t1,f1,c] = max(0, sum_{i,j} x[b, 2t1+i-1-d, 2f1+j-1-d] w0[i,j,c] + b0[c])
+ *                  for t1 < L1_b, else 0
+ *   y[b,t2,f2,c] = sum_{i,j} h[b, 2t2+i-1-d, 2f2+j-1-d, c] w1[i,j,c] + b1[c]
+ * Arguments, layout and errors as dwsub_fused_fwd; a bad pad is
+ * DW_ERR_INVALID_ARG.
+ */
+dw_status dwsub_fused_fwd_ex(const float *x, const float *w0, const float *b0, const float *w1, const float *b1,
+                             const int32_t *lengths, float *y, int64_t B, int64_t T, int64_t F, int64_t C,
+                             dw_pad pad, void *stream);
+
+/* Workspace of dwsub_fused_bwd_ex (0 for invalid sizes or pad). */
+size_t dwsub_fused_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, dw_pad pad);
+
+/*
+ * dwsub_fused_bwd_ex -- dwsub_fused_bwd for either padding mode of
+ * dwsub_fused_fwd_ex (the same gradients with its T2, F2, L1 and indices).
+ */
+dw_status dwsub_fused_bwd_ex(const float *x, const float *w0, const float *b0, const float *w1,
+                             const int32_t *lengths, const float *dy, float *dw0, float *db0, float *dw1, float *db1,
+                             void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
+                             dw_pad pad, void *stream);
 
 /*
  * dwconv2d_fwd_ex -- dwconv2d_fwd with its padding given per axis and side,

@@ -41,6 +41,10 @@ def lib():
     lib.dwsub_fused_bwd_workspace_bytes.argtypes = [i64] * 4
     lib.dwsub_fused_bwd_workspace_bytes.restype = sz
     lib.dwsub_fused_bwd.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [vp]
+    lib.dwsub_fused_fwd_ex.argtypes = [vp] * 7 + [i64] * 4 + [i, vp]
+    lib.dwsub_fused_bwd_workspace_bytes_ex.argtypes = [i64] * 4 + [i]
+    lib.dwsub_fused_bwd_workspace_bytes_ex.restype = sz
+    lib.dwsub_fused_bwd_ex.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [i, vp]
     return lib
 
 
@@ -54,7 +58,8 @@ def test_header_declares_the_four_operations():
     names = declared_functions()
     for f in ("dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
               "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dwconv2d_fwd_ex", "dwconv2d_bwd_ex",
-              "dwconv2d_bwd_workspace_bytes_ex", "dw_abi_version", "dw_last_error"):
+              "dwconv2d_bwd_workspace_bytes_ex", "dwsub_fused_fwd_ex", "dwsub_fused_bwd_ex",
+              "dwsub_fused_bwd_workspace_bytes_ex", "dw_abi_version", "dw_last_error"):
         assert f in names
 
 
@@ -130,6 +135,22 @@ def test_dwsub_fused_bwd_validation(lib):
     assert f(P, N, N, P, N, Q, R, N, N, N, W, need, *args) == INVALID
     assert f(P, P, N, P, N, Q, R, N, N, N, W, need, 4, -1, 80, 256, N) == INVALID
     assert f(P, P, N, P, N, Q, N, N, N, N, N, 0, *args) == OK  # nothing requested
+
+
+def test_dwsub_fused_ex_validation(lib):
+    f = lib.dwsub_fused_fwd_ex
+    assert f(P, P, N, P, N, N, Q, 4, 100, 80, 256, 2, N) == INVALID and "pad" in err(lib)
+    assert f(P, P, N, P, N, N, P, 4, 100, 80, 256, 1, N) == INVALID and "alias" in err(lib)
+    assert f(P, P, N, P, N, N, Q, 0, 100, 80, 256, 1, N) == OK
+    ws = lib.dwsub_fused_bwd_workspace_bytes_ex
+    need = ws(4, 1000, 80, 256, 1)
+    assert need > 0 and ws(4, 1000, 80, 256, 5) == 0
+    assert ws(4, 1000, 80, 256, 0) == lib.dwsub_fused_bwd_workspace_bytes(4, 1000, 80, 256)
+    g = lib.dwsub_fused_bwd_ex
+    R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    assert g(P, P, N, P, N, Q, R, N, N, N, W, need - 1, 4, 1000, 80, 256, 1, N) == WORKSPACE
+    assert g(P, P, N, P, N, Q, R, N, N, N, W, need, 4, 1000, 80, 256, 3, N) == INVALID
+    assert g(P, P, N, P, N, Q, N, N, N, N, N, 0, 4, 1000, 80, 256, 1, N) == OK  # nothing requested
 
 
 def test_dwconv2d_fwd_validation(lib):

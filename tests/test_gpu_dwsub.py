@@ -157,3 +157,78 @@ def test_bwd_front_full_size():
     f["dy"] = datagen.normal((4, 250, 20, 256), 1.0, "c2/dy", device=DEV)
     say("dwsub_fused_bwd full [4,1000,80], dy [4,250,20,256]")
     check_bwd(run_bwd(f), ref_bwd(f), "front bwd full")
+
+
+# ----------------------------------------------------------- causal mode -----
+
+def front_dims_oracle(T, F, causal):
+    pl, ph = oracle.front_pads(causal)
+    T1, F1 = oracle.conv_out_len(T, 3, 2, pl, ph), oracle.conv_out_len(F, 3, 2, pl, ph)
+    return oracle.conv_out_len(T1, 3, 2, pl, ph), oracle.conv_out_len(F1, 3, 2, pl, ph)
+
+
+CAUSAL_SHAPES = SHAPES + [(2, 2, 3, 8), (3, 6, 5, 7), (2, 0, 4, 4), (1, 5, 0, 4)]
+
+
+@pytest.mark.parametrize("B,T,F,C", CAUSAL_SHAPES)
+def test_causal_grid_fwd_bwd(B, T, F, C):
+    f = make(B, T, F, C, lens=datagen.int_uniform(B, 0, T + 2, f"gsc/{B}/{T}/{F}/{C}"))
+    T2, F2 = front_dims_oracle(T, F, True)
+    f["dy"] = datagen.normal((B, T2, F2, C), 1.0, f"gsc/dy/{B}/{T}/{F}/{C}", device=DEV)
+    say(f"dwsub_fused causal B={B} T={T} F={F} C={C} lengths={f['lengths'].tolist()}")
+    y = lib().dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["L"], causal=True)
+    torch.cuda.synchronize()
+    assert y.shape == (B, T2, F2, C)
+    ref = oracle.dwsub_front_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"], causal=True)
+    assert_parity(y, ref, TOL_F32, "causal front")
+    got = lib().dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], f["L"], f["dy"], causal=True)
+    torch.cuda.synchronize()
+    check_bwd(got, oracle.dwsub_front_bwd(f["x"], f["w0"], f["b0"], f["w1"], f["lengths"], f["dy"], causal=True),
+              "causal front bwd")
+
+
+def test_causal_masked_mel_rows_never_read_and_empty_item_is_bias():
+    B, T, F, C = 3, 40, 24, 64
+    f = make(B, T, F, C, lens=[40, 13, 0])
+    T2, F2 = front_dims_oracle(T, F, True)
+    f["dy"] = datagen.normal((B, T2, F2, C), 1.0, "gsc/dy/poison", device=DEV)
+    y = lib().dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["L"], causal=True)
+    g = lib().dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], f["L"], f["dy"], causal=True)
+    xp = f["x"].clone()
+    # L1 = floor(13/2) + 1 = 7 unmasked h rows; h row 6 reads mel rows 10, 11, 12
+    xp[1, 13:] = float("nan")
+    xp[2] = float("nan")
+    yp = lib().dwsub_fused_fwd(xp, f["w0"], f["b0"], f["w1"], f["b1"], f["L"], causal=True)
+    gp = lib().dwsub_fused_bwd(xp, f["w0"], f["b0"], f["w1"], f["L"], f["dy"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y, yp)
+    for a, b in zip(g, gp):
+        assert torch.equal(a, b)
+    assert torch.equal(y[2], f["b1"][None, None, :].expand(T2, F2, C))
+
+
+def test_causal_output_never_looks_ahead():
+    B, T, F, C = 2, 64, 20, 32
+    f = make(B, T, F, C, lens=[64, 64])
+    y = lib().dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["L"], causal=True)
+    x2 = f["x"].clone()
+    x2[:, 4 * 7 + 1:] += 2.0   # output row t2 reads mel rows up to 4 t2
+    y2 = lib().dwsub_fused_fwd(x2, f["w0"], f["b0"], f["w1"], f["b1"], f["L"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:, :8], y2[:, :8]) and not torch.equal(y[:, 8], y2[:, 8])
+
+
+def test_causal_front_full_size():
+    f = datagen.fused_front(device=DEV)
+    f["L"] = f["lengths"].to(DEV)
+    T2, F2 = front_dims_oracle(1000, 80, True)
+    assert (T2, F2) == (251, 21)
+    f["dy"] = datagen.normal((4, T2, F2, 256), 1.0, "c2/dy", device=DEV)
+    say("dwsub_fused causal full [4,1000,80] -> [4,251,21,256]")
+    y = lib().dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["L"], causal=True)
+    got = lib().dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], f["L"], f["dy"], causal=True)
+    torch.cuda.synchronize()
+    assert_parity(y, oracle.dwsub_front_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"], causal=True),
+                  TOL_F32, "causal front full")
+    check_bwd(got, oracle.dwsub_front_bwd(f["x"], f["w0"], f["b0"], f["w1"], f["lengths"], f["dy"], causal=True),
+              "causal front bwd full")
