@@ -54,6 +54,7 @@ def _bind(path: str):
     lib.oracle_dwsub_front_fwd.argtypes = [_F, _F, _F, _F, _F, _I, _D, _L, _L, _L, _L, ctypes.c_int]
     lib.oracle_dwsub_front_bwd.argtypes = [_F, _F, _F, _F, _I, _F, _D, _D, _D, _D, _L, _L, _L, _L, ctypes.c_int]
     lib.oracle_dwconv1d_bwd.argtypes = [_F, _F, _I, _F, _D, _D, _D, _L, _L, _L, _L, ctypes.c_int]
+    lib.oracle_dwconv1d_stream_fwd.argtypes = [_F, _F, _F, _I, _F, _D, _D, _L, _L, _L, _L]
     for f in (lib.oracle_dwconv1d_fwd, lib.oracle_dwconv2d_fwd, lib.oracle_dwconv2d_bwd,
               lib.oracle_dwsub_front_fwd, lib.oracle_dwsub_front_bwd, lib.oracle_dwconv1d_bwd):
         f.restype = ctypes.c_int
@@ -135,6 +136,25 @@ def dwconv1d_fwd(x, w, b, lengths, causal: bool):
     _check(_load().oracle_dwconv1d_fwd(xp, wp, bp, lp, _ptr_d(y), B, T, C, K, int(bool(causal))),
            "oracle_dwconv1d_fwd")
     return y
+
+
+def dwconv1d_stream_fwd(x, w, b, lengths, cache):
+    """(y [B,Tc,C], new cache [B,K-1,C]) of the causal 1-D depthwise conv run on
+    one chunk x [B,Tc,C] after the cached K-1 frames cache [B,K-1,C]."""
+    xa, xp = _f32(x)
+    B, Tc, C = xa.shape
+    wa, wp = _f32(w)
+    K = wa.shape[0]
+    if wa.shape != (K, C):
+        raise ValueError("w must be [K, C]")
+    ba, bp = _f32(b, (C,))
+    la, lp = _lens(lengths, B)
+    ca, cp = _f32(cache, (B, K - 1, C))
+    y = np.empty((B, Tc, C), dtype=np.float64)
+    cache_out = np.empty((B, K - 1, C), dtype=np.float64)
+    _check(_load().oracle_dwconv1d_stream_fwd(xp, wp, bp, lp, cp, _ptr_d(y), _ptr_d(cache_out), B, Tc, C, K),
+           "oracle_dwconv1d_stream_fwd")
+    return y, cache_out
 
 
 def dwconv1d_bwd(x, w, lengths, dy, causal: bool, want=("dx", "dw", "db")):

@@ -411,3 +411,51 @@ int oracle_dwconv1d_bwd(const float *x, const float *w, const int32_t *lengths, 
     }
     return 0;
 }
+
+/*
+ * Streaming form of the causal 1-D depthwise conv: the conv module of a
+ * streaming encoder runs on one chunk of frames per call and keeps a cache of
+ * the last K - 1 input frames between calls (parakeet.cpp PR #102, "What
+ * changes": the streaming encoder's conv with a cache; the reson8 wiki,
+ * "Keep state on the GPU": streaming models carry state between chunks).
+ * Per stream b, with len_b = clamp(lengths[b], 0, Tc) valid frames in this
+ * chunk, the sequence the call convolves is the cache followed by them:
+ *   s[j]              = cache_in[b, j, c]          for j < K - 1
+ *   s[K - 1 + u]      = x[b, u, c]                 for u < len_b
+ *   y[b, t, c]        = sum_{k<K} s[t + k] * w[k, c] + bias[c]   for t < len_b
+ *   y[b, t, c]        = 0                                        for t >= len_b
+ *   cache_out[b, j, c] = s[len_b + j]              for j < K - 1
+ * (the last K - 1 frames of the cache and the chunk together).  Starting
+ * from a zero cache, calling this on consecutive chunks of a sequence gives
+ * the causal convolution of the whole sequence.  x, y [B][Tc][C]; caches
+ * [B][K-1][C]; cache_out is double and holds input values exactly.
+ */
+int oracle_dwconv1d_stream_fwd(const float *x, const float *w, const float *bias,
+                               const int32_t *lengths, const float *cache_in,
+                               double *y, double *cache_out,
+                               long B, long Tc, long C, long K)
+{
+    if (B < 0 || Tc < 0 || C < 0 || K < 1) return -1;
+    long S = K - 1 + Tc;
+    double *sq = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    if (!sq) return -1;
+    for (long b = 0; b < B; ++b) {
+        long len = clamp_len(lengths, b, Tc);
+        for (long c = 0; c < C; ++c) {
+            for (long j = 0; j < K - 1; ++j) sq[j] = (double)cache_in[(b * (K - 1) + j) * C + c];
+            for (long u = 0; u < len; ++u) sq[K - 1 + u] = (double)x[(b * Tc + u) * C + c];
+            for (long t = 0; t < Tc; ++t) {
+                double acc = 0.0;
+                if (t < len) {
+                    for (long k = 0; k < K; ++k)
+                        acc += sq[t + k] * (double)w[k * C + c];
+                    acc += bias ? (double)bias[c] : 0.0;
+                }
+                y[(b * Tc + t) * C + c] = acc;
+            }
+            for (long j = 0; j < K - 1; ++j) cache_out[(b * (K - 1) + j) * C + c] = sq[len + j];
+        }
+    }
+    free(sq);
+    return 0;
+}

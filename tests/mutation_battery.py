@@ -59,6 +59,10 @@ BATTERY = [
     (P.test_1d_bwd_matches_torch_autograd, (2, 50, 3, 15, False)),
     (P.test_1d_bwd_adjoint_closed_forms_and_masks, ()),
     (P.test_1d_bwd_finite_differences_in_w, ()),
+    (P.test_1d_stream_chunks_equal_the_whole_causal_conv, (4,)),
+    (P.test_1d_stream_chunks_equal_the_whole_causal_conv, (9,)),
+    (P.test_1d_stream_delta_kernels_read_the_cache, ()),
+    (P.test_1d_stream_empty_chunk_keeps_the_cache_and_nan_past_length_never_read, ()),
 ]
 
 

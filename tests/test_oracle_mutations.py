@@ -86,6 +86,15 @@ MUTANTS = [
      "if (u < 0 || u >= T) continue;\n                    if (dx) dx[(b * T + u) * C + c]"),
     ("1d bwd pad side swapped", "    long pL = causal ? K - 1 : (K - 1) / 2;\n    if (dx) memset(dx, 0, sizeof(double) * (size_t)(B * T * C));",
      "    long pL = causal ? 0 : (K - 1) / 2;\n    if (dx) memset(dx, 0, sizeof(double) * (size_t)(B * T * C));"),
+    ("stream cache taken from the chunk end", "cache_out[(b * (K - 1) + j) * C + c] = sq[len + j];",
+     "cache_out[(b * (K - 1) + j) * C + c] = sq[Tc + j];"),
+    ("stream cache not shifted", "cache_out[(b * (K - 1) + j) * C + c] = sq[len + j];",
+     "cache_out[(b * (K - 1) + j) * C + c] = sq[j];"),
+    ("stream chunk placed before the cache", "for (long u = 0; u < len; ++u) sq[K - 1 + u] = (double)x[(b * Tc + u) * C + c];",
+     "for (long u = 0; u < len; ++u) sq[u] = (double)x[(b * Tc + u) * C + c];"),
+    ("stream output mask dropped", "                if (t < len) {\n                    for (long k = 0; k < K; ++k)\n                        acc += sq[t + k]",
+     "                if (t < Tc) {\n                    for (long k = 0; k < K; ++k)\n                        acc += sq[t + k]"),
+    ("stream kernel flipped", "acc += sq[t + k] * (double)w[k * C + c];", "acc += sq[t + k] * (double)w[(K - 1 - k) * C + c];"),
     ("front bwd b0 left out of the recompute", "acc += b0 ? (double)b0[c] : 0.0;\n                    size_t q",
      "size_t q"),
 ]

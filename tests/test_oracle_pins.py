@@ -810,3 +810,99 @@ def test_1d_bwd_finite_differences_in_w():
         e = np.zeros_like(w)
         e[idx] = 0.5
         assert abs((loss(w + e) - loss(w - e)) - dw[idx]) <= 1e-9 * (1 + abs(dw[idx]))
+
+
+# ------------------------------------------------- streaming 1-D conv -----
+
+def torch_causal_conv1d_seq(seq, w, b):
+    """Causal depthwise conv of one whole sequence seq [T, C] (torch, fp64)."""
+    T, C = seq.shape
+    K = w.shape[0]
+    xt = torch.from_numpy(seq.astype(np.float64)).t()[None]                 # [1, C, T]
+    xt = Fn.pad(xt, (K - 1, 0))
+    wt = torch.from_numpy(w.astype(np.float64)).t().contiguous()[:, None]  # [C, 1, K]
+    bt = torch.from_numpy(b.astype(np.float64))
+    return Fn.conv1d(xt, wt, bt, groups=C)[0].t().numpy()
+
+
+def run_stream(chunks, lens, w, b, K, C):
+    """Feed chunks [n][B,Tc,C] with per-stream valid lengths through the
+    streaming oracle from a zero cache; returns each stream's valid outputs
+    concatenated, and the final cache."""
+    B = chunks[0].shape[0]
+    cache = np.zeros((B, K - 1, C), np.float32)
+    outs = [[] for _ in range(B)]
+    for x, L in zip(chunks, lens):
+        y, cache64 = oracle.dwconv1d_stream_fwd(x, w, b, L, cache)
+        cache = cache64.astype(np.float32)
+        assert np.array_equal(cache.astype(np.float64), cache64)   # a cache holds input values exactly
+        for bi in range(B):
+            l = min(max(int(L[bi]), 0), x.shape[1])
+            outs[bi].append(y[bi, :l])
+            assert np.all(y[bi, l:] == 0)
+    return [np.concatenate(o, axis=0) for o in outs], cache
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 9, 15])
+def test_1d_stream_chunks_equal_the_whole_causal_conv(K):
+    r = rng(70 + K)
+    B, C, Tc, n = 3, 5, 6, 7
+    chunks = [f32(r.standard_normal((B, Tc, C))) for _ in range(n)]
+    lens = [r.integers(-1, Tc + 2, B).astype(np.int32) for _ in range(n)]
+    lens[2][0] = 0                           # a stream with nothing new in one chunk
+    w, b = f32(r.standard_normal((K, C))), f32(r.standard_normal(C))
+    got, cache = run_stream(chunks, lens, w, b, K, C)
+    for bi in range(B):
+        seq = np.concatenate([x[bi, :min(max(int(L[bi]), 0), Tc)] for x, L in zip(chunks, lens)], axis=0)
+        close(got[bi], torch_causal_conv1d_seq(seq, w, b))
+        tail = np.concatenate([np.zeros((K - 1, C), np.float32), seq], axis=0)[len(seq):]
+        assert np.array_equal(cache[bi], tail)   # the last K-1 frames of the whole sequence
+
+
+def test_1d_stream_single_chunk_from_zero_cache_is_the_causal_conv():
+    r = rng(77)
+    B, T, C, K = 3, 20, 4, 9
+    x = f32(r.standard_normal((B, T, C)))
+    w, b = f32(r.standard_normal((K, C))), f32(r.standard_normal(C))
+    L = np.array([20, 7, 0], np.int32)
+    y, _ = oracle.dwconv1d_stream_fwd(x, w, b, L, np.zeros((B, K - 1, C), np.float32))
+    assert np.array_equal(y, oracle.dwconv1d_fwd(x, w, b, L, True))
+
+
+def test_1d_stream_delta_kernels_read_the_cache():
+    """w = e_0 returns the sequence K-1 frames back (the cache first); w =
+    e_{K-1} is the identity on the chunk."""
+    r = rng(78)
+    B, Tc, C, K = 2, 10, 3, 5
+    x = f32(r.standard_normal((B, Tc, C)))
+    cache = f32(r.standard_normal((B, K - 1, C)))
+    L = np.array([10, 3], np.int32)
+    z = np.zeros(C, np.float32)
+    e0 = np.zeros((K, C), np.float32)
+    e0[0] = 1.0
+    y, c2 = oracle.dwconv1d_stream_fwd(x, e0, z, L, cache)
+    for bi, l in enumerate(L):
+        seq = np.concatenate([cache[bi], x[bi, :l]], axis=0).astype(np.float64)
+        assert np.array_equal(y[bi, :l], seq[:l]) and np.all(y[bi, l:] == 0)
+        assert np.array_equal(c2[bi], seq[l:l + K - 1])
+    eK = np.zeros((K, C), np.float32)
+    eK[K - 1] = 1.0
+    y, _ = oracle.dwconv1d_stream_fwd(x, eK, z, L, cache)
+    for bi, l in enumerate(L):
+        assert np.array_equal(y[bi, :l], x[bi, :l].astype(np.float64))
+
+
+def test_1d_stream_empty_chunk_keeps_the_cache_and_nan_past_length_never_read():
+    r = rng(79)
+    B, Tc, C, K = 2, 6, 3, 4
+    x = f32(r.standard_normal((B, Tc, C)))
+    w, b = f32(r.standard_normal((K, C))), f32(r.standard_normal(C))
+    cache = f32(r.standard_normal((B, K - 1, C)))
+    L = np.array([0, 4], np.int32)
+    y, c2 = oracle.dwconv1d_stream_fwd(x, w, b, L, cache)
+    assert np.all(y[0] == 0) and np.array_equal(c2[0], cache[0].astype(np.float64))
+    xn = x.copy()
+    xn[0] = np.nan
+    xn[1, 4:] = np.nan
+    y2, c3 = oracle.dwconv1d_stream_fwd(xn, w, b, L, cache)
+    assert np.array_equal(y, y2) and np.array_equal(c2, c3)
