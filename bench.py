@@ -10,6 +10,7 @@ size, on synthetic inputs resident in HBM:
   conv1d  dwconv1d_fwd      [16,750,1024] K=9 symmetric                 bf16 storage
   sweep   dwconv1d_fwd      [32,1500,512] causal, K = 3, 4, 5, 9, 15    fp32
           dwconv1d_fwd      [32,1500,200] causal, K = 9                 fp32
+  stream  dwconv1d_stream_fwd  1024 streams x 8-frame chunks, C 1024, K 9, cache  bf16
           dwconv1d_bwd      dx, dw, db of [32,1500,512] causal K = 9    fp32, fp64 sums
   stage   dwconv2d_fwd      [32,1500,64,256] -> [32,750,32,256]         fp32
           dwconv2d_bwd      dx, dw, db of the same                      fp32
@@ -85,6 +86,15 @@ def work_conv1d(c, es):
     L = clamp_lengths(c["lengths"].tolist(), T)
     rd = sum(L) * C * es + (K * C + C) * es + 4 * B
     wr = B * T * C * es
+    flops = 2 * K * C * sum(L)
+    return rd, wr, flops
+
+
+def work_conv1d_stream(c, es):
+    B, Tc, C, K = c["B"], c["Tc"], c["C"], c["K"]
+    L = clamp_lengths(c["lengths"].tolist(), Tc)
+    rd = sum(L) * C * es + B * (K - 1) * C * es + (K + 1) * C * es + 4 * B   # chunk, cache, w, b, lengths
+    wr = B * Tc * C * es + B * (K - 1) * C * es                                # y and the new cache
     flops = 2 * K * C * sum(L)
     return rd, wr, flops
 
@@ -212,6 +222,14 @@ def build_rows(dev):
             *work_conv1d(s, 4),
             (lambda s=s, sL=sL, sy=sy: dw.dwconv1d_fwd(s["x"], s["w"], s["b"], sL, y=sy, causal=True)))
 
+    st = datagen.conv1d_stream(device=dev)
+    stL = st["lengths"].to(dev)
+    sty = torch.empty_like(st["x"])
+    stc = torch.empty_like(st["cache"])
+    add("conv1d_stream_bf16", "dwconv1d_stream_fwd", "1024 streams x 8-frame chunks, C1024 K9, K-1 frame cache, bf16",
+        st["B"] * st["Tc"], *work_conv1d_stream(st, 2),
+        lambda: dw.dwconv1d_stream_fwd(st["x"], st["w"], st["b"], stL, st["cache"], cache_out=stc, y=sty))
+
     s9 = sweep[3]
     assert s9["K"] == 9 and s9["C"] == 512
     s9["dy"] = datagen.normal((s9["B"], s9["T"], s9["C"]), 1.0, "c4/dy/K9/C512", device=dev)
@@ -260,7 +278,7 @@ def build_rows(dev):
     add("stage_bwd_bf16", "dwconv2d_bwd_ex", "dx,dw,db of [32,1500,64,256] bf16 storage, fp32 dw/db",
         g["B"] * g["T"], *work_stage_bwd(g, es=2),
         lambda: dw.dwconv2d_bwd(h["x"], h["w"], gL, h["dy"], dx=hdx, dw=gdw, db=gdb, workspace=ws))
-    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h)
+    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h, stream=st)
     return rows, data
 
 
@@ -279,6 +297,8 @@ def cpu_baseline(data, target_s: float):
     gc = dict(g, dy=data["stage_causal"]["dy"])
     gh = hp(data["stage_bf16"])                    # bf16 values, widened exactly on the host
     gh["x"], gh["dy"] = data["stage_bf16"]["x"], data["stage_bf16"]["dy"]
+    sm = hp(data["stream"])
+    sm["x"], sm["cache"] = data["stream"]["x"], data["stream"]["cache"]
     sweep = []
     for s in data["sweep"]:
         hs = hp(s)
@@ -327,6 +347,12 @@ def cpu_baseline(data, target_s: float):
                 oracle.dwconv1d_bwd(xs, s["w"], s["lengths"][:m], dys, True)
                 secs += time.perf_counter() - t
                 frames += m * s["T"]
+        m = min(n, sm["B"])
+        xs, cs = host(sm["x"], m), host(sm["cache"], m)
+        t = time.perf_counter()
+        oracle.dwconv1d_stream_fwd(xs, sm["w"], sm["b"], sm["lengths"][:m], cs)
+        secs += time.perf_counter() - t
+        frames += m * sm["Tc"]
         m = min(n, g["B"])
         for st, pads in ((g, None), (gc, (2, 1, 2, 1)), (gh, None)):
             xs, dys = host(st["x"], m), host(st["dy"], m)
@@ -466,7 +492,7 @@ def main():
         "data": "synthetic (seeded; log-mel-shaped inputs, lengths ~U[T/2,T])",
         "config": {
             "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd (symmetric and causal); conv-module dwconv1d [16,750,1024] K9 "
-                        "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; depthwise conv2d "
+                        "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; streaming dwconv1d 1024x8x1024 K9 bf16 with cache; depthwise conv2d "
                         "stage [32,1500,64,256] fwd+bwd (symmetric fp32, causal fp32, symmetric bf16)",
             "frames_per_step": frames,
             "alg_bytes_per_step": alg,

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "DwconvError", "abi_version",
-    "dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
+    "dwconv1d_fwd", "dwconv1d_stream_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
     "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
     "conv2d_out_shape", "CAUSAL_PADS_2D", "front_out_shape", "out_len",
 ]
@@ -57,6 +57,8 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dw_last_error.argtypes = []
     lib.dwconv1d_fwd.restype = _int
     lib.dwconv1d_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _vp]
+    lib.dwconv1d_stream_fwd.restype = _int
+    lib.dwconv1d_stream_fwd.argtypes = [_vp] * 7 + [_i64] * 4 + [_int, _vp]
     lib.dwconv1d_bwd_workspace_bytes.restype = _sz
     lib.dwconv1d_bwd_workspace_bytes.argtypes = [_i64] * 4
     lib.dwconv1d_bwd.restype = _int
@@ -153,6 +155,36 @@ def dwconv1d_fwd(x, w, bias=None, lengths=None, y=None, causal: bool = False):
                              DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC,
                              DW_BF16 if dt == torch.bfloat16 else DW_F32, _stream(dev)))
     return y
+
+
+def dwconv1d_stream_fwd(x, w, bias, lengths, cache_in, cache_out=None, y=None):
+    """One chunk x [B,Tc,C] of a causal 1-D depthwise conv after the cached
+    K-1 frames cache_in [B,K-1,C]; returns (y, cache_out).  cache_out must be
+    a different tensor from cache_in (it is allocated when not given)."""
+    if x.dim() != 3:
+        raise ValueError("x must be [B, Tc, C]")
+    dev, dt = x.device, x.dtype
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"x must be float32 or bfloat16, not {dt}")
+    B, Tc, C = x.shape
+    _dev_tensor("x", x, dt, dev)
+    if w.dim() != 2 or w.shape[1] != C:
+        raise ValueError("w must be [K, C]")
+    _dev_tensor("w", w, dt, dev)
+    K = w.shape[0]
+    _dev_tensor("bias", bias, dt, dev, (C,), allow_none=True)
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    _dev_tensor("cache_in", cache_in, dt, dev, (B, K - 1, C))
+    if cache_out is None:
+        cache_out = torch.empty_like(cache_in)
+    _dev_tensor("cache_out", cache_out, dt, dev, (B, K - 1, C))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev_tensor("y", y, dt, dev, (B, Tc, C))
+    _check(_lib.dwconv1d_stream_fwd(_ptr(x), _ptr(w), _ptr(bias), _ptr(lengths), _ptr(cache_in), _ptr(y),
+                                    _ptr(cache_out), B, Tc, C, K, DW_BF16 if dt == torch.bfloat16 else DW_F32,
+                                    _stream(dev)))
+    return y, cache_out
 
 
 def dwconv1d_bwd_workspace_bytes(B, T, C, K) -> int:

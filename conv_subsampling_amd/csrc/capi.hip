@@ -89,6 +89,30 @@ dw_status dwconv1d_fwd(const void* x, const void* w, const void* bias, const int
                                             (hipStream_t)stream), fn);
 }
 
+dw_status dwconv1d_stream_fwd(const void* x, const void* w, const void* bias, const int32_t* lengths,
+                              const void* cache_in, void* y, void* cache_out, int64_t B, int64_t Tc, int64_t C,
+                              int64_t K, dw_dtype dtype, void* stream) {
+    const char* fn = "dwconv1d_stream_fwd";
+    if (B < 0 || Tc < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (K < 1) return fail(DW_ERR_INVALID_ARG, "%s: kernel width K=%lld must be >= 1", fn, (long long)K);
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+    if (B == 0 || C == 0) return ok();
+    const bool has_cache = K > 1;
+    if ((!x && Tc > 0) || !w || (!y && Tc > 0) || (has_cache && (!cache_in || !cache_out)))
+        return fail(DW_ERR_INVALID_ARG, "%s: x, w, y and the caches must not be NULL (unless empty)", fn);
+    if (has_cache && cache_in == (const void*)cache_out)
+        return fail(DW_ERR_INVALID_ARG, "%s: cache_out must be a different buffer from cache_in", fn);
+    if (Tc > 0 && (x == (const void*)y || (has_cache && (y == cache_in || y == (const void*)cache_out))))
+        return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x or a cache", fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    const void* ptrs[6] = {x, w, bias, y, cache_in, cache_out};
+    const int vec = dw::pick_vec(C, es, ptrs, 6, 4);
+    if (!dw::dwconv1d_stream_fits(B, Tc, C, K, es, vec))
+        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    return from_hip(dw::launch_dwconv1d_stream(x, w, bias, lengths, cache_in, y, cache_out, B, Tc, C, K,
+                                               dtype == DW_BF16, vec, (hipStream_t)stream), fn);
+}
+
 size_t dwconv1d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t K) {
     if (B < 0 || T < 0 || C < 0 || !dw::dwconv1d_bwd_supported(K)) return 0;
     return dw::dwconv1d_bwd_workspace(B, T, C, K);

@@ -229,6 +229,179 @@ int pick_vec(int64_t C, int elem_bytes, const void* const* ptrs, int nptrs, int 
 
 
 // ---------------------------------------------------------------------------
+// Streaming form (the streaming encoder's conv with a cache: parakeet.cpp PR
+// #102, "What changes"; state kept on the GPU between chunks).  Per stream,
+// the sequence convolved is the K - 1 cached frames followed by the chunk's
+// len valid frames, s = cache ++ x[:len], causally:
+//   y[t] = sum_k s[t + k] w[k] + bias   (t < len; 0 after)
+//   cache_out[j] = s[len + j]           (j < K - 1: the last K - 1 frames)
+// The grid is the forward's (item, time tile, channel group), plus one tile
+// per item whose threads write the new cache.  Frame s[i] is x frame
+// i - (K - 1) when i >= K - 1 and cache frame i otherwise; where a window or
+// the cache update may need either, both are loaded through their resources
+// (the one out of range reads zero, with no traffic) and a select picks the
+// right one, so cached values are copied bit for bit.  Only tiles with
+// t0 < K - 1 read the cache.  The output cache is a different buffer from the
+// input cache, since the update runs beside the tiles that read it.
+// ---------------------------------------------------------------------------
+
+template <typename S, int V>
+__device__ __forceinline__ Vf<V> stream_frame(rsrc_t xr, rsrc_t cr, int32_t i, int32_t Km1, uint32_t row,
+                                              uint32_t coff) {
+    const Vf<V> xv = Buf<S, V>::load(xr, (uint32_t)((i - Km1) * (int32_t)row) + coff);
+    const Vf<V> cv = Buf<S, V>::load(cr, (uint32_t)(i * (int32_t)row) + coff);
+    Vf<V> r;
+#pragma unroll
+    for (int e = 0; e < V; ++e) r.v[e] = i < Km1 ? cv.v[e] : xv.v[e];
+    return r;
+}
+
+// K > 0: a compile-time width with a register window; K = 0: any width,
+// given at run time, taps read through the cache.
+template <typename S, int V, int K, int TT>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_stream_kernel(
+    const S* __restrict__ x, const S* __restrict__ w, const S* __restrict__ bias,
+    const int32_t* __restrict__ lengths, const S* __restrict__ cache_in, S* __restrict__ y,
+    S* __restrict__ cache_out, int32_t Tc, int32_t C, int32_t Kr, uint32_t n_tiles, uint32_t CG,
+    uint32_t blocks_per_item) {
+    const int32_t Kw = K > 0 ? K : Kr;
+    const int32_t Km1 = Kw - 1;
+    const Tile1d d = decode_1d(n_tiles + 1, CG, blocks_per_item);
+    if (!d.valid) return;
+    const int32_t len = (int32_t)item_length(lengths, d.b, Tc);
+    const uint32_t row = (uint32_t)C * sizeof(S);
+    const rsrc_t xr = make_rsrc(x + (int64_t)d.b * Tc * C, (uint32_t)len * row);
+    const rsrc_t cr = make_rsrc(cache_in + (int64_t)d.b * Km1 * C, (uint32_t)Km1 * row);
+    const int32_t c0 = (int32_t)d.cg * V;
+    const uint32_t coff = (uint32_t)c0 * sizeof(S);
+
+    if (d.tile == n_tiles) {
+        // The new cache: s[len + j], j < K - 1.
+        const rsrc_t co = make_rsrc(cache_out + (int64_t)d.b * Km1 * C, (uint32_t)Km1 * row);
+        if constexpr (K > 0) {
+            Vf<V> v[K > 1 ? K - 1 : 1];
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j) v[j] = stream_frame<S, V>(xr, cr, len + j, Km1, row, coff);
+#pragma unroll
+            for (int j = 0; j < K - 1; ++j) Buf<S, V>::store(co, (uint32_t)j * row + coff, v[j]);
+        } else {
+            for (int32_t j = 0; j < Km1; ++j)
+                Buf<S, V>::store(co, (uint32_t)j * row + coff, stream_frame<S, V>(xr, cr, len + j, Km1, row, coff));
+        }
+        return;
+    }
+
+    const rsrc_t yr = make_rsrc(y + (int64_t)d.b * Tc * C, (uint32_t)Tc * row);
+    const int32_t t0 = (int32_t)d.tile * TT;
+    if (t0 >= len) {
+        const Vf<V> z = vzero<V>();
+#pragma unroll
+        for (int i = 0; i < TT; ++i) Buf<S, V>::store(yr, (uint32_t)(t0 + i) * row + coff, z);
+        return;
+    }
+    const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
+    if constexpr (K > 0) {
+        Vf<V> win[TT + K - 1];
+        if (t0 < K - 1) {
+#pragma unroll
+            for (int r = 0; r < TT + K - 1; ++r) win[r] = stream_frame<S, V>(xr, cr, t0 + r, K - 1, row, coff);
+        } else {
+#pragma unroll
+            for (int r = 0; r < TT + K - 1; ++r)
+                win[r] = Buf<S, V>::load(xr, (uint32_t)((t0 + r - (K - 1)) * (int32_t)row) + coff);
+        }
+        Vf<V> wk[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
+#pragma unroll
+        for (int i = 0; i < TT; ++i) {
+            Vf<V> acc = bv;
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int e = 0; e < V; ++e) acc.v[e] = __builtin_fmaf(win[i + k].v[e], wk[k].v[e], acc.v[e]);
+            const bool keep = t0 + i < len;
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc.v[e] = keep ? acc.v[e] : 0.0f;
+            Buf<S, V>::store(yr, (uint32_t)(t0 + i) * row + coff, acc);
+        }
+    } else {
+        for (int i = 0; i < TT; ++i) {
+            const int32_t t = t0 + i;
+            Vf<V> acc = vzero<V>();
+            if (t < len) {
+                acc = bv;
+                for (int32_t k = 0; k < Kw; ++k) {
+                    const Vf<V> sv = stream_frame<S, V>(xr, cr, t + k, Km1, row, coff);
+                    const Vf<V> wv = load_param<S, V>(w + (int64_t)k * C + c0);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) acc.v[e] = __builtin_fmaf(sv.v[e], wv.v[e], acc.v[e]);
+                }
+            }
+            Buf<S, V>::store(yr, (uint32_t)t * row + coff, acc);
+        }
+    }
+}
+
+bool dwconv1d_stream_fits(int64_t B, int64_t Tc, int64_t C, int64_t K, int elem_bytes, int vec) {
+    if ((Tc + 2 * K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    const int64_t tt = tile_for(K, elem_bytes == 2);
+    const int64_t per_item = ((Tc + tt - 1) / tt + 1) * (C / vec);
+    return B * ((per_item + kBlock1d - 1) / kBlock1d) < ((int64_t)1 << 31);
+}
+
+template <typename S, int V>
+static hipError_t launch_stream_typed(const S* x, const S* w, const S* bias, const int32_t* lengths,
+                                      const S* cache_in, S* y, S* cache_out, int64_t B, int64_t Tc, int64_t C,
+                                      int64_t K, hipStream_t st) {
+    const int tt = tile_for(K, sizeof(S) == 2);
+    const uint32_t n_tiles = (uint32_t)((Tc + tt - 1) / tt);
+    const uint32_t CG = (uint32_t)(C / V);
+    const uint32_t bpi = (uint32_t)(((uint64_t)(n_tiles + 1) * CG + kBlock1d - 1) / kBlock1d);
+    const dim3 grid((uint32_t)(B * bpi)), block(kBlock1d);
+    const int32_t T32 = (int32_t)Tc, C32 = (int32_t)C, K32 = (int32_t)K;
+#define DW1S_CASE(KK)                                                                                    \
+    case KK:                                                                                             \
+        hipLaunchKernelGGL((dwconv1d_stream_kernel<S, V, KK, tile_of<S, KK, V>()>), grid, block, 0, st, x, w, \
+                           bias, lengths, cache_in, y, cache_out, T32, C32, K32, n_tiles, CG, bpi);        \
+        break;
+    switch (K) {
+        DW1S_CASE(3)
+        DW1S_CASE(4)
+        DW1S_CASE(5)
+        DW1S_CASE(9)
+        DW1S_CASE(15)
+        default:
+            hipLaunchKernelGGL((dwconv1d_stream_kernel<S, V, 0, kTileAnyK>), grid, block, 0, st, x, w, bias,
+                               lengths, cache_in, y, cache_out, T32, C32, K32, n_tiles, CG, bpi);
+    }
+#undef DW1S_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias, const int32_t* lengths,
+                                  const void* cache_in, void* y, void* cache_out, int64_t B, int64_t Tc, int64_t C,
+                                  int64_t K, bool bf16, int vec, hipStream_t st) {
+    if (bf16) {
+        auto X = (const uint16_t*)x; auto W = (const uint16_t*)w; auto Bi = (const uint16_t*)bias;
+        auto Ci = (const uint16_t*)cache_in; auto Y = (uint16_t*)y; auto Co = (uint16_t*)cache_out;
+        switch (vec) {
+            case 4: return launch_stream_typed<uint16_t, 4>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+            case 2: return launch_stream_typed<uint16_t, 2>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+            default: return launch_stream_typed<uint16_t, 1>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+        }
+    }
+    auto X = (const float*)x; auto W = (const float*)w; auto Bi = (const float*)bias;
+    auto Ci = (const float*)cache_in; auto Y = (float*)y; auto Co = (float*)cache_out;
+    switch (vec) {
+        case 4: return launch_stream_typed<float, 4>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+        case 2: return launch_stream_typed<float, 2>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+        default: return launch_stream_typed<float, 1>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+    }
+}
+
+
+// ---------------------------------------------------------------------------
 // Backward of the 1-D depthwise conv (the conv module in training): with
 // g = dy at unmasked frames (t < len) and 0 elsewhere,
 //   dx[u, c] = [u < len] sum_k g[u + pL - k, c] w[k, c]

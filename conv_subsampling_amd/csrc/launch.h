@@ -32,6 +32,12 @@ hipError_t launch_dwconv1d_fwd(const void* x, const void* w, const void* bias, c
                                void* y, int64_t B, int64_t T, int64_t C, int64_t K, int64_t pad_left,
                                bool bf16, int vec, hipStream_t stream);
 
+// Streaming 1-D conv (causal over a K-1 frame cache and the chunk).
+bool dwconv1d_stream_fits(int64_t B, int64_t Tc, int64_t C, int64_t K, int elem_bytes, int vec);
+hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias, const int32_t* lengths,
+                                  const void* cache_in, void* y, void* cache_out, int64_t B, int64_t Tc, int64_t C,
+                                  int64_t K, bool bf16, int vec, hipStream_t stream);
+
 // 1-D backward: the widths with a kernel, the widest vector each takes, and
 // the workspace (fp64 partials) it needs.
 bool dwconv1d_bwd_supported(int64_t K);

@@ -122,6 +122,25 @@ def conv1d_causal_sweep(K, device="cpu", seed=DEFAULT_SEED, B=32, T=1500, C=512)
     )
 
 
+def conv1d_stream(device="cpu", seed=DEFAULT_SEED, B=1024, Tc=8, C=1024, K=9, bf16=True):
+    """Streaming conv module: B concurrent streams, one chunk of Tc frames
+    each per call, w ~ N(0, 1/K), b ~ N(0, 0.1), a cache of K-1 frames
+    ~ N(0,1) per stream (a stream mid-utterance), chunk lengths ~U[Tc/2, Tc];
+    all bf16 by default."""
+    d = dict(
+        x=normal((B, Tc, C), 1.0, "c6/x", seed, device),
+        w=normal((K, C), 1.0 / K, "c6/w", seed, device),
+        b=normal((C,), 0.1, "c6/b", seed, device),
+        cache=normal((B, K - 1, C), 1.0, "c6/cache", seed, device),
+        lengths=int_uniform(B, Tc // 2, Tc, "c6/len", seed),
+        B=B, Tc=Tc, C=C, K=K,
+    )
+    if bf16:
+        for k in ("x", "w", "b", "cache"):
+            d[k] = d[k].to(torch.bfloat16)
+    return d
+
+
 def conv2d_stage(device="cpu", seed=DEFAULT_SEED, B=32, T=1500, F=64, C=256, dy_rows_cols=None, bf16=False):
     """Depthwise 3x3 stride-2 conv2d fwd+bwd: x = max(N(0,1), 0) [B,T,F,C],
     dy ~ N(0,1) [B,T',F',C] with (T', F') = dy_rows_cols, by default

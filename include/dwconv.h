@@ -8,6 +8,9 @@
  *   dwconv1d_fwd     the Conformer conv module's depthwise Conv1d in SSM_CONV
  *                    form (PR #102, "What changes")
  *   dwconv1d_bwd     its gradients dx, dw, db (the conv module in training)
+ *   dwconv1d_stream_fwd
+ *                    its streaming form with a K-1 frame cache (same PR:
+ *                    the streaming encoder's conv with a cache)
  *   dwsub_fused_fwd  the depthwise-striding subsampler front: conv0, bias,
  *                    ReLU, time mask and depthwise conv, fused (PR #16114,
  *                    "What does this PR do", first kernel)
@@ -100,6 +103,33 @@ const char *dw_last_error(void);
 dw_status dwconv1d_fwd(const void *x, const void *w, const void *bias, const int32_t *lengths,
                        void *y, int64_t B, int64_t T, int64_t C, int64_t K,
                        dw_pad pad, dw_dtype dtype, void *stream);
+
+/*
+ * dwconv1d_stream_fwd -- the causal depthwise conv of a streaming encoder,
+ * one chunk per call, with a cache of K - 1 frames per stream between calls
+ * (parakeet.cpp PR #102, "What changes": the streaming encoder's conv with a
+ * cache).  Per stream b, with len_b = clamp(lengths[b], 0, Tc) valid frames
+ * in this chunk and s = cache_in[b] followed by x[b, 0:len_b]:
+ *   y[b, t, c]         = sum_{k<K} s[t + k, c] * w[k, c] + bias[c]   for t < len_b, else 0
+ *   cache_out[b, j, c] = s[len_b + j, c]                            for j < K - 1
+ * (the last K - 1 frames of the cache and the chunk together; a stream with
+ * len_b = 0 keeps its cache).  From a zero cache, consecutive calls over the
+ * chunks of a sequence give its causal convolution (dwconv1d_fwd with
+ * DW_PAD_CAUSAL).
+ *
+ * x, y: [B][Tc][C]; w: [K][C]; bias: [C] or NULL; cache_in, cache_out:
+ * [B][K-1][C] (may be NULL when K = 1), in the same storage type as x.
+ * dtype DW_F32 or DW_BF16 (everything bf16; fp32 accumulation; cached values
+ * are copied bit for bit).  Any K >= 1.  cache_out must be a different
+ * buffer from cache_in (callers alternate two), since the new cache is
+ * written while the chunk's first frames are being read from the old one.
+ * Tc may be 0 (the cache is then copied).
+ * Errors: DW_ERR_INVALID_ARG for a NULL required pointer, a negative size,
+ * K < 1, a bad dtype, cache_out == cache_in, or y aliasing x or a cache.
+ */
+dw_status dwconv1d_stream_fwd(const void *x, const void *w, const void *bias, const int32_t *lengths,
+                              const void *cache_in, void *y, void *cache_out, int64_t B, int64_t Tc, int64_t C,
+                              int64_t K, dw_dtype dtype, void *stream);
 
 /*
  * Bytes of device workspace dwconv1d_bwd needs when it computes dw or db (0

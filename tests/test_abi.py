@@ -36,6 +36,7 @@ def lib():
     lib.dwconv2d_bwd_workspace_bytes_ex.restype = sz
     lib.dwconv2d_bwd_ex.argtypes = [vp] * 8 + [sz] + [i64] * 11 + [i, vp]
     lib.dwconv1d_bwd_workspace_bytes.argtypes = [i64] * 4
+    lib.dwconv1d_stream_fwd.argtypes = [vp] * 7 + [i64] * 4 + [i, vp]
     lib.dwconv1d_bwd_workspace_bytes.restype = sz
     lib.dwconv1d_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 4 + [i, i, vp]
     lib.dwsub_fused_bwd_workspace_bytes.argtypes = [i64] * 4
@@ -56,7 +57,7 @@ def declared_functions():
 
 def test_header_declares_the_four_operations():
     names = declared_functions()
-    for f in ("dwconv1d_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
+    for f in ("dwconv1d_fwd", "dwconv1d_stream_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
               "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dwconv2d_fwd_ex", "dwconv2d_bwd_ex",
               "dwconv2d_bwd_workspace_bytes_ex", "dwsub_fused_fwd_ex", "dwsub_fused_bwd_ex",
               "dwsub_fused_bwd_workspace_bytes_ex", "dw_abi_version", "dw_last_error"):
@@ -92,6 +93,21 @@ def test_dwconv1d_validation(lib):
     assert f(N, N, N, N, N, 0, 8, 4, 3, 0, 0, N) == OK
     assert f(P, P, N, N, Q, 2, 0, 4, 3, 1, 1, N) == OK
     assert f(P, P, N, N, Q, 2, 8, 0, 3, 1, 1, N) == OK
+
+
+def test_dwconv1d_stream_validation(lib):
+    f = lib.dwconv1d_stream_fwd
+    R, S = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    # x, w, bias, lengths, cache_in, y, cache_out, B, Tc, C, K, dtype, stream
+    assert f(P, P, N, N, R, Q, R, 4, 8, 16, 9, 0, N) == INVALID and "different" in err(lib)
+    assert f(P, P, N, N, R, Q, N, 4, 8, 16, 9, 0, N) == INVALID
+    assert f(P, P, N, N, R, P, S, 4, 8, 16, 9, 0, N) == INVALID and "alias" in err(lib)
+    assert f(P, P, N, N, R, R, S, 4, 8, 16, 9, 0, N) == INVALID
+    assert f(P, P, N, N, R, Q, S, 4, 8, 16, 0, 0, N) == INVALID and "K=0" in err(lib)
+    assert f(P, P, N, N, R, Q, S, 4, 8, 16, 9, 3, N) == INVALID and "dtype" in err(lib)
+    assert f(P, P, N, N, R, Q, S, -1, 8, 16, 9, 0, N) == INVALID
+    assert f(P, P, N, N, R, Q, S, 0, 8, 16, 9, 0, N) == OK
+    assert f(P, P, N, N, R, Q, S, 4, 8, 0, 9, 0, N) == OK
 
 
 def test_dwconv1d_bwd_validation(lib):
