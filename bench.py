@@ -18,6 +18,7 @@ size, on synthetic inputs resident in HBM:
           dwconv2d_bwd_ex   its dx, dw, db                              fp32
           dwconv2d_fwd_ex   the symmetric stage with bf16 storage       bf16
           dwconv2d_bwd_ex   its dx, dw, db (dw, db in fp32)             bf16
+  stage3  dwconv2d_fwd/bwd  [32,375,20,256] -> [32,188,10,256] (8x)     fp32
 
 The timed region is exactly --steps steps, bracketed by device
 synchronisation.  Per-operation times come from HIP events recorded on the
@@ -278,7 +279,18 @@ def build_rows(dev):
     add("stage_bwd_bf16", "dwconv2d_bwd_ex", "dx,dw,db of [32,1500,64,256] bf16 storage, fp32 dw/db",
         g["B"] * g["T"], *work_stage_bwd(g, es=2),
         lambda: dw.dwconv2d_bwd(h["x"], h["w"], gL, h["dy"], dx=hdx, dw=gdw, db=gdb, workspace=ws))
-    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h, stream=st)
+    # 8x subsampling's third stride-2 stage, on the 4x front output of a 15 s batch
+    g3 = datagen.conv2d_stage(device=dev, B=32, T=375, F=20, C=256)
+    g3L = g3["lengths"].to(dev)
+    g3y = torch.empty((32, 188, 10, 256), device=dev)
+    g3dx = torch.empty_like(g3["x"])
+    ws3 = torch.empty((dw.dwconv2d_bwd_workspace_bytes(32, 375, 20, 256),), dtype=torch.uint8, device=dev)
+    add("stage3_fwd", "dwconv2d_fwd", "[32,375,20,256] -> [32,188,10,256] fp32 (8x third stage)", g3["B"] * g3["T"],
+        *work_stage_fwd(g3), lambda: dw.dwconv2d_fwd(g3["x"], g3["w"], g3["b"], g3L, y=g3y))
+    add("stage3_bwd", "dwconv2d_bwd", "dx,dw,db of [32,375,20,256] fp32 (8x third stage)", g3["B"] * g3["T"],
+        *work_stage_bwd(g3),
+        lambda: dw.dwconv2d_bwd(g3["x"], g3["w"], g3L, g3["dy"], dx=g3dx, dw=gdw, db=gdb, workspace=ws3))
+    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h, stream=st, stage3=g3)
     return rows, data
 
 
@@ -297,6 +309,8 @@ def cpu_baseline(data, target_s: float):
     gc = dict(g, dy=data["stage_causal"]["dy"])
     gh = hp(data["stage_bf16"])                    # bf16 values, widened exactly on the host
     gh["x"], gh["dy"] = data["stage_bf16"]["x"], data["stage_bf16"]["dy"]
+    g3 = hp(data["stage3"])
+    g3["x"], g3["dy"] = data["stage3"]["x"], data["stage3"]["dy"]
     sm = hp(data["stream"])
     sm["x"], sm["cache"] = data["stream"]["x"], data["stream"]["cache"]
     sweep = []
@@ -354,13 +368,13 @@ def cpu_baseline(data, target_s: float):
         secs += time.perf_counter() - t
         frames += m * sm["Tc"]
         m = min(n, g["B"])
-        for st, pads in ((g, None), (gc, (2, 1, 2, 1)), (gh, None)):
+        for st, pads in ((g, None), (gc, (2, 1, 2, 1)), (gh, None), (g3, None)):
             xs, dys = host(st["x"], m), host(st["dy"], m)
             t = time.perf_counter()
             oracle.dwconv2d_fwd(xs, st["w"], st["b"], st["lengths"][:m], pads=pads)
             oracle.dwconv2d_bwd(xs, st["w"], st["lengths"][:m], dys, pads=pads)
             secs += time.perf_counter() - t
-            frames += 2 * m * g["T"]
+            frames += 2 * m * st["T"]
         return secs, frames
 
     s1, _ = one_pass(1)
@@ -493,7 +507,8 @@ def main():
         "config": {
             "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd (symmetric and causal); conv-module dwconv1d [16,750,1024] K9 "
                         "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; streaming dwconv1d 1024x8x1024 K9 bf16 with cache; depthwise conv2d "
-                        "stage [32,1500,64,256] fwd+bwd (symmetric fp32, causal fp32, symmetric bf16)",
+                        "stage [32,1500,64,256] fwd+bwd (symmetric fp32, causal fp32, symmetric bf16); third stage "
+                        "[32,375,20,256] fwd+bwd",
             "frames_per_step": frames,
             "alg_bytes_per_step": alg,
             "parallelism": "single GPU",

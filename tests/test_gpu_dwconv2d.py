@@ -158,3 +158,41 @@ def test_stage_full_size_fwd_and_bwd():
     Lc = s["lengths"].clamp(0, T)
     assert_exact_zero(dx, time_mask(Lc, B, T)[:, :, None, None], "full dx masked rows")
     assert_exact_zero(y, out_mask(Lc, B, (T + 1) // 2)[:, :, None, None], "full y masked rows")
+
+
+def test_third_stage_full_size_fwd_and_bwd():
+    """8x subsampling's third stride-2 stage: the 4x front output of a 15 s
+    batch, [32,375,20,256] -> [32,188,10,256], lengths ~U[T/2, T] in the
+    stage's own frames; whole-batch parity."""
+    s = datagen.conv2d_stage(device=DEV, B=32, T=375, F=20, C=256)
+    L = s["lengths"].to(DEV)
+    say("dwconv2d third stage [32,375,20,256]")
+    y = lib().dwconv2d_fwd(s["x"], s["w"], s["b"], L)
+    dx, dw, db = lib().dwconv2d_bwd(s["x"], s["w"], L, s["dy"])
+    sync()
+    assert y.shape == (32, 188, 10, 256)
+    assert_parity(y, oracle.dwconv2d_fwd(s["x"], s["w"], s["b"], s["lengths"]), TOL_F32, "stage3 y")
+    rdx, rdw, rdb = oracle.dwconv2d_bwd(s["x"], s["w"], s["lengths"], s["dy"])
+    assert_parity(dx, rdx, TOL_F32, "stage3 dx")
+    assert_parity(dw, rdw, TOL_F32, "stage3 dw")
+    assert_parity(db, rdb, TOL_F32, "stage3 db")
+
+
+def test_front_then_third_stage_lengths_compose():
+    """The front (4x) followed by a third depthwise stage (8x), each masking
+    with its own frame lengths: ceil(len/2), then ceil again per stage."""
+    f = datagen.fused_front(device=DEV, B=3, T=96, F=40, C=32)
+    f["lengths"] = torch.tensor([96, 37, 0], dtype=torch.int32)
+    L = f["lengths"].to(DEV)
+    h = lib().dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], L)
+    L2 = (((f["lengths"] + 1) // 2) + 1) // 2          # the front's output frames
+    w3 = datagen.normal((3, 3, 32), 1.0 / 9, "t3/w", device=DEV)
+    b3 = datagen.normal((32,), 0.1, "t3/b", device=DEV)
+    y = lib().dwconv2d_fwd(h, w3, b3, L2.to(DEV))
+    sync()
+    ref_h = oracle.dwsub_front_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"])
+    ref = oracle.dwconv2d_fwd(np.asarray(h.cpu()), w3, b3, L2)
+    assert_parity(h, ref_h, TOL_F32, "front")
+    assert_parity(y, ref, TOL_F32, "third stage")
+    assert y.shape == (3, 12, 5, 32)
+    assert torch.all(y[2] == 0) and torch.all(y[1, 5:] == 0)   # ceil(ceil(ceil(37/2)/2)/2) = 5
