@@ -55,7 +55,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E peak
 VALU_F32_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz, unpacked fp32
-DOMINANT = "dwconv2d_bwd"          # the operation with the largest share of the step
+DOMINANT_ROW = "stage_bwd"         # the row with the largest share of the step
 DOMINANT_KERNEL = "dwconv2d_bwd_kernel"
 DOMINANT_SOURCES = ["conv_subsampling_amd/csrc/dwconv2d.hip", "conv_subsampling_amd/csrc/common.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dwconv2d_bwd_stage_traffic.txt")
@@ -77,6 +77,36 @@ def sources_sha(paths) -> str:
 # Algorithmic work per call: valid input rows, every output element, the
 # parameters and the lengths.  Masked input frames are never needed.
 # --------------------------------------------------------------------------
+
+# Each row's main kernel, as rocprofv3 names it (a prefix of the demangled
+# name, through the opening parenthesis), in the order build_rows adds the
+# rows.  A step launches the rows in this order, so the k-th dispatch of a
+# name within a step belongs to the k-th row listing it; the profile
+# summaries attribute dispatches to rows that way.
+ROW_KERNELS = [
+    ("front", "dw::dwsub_fused_fwd_kernel("),
+    ("front_bwd", "dw::dwsub_fused_bwd_kernel("),
+    ("front_causal", "dw::dwsub_fused_fwd_kernel("),
+    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel("),
+    ("conv1d_bf16", "dw::dwconv1d_fwd_kernel<unsigned short, 4, 9, 12>("),
+    ("conv1d_causal_K3_C512", "dw::dwconv1d_fwd_kernel<float, 4, 3, 4>("),
+    ("conv1d_causal_K4_C512", "dw::dwconv1d_fwd_kernel<float, 4, 4, 6>("),
+    ("conv1d_causal_K5_C512", "dw::dwconv1d_fwd_kernel<float, 4, 5, 8>("),
+    ("conv1d_causal_K9_C512", "dw::dwconv1d_fwd_kernel<float, 4, 9, 8>("),
+    ("conv1d_causal_K15_C512", "dw::dwconv1d_fwd_kernel<float, 4, 15, 12>("),
+    ("conv1d_causal_K9_C200", "dw::dwconv1d_fwd_kernel<float, 4, 9, 8>("),
+    ("conv1d_stream_bf16", "dw::dwconv1d_stream_kernel<unsigned short, 4, 9, 12>("),
+    ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_kernel<2, 9, true, 8>("),
+    ("stage_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
+    ("stage_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
+    ("stage_fwd_causal", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
+    ("stage_bwd_causal", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
+    ("stage_fwd_bf16", "dw::dwconv2d_fwd_kernel<unsigned short, 8, 1, 32>("),
+    ("stage_bwd_bf16", "dw::dwconv2d_bwd_kernel<unsigned short, 4, 2>("),
+    ("stage3_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
+    ("stage3_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
+]
+
 
 def clamp_lengths(L, T):
     return [min(max(int(v), 0), T) for v in L]
@@ -291,6 +321,7 @@ def build_rows(dev):
         *work_stage_bwd(g3),
         lambda: dw.dwconv2d_bwd(g3["x"], g3["w"], g3L, g3["dy"], dx=g3dx, dw=gdw, db=gdb, workspace=ws3))
     data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h, stream=st, stage3=g3)
+    assert [r["name"] for r in rows] == [n for n, _ in ROW_KERNELS], "ROW_KERNELS is out of date"
     return rows, data
 
 
@@ -480,7 +511,7 @@ def main():
         out_rows.append(row)
         log(f"  {r['name']:<22} {us:9.2f} us  {row['gbps']:8.1f} GB/s  ({100 * row['hbm_frac']:.1f}% of 8 TB/s)")
 
-    dom = next(r for r in out_rows if r["op"] == DOMINANT)
+    dom = next(r for r in out_rows if r["row"] == DOMINANT_ROW)
     roofline = dict(kernel=DOMINANT_KERNEL, bound="hbm", achieved=dom["gbps"], peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(dom["gbps"] / HBM_PEAK_GBPS, 4), traffic=read_traffic(),
                     launch_us=dom["us"], alg_bytes_per_launch=dom["alg_bytes"])
@@ -535,29 +566,62 @@ def _csv_rows(pattern):
     return out
 
 
+def attribute_dispatches(disp):
+    """Map each bench row to its dispatches.  disp: [(dispatch id, kernel
+    name, payload)] in any order.  Returns {row: [payload, ...]}."""
+    disp = sorted(disp, key=lambda t: int(t[0]))
+    out = {}
+    for name, prefix in ROW_KERNELS:
+        same = [n for n, p in ROW_KERNELS if p == prefix]
+        k, period = same.index(name), len(same)
+        hits = [pl for _, kn, pl in disp if prefix in kn]
+        out[name] = hits[k::period] if len(hits) % period == 0 else []
+    return out
+
+
 def summarize_profile(d):
     """Write profiles/ summaries from rocprofv3 output under d:
-    d/stats/**/*kernel_stats.csv, d/fetch/**/*counter_collection.csv,
-    d/write/**/*counter_collection.csv (any of them may be missing)."""
+    d/stats/**/*kernel_stats.csv and *kernel_trace.csv (durations),
+    d/fetch/**/*counter_collection.csv and d/write/** (HBM bytes); any may be
+    missing."""
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    cmd = lambda k: (open(os.path.join(d, k, "command.txt")).read().strip()
+                     if os.path.exists(os.path.join(d, k, "command.txt")) else "?")
     stats = _csv_rows(os.path.join(d, "stats", "**", "*kernel_stats.csv"))
+    trace = _csv_rows(os.path.join(d, "stats", "**", "*kernel_trace.csv"))
     if stats:
         lines = ["# rocprofv3 --kernel-trace --stats, one bench.py run on one MI355X",
-                 "# command: " + open(os.path.join(d, "stats", "command.txt")).read().strip()
-                 if os.path.exists(os.path.join(d, "stats", "command.txt")) else "#",
+                 "# command: " + cmd("stats"),
+                 "# per kernel name (every dispatch of the run, warm-up steps included):",
                  f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
         for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
             name = r.get("Name", r.get("KernelName", "?"))
-            short = name.split("(")[0][:60]
+            short = (name[5:] if name.startswith("void ") else name).split("(")[0][:60]
             lines.append(f"{short:<60} {int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
                          f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} {float(r.get('MaxNs', 0)) / 1e3:>10.2f} "
                          f"{float(r.get('Percentage', 0)):>6.2f}")
+        if trace:
+            disp = [(r["Dispatch_Id"], r["Kernel_Name"],
+                     (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3) for r in trace]
+            per_row = attribute_dispatches(disp)
+            lines += ["", "# per bench row: the row's main kernel, its dispatches in this run (warm-up steps",
+                      "# included) and their durations; a row's k-th dispatch of a kernel name within a",
+                      "# step is the k-th row listing that name",
+                      f"{'row':<24} {'kernel':<52} {'n':>4} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
+            for name, prefix in ROW_KERNELS:
+                v = per_row.get(name) or []
+                kshort = prefix.replace("dw::", "").rstrip("(")[:52]
+                if v:
+                    lines.append(f"{name:<24} {kshort:<52} {len(v):>4} {sum(v) / len(v):>9.2f} {min(v):>9.2f} "
+                                 f"{max(v):>9.2f}")
+                else:
+                    lines.append(f"{name:<24} {kshort:<52}    - (no dispatches attributed)")
         with open(os.path.join(ROOT, "profiles", "kernel_stats_bench_step.txt"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
         print("\n".join(lines))
 
     def counter(kind, cname):
-        """{dispatch id: (kernel name, value)} summed over the counter's instances."""
+        """[(dispatch id, kernel name, value summed over the counter's instances)]."""
         per = {}
         for r in _csv_rows(os.path.join(d, kind, "**", "*counter_collection.csv")):
             if r.get("Counter_Name") != cname:
@@ -565,7 +629,7 @@ def summarize_profile(d):
             key = r.get("Dispatch_Id")
             name, v = r.get("Kernel_Name", ""), float(r.get("Counter_Value", 0))
             per[key] = (name, per.get(key, (name, 0.0))[1] + v)
-        return per
+        return [(k, n, v) for k, (n, v) in per.items()]
 
     fetch = counter("fetch", "FETCH_SIZE")
     write = counter("write", "WRITE_SIZE")
@@ -575,28 +639,19 @@ def summarize_profile(d):
 
     def calib(tab):
         # the 1 GiB device copy is the largest copy-engine-kernel dispatch
-        vals = [v for (n, v) in tab.values() if "copyBuffer" in n]
+        vals = [v for (_, n, v) in tab if "copyBuffer" in n]
         return max(vals) if vals else None
 
-    def mean_of(tab, pat):
-        vals = [v for (n, v) in tab.values() if pat in n]
-        return sum(vals) / len(vals) if vals else None
-
     cf, cw = calib(fetch), calib(write)
-    # copy-size reference: the copy reads and writes 1 GiB
-    by_kernel = {}
-    for tab, idx in ((fetch, 0), (write, 1)):
-        for n, v in tab.values():
-            short = n.split("(")[0] if not n.startswith("void ") else n[5:].split("(")[0]
-            by_kernel.setdefault(short[:64], [[], []])[idx].append(v)
-    kf, kw = mean_of(fetch, DOMINANT_KERNEL + "<"), mean_of(write, DOMINANT_KERNEL + "<")
-    cmd = lambda k: (open(os.path.join(d, k, "command.txt")).read().strip()
-                     if os.path.exists(os.path.join(d, k, "command.txt")) else "?")
-    lines = ["# HBM traffic per launch of the dominant kernel, from rocprofv3 --pmc FETCH_SIZE and",
-             "# WRITE_SIZE (KiB per dispatch, separate runs), each scaled by the same counter's reading",
-             "# for a 1 GiB device copy (the copy reads 1 GiB and writes 1 GiB).",
+    f_rows, w_rows = attribute_dispatches(fetch), attribute_dispatches(write)
+    mean = lambda v: sum(v) / len(v) if v else None
+    kf, kw = mean(f_rows.get(DOMINANT_ROW)), mean(w_rows.get(DOMINANT_ROW))
+    lines = ["# HBM traffic per launch of the dominant row's kernel, from rocprofv3 --pmc FETCH_SIZE",
+             "# and WRITE_SIZE (KiB per dispatch, separate runs), each scaled by the same counter's",
+             "# reading for a 1 GiB device copy (the copy reads 1 GiB and writes 1 GiB).",
              "# fetch run: " + cmd("fetch"),
              "# write run: " + cmd("write"),
+             f"row={DOMINANT_ROW}",
              f"kernel={DOMINANT_KERNEL}",
              f"src_sha256={sources_sha(DOMINANT_SOURCES)}",
              f"copy_fetch_kib={cf}", f"copy_write_kib={cw}",
@@ -606,16 +661,14 @@ def summarize_profile(d):
         fb, wb = kf * 1024.0 * sf, kw * 1024.0 * swr
         lines += [f"scale_fetch={sf:.4f}", f"scale_write={swr:.4f}", f"fetch_bytes_per_launch={fb:.0f}",
                   f"write_bytes_per_launch={wb:.0f}", f"hbm_bytes_per_launch={fb + wb:.0f}"]
-        lines.append("# every kernel of the run, mean KiB per dispatch (raw counters): fetch, write")
-        for k in sorted(by_kernel):
-            fv, wv = by_kernel[k]
-            mf = sum(fv) / len(fv) if fv else float("nan")
-            mw = sum(wv) / len(wv) if wv else float("nan")
-            lines.append(f"#   {k:<64} {mf:>14.1f} {mw:>14.1f}")
+        lines.append("# every row's main kernel, HBM bytes per launch from the scaled counters: fetch, write")
+        for name, _ in ROW_KERNELS:
+            a, b = mean(f_rows.get(name)), mean(w_rows.get(name))
+            if a is not None and b is not None:
+                lines.append(f"#   {name:<24} {a * 1024.0 * sf:>16.0f} {b * 1024.0 * swr:>16.0f}")
     with open(TRAFFIC_FILE, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
-
 
 if __name__ == "__main__":
     sys.exit(main())
