@@ -71,6 +71,10 @@ constexpr int kBufferFlags = 0x00020000;  // dword 3 of a raw (untyped) gfx9 buf
 #define DW_STORE_NT 1
 #endif
 constexpr int kNonTemporal = DW_STORE_NT ? 2 : 0;  // store cache policy: 2 = no reuse expected
+#ifndef DW_LOAD_POLICY
+#define DW_LOAD_POLICY 0
+#endif
+constexpr int kLoadPolicy = DW_LOAD_POLICY;      // load cache policy of the streamed operands
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFlags);
@@ -85,14 +89,14 @@ struct Buf<float, V> {
     static __device__ __forceinline__ Vf<V> load(rsrc_t r, uint32_t off) {
         Vf<V> a;
         if constexpr (V == 4) {
-            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
             a.v[0] = __uint_as_float(t.x); a.v[1] = __uint_as_float(t.y);
             a.v[2] = __uint_as_float(t.z); a.v[3] = __uint_as_float(t.w);
         } else if constexpr (V == 2) {
-            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
             a.v[0] = __uint_as_float(t.x); a.v[1] = __uint_as_float(t.y);
         } else {
-            a.v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+            a.v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy));
         }
         return a;
     }
@@ -116,17 +120,17 @@ struct Buf<uint16_t, V> {
     static __device__ __forceinline__ Vf<V> load(rsrc_t r, uint32_t off) {
         Vf<V> a;
         if constexpr (V == 8) {
-            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
             a.v[0] = bf16_lo(t.x); a.v[1] = bf16_hi(t.x); a.v[2] = bf16_lo(t.y); a.v[3] = bf16_hi(t.y);
             a.v[4] = bf16_lo(t.z); a.v[5] = bf16_hi(t.z); a.v[6] = bf16_lo(t.w); a.v[7] = bf16_hi(t.w);
         } else if constexpr (V == 4) {
-            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
             a.v[0] = bf16_lo(t.x); a.v[1] = bf16_hi(t.x); a.v[2] = bf16_lo(t.y); a.v[3] = bf16_hi(t.y);
         } else if constexpr (V == 2) {
-            uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+            uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy);
             a.v[0] = bf16_lo(t); a.v[1] = bf16_hi(t);
         } else {
-            a.v[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
+            a.v[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kLoadPolicy) << 16);
         }
         return a;
     }
