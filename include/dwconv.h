@@ -42,6 +42,10 @@
  *   - Sizes are int64_t.  A forward call with no output elements enqueues
  *     nothing and returns DW_OK without looking at its pointers; a tensor
  *     with no elements may be NULL.
+ *   - The kernels address each batch item with 32-bit byte offsets: an item
+ *     whose tensors (with a few frames of padding) would reach 2^31 bytes is
+ *     refused with DW_ERR_UNSUPPORTED ("sizes too large for one launch").
+ *     The batch as a whole may be larger.
  *   - Errors: every argument is validated on the host before anything is
  *     enqueued.  A failing call returns a negative dw_status, enqueues
  *     nothing (except DW_ERR_HIP, raised when a launch is rejected) and sets
@@ -66,7 +70,7 @@ extern "C" {
 typedef enum {
     DW_OK = 0,
     DW_ERR_INVALID_ARG = -1,  /* null required pointer, negative size, aliasing, bad enum */
-    DW_ERR_UNSUPPORTED = -2,  /* a geometry this library does not implement */
+    DW_ERR_UNSUPPORTED = -2,  /* a geometry, width or size this library does not implement */
     DW_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
     DW_ERR_HIP = -4           /* the HIP runtime rejected a launch */
 } dw_status;
