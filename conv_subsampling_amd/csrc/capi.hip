@@ -106,7 +106,7 @@ dw_status dwconv1d_stream_fwd(const void* x, const void* w, const void* bias, co
         return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x or a cache", fn);
     const int es = dtype == DW_BF16 ? 2 : 4;
     const void* ptrs[6] = {x, w, bias, y, cache_in, cache_out};
-    const int vec = dw::pick_vec(C, es, ptrs, 6, 4);
+    const int vec = dw::pick_vec(C, es, ptrs, 6, dw::dwconv1d_stream_max_vec(K, dtype == DW_BF16));
     if (!dw::dwconv1d_stream_fits(B, Tc, C, K, es, vec))
         return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
     return from_hip(dw::launch_dwconv1d_stream(x, w, bias, lengths, cache_in, y, cache_out, B, Tc, C, K,

@@ -343,27 +343,58 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_stream_kernel(
     }
 }
 
+// Streaming chunks are short: a chunk of at most kStreamShort frames takes a
+// tile of that length instead of the forward's (a longer tile would only
+// compute frames past the chunk).
+#ifndef DW1S_SHORT_TILE
+#define DW1S_SHORT_TILE 8
+#endif
+constexpr int kStreamShort = DW1S_SHORT_TILE;
+
+static int stream_tile(int64_t K, bool bf16, int64_t Tc) {
+    const int tt = tile_for(K, bf16);
+    const bool specialised = K == 3 || K == 4 || K == 5 || K == 9 || K == 15;
+    return (kStreamShort > 0 && specialised && Tc <= kStreamShort && kStreamShort < tt) ? kStreamShort : tt;
+}
+
 bool dwconv1d_stream_fits(int64_t B, int64_t Tc, int64_t C, int64_t K, int elem_bytes, int vec) {
     if ((Tc + 2 * K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
-    const int64_t tt = tile_for(K, elem_bytes == 2);
+    const int64_t tt = stream_tile(K, elem_bytes == 2, Tc);
     const int64_t per_item = ((Tc + tt - 1) / tt + 1) * (C / vec);
     return B * ((per_item + kBlock1d - 1) / kBlock1d) < ((int64_t)1 << 31);
+}
+
+// bf16 streaming takes 16-byte lanes (8 channels) up to this width; wider
+// kernels keep 8-byte lanes, whose register window fits two waves per SIMD.
+#ifndef DW1S_BF16_VEC
+#define DW1S_BF16_VEC 8
+#endif
+constexpr int kStreamWideMaxK = 9;
+
+int dwconv1d_stream_max_vec(int64_t K, bool bf16) {
+    return bf16 ? (DW1S_BF16_VEC >= 8 && K <= kStreamWideMaxK ? 8 : 4) : 4;
 }
 
 template <typename S, int V>
 static hipError_t launch_stream_typed(const S* x, const S* w, const S* bias, const int32_t* lengths,
                                       const S* cache_in, S* y, S* cache_out, int64_t B, int64_t Tc, int64_t C,
                                       int64_t K, hipStream_t st) {
-    const int tt = tile_for(K, sizeof(S) == 2);
+    const int tt = stream_tile(K, sizeof(S) == 2, Tc);
+    const bool short_tile = kStreamShort > 0 && tt == kStreamShort;
     const uint32_t n_tiles = (uint32_t)((Tc + tt - 1) / tt);
     const uint32_t CG = (uint32_t)(C / V);
     const uint32_t bpi = (uint32_t)(((uint64_t)(n_tiles + 1) * CG + kBlock1d - 1) / kBlock1d);
     const dim3 grid((uint32_t)(B * bpi)), block(kBlock1d);
     const int32_t T32 = (int32_t)Tc, C32 = (int32_t)C, K32 = (int32_t)K;
+    constexpr int TS = kStreamShort > 0 ? kStreamShort : 1;
 #define DW1S_CASE(KK)                                                                                    \
     case KK:                                                                                             \
-        hipLaunchKernelGGL((dwconv1d_stream_kernel<S, V, KK, tile_of<S, KK, V>()>), grid, block, 0, st, x, w, \
-                           bias, lengths, cache_in, y, cache_out, T32, C32, K32, n_tiles, CG, bpi);        \
+        if (short_tile)                                                                                  \
+            hipLaunchKernelGGL((dwconv1d_stream_kernel<S, V, KK, TS>), grid, block, 0, st, x, w, bias,   \
+                               lengths, cache_in, y, cache_out, T32, C32, K32, n_tiles, CG, bpi);        \
+        else                                                                                             \
+            hipLaunchKernelGGL((dwconv1d_stream_kernel<S, V, KK, tile_of<S, KK, V>()>), grid, block, 0, st, x, \
+                               w, bias, lengths, cache_in, y, cache_out, T32, C32, K32, n_tiles, CG, bpi); \
         break;
     switch (K) {
         DW1S_CASE(3)
@@ -386,6 +417,10 @@ hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias
         auto X = (const uint16_t*)x; auto W = (const uint16_t*)w; auto Bi = (const uint16_t*)bias;
         auto Ci = (const uint16_t*)cache_in; auto Y = (uint16_t*)y; auto Co = (uint16_t*)cache_out;
         switch (vec) {
+            case 8:
+                if constexpr (DW1S_BF16_VEC >= 8)
+                    return launch_stream_typed<uint16_t, 8>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
+                return launch_stream_typed<uint16_t, 4>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
             case 4: return launch_stream_typed<uint16_t, 4>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
             case 2: return launch_stream_typed<uint16_t, 2>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);
             default: return launch_stream_typed<uint16_t, 1>(X, W, Bi, lengths, Ci, Y, Co, B, Tc, C, K, st);

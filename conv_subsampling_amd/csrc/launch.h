@@ -34,6 +34,7 @@ hipError_t launch_dwconv1d_fwd(const void* x, const void* w, const void* bias, c
 
 // Streaming 1-D conv (causal over a K-1 frame cache and the chunk).
 bool dwconv1d_stream_fits(int64_t B, int64_t Tc, int64_t C, int64_t K, int elem_bytes, int vec);
+int dwconv1d_stream_max_vec(int64_t K, bool bf16);
 hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias, const int32_t* lengths,
                                   const void* cache_in, void* y, void* cache_out, int64_t B, int64_t Tc, int64_t C,
                                   int64_t K, bool bf16, int vec, hipStream_t stream);
