@@ -136,8 +136,13 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_anyk_kernel(
 #endif
 template <int K>
 constexpr int tile_1d_f32() { return DW1D_TILE > 0 ? DW1D_TILE : (K <= 3 ? 4 : K == 4 ? 6 : K <= 9 ? 8 : 12); }
+#ifndef DW1D_TILE_BF16
+#define DW1D_TILE_BF16 0  // 0: the per-width choice below
+#endif
 template <int K>
-constexpr int tile_1d_bf16() { return DW1D_TILE > 0 ? DW1D_TILE : (K <= 4 ? 8 : 12); }
+constexpr int tile_1d_bf16() {
+    return DW1D_TILE > 0 ? DW1D_TILE : DW1D_TILE_BF16 > 0 ? DW1D_TILE_BF16 : (K <= 4 ? 8 : 12);
+}
 constexpr int kTileAnyK = 8;
 
 // (The tile depends on the storage type and K only, so host and device agree
