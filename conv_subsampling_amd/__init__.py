@@ -193,25 +193,27 @@ def dwconv1d_bwd_workspace_bytes(B, T, C, K) -> int:
 
 def dwconv1d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None, causal: bool = False,
                  need=("dx", "dw", "db")):
-    """Gradients (dx, dw, db) of dwconv1d_fwd given dy [B,T,C] (float32)."""
+    """Gradients (dx, dw, db) of dwconv1d_fwd given dy [B,T,C].  x, w, dy and
+    dx share one storage type (float32 or bfloat16); dw and db are float32."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, C]")
     dev, f32 = x.device, torch.float32
+    st, code = _storage(x)
     B, T, C = x.shape
-    _dev_tensor("x", x, f32, dev)
+    _dev_tensor("x", x, st, dev)
     if w.dim() != 2 or w.shape[1] != C:
         raise ValueError("w must be [K, C]")
-    _dev_tensor("w", w, f32, dev)
+    _dev_tensor("w", w, st, dev)
     K = w.shape[0]
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
-    _dev_tensor("dy", dy, f32, dev, (B, T, C))
+    _dev_tensor("dy", dy, st, dev, (B, T, C))
     if dx is None and "dx" in need:
         dx = torch.empty_like(x)
     if dw is None and "dw" in need:
         dw = torch.empty((K, C), dtype=f32, device=dev)
     if db is None and "db" in need:
         db = torch.empty((C,), dtype=f32, device=dev)
-    _dev_tensor("dx", dx, f32, dev, (B, T, C), allow_none=True)
+    _dev_tensor("dx", dx, st, dev, (B, T, C), allow_none=True)
     _dev_tensor("dw", dw, f32, dev, (K, C), allow_none=True)
     _dev_tensor("db", db, f32, dev, (C,), allow_none=True)
     ws_bytes = 0
@@ -223,7 +225,7 @@ def dwconv1d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None, c
         ws_bytes = workspace.numel()
     _check(_lib.dwconv1d_bwd(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
                              _ptr(workspace), ws_bytes, B, T, C, K,
-                             DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, DW_F32, _stream(dev)))
+                             DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, code, _stream(dev)))
     return dx, dw, db
 
 

@@ -126,7 +126,6 @@ dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, con
     if (K < 1) return fail(DW_ERR_INVALID_ARG, "%s: kernel width K=%lld must be >= 1", fn, (long long)K);
     if (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL) return fail(DW_ERR_INVALID_ARG, "%s: unknown pad mode %d", fn, (int)pad);
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
-    if (dtype != DW_F32) return fail(DW_ERR_UNSUPPORTED, "%s: only float32 storage is implemented", fn);
     if (!dw::dwconv1d_bwd_supported(K))
         return fail(DW_ERR_UNSUPPORTED, "%s: kernel width K=%lld has no backward kernel (3, 4, 5, 7, 9, 15, 31)", fn, (long long)K);
     const bool want_wb = dw_ || db;
@@ -140,12 +139,12 @@ dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, con
         if (!workspace || workspace_bytes < need)
             return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
     }
-    if (!dw::dwconv1d_bwd_fits(B, T, C, K)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
-    const void* ptrs[5] = {x, w, dy, dx, dw_};
-    const int vec = dw::pick_vec(C, 4, ptrs, 5, dw::dwconv1d_bwd_max_vec(K));
-    return from_hip(dw::launch_dwconv1d_bwd((const float*)x, (const float*)w, lengths, (const float*)dy, (float*)dx,
-                                            dw_, db, workspace, B, T, C, K, pad == DW_PAD_CAUSAL, vec,
-                                            (hipStream_t)stream), fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    if (!dw::dwconv1d_bwd_fits(B, T, C, K, es)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    const void* ptrs[4] = {x, w, dy, dx};
+    const int vec = dw::pick_vec(C, es, ptrs, 4, dw::dwconv1d_bwd_max_vec(K));
+    return from_hip(dw::launch_dwconv1d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, T, C, K,
+                                            pad == DW_PAD_CAUSAL, dtype == DW_BF16, vec, (hipStream_t)stream), fn);
 }
 
 dw_status dwsub_fused_fwd_ex(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,

@@ -464,10 +464,10 @@ constexpr int kBwdTile1d = 8;
 #define DW1D_BWD_WGS 256
 #endif
 
-template <int V, int K, bool CAUSAL, int TT>
+template <typename S, int V, int K, bool CAUSAL, int TT>
 __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
-    const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
-    const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
+    const S* __restrict__ x, const S* __restrict__ w, const int32_t* __restrict__ lengths,
+    const S* __restrict__ dy, S* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
     uint32_t n_tb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
     constexpr int pL = CAUSAL ? K - 1 : (K - 1) / 2;
     __shared__ double red[kSubs1b - 1][K + 1][kLanes1b * V];
@@ -478,11 +478,11 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
     const uint32_t cg = cblk * kLanes1b + lane;
     const bool cvalid = cg < CG;
     const int32_t c0 = (int32_t)(cvalid ? cg : 0) * V;
-    const uint32_t row = (uint32_t)C * 4, coff = (uint32_t)c0 * 4;
+    const uint32_t row = (uint32_t)C * sizeof(S), coff = (uint32_t)c0 * sizeof(S);
 
     Vf<V> wk[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
+    for (int k = 0; k < K; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
     double gw[K][V], gb[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
             // masked input frames: dx is zero, and there is nothing to add
             if (dx) {
 #pragma unroll
-                for (int i = 0; i < TT; ++i) Buf<float, V>::store(dxr, (uint32_t)(u0 + i) * row + coff, vzero<V>());
+                for (int i = 0; i < TT; ++i) Buf<S, V>::store(dxr, (uint32_t)(u0 + i) * row + coff, vzero<V>());
             }
             continue;
         }
@@ -512,9 +512,9 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
         Vf<V> gwin[TT + K - 1], xv[TT];
 #pragma unroll
         for (int r = 0; r < TT + K - 1; ++r)
-            gwin[r] = Buf<float, V>::load(gr, (uint32_t)((u0 + pL - (K - 1) + r) * (int32_t)row) + coff);
+            gwin[r] = Buf<S, V>::load(gr, (uint32_t)((u0 + pL - (K - 1) + r) * (int32_t)row) + coff);
 #pragma unroll
-        for (int i = 0; i < TT; ++i) xv[i] = Buf<float, V>::load(xr, (uint32_t)(u0 + i) * row + coff);
+        for (int i = 0; i < TT; ++i) xv[i] = Buf<S, V>::load(xr, (uint32_t)(u0 + i) * row + coff);
 #pragma unroll
         for (int i = 0; i < TT; ++i) {
             Vf<V> d = vzero<V>();
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
                 gb[e] += (double)gwin[i + K - 1 - pL].v[e];
                 d.v[e] = u0 + i < len ? d.v[e] : 0.0f;
             }
-            if (dx) Buf<float, V>::store(dxr, (uint32_t)(u0 + i) * row + coff, d);
+            if (dx) Buf<S, V>::store(dxr, (uint32_t)(u0 + i) * row + coff, d);
         }
     }
 
@@ -579,8 +579,8 @@ bool dwconv1d_bwd_supported(int64_t K) {
 
 int dwconv1d_bwd_max_vec(int64_t K) { return K <= 5 ? 4 : (K <= 15 ? 2 : 1); }
 
-bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K) {
-    if ((T + K + 32) * C * 4 >= ((int64_t)1 << 31)) return false;
+bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
+    if ((T + K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
     return (uint64_t)B * ((T + kBwdTile1d - 1) / kBwdTile1d) < ((uint64_t)1 << 31);
 }
 
@@ -590,37 +590,45 @@ size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
     return (size_t)((P + (ch > 0 ? ch : 1)) * (K + 1) * C * (int64_t)sizeof(double));
 }
 
-template <int V, int K, bool CAUSAL>
-static hipError_t launch_bwd1d_typed(const float* x, const float* w, const int32_t* lengths, const float* dy,
-                                     float* dx, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+template <typename S, int V, int K, bool CAUSAL>
+static hipError_t launch_bwd1d_typed(const S* x, const S* w, const int32_t* lengths, const S* dy, S* dx,
+                                     double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
     const Bwd1dGrid g = bwd1d_grid(B, T);
     const uint32_t CG = (uint32_t)(C / V);
     const uint32_t n_cblk = (CG + kLanes1b - 1) / kLanes1b;
     if (g.G == 0 || (!dx && !partial)) return hipSuccess;
-    hipLaunchKernelGGL((dwconv1d_bwd_kernel<V, K, CAUSAL, kBwdTile1d>), dim3(g.G * n_cblk), dim3(kBlock1d), 0, st, x,
+    hipLaunchKernelGGL((dwconv1d_bwd_kernel<S, V, K, CAUSAL, kBwdTile1d>), dim3(g.G * n_cblk), dim3(kBlock1d), 0, st, x,
                        w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk, g.groups_per_item,
                        g.n_groups);
     return hipGetLastError();
 }
 
-template <int K, bool CAUSAL>
-static hipError_t launch_bwd1d_k(int vec, const float* x, const float* w, const int32_t* lengths, const float* dy,
-                                 float* dx, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+template <typename S, int K, bool CAUSAL>
+static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const int32_t* lengths, const void* dyv,
+                                 void* dxv, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
     constexpr int VMAX = K <= 5 ? 4 : (K <= 15 ? 2 : 1);
-    if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<(VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
-    if (vec >= 2 && VMAX >= 2) return launch_bwd1d_typed<(VMAX >= 2 ? 2 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
-    return launch_bwd1d_typed<1, K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    const S* x = (const S*)xv;
+    const S* w = (const S*)wv;
+    const S* dy = (const S*)dyv;
+    S* dx = (S*)dxv;
+    if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<S, (VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    if (vec >= 2 && VMAX >= 2) return launch_bwd1d_typed<S, (VMAX >= 2 ? 2 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    return launch_bwd1d_typed<S, 1, K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
 }
 
-hipError_t launch_dwconv1d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
                                float* dw, float* db, void* workspace, int64_t B, int64_t T, int64_t C, int64_t K,
-                               bool causal, int vec, hipStream_t st) {
+                               bool causal, bool bf16, int vec, hipStream_t st) {
     double* partial = (dw || db) ? (double*)workspace : nullptr;
     hipError_t e = hipSuccess;
 #define DW1B_CASE(KK)                                                                                        \
     case KK:                                                                                                 \
-        e = causal ? launch_bwd1d_k<KK, true>(vec, x, w, lengths, dy, dx, partial, B, T, C, st)              \
-                   : launch_bwd1d_k<KK, false>(vec, x, w, lengths, dy, dx, partial, B, T, C, st);            \
+        if (bf16)                                                                                            \
+            e = causal ? launch_bwd1d_k<uint16_t, KK, true>(vec, x, w, lengths, dy, dx, partial, B, T, C, st)   \
+                       : launch_bwd1d_k<uint16_t, KK, false>(vec, x, w, lengths, dy, dx, partial, B, T, C, st); \
+        else                                                                                                 \
+            e = causal ? launch_bwd1d_k<float, KK, true>(vec, x, w, lengths, dy, dx, partial, B, T, C, st)      \
+                       : launch_bwd1d_k<float, KK, false>(vec, x, w, lengths, dy, dx, partial, B, T, C, st);    \
         break;
     switch (K) {
         DW1B_CASE(3)

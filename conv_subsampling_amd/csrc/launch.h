@@ -43,11 +43,11 @@ hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias
 // the workspace (fp64 partials) it needs.
 bool dwconv1d_bwd_supported(int64_t K);
 int dwconv1d_bwd_max_vec(int64_t K);
-bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K);
+bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes);
 size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K);
-hipError_t launch_dwconv1d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
                                float* dw, float* db, void* workspace, int64_t B, int64_t T, int64_t C, int64_t K,
-                               bool causal, int vec, hipStream_t stream);
+                               bool causal, bool bf16, int vec, hipStream_t stream);
 
 // Sizes of the front's two stages for pad shift d (0 symmetric, 1 causal).
 struct FrontDims {

@@ -153,9 +153,10 @@ size_t dwconv1d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t K);
  * in a fixed order, so repeated calls give bitwise-identical results.
  *
  * x, dy, dx: [B][T][C]; w: [K][C]; dx, dw ([K][C]) and db ([C], float) may be
- * NULL (not computed).  dtype: DW_F32 only (DW_BF16 returns
- * DW_ERR_UNSUPPORTED).  K must be one of 3, 4, 5, 7, 9, 15, 31, else
- * DW_ERR_UNSUPPORTED.  workspace: at least dwconv1d_bwd_workspace_bytes(...)
+ * NULL (not computed).  dtype DW_F32: x, w, dy, dx are float; DW_BF16: they
+ * are bf16 (dx rounded to nearest even), dw and db stay float, summed in fp64
+ * from the exactly widened values.  K must be one of 3, 4, 5, 7, 9, 15, 31,
+ * else DW_ERR_UNSUPPORTED.  workspace: at least dwconv1d_bwd_workspace_bytes(...)
  * bytes of device memory when dw or db is requested.
  * Errors: DW_ERR_INVALID_ARG for a null x, w or dy that holds elements, a
  * negative size, K < 1, a bad enum, or dx aliasing x or dy;

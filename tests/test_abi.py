@@ -118,7 +118,7 @@ def test_dwconv1d_bwd_validation(lib):
     R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
     args = (32, 1500, 512)
     assert f(P, P, N, Q, R, W, N, W, need, *args, 6, 1, 0, N) == UNSUPPORTED and "K=6" in err(lib)
-    assert f(P, P, N, Q, R, W, N, W, need, *args, 9, 1, 1, N) == UNSUPPORTED and "float32" in err(lib)
+    assert f(P, P, N, Q, R, W, N, W, need, *args, 9, 1, 2, N) == INVALID and "dtype" in err(lib)
     assert f(P, P, N, Q, R, W, N, W, need - 1, *args, 9, 1, 0, N) == WORKSPACE
     assert f(P, P, N, Q, P, W, N, W, need, *args, 9, 1, 0, N) == INVALID and "alias" in err(lib)
     assert f(N, P, N, Q, R, W, N, W, need, *args, 9, 1, 0, N) == INVALID

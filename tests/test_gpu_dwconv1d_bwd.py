@@ -4,7 +4,7 @@ import torch
 
 import datagen
 import oracle
-from gpu_util import TOL_F32, assert_exact_zero, assert_parity, say, time_mask
+from gpu_util import TOL_BF16, TOL_F32, assert_exact_zero, assert_parity, say, time_mask
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
@@ -128,3 +128,48 @@ def test_conv_module_full_size(K):
     c = datagen.conv1d_causal_sweep(K, device=DEV)
     dy = datagen.normal((c["B"], c["T"], c["C"]), 1.0, f"c4/dy/K{K}/C{c['C']}", device=DEV)
     check(c["x"], c["w"], c["lengths"].to(DEV), dy, True, f"full [32,1500,512] K={K}")
+
+
+# ----------------------------------------------------------- bf16 storage -----
+
+BF16_GRID = [(1, 1, 4, 3, False), (3, 7, 3, 4, True), (2, 50, 8, 15, False), (3, 45, 200, 9, True),
+             (2, 64, 128, 31, False), (5, 97, 44, 5, True), (2, 129, 512, 9, True), (2, 17, 256, 3, False)]
+
+
+@pytest.mark.parametrize("B,T,C,K,causal", BF16_GRID)
+def test_bf16_grid(B, T, C, K, causal):
+    x, w, dy, L = make(B, T, C, K)
+    x, w, dy = x.to(torch.bfloat16), w.to(torch.bfloat16), dy.to(torch.bfloat16)
+    say(f"dwconv1d_bwd bf16: B={B} T={T} C={C} K={K} causal={causal}")
+    gx, gw, gb = run(x, w, L, dy, causal)
+    assert gx.dtype == torch.bfloat16 and gw.dtype == torch.float32
+    rx, rw, rb = oracle.dwconv1d_bwd(x, w, L, dy, causal)
+    assert_parity(gx, rx, TOL_BF16, "bf16 dx")
+    assert_parity(gw, rw, TOL_F32, "bf16 dw")      # float outputs, fp64 sums of exact products
+    assert_parity(gb, rb, TOL_F32, "bf16 db")
+    assert_exact_zero(gx, time_mask(L.cpu(), B, T)[:, :, None], "bf16 dx")
+
+
+@pytest.mark.parametrize("K", [5, 9])
+def test_bf16_is_the_fp32_kernel_rounded(K):
+    """Same arithmetic on exactly widened values: dx is the fp32 result rounded
+    to nearest even, dw and db are identical."""
+    x, w, dy, L = make(3, 80, 64, K)
+    x, w, dy = x.to(torch.bfloat16), w.to(torch.bfloat16), dy.to(torch.bfloat16)
+    a = run(x, w, L, dy, True)
+    b = run(x.float(), w.float(), L, dy.float(), True)
+    assert torch.equal(a[0], b[0].to(torch.bfloat16))
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+def test_bf16_conv_module_full_size():
+    c = datagen.conv1d_causal_sweep(9, device=DEV)
+    dy = datagen.normal((c["B"], c["T"], c["C"]), 1.0, "c4/dy/K9/C512", device=DEV).to(torch.bfloat16)
+    x, w = c["x"].to(torch.bfloat16), c["w"].to(torch.bfloat16)
+    L = c["lengths"].to(DEV)
+    say("dwconv1d_bwd bf16 full [32,1500,512] K9")
+    gx, gw, gb = run(x, w, L, dy, True)
+    rx, rw, rb = oracle.dwconv1d_bwd(x, w, L, dy, True)
+    assert_parity(gx, rx, TOL_BF16, "full bf16 dx")
+    assert_parity(gw, rw, TOL_F32, "full bf16 dw")
+    assert_parity(gb, rb, TOL_F32, "full bf16 db")
