@@ -241,3 +241,22 @@ def test_last_error_is_per_thread(lib):
     t.join()
     assert seen["msg"] == ""
     assert "K=0" in err(lib)
+
+
+def test_header_is_c99_and_the_library_links_from_c(tmp_path):
+    """A plain C consumer: gcc -std=c99 -pedantic compiles the header, links
+    libdwconv.so and runs host-side validation calls (no GPU needed)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc is not available")
+    exe = str(tmp_path / "abi_check")
+    src = os.path.join(ROOT, "tests", "c", "abi_check.c")
+    libdir = os.path.dirname(LIB)
+    r = subprocess.run([gcc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        src, "-o", exe, "-L", libdir, "-ldwconv", "-Wl,-rpath," + libdir],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c abi check: ok" in r.stdout, r.stdout + r.stderr
