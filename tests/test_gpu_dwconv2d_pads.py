@@ -146,30 +146,32 @@ def test_empty_time_axis_with_output_rows():
     assert y.shape == (2, 1, 3, 8) and torch.all(y == 0)
 
 
-@pytest.mark.parametrize("bf16", [False, True], ids=["f32", "bf16"])
-def test_causal_stage_full_size(bf16):
-    """The subsampler-stage workload [32,1500,64,256] with causal padding:
-    dw and db over the whole batch, y and dx on a sample of items."""
+@pytest.mark.parametrize("pads,bf16", [(CAUSAL, False), (CAUSAL, True), ((1, 1, 1, 1), True)],
+                         ids=["causal-f32", "causal-bf16", "symmetric-bf16"])
+def test_stage_full_size(pads, bf16):
+    """The subsampler-stage workload [32,1500,64,256] as the bench times it,
+    with causal padding or bf16 storage: dw and db over the whole batch, y
+    and dx on a sample of items."""
     T, F = 1500, 64
-    s = datagen.conv2d_stage(device=DEV, dy_rows_cols=out_rc(T, F, CAUSAL), bf16=bf16)
+    s = datagen.conv2d_stage(device=DEV, dy_rows_cols=out_rc(T, F, pads), bf16=bf16)
     L = s["lengths"].to(DEV)
     tol = TOL_BF16 if bf16 else TOL_F32
-    say(f"dwconv2d_ex full causal bf16={bf16}: fwd")
-    y = lib().dwconv2d_fwd(s["x"], s["w"], s["b"], L, pads=CAUSAL)
-    say(f"dwconv2d_ex full causal bf16={bf16}: bwd")
-    dx, dw, db = lib().dwconv2d_bwd(s["x"], s["w"], L, s["dy"], pads=CAUSAL)
+    say(f"dwconv2d_ex full pads={pads} bf16={bf16}: fwd")
+    y = lib().dwconv2d_fwd(s["x"], s["w"], s["b"], L, pads=pads)
+    say(f"dwconv2d_ex full pads={pads} bf16={bf16}: bwd")
+    dx, dw, db = lib().dwconv2d_bwd(s["x"], s["w"], L, s["dy"], pads=pads)
     sync()
-    assert y.shape == (32, 751, 33, 256)
+    assert y.shape == (32,) + out_rc(T, F, pads) + (256,)
     say("oracle")
-    _, rdw, rdb = oracle.dwconv2d_bwd(s["x"], s["w"], s["lengths"], s["dy"], want=("dw", "db"), pads=CAUSAL)
+    _, rdw, rdb = oracle.dwconv2d_bwd(s["x"], s["w"], s["lengths"], s["dy"], want=("dw", "db"), pads=pads)
     assert_parity(dw, rdw, TOL_F32, "full dw")
     assert_parity(db, rdb, TOL_F32, "full db")
     B = s["x"].shape[0]
     for bi in (0, 17, B - 1):
         xs, dys, Ls = s["x"][bi:bi + 1], s["dy"][bi:bi + 1], s["lengths"][bi:bi + 1]
-        assert_parity(y[bi:bi + 1], oracle.dwconv2d_fwd(xs, s["w"], s["b"], Ls, pads=CAUSAL), tol, f"y item {bi}")
-        rdx, _, _ = oracle.dwconv2d_bwd(xs, s["w"], Ls, dys, want=("dx",), pads=CAUSAL)
+        assert_parity(y[bi:bi + 1], oracle.dwconv2d_fwd(xs, s["w"], s["b"], Ls, pads=pads), tol, f"y item {bi}")
+        rdx, _, _ = oracle.dwconv2d_bwd(xs, s["w"], Ls, dys, want=("dx",), pads=pads)
         assert_parity(dx[bi:bi + 1], rdx, tol, f"dx item {bi}")
     Lc = s["lengths"].clamp(0, T)
     assert_exact_zero(dx, time_mask(Lc, B, T)[:, :, None, None], "full dx masked rows")
-    assert_exact_zero(y, out_mask(Lc, y.shape[1], CAUSAL)[:, :, None, None], "full y masked rows")
+    assert_exact_zero(y, out_mask(Lc, y.shape[1], pads)[:, :, None, None], "full y masked rows")
