@@ -16,9 +16,10 @@
 // that ends at its valid length (rows t >= len read as zero: the pre-mask)
 // and dy through one that ends at len' = floor((len + pt0 + pt1 - 3)/2) + 1
 // (masked gradient rows read as zero), and a negative row offset is out of
-// range as well, which gives the top padding rows.  Only the frequency
-// padding needs an explicit zero, since a column offset past either edge
-// lands in a neighbouring row.
+// range as well, which gives the top padding rows.  The frequency padding
+// needs care: a column offset past either edge would land in a neighbouring
+// row, so such a column is addressed out of range (kOutOfRange below) or, for
+// the backward's dy column, loaded and then selected away.
 //
 // Forward mapping.  A thread owns V channels of TO consecutive output rows of
 // one item and walks left to right over a chunk of the F' output columns.  At
@@ -106,9 +107,10 @@ __device__ __forceinline__ Vf<V> select_v(bool keep, const Vf<V>& a) {
 }
 
 // A column offset past either edge of a row would land in a neighbouring row,
-// so such a column is addressed at this offset instead: added to any row
-// offset the kernels form (below 2^31 - 2 rows, or a row -1 that wrapped),
-// it is at or past every resource's size, and the load returns zero.
+// so such a column is addressed at this offset instead.  Added to any row
+// offset the kernels form (at most T + 2 rows, below 2^31 - 2 rows by
+// dwconv2d_fits, or a row -1 or -2 that wrapped below 2^32), the sum is at or
+// past every resource's size, and the load returns zero.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // Geometry handed to the kernels (all sizes fit in 32 bits: dwconv2d_fits).
