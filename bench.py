@@ -32,7 +32,8 @@ Prints one JSON line on stdout (progress goes to stderr):
   hbm          algorithmic bytes per step / step time, and its fraction of
                the 8 TB/s HBM peak
   roofline     the dominant kernel's achieved algorithmic GB/s against 8 TB/s
-  rows         the same figures for every operation
+  rows         the same figures for every operation (mean time per call, and
+               its median, minimum and 90th percentile over the steps)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 `python bench.py --summarize-profile DIR` turns rocprofv3 output under DIR
@@ -497,9 +498,11 @@ def main():
     alg = sum(r["read"] + r["write"] for r in rows)
     out_rows = []
     for j, r in enumerate(rows):
-        us = sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) * 1e3 / args.steps
+        ts = sorted(ev[s][j][0].elapsed_time(ev[s][j][1]) * 1e3 for s in range(args.steps))
+        us = sum(ts) / len(ts)
         b = r["read"] + r["write"]
-        row = dict(row=r["name"], op=r["op"], config=r["cfg"], us=round(us, 2),
+        row = dict(row=r["name"], op=r["op"], config=r["cfg"], us=round(us, 2), us_median=round(ts[len(ts) // 2], 2),
+                   us_min=round(ts[0], 2), us_p90=round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 2),
                    frames_per_s=round(r["frames"] / (us * 1e-6)), alg_bytes=b,
                    gbps=round(b / (us * 1e-6) / 1e9, 1), hbm_frac=round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
         if r["bound"] == "alu":
