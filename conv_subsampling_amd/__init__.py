@@ -64,11 +64,11 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dwconv1d_bwd.restype = _int
     lib.dwconv1d_bwd.argtypes = [_vp] * 8 + [_sz] + [_i64] * 4 + [_int, _int, _vp]
     lib.dwsub_fused_fwd_ex.restype = _int
-    lib.dwsub_fused_fwd_ex.argtypes = [_vp] * 7 + [_i64] * 4 + [_int, _vp]
+    lib.dwsub_fused_fwd_ex.argtypes = [_vp] * 7 + [_i64] * 4 + [_int, _int, _vp]
     lib.dwsub_fused_bwd_workspace_bytes_ex.restype = _sz
     lib.dwsub_fused_bwd_workspace_bytes_ex.argtypes = [_i64] * 4 + [_int]
     lib.dwsub_fused_bwd_ex.restype = _int
-    lib.dwsub_fused_bwd_ex.argtypes = [_vp] * 11 + [_sz] + [_i64] * 4 + [_int, _vp]
+    lib.dwsub_fused_bwd_ex.argtypes = [_vp] * 11 + [_sz] + [_i64] * 4 + [_int, _int, _vp]
     lib.dwsub_fused_fwd.restype = _int
     lib.dwsub_fused_fwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]
     lib.dwsub_fused_bwd_workspace_bytes.restype = _sz
@@ -238,26 +238,28 @@ def front_out_shape(T, F, causal: bool = False):
 
 
 def dwsub_fused_fwd(x, w0, b0, w1, b1, lengths=None, y=None, causal: bool = False):
-    """Fused subsampler front; x [B,T,F] float32 mel -> y [B,T2,F2,C]."""
+    """Fused subsampler front; x [B,T,F] mel -> y [B,T2,F2,C].  x, the
+    parameters and y share one storage type (float32 or bfloat16)."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, F]")
-    dev, f32 = x.device, torch.float32
+    dev = x.device
+    st, code = _storage(x)
     B, T, F = x.shape
-    _dev_tensor("x", x, f32, dev)
+    _dev_tensor("x", x, st, dev)
     if w0.dim() != 3 or w0.shape[:2] != (3, 3):
         raise ValueError("w0 must be [3, 3, C]")
     C = w0.shape[2]
-    _dev_tensor("w0", w0, f32, dev)
-    _dev_tensor("b0", b0, f32, dev, (C,), allow_none=True)
-    _dev_tensor("w1", w1, f32, dev, (3, 3, C))
-    _dev_tensor("b1", b1, f32, dev, (C,), allow_none=True)
+    _dev_tensor("w0", w0, st, dev)
+    _dev_tensor("b0", b0, st, dev, (C,), allow_none=True)
+    _dev_tensor("w1", w1, st, dev, (3, 3, C))
+    _dev_tensor("b1", b1, st, dev, (C,), allow_none=True)
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
     T2, F2 = front_out_shape(T, F, causal)
     if y is None:
-        y = torch.empty((B, T2, F2, C), dtype=f32, device=dev)
-    _dev_tensor("y", y, f32, dev, (B, T2, F2, C))
+        y = torch.empty((B, T2, F2, C), dtype=st, device=dev)
+    _dev_tensor("y", y, st, dev, (B, T2, F2, C))
     _check(_lib.dwsub_fused_fwd_ex(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(b1), _ptr(lengths), _ptr(y),
-                                   B, T, F, C, DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, _stream(dev)))
+                                   B, T, F, C, DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, code, _stream(dev)))
     return y
 
 
@@ -267,21 +269,24 @@ def dwsub_fused_bwd_workspace_bytes(B, T, F, C, causal: bool = False) -> int:
 
 def dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0=None, db0=None, dw1=None, db1=None, workspace=None,
                     need=("dw0", "db0", "dw1", "db1"), causal: bool = False):
-    """Parameter gradients (dw0, db0, dw1, db1) of dwsub_fused_fwd given dy [B,T2,F2,C]."""
+    """Parameter gradients (dw0, db0, dw1, db1) of dwsub_fused_fwd given dy
+    [B,T2,F2,C].  x, w0, b0, w1 and dy share one storage type; the gradients
+    are float32."""
     if x.dim() != 3:
         raise ValueError("x must be [B, T, F]")
     dev, f32 = x.device, torch.float32
+    st, code = _storage(x)
     B, T, F = x.shape
-    _dev_tensor("x", x, f32, dev)
+    _dev_tensor("x", x, st, dev)
     if w0.dim() != 3 or w0.shape[:2] != (3, 3):
         raise ValueError("w0 must be [3, 3, C]")
     C = w0.shape[2]
-    _dev_tensor("w0", w0, f32, dev)
-    _dev_tensor("b0", b0, f32, dev, (C,), allow_none=True)
-    _dev_tensor("w1", w1, f32, dev, (3, 3, C))
+    _dev_tensor("w0", w0, st, dev)
+    _dev_tensor("b0", b0, st, dev, (C,), allow_none=True)
+    _dev_tensor("w1", w1, st, dev, (3, 3, C))
     _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
     T2, F2 = front_out_shape(T, F, causal)
-    _dev_tensor("dy", dy, f32, dev, (B, T2, F2, C))
+    _dev_tensor("dy", dy, st, dev, (B, T2, F2, C))
     outs = {}
     for name, t, shape in (("dw0", dw0, (3, 3, C)), ("db0", db0, (C,)), ("dw1", dw1, (3, 3, C)), ("db1", db1, (C,))):
         if t is None and name in need:
@@ -294,7 +299,7 @@ def dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0=None, db0=None, dw1=None, db
     _check(_lib.dwsub_fused_bwd_ex(_ptr(x), _ptr(w0), _ptr(b0), _ptr(w1), _ptr(lengths), _ptr(dy),
                                    _ptr(outs["dw0"]), _ptr(outs["db0"]), _ptr(outs["dw1"]), _ptr(outs["db1"]),
                                    _ptr(workspace), workspace.numel(), B, T, F, C,
-                                   DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, _stream(dev)))
+                                   DW_PAD_CAUSAL if causal else DW_PAD_SYMMETRIC, code, _stream(dev)))
     return outs["dw0"], outs["db0"], outs["dw1"], outs["db1"]
 
 

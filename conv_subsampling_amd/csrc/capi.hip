@@ -147,29 +147,31 @@ dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, con
                                             pad == DW_PAD_CAUSAL, dtype == DW_BF16, vec, (hipStream_t)stream), fn);
 }
 
-dw_status dwsub_fused_fwd_ex(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,
-                             const int32_t* lengths, float* y, int64_t B, int64_t T, int64_t F, int64_t C,
-                             dw_pad pad, void* stream) {
+dw_status dwsub_fused_fwd_ex(const void* x, const void* w0, const void* b0, const void* w1, const void* b1,
+                             const int32_t* lengths, void* y, int64_t B, int64_t T, int64_t F, int64_t C,
+                             dw_pad pad, dw_dtype dtype, void* stream) {
     const char* fn = "dwsub_fused_fwd";
     if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
     const dw_status ps = check_pad(fn, pad);
     if (ps != DW_OK) return ps;
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const bool causal = pad == DW_PAD_CAUSAL;
     const dw::FrontDims fd = dw::front_dims(T, F, causal ? 1 : 0);
     if (B == 0 || fd.T2 == 0 || fd.F2 == 0 || C == 0) return ok();
     if ((!x && T * F > 0) || !w0 || !w1 || !y)
         return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and y must not be NULL", fn);
-    if ((const void*)x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
-    if (!dw::dwsub_fused_fwd_fits(B, T, F, C, causal))
+    if (x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    if (!dw::dwsub_fused_fwd_fits(B, T, F, C, causal, es))
         return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
-    return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, causal,
+    return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, causal, dtype == DW_BF16,
                                                (hipStream_t)stream), fn);
 }
 
 dw_status dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1, const float* b1,
                           const int32_t* lengths, float* y, int64_t B, int64_t T, int64_t F, int64_t C,
                           void* stream) {
-    return dwsub_fused_fwd_ex(x, w0, b0, w1, b1, lengths, y, B, T, F, C, DW_PAD_SYMMETRIC, stream);
+    return dwsub_fused_fwd_ex(x, w0, b0, w1, b1, lengths, y, B, T, F, C, DW_PAD_SYMMETRIC, DW_F32, stream);
 }
 
 size_t dwsub_fused_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, dw_pad pad) {
@@ -181,14 +183,15 @@ size_t dwsub_fused_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t 
     return dwsub_fused_bwd_workspace_bytes_ex(B, T, F, C, DW_PAD_SYMMETRIC);
 }
 
-dw_status dwsub_fused_bwd_ex(const float* x, const float* w0, const float* b0, const float* w1,
-                             const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1, float* db1,
-                             void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
-                             dw_pad pad, void* stream) {
+dw_status dwsub_fused_bwd_ex(const void* x, const void* w0, const void* b0, const void* w1, const int32_t* lengths,
+                             const void* dy, float* dw0, float* db0, float* dw1, float* db1, void* workspace,
+                             size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C, dw_pad pad,
+                             dw_dtype dtype, void* stream) {
     const char* fn = "dwsub_fused_bwd";
     if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
     const dw_status ps = check_pad(fn, pad);
     if (ps != DW_OK) return ps;
+    if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const bool causal = pad == DW_PAD_CAUSAL;
     if (!dw0 && !db0 && !dw1 && !db1) return ok();
     if (C == 0) return ok();
@@ -199,10 +202,11 @@ dw_status dwsub_fused_bwd_ex(const float* x, const float* w0, const float* b0, c
     if (!workspace || workspace_bytes < need)
         return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
                     workspace ? workspace_bytes : (size_t)0, need);
-    if (!dw::dwsub_fused_bwd_fits(B, T, F, C, causal))
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    if (!dw::dwsub_fused_bwd_fits(B, T, F, C, causal, es))
         return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
     return from_hip(dw::launch_dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, B, T, F, C,
-                                               causal, (hipStream_t)stream), fn);
+                                               causal, dtype == DW_BF16, (hipStream_t)stream), fn);
 }
 
 dw_status dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
@@ -210,7 +214,7 @@ dw_status dwsub_fused_bwd(const float* x, const float* w0, const float* b0, cons
                           void* workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
                           void* stream) {
     return dwsub_fused_bwd_ex(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, workspace_bytes, B, T, F, C,
-                              DW_PAD_SYMMETRIC, stream);
+                              DW_PAD_SYMMETRIC, DW_F32, stream);
 }
 
 dw_status dwconv2d_fwd_ex(const void* x, const void* w, const void* bias, const int32_t* lengths, void* y,

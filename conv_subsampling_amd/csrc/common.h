@@ -183,6 +183,10 @@ __device__ __forceinline__ Vf<V> load_param(const S* p) {
     return a;
 }
 
+// One stored value (fp32, or bf16 bits) widened exactly to fp32.
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
 template <int V>
 __device__ __forceinline__ Vf<V> vzero() {
     Vf<V> r;

@@ -26,7 +26,9 @@
 // masked stores the output bias without computing.  Only the one h row and
 // column shared with neighbouring tiles is computed twice.
 //
-// Arithmetic is IEEE fp32 FMA throughout, the bias seeding each sum.
+// Storage is fp32 or bf16 (the mel input, the parameters and y alike); bf16
+// values are widened exactly, arithmetic is IEEE fp32 FMA throughout with the
+// bias seeding each sum, and a bf16 y is rounded to nearest even.
 #include <type_traits>
 
 #include "common.h"
@@ -56,10 +58,11 @@ constexpr int kSubCols = DWSUB_COLS;  // output columns per thread
 constexpr int kPatchRows = 4 * kSubRows + 3;
 constexpr int kPatchCols = 4 * kSubCols + 8;
 
+template <typename S>
 __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
-    const float* __restrict__ x, const float* __restrict__ w0, const float* __restrict__ b0,
-    const float* __restrict__ w1, const float* __restrict__ b1, const int32_t* __restrict__ lengths,
-    float* __restrict__ y, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2, int32_t F2,
+    const S* __restrict__ x, const S* __restrict__ w0, const S* __restrict__ b0,
+    const S* __restrict__ w1, const S* __restrict__ b1, const int32_t* __restrict__ lengths,
+    S* __restrict__ y, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2, int32_t F2,
     int32_t d, uint32_t n_rt, uint32_t n_ft, uint32_t n_cblk) {
     __shared__ __align__(16) float patch[kPatchRows][kPatchCols];
 
@@ -77,11 +80,11 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     const int32_t L1 = len > 0 ? (len - 1 + d) / 2 + 1 : 0;
 
     // Stage the zero-padded mel patch.  The input is not length-masked.
-    const float* xb = x + (int64_t)b * T * F;
+    const S* xb = x + (int64_t)b * T * F;
     for (int i = threadIdx.x; i < kPatchRows * kPatchCols; i += kSubBlock) {
         const int r = i / kPatchCols, q = i % kPatchCols;
         const int32_t t = 4 * t0 - 3 - 3 * d + r, f = 4 * f0 - 5 - 3 * d + q;
-        patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? xb[(int64_t)t * F + f] : 0.0f;
+        patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? to_f32(xb[(int64_t)t * F + f]) : 0.0f;
     }
     __syncthreads();
 
@@ -91,11 +94,12 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     float wa[9], wb[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        wa[k] = w0[(int64_t)k * C + c];
-        wb[k] = w1[(int64_t)k * C + c];
+        wa[k] = to_f32(w0[(int64_t)k * C + c]);
+        wb[k] = to_f32(w1[(int64_t)k * C + c]);
     }
-    const float ba = b0 ? b0[c] : 0.0f;
-    const float bb = b1 ? b1[c] : 0.0f;
+    const float ba = b0 ? to_f32(b0[c]) : 0.0f;
+    const float bb = b1 ? to_f32(b1[c]) : 0.0f;
+    constexpr uint32_t es = sizeof(S);
 
     // h rows 2*t0-1-d+l, l = 0..2*TY, read mel patch rows 2l .. 2l+2.
     // h row validity: inside [0, T1) and before the time mask.
@@ -109,16 +113,19 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     }
 
     const int32_t ncols = min(kSubCols, F2 - f0);
-    const uint32_t yrow = (uint32_t)F2 * C * 4;
+    const uint32_t yrow = (uint32_t)F2 * C * es;
     const rsrc_t yr = make_rsrc(y + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * yrow);
+    auto store = [&](uint32_t off, float v) {
+        Vf<1> o;
+        o.v[0] = v;
+        Buf<S, 1>::store(yr, off, o);
+    };
     if (!any_ok) {
         // Every h row this tile reads is masked or padding: y is the bias.
         for (int s = 0; s < ncols; ++s)
 #pragma unroll
             for (int i = 0; i < kSubRows; ++i)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bb), yr,
-                                                      (uint32_t)(t0 + i) * yrow + ((uint32_t)(f0 + s) * C + c) * 4, 0,
-                                                      kNonTemporal);
+                store((uint32_t)(t0 + i) * yrow + ((uint32_t)(f0 + s) * C + c) * es, bb);
         return;
     }
 
@@ -162,8 +169,7 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
                 a = __builtin_fmaf(he[2 * i + r], wb[3 * r + 1], a);
                 a = __builtin_fmaf(ho[2 * i + r], wb[3 * r + 2], a);
             }
-            const uint32_t off = (uint32_t)(t0 + i) * yrow + ((uint32_t)f2 * C + c) * 4;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a), yr, off, 0, kNonTemporal);
+            store((uint32_t)(t0 + i) * yrow + ((uint32_t)f2 * C + c) * es, a);
         }
 #pragma unroll
         for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = ho[l];
@@ -181,19 +187,20 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     if (last_odd_pad && s < ncols) step(s, std::false_type{}, std::true_type{});
 }
 
-bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal) {
+bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes) {
     const FrontDims fd = front_dims(T, F, causal ? 1 : 0);
     const int64_t T2 = fd.T2, F2 = fd.F2;
-    if ((T2 + kSubRows) * F2 * C * 4 >= ((int64_t)1 << 31)) return false;
+    if ((T2 + kSubRows) * F2 * C * elem_bytes >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28)) return false;
     const int64_t blocks = B * ((T2 + kSubRows - 1) / kSubRows) * ((F2 + kSubCols - 1) / kSubCols) *
                            ((C + kSubBlock - 1) / kSubBlock);
     return blocks < ((int64_t)1 << 31);
 }
 
-hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1,
-                                  const float* b1, const int32_t* lengths, float* y,
-                                  int64_t B, int64_t T, int64_t F, int64_t C, bool causal, hipStream_t st) {
+template <typename S>
+static hipError_t launch_front_fwd_typed(const S* x, const S* w0, const S* b0, const S* w1, const S* b1,
+                                         const int32_t* lengths, S* y, int64_t B, int64_t T, int64_t F, int64_t C,
+                                         bool causal, hipStream_t st) {
     const int d = causal ? 1 : 0;
     const FrontDims fd = front_dims(T, F, d);
     const int64_t T1 = fd.T1, F1 = fd.F1, T2 = fd.T2, F2 = fd.F2;
@@ -201,10 +208,21 @@ hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* 
     const uint32_t n_ft = (uint32_t)((F2 + kSubCols - 1) / kSubCols);
     const uint32_t n_cblk = (uint32_t)((C + kSubBlock - 1) / kSubBlock);
     const uint64_t blocks = (uint64_t)B * n_rt * n_ft * n_cblk;
-    hipLaunchKernelGGL(dwsub_fused_fwd_kernel, dim3((uint32_t)blocks), dim3(kSubBlock), 0, st, x, w0, b0, w1, b1,
+    hipLaunchKernelGGL(dwsub_fused_fwd_kernel<S>, dim3((uint32_t)blocks), dim3(kSubBlock), 0, st, x, w0, b0, w1, b1,
                        lengths, y, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1, (int32_t)T2,
                        (int32_t)F2, (int32_t)d, n_rt, n_ft, n_cblk);
     return hipGetLastError();
+}
+
+hipError_t launch_dwsub_fused_fwd(const void* x, const void* w0, const void* b0, const void* w1, const void* b1,
+                                  const int32_t* lengths, void* y, int64_t B, int64_t T, int64_t F, int64_t C,
+                                  bool causal, bool bf16, hipStream_t st) {
+    if (bf16)
+        return launch_front_fwd_typed<uint16_t>((const uint16_t*)x, (const uint16_t*)w0, (const uint16_t*)b0,
+                                                (const uint16_t*)w1, (const uint16_t*)b1, lengths, (uint16_t*)y, B, T,
+                                                F, C, causal, st);
+    return launch_front_fwd_typed<float>((const float*)x, (const float*)w0, (const float*)b0, (const float*)w1,
+                                         (const float*)b1, lengths, (float*)y, B, T, F, C, causal, st);
 }
 
 
@@ -256,9 +274,10 @@ constexpr int kBPatchRows = 4 * kBQR + 1;      // mel rows 4*t0-1-3d .. 4*t0+4*Q
 constexpr int kBPatchCols = 4 * kBQC + 1;      // mel columns 4*f0-1-3d .. 4*f0+4*QC-1-3d
 constexpr int kFrontGrads = 20;                // dw0 (9), db0, dw1 (9), db1
 
+template <typename S>
 __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
-    const float* __restrict__ x, const float* __restrict__ w0, const float* __restrict__ b0,
-    const float* __restrict__ w1, const int32_t* __restrict__ lengths, const float* __restrict__ dy,
+    const S* __restrict__ x, const S* __restrict__ w0, const S* __restrict__ b0,
+    const S* __restrict__ w1, const int32_t* __restrict__ lengths, const S* __restrict__ dy,
     double* __restrict__ partial, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2,
     int32_t F2, int32_t d, uint32_t n_rt, uint32_t n_ft, uint32_t n_tiles, uint32_t n_cblk) {
     __shared__ double patch[kBPatchRows][kBPatchCols];
@@ -271,16 +290,17 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
     double wa[9], wb[9], ba = 0.0;
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        wa[k] = active ? (double)w0[(int64_t)k * C + c] : 0.0;
-        wb[k] = active ? (double)w1[(int64_t)k * C + c] : 0.0;
+        wa[k] = active ? (double)to_f32(w0[(int64_t)k * C + c]) : 0.0;
+        wb[k] = active ? (double)to_f32(w1[(int64_t)k * C + c]) : 0.0;
     }
-    if (active && b0) ba = (double)b0[c];
+    if (active && b0) ba = (double)to_f32(b0[c]);
 
     double gw0[9], gw1[9], gb0 = 0.0, gb1 = 0.0;
 #pragma unroll
     for (int k = 0; k < 9; ++k) gw0[k] = gw1[k] = 0.0;
 
-    const uint32_t grow = (uint32_t)F2 * C * 4;
+    constexpr uint32_t es = sizeof(S);
+    const uint32_t grow = (uint32_t)F2 * C * es;
     for (uint32_t j = g; j < n_tiles; j += G) {
         const uint32_t ft = j % n_ft, rest = j / n_ft;
         const uint32_t rt = rest % n_rt, b = rest / n_rt;
@@ -292,21 +312,20 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
         // (rows past T2 read zero through the buffer; column f0+QC past F2 is
         // zeroed below), so their latency overlaps the patch staging.
         const rsrc_t gr = make_rsrc(dy + (int64_t)b * T2 * F2 * C, (uint32_t)T2 * grow);
-        const uint32_t coff = (uint32_t)(active ? c : 0) * 4;
+        const uint32_t coff = (uint32_t)(active ? c : 0) * es;
         float gt[kBQR + 1][kBQC + 1];
 #pragma unroll
         for (int q = 0; q <= kBQR; ++q)
 #pragma unroll
             for (int e = 0; e <= kBQC; ++e)
-                gt[q][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    gr, (uint32_t)(t0 + q) * grow + (uint32_t)(f0 + e) * C * 4 + coff, 0, 0));
+                gt[q][e] = Buf<S, 1>::load(gr, (uint32_t)(t0 + q) * grow + (uint32_t)(f0 + e) * C * es + coff).v[0];
 
         __syncthreads();  // every thread is done with the previous tile's patch
-        const float* xb = x + (int64_t)b * T * F;
+        const S* xb = x + (int64_t)b * T * F;
         for (int i = threadIdx.x; i < kBPatchRows * kBPatchCols; i += kSubBlock) {
             const int r = i / kBPatchCols, q = i % kBPatchCols;
             const int32_t t = 4 * t0 - 1 - 3 * d + r, f = 4 * f0 - 1 - 3 * d + q;
-            patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? (double)xb[(int64_t)t * F + f] : 0.0;
+            patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? (double)to_f32(xb[(int64_t)t * F + f]) : 0.0;
         }
         __syncthreads();
         if (!active) continue;
@@ -432,10 +451,10 @@ static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F, int d) {
     return g;
 }
 
-bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal) {
+bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes) {
     const FrontDims fd = front_dims(T, F, causal ? 1 : 0);
     const int64_t T2 = fd.T2, F2 = fd.F2;
-    if ((T2 + kBQR + 1) * F2 * C * 4 >= ((int64_t)1 << 31)) return false;
+    if ((T2 + kBQR + 1) * F2 * C * elem_bytes >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28) || C >= ((int64_t)1 << 24)) return false;
     return (uint64_t)B * ((T2 + kBQR - 1) / kBQR) * ((F2 + kBQC - 1) / kBQC) < ((uint64_t)1 << 31);
 }
@@ -446,10 +465,10 @@ size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C, boo
     return (size_t)((P + (ch > 0 ? ch : 1)) * kFrontGrads * C * (int64_t)sizeof(double));
 }
 
-hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
-                                  const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1,
+hipError_t launch_dwsub_fused_bwd(const void* x, const void* w0, const void* b0, const void* w1,
+                                  const int32_t* lengths, const void* dy, float* dw0, float* db0, float* dw1,
                                   float* db1, void* workspace, int64_t B, int64_t T, int64_t F, int64_t C,
-                                  bool causal, hipStream_t st) {
+                                  bool causal, bool bf16, hipStream_t st) {
     const int d = causal ? 1 : 0;
     const FrontDims fd = front_dims(T, F, d);
     const int64_t T1 = fd.T1, F1 = fd.F1, T2 = fd.T2, F2 = fd.F2;
@@ -457,9 +476,17 @@ hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* 
     const uint32_t n_cblk = (uint32_t)((C + kSubBlock - 1) / kSubBlock);
     double* partial = (double*)workspace;
     if (g.G > 0) {
-        hipLaunchKernelGGL(dwsub_fused_bwd_kernel, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st, x, w0, b0, w1,
-                           lengths, dy, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1,
-                           (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
+        if (bf16)
+            hipLaunchKernelGGL(dwsub_fused_bwd_kernel<uint16_t>, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st,
+                               (const uint16_t*)x, (const uint16_t*)w0, (const uint16_t*)b0, (const uint16_t*)w1,
+                               lengths, (const uint16_t*)dy, partial, (int32_t)T, (int32_t)F, (int32_t)C,
+                               (int32_t)T1, (int32_t)F1, (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft,
+                               g.n_tiles, n_cblk);
+        else
+            hipLaunchKernelGGL(dwsub_fused_bwd_kernel<float>, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st,
+                               (const float*)x, (const float*)w0, (const float*)b0, (const float*)w1, lengths,
+                               (const float*)dy, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1,
+                               (int32_t)F1, (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -56,20 +56,20 @@ struct FrontDims {
 FrontDims front_dims(int64_t T, int64_t F, int d);
 
 // The fused front; causal selects its causal padding (2 before, 1 after).
-bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal);
+bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes);
 
-hipError_t launch_dwsub_fused_fwd(const float* x, const float* w0, const float* b0, const float* w1,
-                                  const float* b1, const int32_t* lengths, float* y,
-                                  int64_t B, int64_t T, int64_t F, int64_t C, bool causal, hipStream_t stream);
+hipError_t launch_dwsub_fused_fwd(const void* x, const void* w0, const void* b0, const void* w1, const void* b1,
+                                  const int32_t* lengths, void* y, int64_t B, int64_t T, int64_t F, int64_t C,
+                                  bool causal, bool bf16, hipStream_t stream);
 
-bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal);
+bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes);
 
 size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C, bool causal);
 
-hipError_t launch_dwsub_fused_bwd(const float* x, const float* w0, const float* b0, const float* w1,
-                                  const int32_t* lengths, const float* dy, float* dw0, float* db0, float* dw1,
+hipError_t launch_dwsub_fused_bwd(const void* x, const void* w0, const void* b0, const void* w1,
+                                  const int32_t* lengths, const void* dy, float* dw0, float* db0, float* dw1,
                                   float* db1, void* workspace, int64_t B, int64_t T, int64_t F, int64_t C,
-                                  bool causal, hipStream_t stream);
+                                  bool causal, bool bf16, hipStream_t stream);
 
 // A 3x3, stride-2 depthwise conv2d with pt0 / pt1 zero rows before / after
 // the input in time and pf0 / pf1 columns in frequency, and its output extent.

@@ -23,7 +23,8 @@
  *                    the same with per-side padding (the causal padding of
  *                    the same section) and bf16 storage
  *   dwsub_fused_fwd_ex, dwsub_fused_bwd_ex
- *                    the front with its causal mode (same section)
+ *                    the front with its causal mode (same section) and bf16
+ *                    storage
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, contiguous and channel-last (channel index fastest):
@@ -295,24 +296,28 @@ dw_status dwconv2d_bwd(const float *x, const float *w, const int32_t *lengths, c
  *   h[b,t1,f1,c] = max(0, sum_{i,j} x[b, 2t1+i-1-d, 2f1+j-1-d] w0[i,j,c] + b0[c])
  *                  for t1 < L1_b, else 0
  *   y[b,t2,f2,c] = sum_{i,j} h[b, 2t2+i-1-d, 2f2+j-1-d, c] w1[i,j,c] + b1[c]
- * Arguments, layout and errors as dwsub_fused_fwd; a bad pad is
- * DW_ERR_INVALID_ARG.
+ * dtype DW_F32: x, w0, b0, w1, b1 and y are float.  DW_BF16: they are bf16
+ * (uint16 bit patterns), widened exactly, summed in fp32, y rounded to
+ * nearest even.  Arguments, layout and errors otherwise as dwsub_fused_fwd;
+ * a bad pad or dtype is DW_ERR_INVALID_ARG.
  */
-dw_status dwsub_fused_fwd_ex(const float *x, const float *w0, const float *b0, const float *w1, const float *b1,
-                             const int32_t *lengths, float *y, int64_t B, int64_t T, int64_t F, int64_t C,
-                             dw_pad pad, void *stream);
+dw_status dwsub_fused_fwd_ex(const void *x, const void *w0, const void *b0, const void *w1, const void *b1,
+                             const int32_t *lengths, void *y, int64_t B, int64_t T, int64_t F, int64_t C,
+                             dw_pad pad, dw_dtype dtype, void *stream);
 
 /* Workspace of dwsub_fused_bwd_ex (0 for invalid sizes or pad). */
 size_t dwsub_fused_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, dw_pad pad);
 
 /*
- * dwsub_fused_bwd_ex -- dwsub_fused_bwd for either padding mode of
- * dwsub_fused_fwd_ex (the same gradients with its T2, F2, L1 and indices).
+ * dwsub_fused_bwd_ex -- dwsub_fused_bwd for either padding mode and storage
+ * type of dwsub_fused_fwd_ex (the same gradients with its T2, F2, L1 and
+ * indices).  With DW_BF16, x, w0, b0, w1 and dy are bf16; dw0, db0, dw1, db1
+ * are always float (summed in fp64).
  */
-dw_status dwsub_fused_bwd_ex(const float *x, const float *w0, const float *b0, const float *w1,
-                             const int32_t *lengths, const float *dy, float *dw0, float *db0, float *dw1, float *db1,
+dw_status dwsub_fused_bwd_ex(const void *x, const void *w0, const void *b0, const void *w1,
+                             const int32_t *lengths, const void *dy, float *dw0, float *db0, float *dw1, float *db1,
                              void *workspace, size_t workspace_bytes, int64_t B, int64_t T, int64_t F, int64_t C,
-                             dw_pad pad, void *stream);
+                             dw_pad pad, dw_dtype dtype, void *stream);
 
 /*
  * dwconv2d_fwd_ex -- dwconv2d_fwd with its padding given per axis and side,

@@ -39,8 +39,8 @@ int main(void) {
     expect(dwconv1d_bwd(p, p, NULL, q, r, NULL, NULL, NULL, 0, 32, 1500, 512, 6, DW_PAD_CAUSAL, DW_F32, NULL)
                == DW_ERR_UNSUPPORTED, "1-D bwd width 6");
 
-    expect(dwsub_fused_fwd_ex(p, p, NULL, p, NULL, NULL, q, 4, 1000, 80, 256, (dw_pad)7, NULL) == DW_ERR_INVALID_ARG,
-           "front bad pad");
+    expect(dwsub_fused_fwd_ex(p, p, NULL, p, NULL, NULL, q, 4, 1000, 80, 256, (dw_pad)7, DW_BF16, NULL)
+               == DW_ERR_INVALID_ARG, "front bad pad");
     need = dwsub_fused_bwd_workspace_bytes_ex(4, 1000, 80, 256, DW_PAD_CAUSAL);
     expect(need > 0 && need == dwsub_fused_bwd_workspace_bytes_ex(4, 1000, 80, 256, DW_PAD_CAUSAL), "front ws");
 

@@ -42,10 +42,10 @@ def lib():
     lib.dwsub_fused_bwd_workspace_bytes.argtypes = [i64] * 4
     lib.dwsub_fused_bwd_workspace_bytes.restype = sz
     lib.dwsub_fused_bwd.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [vp]
-    lib.dwsub_fused_fwd_ex.argtypes = [vp] * 7 + [i64] * 4 + [i, vp]
+    lib.dwsub_fused_fwd_ex.argtypes = [vp] * 7 + [i64] * 4 + [i, i, vp]
     lib.dwsub_fused_bwd_workspace_bytes_ex.argtypes = [i64] * 4 + [i]
     lib.dwsub_fused_bwd_workspace_bytes_ex.restype = sz
-    lib.dwsub_fused_bwd_ex.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [i, vp]
+    lib.dwsub_fused_bwd_ex.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [i, i, vp]
     return lib
 
 
@@ -155,18 +155,20 @@ def test_dwsub_fused_bwd_validation(lib):
 
 def test_dwsub_fused_ex_validation(lib):
     f = lib.dwsub_fused_fwd_ex
-    assert f(P, P, N, P, N, N, Q, 4, 100, 80, 256, 2, N) == INVALID and "pad" in err(lib)
-    assert f(P, P, N, P, N, N, P, 4, 100, 80, 256, 1, N) == INVALID and "alias" in err(lib)
-    assert f(P, P, N, P, N, N, Q, 0, 100, 80, 256, 1, N) == OK
+    assert f(P, P, N, P, N, N, Q, 4, 100, 80, 256, 2, 0, N) == INVALID and "pad" in err(lib)
+    assert f(P, P, N, P, N, N, Q, 4, 100, 80, 256, 1, 5, N) == INVALID and "dtype" in err(lib)
+    assert f(P, P, N, P, N, N, P, 4, 100, 80, 256, 1, 1, N) == INVALID and "alias" in err(lib)
+    assert f(P, P, N, P, N, N, Q, 0, 100, 80, 256, 1, 1, N) == OK
     ws = lib.dwsub_fused_bwd_workspace_bytes_ex
     need = ws(4, 1000, 80, 256, 1)
     assert need > 0 and ws(4, 1000, 80, 256, 5) == 0
     assert ws(4, 1000, 80, 256, 0) == lib.dwsub_fused_bwd_workspace_bytes(4, 1000, 80, 256)
     g = lib.dwsub_fused_bwd_ex
     R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
-    assert g(P, P, N, P, N, Q, R, N, N, N, W, need - 1, 4, 1000, 80, 256, 1, N) == WORKSPACE
-    assert g(P, P, N, P, N, Q, R, N, N, N, W, need, 4, 1000, 80, 256, 3, N) == INVALID
-    assert g(P, P, N, P, N, Q, N, N, N, N, N, 0, 4, 1000, 80, 256, 1, N) == OK  # nothing requested
+    assert g(P, P, N, P, N, Q, R, N, N, N, W, need - 1, 4, 1000, 80, 256, 1, 1, N) == WORKSPACE
+    assert g(P, P, N, P, N, Q, R, N, N, N, W, need, 4, 1000, 80, 256, 3, 0, N) == INVALID
+    assert g(P, P, N, P, N, Q, R, N, N, N, W, need, 4, 1000, 80, 256, 1, 4, N) == INVALID and "dtype" in err(lib)
+    assert g(P, P, N, P, N, Q, N, N, N, N, N, 0, 4, 1000, 80, 256, 1, 0, N) == OK  # nothing requested
 
 
 def test_dwconv2d_fwd_validation(lib):

@@ -232,3 +232,58 @@ def test_causal_front_full_size():
                   TOL_F32, "causal front full")
     check_bwd(got, oracle.dwsub_front_bwd(f["x"], f["w0"], f["b0"], f["w1"], f["lengths"], f["dy"], causal=True),
               "causal front bwd full")
+
+
+# ----------------------------------------------------------- bf16 storage -----
+
+def to_bf16(f, keys=("x", "w0", "b0", "w1", "b1", "dy")):
+    return dict(f, **{k: f[k].to(torch.bfloat16) for k in keys if k in f})
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["symmetric", "causal"])
+@pytest.mark.parametrize("B,T,F,C", [(1, 1, 1, 4), (2, 16, 12, 8), (3, 13, 9, 5), (2, 37, 80, 64), (2, 50, 17, 300)])
+def test_bf16_grid_fwd_bwd(B, T, F, C, causal):
+    f = make(B, T, F, C, lens=datagen.int_uniform(B, 0, T + 2, f"gsh/{B}/{T}/{F}/{C}"))
+    T2, F2 = front_dims_oracle(T, F, causal)
+    f["dy"] = datagen.normal((B, T2, F2, C), 1.0, f"gsh/dy/{B}/{T}/{F}/{C}", device=DEV)
+    h = to_bf16(f)
+    say(f"dwsub_fused bf16 causal={causal} B={B} T={T} F={F} C={C}")
+    y = lib().dwsub_fused_fwd(h["x"], h["w0"], h["b0"], h["w1"], h["b1"], h["L"], causal=causal)
+    got = lib().dwsub_fused_bwd(h["x"], h["w0"], h["b0"], h["w1"], h["L"], h["dy"], causal=causal)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.bfloat16 and got[0].dtype == torch.float32
+    ref = oracle.dwsub_front_fwd(h["x"], h["w0"], h["b0"], h["w1"], h["b1"], h["lengths"], causal=causal)
+    assert_parity(y, ref, 2e-2, "bf16 front")
+    check_bwd(got, oracle.dwsub_front_bwd(h["x"], h["w0"], h["b0"], h["w1"], h["lengths"], h["dy"], causal=causal),
+              "bf16 front bwd")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["symmetric", "causal"])
+def test_bf16_is_the_fp32_kernel_rounded(causal):
+    f = make(3, 64, 40, 128, lens=[64, 29, 1])
+    T2, F2 = front_dims_oracle(64, 40, causal)
+    f["dy"] = datagen.normal((3, T2, F2, 128), 1.0, "gsh/dy/bitwise", device=DEV)
+    h = to_bf16(f)
+    w = {k: h[k].float() for k in ("x", "w0", "b0", "w1", "b1", "dy")}
+    y16 = lib().dwsub_fused_fwd(h["x"], h["w0"], h["b0"], h["w1"], h["b1"], h["L"], causal=causal)
+    y32 = lib().dwsub_fused_fwd(w["x"], w["w0"], w["b0"], w["w1"], w["b1"], h["L"], causal=causal)
+    g16 = lib().dwsub_fused_bwd(h["x"], h["w0"], h["b0"], h["w1"], h["L"], h["dy"], causal=causal)
+    g32 = lib().dwsub_fused_bwd(w["x"], w["w0"], w["b0"], w["w1"], h["L"], w["dy"], causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y32.to(torch.bfloat16))
+    for a, b in zip(g16, g32):
+        assert torch.equal(a, b)
+
+
+def test_bf16_front_full_size():
+    f = datagen.fused_front(device=DEV)
+    f["L"] = f["lengths"].to(DEV)
+    f["dy"] = datagen.normal((4, 250, 20, 256), 1.0, "c2/dy", device=DEV)
+    h = to_bf16(f)
+    say("dwsub_fused bf16 full [4,1000,80]")
+    y = lib().dwsub_fused_fwd(h["x"], h["w0"], h["b0"], h["w1"], h["b1"], h["L"])
+    got = lib().dwsub_fused_bwd(h["x"], h["w0"], h["b0"], h["w1"], h["L"], h["dy"])
+    torch.cuda.synchronize()
+    assert_parity(y, oracle.dwsub_front_fwd(h["x"], h["w0"], h["b0"], h["w1"], h["b1"], h["lengths"]), 2e-2,
+                  "bf16 front full")
+    check_bwd(got, oracle.dwsub_front_bwd(h["x"], h["w0"], h["b0"], h["w1"], h["lengths"], h["dy"]), "bf16 bwd full")
