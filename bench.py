@@ -85,10 +85,10 @@ def sources_sha(paths) -> str:
 # name within a step belongs to the k-th row listing it; the profile
 # summaries attribute dispatches to rows that way.
 ROW_KERNELS = [
-    ("front", "dw::dwsub_fused_fwd_kernel("),
-    ("front_bwd", "dw::dwsub_fused_bwd_kernel("),
-    ("front_causal", "dw::dwsub_fused_fwd_kernel("),
-    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel("),
+    ("front", "dw::dwsub_fused_fwd_kernel<float>("),
+    ("front_bwd", "dw::dwsub_fused_bwd_kernel<float>("),
+    ("front_causal", "dw::dwsub_fused_fwd_kernel<float>("),
+    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel<float>("),
     ("conv1d_bf16", "dw::dwconv1d_fwd_kernel<unsigned short, 4, 9, 12>("),
     ("conv1d_causal_K3_C512", "dw::dwconv1d_fwd_kernel<float, 4, 3, 4>("),
     ("conv1d_causal_K4_C512", "dw::dwconv1d_fwd_kernel<float, 4, 4, 6>("),
@@ -97,7 +97,7 @@ ROW_KERNELS = [
     ("conv1d_causal_K15_C512", "dw::dwconv1d_fwd_kernel<float, 4, 15, 12>("),
     ("conv1d_causal_K9_C200", "dw::dwconv1d_fwd_kernel<float, 4, 9, 8>("),
     ("conv1d_stream_bf16", "dw::dwconv1d_stream_kernel<unsigned short, 8, 9, 8>("),
-    ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_kernel<2, 9, true, 8>("),
+    ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_kernel<float, 2, 9, true, 8>("),
     ("stage_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
     ("stage_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
     ("stage_fwd_causal", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),

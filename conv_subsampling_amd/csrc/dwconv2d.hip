@@ -148,6 +148,16 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
     const uint32_t G = gridDim.x / n_cblk;
     const uint32_t g0 = blk0 / n_cblk, cb0 = blk0 - g0 * n_cblk;
     const uint32_t cg = cb0 * LANES + threadIdx.x % LANES;
+    // A thread keeps its channels for the whole kernel: taps and bias are
+    // loaded once.
+    Vf<V> wk[9], bv = vzero<V>();
+#pragma unroll
+    for (int k = 0; k < 9; ++k) wk[k] = vzero<V>();
+    if (cg < CG) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + (int32_t)cg * V);
+        if (bias) bv = load_param<S, V>(bias + (int32_t)cg * V);
+    }
     for (uint32_t j = g0; j < (uint32_t)B_items * groups_per_item; j += G) {
         const uint32_t b = j / groups_per_item;
         const uint32_t rb = (j - b * groups_per_item) * kRB + threadIdx.x / LANES;
@@ -173,11 +183,6 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
                     Buf<S, V>::store(yr, (uint32_t)(t0 + i) * yrow + (uint32_t)(f * pix) + coff, z);
             continue;
         }
-
-        Vf<V> wk[9];
-#pragma unroll
-        for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
-        const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
 
         // Input rows 2t0-1-dt+r, r = 0 .. 2*TO; byte offset of each row start
         // (a negative row wraps out of range and reads zero).
@@ -251,6 +256,15 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
         for (int k = 0; k < 9; ++k) gw[k][e] = 0.0;
     }
 
+    // Taps, loaded once: a thread keeps its channels for the whole kernel.
+    Vf<V> wk[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) wk[k] = vzero<V>();
+    if (cg < CG) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
+    }
+
     for (uint32_t j = g; j < n_groups; j += G) {
         const uint32_t b = j / groups_per_item;
         const uint32_t rb = (j - b * groups_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
@@ -279,9 +293,6 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
             }
             continue;
         }
-        Vf<V> wk[9];
-#pragma unroll
-        for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
         // g rows t0 .. t0+TQ (the last one belongs to the next block), column 0.
         Vf<V> gcur[TQ + 1];
         const uint32_t no0 = Fo > 0 ? 0u : kOutOfRange;
