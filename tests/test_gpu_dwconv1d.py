@@ -57,6 +57,10 @@ GRID = [
     (2, 13, 4, 2, False), (2, 13, 4, 2, True), (1, 33, 100, 9, False), (3, 45, 200, 9, True),
     (2, 17, 256, 3, True), (2, 40, 12, 7, False), (2, 40, 12, 16, True), (1, 100, 1, 9, False),
     (2, 64, 128, 31, False), (3, 49, 6, 9, False), (1, 300, 64, 5, False),
+    # whole 64-lane slabs of 4-channel groups at K = 9, 15 (the LDS-staged fp32 form):
+    # ragged 32-frame tiles, T below the tile and below K, several slabs
+    (3, 70, 256, 9, False), (4, 31, 256, 9, True), (2, 33, 512, 15, True), (1, 5, 256, 15, False),
+    (2, 97, 768, 9, True), (3, 64, 256, 15, False),
 ]
 
 
