@@ -372,11 +372,20 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
             for (int q = 0; q <= TQ; ++q) gcur[q] = gnext[q];
         };
 
-        for (int32_t n = na; n < nb; ++n) {
-            Vf<V> gn[TQ + 1], xe[2 * TQ], xo[2 * TQ];
-            load_col(n, gn, xe, xo);
-            quads(n, gn, xe, xo);
+        // Column n + 1's loads are issued before column n's arithmetic, so a
+        // wave keeps two columns of loads in flight.
+        Vf<V> ga[TQ + 1], xea[2 * TQ], xoa[2 * TQ];
+        load_col(na, ga, xea, xoa);
+        for (int32_t n = na; n + 1 < nb; ++n) {
+            Vf<V> gb2[TQ + 1], xeb[2 * TQ], xob[2 * TQ];
+            load_col(n + 1, gb2, xeb, xob);
+            quads(n, ga, xea, xoa);
+#pragma unroll
+            for (int q = 0; q <= TQ; ++q) ga[q] = gb2[q];
+#pragma unroll
+            for (int r = 0; r < 2 * TQ; ++r) { xea[r] = xeb[r]; xoa[r] = xob[r]; }
         }
+        quads(nb - 1, ga, xea, xoa);
     }
 
     if (!partial) return;  // uniform: dw and db not requested
