@@ -32,6 +32,8 @@ SHAPES = [
     # (B, T, F, C)
     (1, 1, 1, 4), (2, 2, 2, 3), (2, 9, 7, 4), (3, 10, 8, 8), (2, 17, 13, 1), (2, 33, 16, 64),
     (1, 40, 64, 256), (2, 15, 9, 100), (2, 12, 6, 260), (3, 25, 32, 12),
+    # column chunks with a shorter last chunk (31 and 23 quad / output columns)
+    (2, 21, 62, 8), (2, 14, 46, 260),
 ]
 
 

@@ -45,7 +45,7 @@ PADS = [CAUSAL, (2, 1, 1, 1), (1, 1, 2, 1), (1, 0, 1, 0), (2, 2, 2, 2), (1, 2, 2
 SHAPES = [
     # (B, T, F, C)
     (1, 1, 1, 4), (2, 2, 3, 3), (2, 9, 7, 4), (3, 10, 8, 8), (2, 17, 13, 1), (2, 33, 16, 64), (2, 15, 9, 100),
-    (2, 12, 6, 260),
+    (2, 12, 6, 260), (2, 21, 62, 8),
 ]
 
 
@@ -69,7 +69,7 @@ def test_fwd_bwd_grid_pads(B, T, F, C, pads):
 
 @pytest.mark.parametrize("pads", [(1, 1, 1, 1), CAUSAL], ids=["symmetric", "causal"])
 @pytest.mark.parametrize("B,T,F,C", [(1, 1, 1, 4), (2, 9, 7, 4), (3, 10, 8, 8), (2, 17, 13, 2), (2, 33, 16, 64),
-                                     (2, 15, 9, 100), (1, 40, 64, 256)])
+                                     (2, 15, 9, 100), (1, 40, 64, 256), (2, 21, 62, 8), (2, 11, 30, 64)])
 def test_bf16_grid(B, T, F, C, pads):
     s = make(B, T, F, C, pads, bf16=True, lens=datagen.int_uniform(B, 0, T + 2, f"g2h/{B}/{T}/{F}/{C}"))
     say(f"dwconv2d_ex bf16 B={B} T={T} F={F} C={C} pads={pads} lengths={s['lengths'].tolist()}")
@@ -93,7 +93,9 @@ def test_bf16_grid(B, T, F, C, pads):
 def test_bf16_is_the_fp32_kernel_rounded(pads):
     """The bf16 kernels run the fp32 kernels' arithmetic on the exactly
     widened inputs: y and dx are the fp32 results rounded to nearest even,
-    bit for bit, and dw, db (fp64 sums in the same order) are identical."""
+    bit for bit.  dw and db are the same fp64 sums of exact products, added
+    in another order (the bf16 backward takes two quad rows per thread and
+    its own column chunks), so they agree to within one float32 ulp."""
     s = make(3, 30, 20, 64, pads, bf16=True, lens=[30, 17, 4])
     f32 = {k: s[k].float() for k in ("x", "w", "b", "dy")}
     y16 = lib().dwconv2d_fwd(s["x"], s["w"], s["b"], s["L"], pads=pads)
@@ -103,7 +105,10 @@ def test_bf16_is_the_fp32_kernel_rounded(pads):
     sync()
     assert torch.equal(y16, y32.to(torch.bfloat16))
     assert torch.equal(g16[0], g32[0].to(torch.bfloat16))
-    assert torch.equal(g16[1], g32[1]) and torch.equal(g16[2], g32[2])
+    for a, b in ((g16[1], g32[1]), (g16[2], g32[2])):
+        mag = torch.maximum(a.abs(), b.abs())
+        ulp = torch.nextafter(mag, torch.full_like(mag, float("inf"))) - mag
+        assert torch.all((a - b).abs() <= ulp)
 
 
 def test_causal_masked_inputs_never_read_and_repeatable():
