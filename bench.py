@@ -113,31 +113,34 @@ def clamp_lengths(L, T):
     return [min(max(int(v), 0), T) for v in L]
 
 
+# Each work_* function returns (algorithmic read bytes, write bytes, flops,
+# dense read bytes): the last reads every frame, masked or not.
+
 def work_conv1d(c, es):
     B, T, C, K = c["B"], c["T"], c["C"], c["K"]
     L = clamp_lengths(c["lengths"].tolist(), T)
-    rd = sum(L) * C * es + (K * C + C) * es + 4 * B
+    rd = lambda L: sum(L) * C * es + (K * C + C) * es + 4 * B
     wr = B * T * C * es
     flops = 2 * K * C * sum(L)
-    return rd, wr, flops
+    return rd(L), wr, flops, rd([T] * B)
 
 
 def work_conv1d_stream(c, es):
     B, Tc, C, K = c["B"], c["Tc"], c["C"], c["K"]
     L = clamp_lengths(c["lengths"].tolist(), Tc)
-    rd = sum(L) * C * es + B * (K - 1) * C * es + (K + 1) * C * es + 4 * B   # chunk, cache, w, b, lengths
-    wr = B * Tc * C * es + B * (K - 1) * C * es                                # y and the new cache
+    rd = lambda L: sum(L) * C * es + B * (K - 1) * C * es + (K + 1) * C * es + 4 * B  # chunk, cache, w, b, lengths
+    wr = B * Tc * C * es + B * (K - 1) * C * es                                       # y and the new cache
     flops = 2 * K * C * sum(L)
-    return rd, wr, flops
+    return rd(L), wr, flops, rd([Tc] * B)
 
 
 def work_conv1d_bwd(c):
     B, T, C, K = c["B"], c["T"], c["C"], c["K"]
     L = clamp_lengths(c["lengths"].tolist(), T)
-    rd = 2 * sum(L) * C * 4 + K * C * 4 + 4 * B   # x and dy at unmasked frames, w, lengths
-    wr = B * T * C * 4 + (K + 1) * C * 4           # dx (zeros past the length), dw, db
+    rd = lambda L: 2 * sum(L) * C * 4 + K * C * 4 + 4 * B   # x and dy at unmasked frames, w, lengths
+    wr = B * T * C * 4 + (K + 1) * C * 4                     # dx (zeros past the length), dw, db
     flops = 2 * K * C * sum(L) * 2 + C * sum(L)
-    return rd, wr, flops
+    return rd(L), wr, flops, rd([T] * B)
 
 
 def front_half(n, d):
@@ -154,7 +157,7 @@ def work_front(c, d=0):
     rd = rows_read * F * 4 + 20 * C * 4 + 4 * B
     wr = B * T2 * F2 * C * 4
     flops = 2 * 9 * C * F1 * sum(min(l1, T1) for l1 in L1) + 2 * 9 * B * T2 * F2 * C
-    return rd, wr, flops
+    return rd, wr, flops, B * T * F * 4 + 20 * C * 4 + 4 * B
 
 
 def work_front_bwd(c, d=0):
@@ -168,7 +171,7 @@ def work_front_bwd(c, d=0):
     wr = 20 * C * 4
     hpos = sum(L1) * F1 * C                       # unmasked h positions
     flops = hpos * (18 + 18 + 1) + B * T2 * F2 * C * (18 + 18 + 1)
-    return rd, wr, flops
+    return rd, wr, flops, B * T * F * 4 + B * T2 * F2 * C * 4 + 19 * C * 4 + 4 * B
 
 
 def stage_out(n, pl, ph):
@@ -180,10 +183,10 @@ def work_stage_fwd(c, pads=(1, 1, 1, 1), es=4):
     To, Fo = stage_out(T, pads[0], pads[1]), stage_out(F, pads[2], pads[3])
     L = clamp_lengths(c["lengths"].tolist(), T)
     Lo = [min(stage_out(l, pads[0], pads[1]), To) if l > 0 else 0 for l in L]
-    rd = sum(L) * F * C * es + 10 * C * es + 4 * B
+    rd = lambda L: sum(L) * F * C * es + 10 * C * es + 4 * B
     wr = B * To * Fo * C * es
     flops = 2 * 9 * C * Fo * sum(Lo)
-    return rd, wr, flops
+    return rd(L), wr, flops, rd([T] * B)
 
 
 def work_stage_bwd(c, pads=(1, 1, 1, 1), es=4):
@@ -194,7 +197,7 @@ def work_stage_bwd(c, pads=(1, 1, 1, 1), es=4):
     rd = sum(L) * F * C * es + sum(Lo) * Fo * C * es + 9 * C * es + 4 * B
     wr = B * T * F * C * es + 10 * C * 4
     flops = 2 * 2 * 9 * C * Fo * sum(Lo) + C * Fo * sum(Lo)
-    return rd, wr, flops
+    return rd, wr, flops, B * T * F * C * es + B * To * Fo * C * es + 9 * C * es + 4 * B
 
 
 # --------------------------------------------------------------------------
@@ -207,9 +210,9 @@ def build_rows(dev):
 
     rows = []
 
-    def add(name, op, cfg, frames, rd, wr, flops, fn, bound="hbm"):
-        rows.append(dict(name=name, op=op, cfg=cfg, frames=frames, read=rd, write=wr, flops=flops, fn=fn,
-                         bound=bound))
+    def add(name, op, cfg, frames, rd, wr, flops, rd_dense, fn, bound="hbm"):
+        rows.append(dict(name=name, op=op, cfg=cfg, frames=frames, read=rd, write=wr, flops=flops,
+                         read_dense=rd_dense, fn=fn, bound=bound))
 
     f = datagen.fused_front(device=dev)
     fL = f["lengths"].to(dev)
@@ -504,7 +507,9 @@ def main():
         row = dict(row=r["name"], op=r["op"], config=r["cfg"], us=round(us, 2), us_median=round(ts[len(ts) // 2], 2),
                    us_min=round(ts[0], 2), us_p90=round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 2),
                    frames_per_s=round(r["frames"] / (us * 1e-6)), alg_bytes=b,
-                   gbps=round(b / (us * 1e-6) / 1e9, 1), hbm_frac=round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4))
+                   gbps=round(b / (us * 1e-6) / 1e9, 1), hbm_frac=round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                   dense_bytes=r["read_dense"] + r["write"],
+                   dense_gbps=round((r["read_dense"] + r["write"]) / (us * 1e-6) / 1e9, 1))
         if r["bound"] == "alu":
             tf = r["flops"] / (us * 1e-6) / 1e12
             row.update(bound="alu", alg_flops=r["flops"], tflops=round(tf, 2),
