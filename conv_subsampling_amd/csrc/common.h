@@ -86,17 +86,19 @@ struct Buf;
 template <int V>
 struct Buf<float, V> {
     static_assert(V == 1 || V == 2 || V == 4, "float vectors are 4, 8 or 16 bytes");
+    // P: the cache policy bits of the load (the streamed operands' default).
+    template <int P = kLoadPolicy>
     static __device__ __forceinline__ Vf<V> load(rsrc_t r, uint32_t off) {
         Vf<V> a;
         if constexpr (V == 4) {
-            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
+            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, P);
             a.v[0] = __uint_as_float(t.x); a.v[1] = __uint_as_float(t.y);
             a.v[2] = __uint_as_float(t.z); a.v[3] = __uint_as_float(t.w);
         } else if constexpr (V == 2) {
-            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
+            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, P);
             a.v[0] = __uint_as_float(t.x); a.v[1] = __uint_as_float(t.y);
         } else {
-            a.v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy));
+            a.v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, P));
         }
         return a;
     }
@@ -117,20 +119,22 @@ struct Buf<float, V> {
 template <int V>
 struct Buf<uint16_t, V> {
     static_assert(V == 1 || V == 2 || V == 4 || V == 8, "bf16 vectors are 2 to 16 bytes");
+    // P: the cache policy bits of the load (the streamed operands' default).
+    template <int P = kLoadPolicy>
     static __device__ __forceinline__ Vf<V> load(rsrc_t r, uint32_t off) {
         Vf<V> a;
         if constexpr (V == 8) {
-            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kLoadPolicy);
+            u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, P);
             a.v[0] = bf16_lo(t.x); a.v[1] = bf16_hi(t.x); a.v[2] = bf16_lo(t.y); a.v[3] = bf16_hi(t.y);
             a.v[4] = bf16_lo(t.z); a.v[5] = bf16_hi(t.z); a.v[6] = bf16_lo(t.w); a.v[7] = bf16_hi(t.w);
         } else if constexpr (V == 4) {
-            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kLoadPolicy);
+            u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, P);
             a.v[0] = bf16_lo(t.x); a.v[1] = bf16_hi(t.x); a.v[2] = bf16_lo(t.y); a.v[3] = bf16_hi(t.y);
         } else if constexpr (V == 2) {
-            uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kLoadPolicy);
+            uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, P);
             a.v[0] = bf16_lo(t); a.v[1] = bf16_hi(t);
         } else {
-            a.v[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kLoadPolicy) << 16);
+            a.v[0] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, P) << 16);
         }
         return a;
     }

@@ -569,6 +569,13 @@ constexpr int kBwdTile1d = 8;
 #ifndef DW1D_BWD_WGS
 #define DW1D_BWD_WGS 256
 #endif
+#ifndef DW1D_BWD_XPOL
+#define DW1D_BWD_XPOL 2
+#endif
+// Cache policy of the backward's x loads: each x frame is read by one tile
+// only, so non-temporally (2); the dy frames, which neighbouring tiles share,
+// keep the default.
+constexpr int kBwdXPolicy1d = DW1D_BWD_XPOL;
 
 template <typename S, int V, int K, bool CAUSAL, int TT>
 __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
@@ -620,7 +627,7 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
         for (int r = 0; r < TT + K - 1; ++r)
             gwin[r] = Buf<S, V>::load(gr, (uint32_t)((u0 + pL - (K - 1) + r) * (int32_t)row) + coff);
 #pragma unroll
-        for (int i = 0; i < TT; ++i) xv[i] = Buf<S, V>::load(xr, (uint32_t)(u0 + i) * row + coff);
+        for (int i = 0; i < TT; ++i) xv[i] = Buf<S, V>::template load<kBwdXPolicy1d>(xr, (uint32_t)(u0 + i) * row + coff);
 #pragma unroll
         for (int i = 0; i < TT; ++i) {
             Vf<V> d = vzero<V>();

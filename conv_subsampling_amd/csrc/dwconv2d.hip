@@ -67,6 +67,19 @@ constexpr int kRowsPerBlock = kBlock2d / kLanes2d;  // row blocks per workgroup
 #ifndef DW2D_FWD_PERSIST
 #define DW2D_FWD_PERSIST 512  // workgroups of the persistent forward grid
 #endif
+#ifndef DW2D_BWD_XPOL
+#define DW2D_BWD_XPOL 2
+#endif
+// Cache policy of the backward's x loads: every x element is read by exactly
+// one quad, so they are loaded non-temporally (2) and leave the cache to the
+// g rows that neighbouring quad rows share.
+constexpr int kBwdXPolicy = DW2D_BWD_XPOL;
+#ifndef DW2D_FWD_MIDPOL
+#define DW2D_FWD_MIDPOL 2
+#endif
+// Cache policy of the forward's loads of input rows 2t', which no other
+// output row reads: non-temporal (2), leaving the cache to the shared rows.
+constexpr int kFwdMidPolicy = DW2D_FWD_MIDPOL;
 #ifndef DW2D_BWD_ROWS
 #define DW2D_BWD_ROWS 1
 #endif
@@ -203,8 +216,15 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
             Vf<V> xe[2 * TO + 1], xo[2 * TO + 1];
 #pragma unroll
             for (int r = 0; r < 2 * TO + 1; ++r) {
-                xe[r] = Buf<S, V>::load(xr, roff[r] + eo);
-                xo[r] = Buf<S, V>::load(xr, roff[r] + oo);
+                // rows 2t' (odd r) are read by this row block alone; the even
+                // r are shared with a neighbouring output row
+                if (r % 2 == 1 && kFwdMidPolicy != kLoadPolicy) {
+                    xe[r] = Buf<S, V>::template load<kFwdMidPolicy>(xr, roff[r] + eo);
+                    xo[r] = Buf<S, V>::template load<kFwdMidPolicy>(xr, roff[r] + oo);
+                } else {
+                    xe[r] = Buf<S, V>::load(xr, roff[r] + eo);
+                    xo[r] = Buf<S, V>::load(xr, roff[r] + oo);
+                }
             }
 #pragma unroll
             for (int i = 0; i < TO; ++i) {
@@ -317,8 +337,8 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
 #pragma unroll
             for (int r = 0; r < 2 * TQ; ++r) {
                 const uint32_t ro = (uint32_t)((xr0 + r) * (int32_t)xrow) + coff;
-                xe[r] = Buf<S, V>::load(xr, ro + eo);
-                xo[r] = Buf<S, V>::load(xr, ro + oo);
+                xe[r] = Buf<S, V>::template load<kBwdXPolicy>(xr, ro + eo);
+                xo[r] = Buf<S, V>::template load<kBwdXPolicy>(xr, ro + oo);
             }
         };
         // The quads of column n, given its loads; g column n+1 becomes the
