@@ -114,8 +114,12 @@ def test_guard_bands_untouched():
     assert_parity(y, oracle.dwconv1d_fwd(x, w, b, lengths, True), TOL_F32, "guard")
 
 
-def test_unaligned_pointers_take_the_narrow_path():
-    B, T, C, K = 2, 40, 16, 9
+@pytest.mark.parametrize("C,K", [(16, 9), (256, 9), (512, 15), (128, 5)])
+def test_unaligned_pointers_take_the_narrow_path(C, K):
+    """A pointer off 16-byte alignment gets one-channel lanes; at C = 256 and
+    512 those still fill whole 64-lane slabs, so K = 9 and 15 run the
+    LDS-staged form with one channel per lane."""
+    B, T = 2, 40
     x, w, b, lengths = make(B, T, C, K)
     xs = torch.empty(x.numel() + 1, device=DEV)[1:].view(B, T, C)
     xs.copy_(x)
