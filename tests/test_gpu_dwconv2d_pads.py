@@ -180,3 +180,32 @@ def test_stage_full_size(pads, bf16):
     Lc = s["lengths"].clamp(0, T)
     assert_exact_zero(dx, time_mask(Lc, B, T)[:, :, None, None], "full dx masked rows")
     assert_exact_zero(y, out_mask(Lc, y.shape[1], pads)[:, :, None, None], "full y masked rows")
+
+
+def _shifted(t):
+    """A copy of t whose storage starts one element past an aligned address."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    out = buf[1:].view(t.shape)
+    out.copy_(t)
+    return out
+
+
+@pytest.mark.parametrize("bf16", [False, True], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("pads", [(1, 1, 1, 1), CAUSAL], ids=["symmetric", "causal"])
+def test_unaligned_pointers_take_the_narrow_path(pads, bf16):
+    """Tensors that start off 16-byte alignment get one-channel lanes, with the
+    same results; no alignment is ever rejected."""
+    B, T, F, C = 2, 21, 18, 64
+    s = make(B, T, F, C, pads, bf16=bf16, lens=[21, 9])
+    say(f"dwconv2d unaligned pads={pads} bf16={bf16}")
+    x, dy = _shifted(s["x"]), _shifted(s["dy"])
+    To, Fo = out_rc(T, F, pads)
+    y = _shifted(torch.zeros((B, To, Fo, C), dtype=x.dtype, device=DEV))
+    dx = _shifted(torch.zeros_like(s["x"]))
+    lib().dwconv2d_fwd(x, s["w"], s["b"], s["L"], y=y, pads=pads)
+    lib().dwconv2d_bwd(x, s["w"], s["L"], dy, dx=dx, pads=pads)
+    sync()
+    tol = TOL_BF16 if bf16 else TOL_F32
+    assert_parity(y, oracle.dwconv2d_fwd(s["x"], s["w"], s["b"], s["L"], pads=pads), tol, "unaligned fwd")
+    rdx, _, _ = oracle.dwconv2d_bwd(s["x"], s["w"], s["L"], s["dy"], pads=pads)
+    assert_parity(dx, rdx, tol, "unaligned dx")
