@@ -120,3 +120,26 @@ def test_stream_workload_full():
     L = s["lengths"].to(DEV)
     say("dwconv1d_stream full [1024,8,1024] K9 bf16")
     check(s["x"], s["w"], s["b"], s["cache"], L, "stream workload")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_unaligned_pointers_take_the_narrow_path(dtype):
+    """Chunk, cache and output tensors that start one element past an aligned
+    address get one-channel lanes, with the same results."""
+    x, w, b, cache, L = make(3, 8, 1024, 9, dtype, lens=[8, 3, 0])
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        out = buf[1:].view(t.shape)
+        out.copy_(t)
+        return out
+
+    xs, cs = shifted(x), shifted(cache)
+    y = shifted(torch.zeros_like(x))
+    c2 = shifted(torch.zeros_like(cache))
+    say(f"dwconv1d_stream unaligned dtype={dtype}")
+    lib().dwconv1d_stream_fwd(xs, w, b, L, cs, cache_out=c2, y=y)
+    torch.cuda.synchronize()
+    ry, rc = oracle.dwconv1d_stream_fwd(x, w, b, L, cache)
+    assert_parity(y, ry, TOL_BF16 if dtype == torch.bfloat16 else TOL_F32, "unaligned")
+    assert np.array_equal(c2.float().cpu().numpy().astype(np.float64), rc), "unaligned: cache differs"
