@@ -413,7 +413,13 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_stream_kernel(
     const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
     if constexpr (K > 0) {
         Vf<V> win[TT + K - 1];
-        if (t0 < K - 1) {
+        if (t0 == 0) {
+            // the first tile: window frames 0 .. K-2 are the cache, the rest the chunk
+#pragma unroll
+            for (int r = 0; r < TT + K - 1; ++r)
+                win[r] = r < K - 1 ? Buf<S, V>::load(cr, (uint32_t)r * row + coff)
+                                   : Buf<S, V>::load(xr, (uint32_t)(r - (K - 1)) * row + coff);
+        } else if (t0 < K - 1) {
 #pragma unroll
             for (int r = 0; r < TT + K - 1; ++r) win[r] = stream_frame<S, V>(xr, cr, t0 + r, K - 1, row, coff);
         } else {
