@@ -99,13 +99,13 @@ ROW_KERNELS = [
     ("conv1d_stream_bf16", "dw::dwconv1d_stream_kernel<unsigned short, 8, 9, 8>("),
     ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_kernel<float, 2, 9, true, 8>("),
     ("stage_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
-    ("stage_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
+    ("stage_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1, 0, 0>("),
     ("stage_fwd_causal", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
-    ("stage_bwd_causal", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
+    ("stage_bwd_causal", "dw::dwconv2d_bwd_kernel<float, 4, 1, 1, 1>("),
     ("stage_fwd_bf16", "dw::dwconv2d_fwd_kernel<unsigned short, 8, 1, 32>("),
-    ("stage_bwd_bf16", "dw::dwconv2d_bwd_kernel<unsigned short, 4, 2>("),
+    ("stage_bwd_bf16", "dw::dwconv2d_bwd_kernel<unsigned short, 4, 2, 0, 0>("),
     ("stage3_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
-    ("stage3_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1>("),
+    ("stage3_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1, 0, 0>("),
 ]
 
 

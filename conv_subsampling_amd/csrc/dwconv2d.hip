@@ -29,22 +29,28 @@
 // block comes from L2.
 //
 // Backward mapping.  dx is gathered, not scattered: output-parity phases.
-// With x rows 2m-dt, 2m+1-dt and columns 2n-df, 2n+1-df as one "quad" (m, n),
-// and writing t' = m, f' = n:
+// Take x rows 2m, 2m+1 and columns 2n, 2n+1 as one "quad" (m, n).  Along an
+// axis with one zero before it, output o reads inputs 2o-1 .. 2o+1, so input
+// 2n meets tap 1 of output n, and input 2n+1 taps 2 of output n and 0 of
+// output n+1; with two zeros before it (the causal padding), output o reads
+// 2o-2 .. 2o, so input 2n meets tap 2 of output n and tap 0 of output n+1,
+// and input 2n+1 tap 1 of output n+1 (AxisTerms below).  With one zero
+// before both axes, writing t' = m, f' = n:
 //   dx[2t',  2f'  ] = g[t',f'] w11
 //   dx[2t',  2f'+1] = g[t',f'] w12 + g[t',f'+1] w10
 //   dx[2t'+1,2f'  ] = g[t',f'] w21 + g[t'+1,f'] w01
 //   dx[2t'+1,2f'+1] = g[t',f'] w22 + g[t',f'+1] w20 + g[t'+1,f'] w02 + g[t'+1,f'+1] w00
-// and the same (g, x) pairs give the weight gradient: each pair above adds
+// and the same (g, x) pairs give the weight gradient: each pair adds
 // g * x(quad element) to the tap it multiplies.  Every (input, output) pair
 // of the convolution belongs to exactly one quad, so dw is complete and no
-// pair is counted twice; db adds g[t',f'] once per quad.  (The top pad only
-// shifts which x rows a quad holds: x row t is hit by the taps i with
-// t = 2t' + i - pt0, one tap when t + dt is even and two when it is odd.)
-// The quad grid spans max(ceil((T+dt)/2), T') rows and max(ceil((F+df)/2), F')
-// columns, so it covers every x element and every g element.  A thread walks a
-// chunk of the quad columns of one row block left to right, carrying the g
-// column f'+1 (a chunk starts by loading its first g column).  dw and db
+// pair is counted twice; db adds g[t',f'] once per quad.  The quad grid
+// spans max(ceil(T/2), T') rows, and max(ceil(F/2), F') columns with one
+// zero before the columns, so every g element is some quad's g[t',f'].  With
+// two zeros before the columns F' can be ceil(F/2) + 1; the grid then keeps
+// max(ceil(F/2), F'-1) columns, so that a row splits into equal chunks, and
+// the last g column is added to db by the chunk that ends the row.  A thread
+// walks a chunk of the quad columns of one row block left to right, carrying
+// the g column f'+1 (a chunk starts by loading its first g column).  dw and db
 // are accumulated in fp64 from the start (an fp32 x fp32 product is exact in
 // fp64, and fp64 FMA runs at the fp32 rate here), because a sum of ~10^6
 // terms can cancel to a value far smaller than its terms.  They are summed
@@ -246,7 +252,22 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_fwd_kernel(
 
 // ------------------------------------------------------------------ bwd ----
 
-template <typename S, int V, int TQ>
+// The terms of one axis of the backward's gather.  Input positions 2n and
+// 2n+1 form a pair; with padding P+1 before the axis (P = 0 or 1), output o
+// reads inputs 2o-1-P .. 2o+1-P through taps 0, 1, 2, so the outputs and taps
+// reaching the pair are, as (output - n, tap):
+//   P = 0:  2n <- (0, 1);           2n+1 <- (0, 2), (1, 0)
+//   P = 1:  2n <- (0, 2), (1, 0);   2n+1 <- (1, 1)
+template <int P>
+struct AxisTerms {
+    static constexpr int count(int e) { return (P == 0) == (e == 0) ? 1 : 2; }
+    static constexpr int off(int e, int a) { return P == 0 ? (e == 0 ? 0 : a) : (e == 0 ? a : 1); }
+    static constexpr int tap(int e, int a) {
+        return P == 0 ? (e == 0 ? 1 : (a == 0 ? 2 : 0)) : (e == 0 ? (a == 0 ? 2 : 0) : 1);
+    }
+};
+
+template <typename S, int V, int TQ, int PR, int PC>
 __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     const S* __restrict__ x, const S* __restrict__ w, const int32_t* __restrict__ lengths,
     const S* __restrict__ dy, S* __restrict__ dx, double* __restrict__ partial, Geo2d geo,
@@ -298,7 +319,7 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
         const rsrc_t dxr = make_rsrc(dx ? dx + xitem : x, dx ? (uint32_t)T * xrow : 0u);
         const uint32_t coff = (uint32_t)(c0 * es);
         const int32_t t0 = (int32_t)(rb / geo.nqc) * TQ;  // first quad row
-        const int32_t xr0 = 2 * t0 - geo.dt;              // its first x row
+        const int32_t xr0 = 2 * t0;                        // its first x row
         const int32_t na = (int32_t)(rb % geo.nqc) * geo.qcols;  // quad columns na .. nb-1
         const int32_t nb = min(geo.NQf, na + geo.qcols);
 
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
             // adds to db: dx is zero and nothing adds to dw or db.
             if (dx) {
                 const Vf<V> z = vzero<V>();
-                const int32_t fa = max(0, 2 * na - geo.df), fb = min(F, 2 * nb - geo.df);
+                const int32_t fa = 2 * na, fb = min(F, 2 * nb);
                 for (int32_t f = fa; f < fb; ++f)
 #pragma unroll
                     for (int r = 0; r < 2 * TQ; ++r)
@@ -321,18 +342,18 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
 #pragma unroll
         for (int q = 0; q <= TQ; ++q) gcur[q] = Buf<S, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow) + coff + no0);
 
-        // Loads for quad column n: g column n+1, and x columns 2n-df and
-        // 2n-df+1, each replaced by an out-of-range offset (which reads zero
-        // with no memory traffic) where it does not exist.
+        // Loads for quad column n: g column n+1, and x columns 2n and 2n+1,
+        // each replaced by an out-of-range offset (which reads zero with no
+        // memory traffic) where it does not exist.
         auto load_col = [&](int32_t n, Vf<V>(&gn)[TQ + 1], Vf<V>(&xe)[2 * TQ], Vf<V>(&xo)[2 * TQ]) {
-            const int32_t ce = 2 * n - geo.df;
+            const int32_t ce = 2 * n;
             // g column n+1 (past the last column it is loaded from the next
             // row, or read as zero past the valid rows, and then discarded)
 #pragma unroll
             for (int q = 0; q <= TQ; ++q)
                 gn[q] = select_v<V>(n + 1 < Fo,
                                     Buf<S, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow + (n + 1) * pix) + coff));
-            const uint32_t eo = ce >= 0 && ce < F ? (uint32_t)(ce * pix) : kOutOfRange;
+            const uint32_t eo = ce < F ? (uint32_t)(ce * pix) : kOutOfRange;
             const uint32_t oo = ce + 1 < F ? (uint32_t)((ce + 1) * pix) : kOutOfRange;
 #pragma unroll
             for (int r = 0; r < 2 * TQ; ++r) {
@@ -342,50 +363,59 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
             }
         };
         // The quads of column n, given its loads; g column n+1 becomes the
-        // current column afterwards.
+        // current column afterwards.  Each pair of x rows and each pair of x
+        // columns takes its terms from AxisTerms; db adds g[m][n] once per
+        // quad (and the g column past the last quad after the walk).
         auto quads = [&](int32_t n, const Vf<V>(&gnext)[TQ + 1], const Vf<V>(&xe)[2 * TQ],
                          const Vf<V>(&xo)[2 * TQ]) {
-            const int32_t ce = 2 * n - geo.df;
-            const bool ce_ok = ce >= 0 && ce < F, co_ok = ce + 1 < F;
+            using R = AxisTerms<PR>;
+            using Cc = AxisTerms<PC>;
+            const int32_t ce = 2 * n;
+            const bool col_ok[2] = {ce < F, ce + 1 < F};
 #pragma unroll
             for (int q = 0; q < TQ; ++q) {
-                const Vf<V>& g00 = gcur[q];       // g[t', f']
-                const Vf<V>& g01 = gnext[q];      // g[t', f'+1]
-                const Vf<V>& g10 = gcur[q + 1];   // g[t'+1, f']
-                const Vf<V>& g11 = gnext[q + 1];  // g[t'+1, f'+1]
-                const Vf<V>& x00 = xe[2 * q];
-                const Vf<V>& x01 = xo[2 * q];
-                const Vf<V>& x10 = xe[2 * q + 1];
-                const Vf<V>& x11 = xo[2 * q + 1];
-                // tap index k = 3*i + j of w[i][j]
-                Vf<V> d00 = vzero<V>(), d01 = vzero<V>(), d10 = vzero<V>(), d11 = vzero<V>();
-                fma_v<V>(d00, g00, wk[4]);
-                fma_v<V>(d01, g00, wk[5]); fma_v<V>(d01, g01, wk[3]);
-                fma_v<V>(d10, g00, wk[7]); fma_v<V>(d10, g10, wk[1]);
-                fma_v<V>(d11, g00, wk[8]); fma_v<V>(d11, g01, wk[6]);
-                fma_v<V>(d11, g10, wk[2]); fma_v<V>(d11, g11, wk[0]);
-                fma_d<V>(gw[4], g00, x00);
-                fma_d<V>(gw[5], g00, x01); fma_d<V>(gw[3], g01, x01);
-                fma_d<V>(gw[7], g00, x10); fma_d<V>(gw[1], g10, x10);
-                fma_d<V>(gw[8], g00, x11); fma_d<V>(gw[6], g01, x11);
-                fma_d<V>(gw[2], g10, x11); fma_d<V>(gw[0], g11, x11);
+                const Vf<V> G[2][2] = {{gcur[q], gnext[q]}, {gcur[q + 1], gnext[q + 1]}};  // g[m+i][n+j]
+                const Vf<V> X[2][2] = {{xe[2 * q], xo[2 * q]}, {xe[2 * q + 1], xo[2 * q + 1]}};
+                // dx of the four x elements, then the (g, x) pairs for dw
+                Vf<V> D[2][2];
 #pragma unroll
-                for (int e = 0; e < V; ++e) gb[e] += (double)g00.v[e];
+                for (int er = 0; er < 2; ++er)
+#pragma unroll
+                    for (int ec = 0; ec < 2; ++ec) {
+                        D[er][ec] = vzero<V>();
+#pragma unroll
+                        for (int a = 0; a < 2; ++a)
+#pragma unroll
+                            for (int bb = 0; bb < 2; ++bb)
+                                if (a < R::count(er) && bb < Cc::count(ec))  // w[i][j] is tap 3i+j
+                                    fma_v<V>(D[er][ec], G[R::off(er, a)][Cc::off(ec, bb)],
+                                             wk[3 * R::tap(er, a) + Cc::tap(ec, bb)]);
+                    }
+#pragma unroll
+                for (int er = 0; er < 2; ++er)
+#pragma unroll
+                    for (int ec = 0; ec < 2; ++ec)
+#pragma unroll
+                        for (int a = 0; a < 2; ++a)
+#pragma unroll
+                            for (int bb = 0; bb < 2; ++bb)
+                                if (a < R::count(er) && bb < Cc::count(ec))
+                                    fma_d<V>(gw[3 * R::tap(er, a) + Cc::tap(ec, bb)],
+                                             G[R::off(er, a)][Cc::off(ec, bb)], X[er][ec]);
+#pragma unroll
+                for (int e = 0; e < V; ++e) gb[e] += (double)G[0][0].v[e];
                 if (dx) {
-                    // Row xr0 + 2q may be -1 (top padding): its offset is
-                    // negative, out of range, and the store is dropped.  A
-                    // column outside [0, F) would land in a neighbouring
-                    // row, so those stores are skipped.
+                    // A column at or past F would land in the next row, so
+                    // those stores are skipped; rows at or past T are past the
+                    // resource and dropped.
                     const int32_t te = xr0 + 2 * q;
-                    const uint32_t o = (uint32_t)(te * (int32_t)xrow + ce * pix) + coff;  // used where ce_ok
-                    if (ce_ok) {
-                        Buf<S, V>::store(dxr, o, select_v<V>(te < len, d00));
-                        Buf<S, V>::store(dxr, o + xrow, select_v<V>(te + 1 < len, d10));
-                    }
-                    if (co_ok) {
-                        Buf<S, V>::store(dxr, o + (uint32_t)pix, select_v<V>(te < len, d01));
-                        Buf<S, V>::store(dxr, o + xrow + (uint32_t)pix, select_v<V>(te + 1 < len, d11));
-                    }
+#pragma unroll
+                    for (int ec = 0; ec < 2; ++ec)
+#pragma unroll
+                        for (int er = 0; er < 2; ++er)
+                            if (col_ok[ec])
+                                Buf<S, V>::store(dxr, (uint32_t)((te + er) * (int32_t)xrow + (ce + ec) * pix) + coff,
+                                                 select_v<V>(te + er < len, D[er][ec]));
                 }
             }
 #pragma unroll
@@ -406,6 +436,19 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
             for (int r = 0; r < 2 * TQ; ++r) { xea[r] = xeb[r]; xoa[r] = xob[r]; }
         }
         quads(nb - 1, ga, xea, xoa);
+
+        // With two columns of padding before, F' can be one more than the
+        // quad columns: g column NQf then belongs to no quad as its own and is
+        // added to db here, by the chunk that ends the row (as zero where it
+        // does not exist).
+        if constexpr (PC == 1) {
+            if (nb == geo.NQf) {
+#pragma unroll
+                for (int q = 0; q < TQ; ++q)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) gb[e] += (double)gcur[q].v[e];
+            }
+        }
     }
 
     if (!partial) return;  // uniform: dw and db not requested
@@ -492,9 +535,20 @@ static Geo2d device_geo(const Conv2dGeom& c, int tq) {
     g.To = (int32_t)c.To; g.Fo = (int32_t)c.Fo;
     g.dt = (int32_t)(c.pt0 - 1); g.df = (int32_t)(c.pf0 - 1);
     g.len_add = (int32_t)(c.pt0 + c.pt1 - 3);
-    const int64_t nqt = (c.T + g.dt + 1) / 2, nqf = (c.F + g.df + 1) / 2;
+    // Quads pair x rows 2m, 2m+1 and columns 2n, 2n+1.  Every g row is row
+    // m of some quad: NQt = max(ceil(T/2), T').  With one column of padding
+    // before, every g column is column n of some quad likewise; with two,
+    // F' can be ceil(F/2) + 1 and the last g column is added to db apart
+    // (so that a row keeps ceil(F/2) quad columns, which chunk evenly).
+    const int64_t nqt = (c.T + 1) / 2, nqf = (c.F + 1) / 2;
     g.NQt = (int32_t)(nqt > c.To ? nqt : c.To);
-    g.NQf = (int32_t)(nqf > c.Fo ? nqf : c.Fo);
+    if (g.df == 0) {
+        g.NQf = (int32_t)(nqf > c.Fo ? nqf : c.Fo);
+    } else {
+        int64_t q = nqf > c.Fo - 1 ? nqf : c.Fo - 1;
+        if (q == 0 && c.Fo > 0) q = 1;
+        g.NQf = (int32_t)q;
+    }
     g.fcols = fwd_cols(c.Fo);
     g.qcols = bwd_qcols(g.NQf, tq);
     g.nqc = g.NQf > 0 ? (g.NQf + g.qcols - 1) / g.qcols : 1;
@@ -605,8 +659,19 @@ static hipError_t launch_bwd_typed(const S* x, const S* w, const int32_t* length
     const uint32_t n_cblk = (CG + kLanes2d - 1) / kLanes2d;
     const uint64_t blocks = (uint64_t)g.G * n_cblk;
     if (blocks > 0 && (dx || partial)) {
-        hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ>), dim3((uint32_t)blocks), dim3(kBlock2d), 0, st, x,
-                           w, lengths, dy, dx, partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
+        const dim3 grid((uint32_t)blocks), block(kBlock2d);
+        if (geo.dt == 0 && geo.df == 0)
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 0, 0>), grid, block, 0, st, x, w, lengths, dy, dx,
+                               partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
+        else if (geo.dt == 1 && geo.df == 1)
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 1, 1>), grid, block, 0, st, x, w, lengths, dy, dx,
+                               partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
+        else if (geo.dt == 1)
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 1, 0>), grid, block, 0, st, x, w, lengths, dy, dx,
+                               partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
+        else
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 0, 1>), grid, block, 0, st, x, w, lengths, dy, dx,
+                               partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
