@@ -86,9 +86,9 @@ def sources_sha(paths) -> str:
 # summaries attribute dispatches to rows that way.
 ROW_KERNELS = [
     ("front", "dw::dwsub_fused_fwd_kernel<float>("),
-    ("front_bwd", "dw::dwsub_fused_bwd_kernel<float>("),
+    ("front_bwd", "dw::dwsub_fused_bwd_kernel<float, 4>("),
     ("front_causal", "dw::dwsub_fused_fwd_kernel<float>("),
-    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel<float>("),
+    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel<float, 3>("),
     ("conv1d_bf16", "dw::dwconv1d_fwd_kernel<unsigned short, 4, 9, 12>("),
     ("conv1d_causal_K3_C512", "dw::dwconv1d_fwd_kernel<float, 4, 3, 4>("),
     ("conv1d_causal_K4_C512", "dw::dwconv1d_fwd_kernel<float, 4, 4, 6>("),

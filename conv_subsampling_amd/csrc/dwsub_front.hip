@@ -262,24 +262,30 @@ hipError_t launch_dwsub_fused_fwd(const void* x, const void* w0, const void* b0,
 #ifndef DWSUB_BWD_QROWS
 #define DWSUB_BWD_QROWS 2
 #endif
-#ifndef DWSUB_BWD_QCOLS
-#define DWSUB_BWD_QCOLS 5
-#endif
 #ifndef DWSUB_BWD_WGS
 #define DWSUB_BWD_WGS 512
 #endif
 constexpr int kBQR = DWSUB_BWD_QROWS;          // quad rows per tile
-constexpr int kBQC = DWSUB_BWD_QCOLS;          // quad columns per tile
 constexpr int kBPatchRows = 4 * kBQR + 1;      // mel rows 4*t0-1-3d .. 4*t0+4*QR-1-3d
-constexpr int kBPatchCols = 4 * kBQC + 1;      // mel columns 4*f0-1-3d .. 4*f0+4*QC-1-3d
+
+// Quad columns per tile: an exact divisor of F2 from a short list measured on
+// MI355X (F2 = 20: 4 columns 41.7 us, 5 columns 44.7; F2 = 21: 3 columns
+// 43.7, 5 columns 44.3), else 5.
+static int front_bwd_qcols(int64_t F2) {
+    for (int q : {4, 3, 5})
+        if (F2 > 0 && F2 % q == 0) return q;
+    return 5;
+}
 constexpr int kFrontGrads = 20;                // dw0 (9), db0, dw1 (9), db1
 
-template <typename S>
+template <typename S, int QC>
 __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
     const S* __restrict__ x, const S* __restrict__ w0, const S* __restrict__ b0,
     const S* __restrict__ w1, const int32_t* __restrict__ lengths, const S* __restrict__ dy,
     double* __restrict__ partial, int32_t T, int32_t F, int32_t C, int32_t T1, int32_t F1, int32_t T2,
     int32_t F2, int32_t d, uint32_t n_rt, uint32_t n_ft, uint32_t n_tiles, uint32_t n_cblk) {
+    constexpr int kBQC = QC;                   // quad columns per tile
+    constexpr int kBPatchCols = 4 * kBQC + 1;  // mel columns 4*f0-1-3d .. 4*f0+4*QC-1-3d
     __shared__ double patch[kBPatchRows][kBPatchCols];
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
     const uint32_t G = gridDim.x / n_cblk;
@@ -435,6 +441,7 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
 
 struct FrontBwdGrid {
     uint32_t n_rt, n_ft, n_tiles, G;
+    int qc;
 };
 
 // The quad grid is T2 x F2 in both modes: ceil((T1 + d)/2) = T2 quad rows
@@ -443,8 +450,9 @@ static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F, int d) {
     const FrontDims fd = front_dims(T, F, d);
     const int64_t T2 = fd.T2, F2 = fd.F2;
     FrontBwdGrid g;
+    g.qc = front_bwd_qcols(F2);
     g.n_rt = (uint32_t)((T2 + kBQR - 1) / kBQR);
-    g.n_ft = (uint32_t)((F2 + kBQC - 1) / kBQC);
+    g.n_ft = (uint32_t)((F2 + g.qc - 1) / g.qc);
     const uint64_t n = (uint64_t)B * g.n_rt * g.n_ft;
     g.n_tiles = (uint32_t)n;
     g.G = (uint32_t)(n < DWSUB_BWD_WGS ? n : DWSUB_BWD_WGS);
@@ -456,7 +464,8 @@ bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causa
     const int64_t T2 = fd.T2, F2 = fd.F2;
     if ((T2 + kBQR + 1) * F2 * C * elem_bytes >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28) || C >= ((int64_t)1 << 24)) return false;
-    return (uint64_t)B * ((T2 + kBQR - 1) / kBQR) * ((F2 + kBQC - 1) / kBQC) < ((uint64_t)1 << 31);
+    const int qc = front_bwd_qcols(F2);
+    return (uint64_t)B * ((T2 + kBQR - 1) / kBQR) * ((F2 + qc - 1) / qc) < ((uint64_t)1 << 31);
 }
 
 size_t dwsub_fused_bwd_workspace(int64_t B, int64_t T, int64_t F, int64_t C, bool causal) {
@@ -476,17 +485,24 @@ hipError_t launch_dwsub_fused_bwd(const void* x, const void* w0, const void* b0,
     const uint32_t n_cblk = (uint32_t)((C + kSubBlock - 1) / kSubBlock);
     double* partial = (double*)workspace;
     if (g.G > 0) {
-        if (bf16)
-            hipLaunchKernelGGL(dwsub_fused_bwd_kernel<uint16_t>, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st,
-                               (const uint16_t*)x, (const uint16_t*)w0, (const uint16_t*)b0, (const uint16_t*)w1,
-                               lengths, (const uint16_t*)dy, partial, (int32_t)T, (int32_t)F, (int32_t)C,
-                               (int32_t)T1, (int32_t)F1, (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft,
-                               g.n_tiles, n_cblk);
-        else
-            hipLaunchKernelGGL(dwsub_fused_bwd_kernel<float>, dim3(g.G * n_cblk), dim3(kSubBlock), 0, st,
-                               (const float*)x, (const float*)w0, (const float*)b0, (const float*)w1, lengths,
-                               (const float*)dy, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1,
-                               (int32_t)F1, (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
+        const dim3 grid(g.G * n_cblk), block(kSubBlock);
+#define DWSUB_BWD_LAUNCH(QQ)                                                                                   \
+    if (bf16)                                                                                                   \
+        hipLaunchKernelGGL((dwsub_fused_bwd_kernel<uint16_t, QQ>), grid, block, 0, st, (const uint16_t*)x,        \
+                           (const uint16_t*)w0, (const uint16_t*)b0, (const uint16_t*)w1, lengths,                \
+                           (const uint16_t*)dy, partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1,        \
+                           (int32_t)F1, (int32_t)T2, (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk); \
+    else                                                                                                        \
+        hipLaunchKernelGGL((dwsub_fused_bwd_kernel<float, QQ>), grid, block, 0, st, (const float*)x,              \
+                           (const float*)w0, (const float*)b0, (const float*)w1, lengths, (const float*)dy,      \
+                           partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1, (int32_t)T2,  \
+                           (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
+        switch (g.qc) {
+            case 3: DWSUB_BWD_LAUNCH(3) break;
+            case 4: DWSUB_BWD_LAUNCH(4) break;
+            default: DWSUB_BWD_LAUNCH(5) break;
+        }
+#undef DWSUB_BWD_LAUNCH
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
