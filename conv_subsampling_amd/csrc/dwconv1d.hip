@@ -571,6 +571,12 @@ hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias
 // ---------------------------------------------------------------------------
 
 constexpr int kLanes1b = 64, kSubs1b = kBlock1d / kLanes1b;
+#ifndef DW1B_VMAX_K9
+#define DW1B_VMAX_K9 4
+#endif
+// Widest lane access of the backward per width (fp64 accumulators for K + 1
+// sums per channel must fit beside the K + 7 frame window).
+constexpr int bwd1d_vmax(int K) { return K <= 5 ? 4 : (K == 9 ? DW1B_VMAX_K9 : (K <= 15 ? 2 : 1)); }
 constexpr int kBwdTile1d = 8;
 #ifndef DW1D_BWD_WGS
 #define DW1D_BWD_WGS 256
@@ -682,13 +688,26 @@ struct Bwd1dGrid {
     uint32_t n_tb, groups_per_item, n_groups, G;
 };
 
-static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T) {
+// The lane width a launch takes for the caller's widest aligned width vec.
+static int bwd1d_vec(int vec, int64_t K) {
+    const int vm = bwd1d_vmax((int)K);
+    return vec >= 4 && vm >= 4 ? 4 : (vec >= 2 && vm >= 2 ? 2 : 1);
+}
+
+// Persistent grid: G workgroups per channel block.  With 16-byte lanes
+// about DW1D_BWD_WGS workgroups in all (one per CU), with narrower lanes
+// DW1D_BWD_WGS per channel block (measured on MI355X at [32..128,1500,512]:
+// K9 and K5 on 16-byte lanes 2-6% faster with 256 in all than with 512;
+// K15 on 8-byte lanes 3% slower with 512 in all than with 1024).
+static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V) {
     Bwd1dGrid g;
     g.n_tb = (uint32_t)((T + kBwdTile1d - 1) / kBwdTile1d);
     g.groups_per_item = (g.n_tb + kSubs1b - 1) / kSubs1b;
     const uint64_t n = (uint64_t)B * g.groups_per_item;
     g.n_groups = (uint32_t)n;
-    g.G = (uint32_t)(n < DW1D_BWD_WGS ? n : DW1D_BWD_WGS);
+    const int64_t n_cblk = ((C + V - 1) / V + kLanes1b - 1) / kLanes1b;
+    const int64_t per = V >= 4 ? (n_cblk > 0 ? (DW1D_BWD_WGS + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
+    g.G = (uint32_t)(n < (uint64_t)per ? n : (uint64_t)per);
     return g;
 }
 
@@ -696,7 +715,7 @@ bool dwconv1d_bwd_supported(int64_t K) {
     return K == 3 || K == 4 || K == 5 || K == 7 || K == 9 || K == 15 || K == 31;
 }
 
-int dwconv1d_bwd_max_vec(int64_t K) { return K <= 5 ? 4 : (K <= 15 ? 2 : 1); }
+int dwconv1d_bwd_max_vec(int64_t K) { return bwd1d_vmax((int)K); }
 
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
     if ((T + K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
@@ -704,7 +723,12 @@ bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
 }
 
 size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
-    const int64_t P = bwd1d_grid(B, T).G;
+    // enough for whichever lane width the pointers' alignment allows
+    int64_t P = 0;
+    for (int v : {1, 2, 4}) {
+        const int64_t p = bwd1d_grid(B, T, C, v).G;
+        P = p > P ? p : P;
+    }
     const int64_t ch = partial_reduce_chunks(P);
     return (size_t)((P + (ch > 0 ? ch : 1)) * (K + 1) * C * (int64_t)sizeof(double));
 }
@@ -712,7 +736,7 @@ size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
 template <typename S, int V, int K, bool CAUSAL>
 static hipError_t launch_bwd1d_typed(const S* x, const S* w, const int32_t* lengths, const S* dy, S* dx,
                                      double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
-    const Bwd1dGrid g = bwd1d_grid(B, T);
+    const Bwd1dGrid g = bwd1d_grid(B, T, C, V);
     const uint32_t CG = (uint32_t)(C / V);
     const uint32_t n_cblk = (CG + kLanes1b - 1) / kLanes1b;
     if (g.G == 0 || (!dx && !partial)) return hipSuccess;
@@ -725,7 +749,7 @@ static hipError_t launch_bwd1d_typed(const S* x, const S* w, const int32_t* leng
 template <typename S, int K, bool CAUSAL>
 static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const int32_t* lengths, const void* dyv,
                                  void* dxv, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
-    constexpr int VMAX = K <= 5 ? 4 : (K <= 15 ? 2 : 1);
+    constexpr int VMAX = bwd1d_vmax(K);
     const S* x = (const S*)xv;
     const S* w = (const S*)wv;
     const S* dy = (const S*)dyv;
@@ -761,7 +785,7 @@ hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* leng
     }
 #undef DW1B_CASE
     if (e != hipSuccess || !partial) return e;
-    const int64_t P = bwd1d_grid(B, T).G;
+    const int64_t P = bwd1d_grid(B, T, C, bwd1d_vec(vec, K)).G;
     RowOutputs out = {};
     out.n = 2;
     out.p[0] = dw; out.first[0] = 0; out.count[0] = (int32_t)K;
