@@ -88,7 +88,7 @@ ROW_KERNELS = [
     ("front", "dw::dwsub_fused_fwd_kernel<float>("),
     ("front_bwd", "dw::dwsub_fused_bwd_kernel<float, 4>("),
     ("front_causal", "dw::dwsub_fused_fwd_kernel<float>("),
-    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel<float, 3>("),
+    ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel<float, 5>("),
     ("conv1d_bf16", "dw::dwconv1d_fwd_kernel<unsigned short, 4, 9, 12>("),
     ("conv1d_causal_K3_C512", "dw::dwconv1d_fwd_kernel<float, 4, 3, 4>("),
     ("conv1d_causal_K4_C512", "dw::dwconv1d_fwd_kernel<float, 4, 4, 6>("),

@@ -268,14 +268,10 @@ hipError_t launch_dwsub_fused_fwd(const void* x, const void* w0, const void* b0,
 constexpr int kBQR = DWSUB_BWD_QROWS;          // quad rows per tile
 constexpr int kBPatchRows = 4 * kBQR + 1;      // mel rows 4*t0-1-3d .. 4*t0+4*QR-1-3d
 
-// Quad columns per tile: an exact divisor of F2 from a short list measured on
-// MI355X (F2 = 20: 4 columns 41.7 us, 5 columns 44.7; F2 = 21: 3 columns
-// 43.7, 5 columns 44.3), else 5.
-static int front_bwd_qcols(int64_t F2) {
-    for (int q : {4, 3, 5})
-        if (F2 > 0 && F2 % q == 0) return q;
-    return 5;
-}
+// Quad columns per tile: 4 where they divide F2, else 5 (measured on MI355X
+// within the whole bench step: F2 = 20 with 4 columns 42.6 us, with 5 45.5;
+// F2 = 21 with 5 columns 43.2, with 3 45.3).
+static int front_bwd_qcols(int64_t F2) { return F2 > 0 && F2 % 4 == 0 ? 4 : 5; }
 constexpr int kFrontGrads = 20;                // dw0 (9), db0, dw1 (9), db1
 
 template <typename S, int QC>
@@ -497,10 +493,10 @@ hipError_t launch_dwsub_fused_bwd(const void* x, const void* w0, const void* b0,
                            (const float*)w0, (const float*)b0, (const float*)w1, lengths, (const float*)dy,      \
                            partial, (int32_t)T, (int32_t)F, (int32_t)C, (int32_t)T1, (int32_t)F1, (int32_t)T2,  \
                            (int32_t)F2, (int32_t)d, g.n_rt, g.n_ft, g.n_tiles, n_cblk);
-        switch (g.qc) {
-            case 3: DWSUB_BWD_LAUNCH(3) break;
-            case 4: DWSUB_BWD_LAUNCH(4) break;
-            default: DWSUB_BWD_LAUNCH(5) break;
+        if (g.qc == 4) {
+            DWSUB_BWD_LAUNCH(4)
+        } else {
+            DWSUB_BWD_LAUNCH(5)
         }
 #undef DWSUB_BWD_LAUNCH
         const hipError_t e = hipGetLastError();
