@@ -102,16 +102,18 @@ struct Buf<float, V> {
         }
         return a;
     }
+    // P: the cache policy bits of the store (non-temporal by default).
+    template <int P = kNonTemporal>
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const Vf<V>& a) {
         if constexpr (V == 4) {
             u32x4 t = {__float_as_uint(a.v[0]), __float_as_uint(a.v[1]), __float_as_uint(a.v[2]),
                        __float_as_uint(a.v[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, P);
         } else if constexpr (V == 2) {
             u32x2 t = {__float_as_uint(a.v[0]), __float_as_uint(a.v[1])};
-            __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, P);
         } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.v[0]), r, off, 0, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(a.v[0]), r, off, 0, P);
         }
     }
 };
@@ -138,19 +140,20 @@ struct Buf<uint16_t, V> {
         }
         return a;
     }
+    // P: the cache policy bits of the store (non-temporal by default).
+    template <int P = kNonTemporal>
     static __device__ __forceinline__ void store(rsrc_t r, uint32_t off, const Vf<V>& a) {
         if constexpr (V == 8) {
             u32x4 t = {pack_bf16x2(a.v[0], a.v[1]), pack_bf16x2(a.v[2], a.v[3]),
                        pack_bf16x2(a.v[4], a.v[5]), pack_bf16x2(a.v[6], a.v[7])};
-            __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, P);
         } else if constexpr (V == 4) {
             u32x2 t = {pack_bf16x2(a.v[0], a.v[1]), pack_bf16x2(a.v[2], a.v[3])};
-            __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, P);
         } else if constexpr (V == 2) {
-            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a.v[0], a.v[1]), r, off, 0, kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a.v[0], a.v[1]), r, off, 0, P);
         } else {
-            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits_rne(a.v[0]), r, off, 0,
-                                                  kNonTemporal);
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_bits_rne(a.v[0]), r, off, 0, P);
         }
     }
 };
