@@ -57,3 +57,20 @@ def test_dispatch_attribution_refuses_a_partial_step():
     assert len(same) > 1  # the last row shares its kernel with earlier rows
     disp = [(k, prefix + ")", k) for k in range(len(same) + 1)]   # one dispatch too many
     assert bench.attribute_dispatches(disp)[name] == []
+
+
+def test_import_without_the_library_fails_loudly(tmp_path):
+    """The binding has no other implementation: without libdwconv.so the
+    package refuses to import, naming the missing file."""
+    import os
+    import shutil
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    pkg = tmp_path / "conv_subsampling_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(root, "conv_subsampling_amd", "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import conv_subsampling_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libdwconv.so is missing" in r.stderr
