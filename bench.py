@@ -95,7 +95,7 @@ ROW_KERNELS = [
     ("conv1d_causal_K5_C512", "dw::dwconv1d_fwd_kernel<float, 4, 5, 8>("),
     ("conv1d_causal_K9_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 9, 32>("),
     ("conv1d_causal_K15_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 15, 32>("),
-    ("conv1d_causal_K9_C200", "dw::dwconv1d_fwd_kernel<float, 4, 9, 8>("),
+    ("conv1d_causal_K9_C200", "dw::dwconv1d_fwd_lds_kernel<float, 4, 9, 32>("),
     ("conv1d_stream_bf16", "dw::dwconv1d_stream_kernel<unsigned short, 8, 9, 8>("),
     ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_kernel<float, 4, 9, true, 8>("),
     ("stage_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),

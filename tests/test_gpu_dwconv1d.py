@@ -61,6 +61,8 @@ GRID = [
     # ragged 32-frame tiles, T below the tile and below K, several slabs
     (3, 70, 256, 9, False), (4, 31, 256, 9, True), (2, 33, 512, 15, True), (1, 5, 256, 15, False),
     (2, 97, 768, 9, True), (3, 64, 256, 15, False),
+    # partial last slabs of the LDS-staged form: 50, 45 and 65 (= 64 + 1) channel groups
+    (2, 70, 200, 9, True), (2, 40, 180, 15, False), (2, 70, 260, 9, True),
 ]
 
 
