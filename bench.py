@@ -418,7 +418,14 @@ def cpu_baseline(data, target_s: float):
     while reps == 0 or secs < target_s:
         ds, df = one_pass(n)
         secs, frames, reps = secs + ds, frames + df, reps + 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=round(frames / secs, 1), unit="frames/s", cores=1, kind="oracle",
+                cpu_model=model, host_cpus=os.cpu_count(),
                 sample=(f"every operation of the step on the first {n} items of its batch (at most its batch "
                         f"size), same shapes and lengths, {reps} pass(es): {frames} frames in {secs:.2f} s; "
                         f"the oracle is single-threaded C with fp64 accumulation"))

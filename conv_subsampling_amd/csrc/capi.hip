@@ -50,6 +50,22 @@ dw_status check_geometry_2d(const char* fn, int64_t KH, int64_t KW, int64_t stri
     return DW_OK;
 }
 
+// True when every extent is positive: a tensor with these extents holds
+// elements.  (Multiplying the extents could overflow.)
+template <typename... I>
+bool nonempty(I... n) {
+    return ((n > 0) && ...);
+}
+
+// Whether every extent is below dw::kMaxExtent (the launchers' size checks
+// add extents together and need that bound; larger ones cannot fit anyway).
+template <typename... I>
+bool extents_ok(I... n) {
+    return ((n < dw::kMaxExtent) && ...);
+}
+
+dw_status too_large(const char* fn) { return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn); }
+
 bool geometry_ok_2d(int64_t KH, int64_t KW, int64_t stride, int64_t pt0, int64_t pt1, int64_t pf0, int64_t pf1) {
     return KH == 3 && KW == 3 && stride == 2 && dw::dwconv2d_pads_supported(pt0, pt1, pf0, pf1);
 }
@@ -77,6 +93,7 @@ dw_status dwconv1d_fwd(const void* x, const void* w, const void* bias, const int
     if (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL) return fail(DW_ERR_INVALID_ARG, "%s: unknown pad mode %d", fn, (int)pad);
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     if (B == 0 || T == 0 || C == 0) return ok();
+    if (!extents_ok(B, T, C, K)) return too_large(fn);
     if (!x || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
     if (x == y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
     const int es = dtype == DW_BF16 ? 2 : 4;
@@ -97,6 +114,7 @@ dw_status dwconv1d_stream_fwd(const void* x, const void* w, const void* bias, co
     if (K < 1) return fail(DW_ERR_INVALID_ARG, "%s: kernel width K=%lld must be >= 1", fn, (long long)K);
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     if (B == 0 || C == 0) return ok();
+    if (!extents_ok(B, Tc, C, K)) return too_large(fn);
     const bool has_cache = K > 1;
     if ((!x && Tc > 0) || !w || (!y && Tc > 0) || (has_cache && (!cache_in || !cache_out)))
         return fail(DW_ERR_INVALID_ARG, "%s: x, w, y and the caches must not be NULL (unless empty)", fn);
@@ -107,14 +125,14 @@ dw_status dwconv1d_stream_fwd(const void* x, const void* w, const void* bias, co
     const int es = dtype == DW_BF16 ? 2 : 4;
     const void* ptrs[6] = {x, w, bias, y, cache_in, cache_out};
     const int vec = dw::pick_vec(C, es, ptrs, 6, dw::dwconv1d_stream_max_vec(K, dtype == DW_BF16));
-    if (!dw::dwconv1d_stream_fits(B, Tc, C, K, es, vec))
-        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    if (!dw::dwconv1d_stream_fits(B, Tc, C, K, es, vec)) return too_large(fn);
     return from_hip(dw::launch_dwconv1d_stream(x, w, bias, lengths, cache_in, y, cache_out, B, Tc, C, K,
                                                dtype == DW_BF16, vec, (hipStream_t)stream), fn);
 }
 
 size_t dwconv1d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t C, int64_t K) {
     if (B < 0 || T < 0 || C < 0 || !dw::dwconv1d_bwd_supported(K)) return 0;
+    if (!extents_ok(B, T, C) || !dw::dwconv1d_bwd_fits(B, T, C, K, 2)) return 0;
     return dw::dwconv1d_bwd_workspace(B, T, C, K);
 }
 
@@ -131,16 +149,16 @@ dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, con
     const bool want_wb = dw_ || db;
     if (!dx && !want_wb) return ok();
     if (C == 0) return ok();
-    if ((!x && B * T > 0) || (!dy && B * T > 0) || !w)
+    if ((!x && nonempty(B, T)) || (!dy && nonempty(B, T)) || !w)
         return fail(DW_ERR_INVALID_ARG, "%s: x, w and dy must not be NULL (unless empty)", fn);
     if (dx && (dx == x || dx == dy)) return fail(DW_ERR_INVALID_ARG, "%s: dx must not alias x or dy", fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    if (!extents_ok(B, T, C) || !dw::dwconv1d_bwd_fits(B, T, C, K, es)) return too_large(fn);
     if (want_wb) {
         const size_t need = dw::dwconv1d_bwd_workspace(B, T, C, K);
         if (!workspace || workspace_bytes < need)
             return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
     }
-    const int es = dtype == DW_BF16 ? 2 : 4;
-    if (!dw::dwconv1d_bwd_fits(B, T, C, K, es)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
     const void* ptrs[4] = {x, w, dy, dx};
     const int vec = dw::pick_vec(C, es, ptrs, 4, dw::dwconv1d_bwd_max_vec(K));
     return from_hip(dw::launch_dwconv1d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, T, C, K,
@@ -156,14 +174,14 @@ dw_status dwsub_fused_fwd_ex(const void* x, const void* w0, const void* b0, cons
     if (ps != DW_OK) return ps;
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const bool causal = pad == DW_PAD_CAUSAL;
+    if (!extents_ok(B, T, F, C)) return too_large(fn);
     const dw::FrontDims fd = dw::front_dims(T, F, causal ? 1 : 0);
     if (B == 0 || fd.T2 == 0 || fd.F2 == 0 || C == 0) return ok();
-    if ((!x && T * F > 0) || !w0 || !w1 || !y)
+    if ((!x && nonempty(T, F)) || !w0 || !w1 || !y)
         return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and y must not be NULL", fn);
     if (x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
     const int es = dtype == DW_BF16 ? 2 : 4;
-    if (!dw::dwsub_fused_fwd_fits(B, T, F, C, causal, es))
-        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    if (!dw::dwsub_fused_fwd_fits(B, T, F, C, causal, es)) return too_large(fn);
     return from_hip(dw::launch_dwsub_fused_fwd(x, w0, b0, w1, b1, lengths, y, B, T, F, C, causal, dtype == DW_BF16,
                                                (hipStream_t)stream), fn);
 }
@@ -176,6 +194,7 @@ dw_status dwsub_fused_fwd(const float* x, const float* w0, const float* b0, cons
 
 size_t dwsub_fused_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t C, dw_pad pad) {
     if (B < 0 || T < 0 || F < 0 || C < 0 || (pad != DW_PAD_SYMMETRIC && pad != DW_PAD_CAUSAL)) return 0;
+    if (!extents_ok(B, T, F, C) || !dw::dwsub_fused_bwd_fits(B, T, F, C, pad == DW_PAD_CAUSAL, 2)) return 0;
     return dw::dwsub_fused_bwd_workspace(B, T, F, C, pad == DW_PAD_CAUSAL);
 }
 
@@ -195,16 +214,16 @@ dw_status dwsub_fused_bwd_ex(const void* x, const void* w0, const void* b0, cons
     const bool causal = pad == DW_PAD_CAUSAL;
     if (!dw0 && !db0 && !dw1 && !db1) return ok();
     if (C == 0) return ok();
+    if (!extents_ok(B, T, F, C)) return too_large(fn);
     const dw::FrontDims fd = dw::front_dims(T, F, causal ? 1 : 0);
-    if ((!x && B * T * F > 0) || (!dy && B * fd.T2 * fd.F2 * C > 0) || !w0 || !w1)
+    if ((!x && nonempty(B, T, F)) || (!dy && nonempty(B, fd.T2, fd.F2, C)) || !w0 || !w1)
         return fail(DW_ERR_INVALID_ARG, "%s: x, w0, w1 and dy must not be NULL (unless empty)", fn);
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    if (!dw::dwsub_fused_bwd_fits(B, T, F, C, causal, es)) return too_large(fn);
     const size_t need = dw::dwsub_fused_bwd_workspace(B, T, F, C, causal);
     if (!workspace || workspace_bytes < need)
         return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
                     workspace ? workspace_bytes : (size_t)0, need);
-    const int es = dtype == DW_BF16 ? 2 : 4;
-    if (!dw::dwsub_fused_bwd_fits(B, T, F, C, causal, es))
-        return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
     return from_hip(dw::launch_dwsub_fused_bwd(x, w0, b0, w1, lengths, dy, dw0, db0, dw1, db1, workspace, B, T, F, C,
                                                causal, dtype == DW_BF16, (hipStream_t)stream), fn);
 }
@@ -226,14 +245,15 @@ dw_status dwconv2d_fwd_ex(const void* x, const void* w, const void* bias, const 
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const dw_status gs = check_geometry_2d(fn, KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1);
     if (gs != DW_OK) return gs;
+    if (!extents_ok(B, T, F, C)) return too_large(fn);
     const dw::Conv2dGeom g = dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1);
     if (B == 0 || g.To == 0 || g.Fo == 0 || C == 0) return ok();
-    if ((!x && T * F > 0) || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
+    if ((!x && nonempty(T, F)) || !w || !y) return fail(DW_ERR_INVALID_ARG, "%s: x, w and y must not be NULL", fn);
     if (x == (const void*)y) return fail(DW_ERR_INVALID_ARG, "%s: y must not alias x", fn);
     const int es = dtype == DW_BF16 ? 2 : 4;
     const void* ptrs[4] = {x, w, bias, y};
     const int vec = dw::pick_vec(C, es, ptrs, 4, dtype == DW_BF16 ? 8 : 4);
-    if (!dw::dwconv2d_fits(B, g, es)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
+    if (!dw::dwconv2d_fits(B, g, es)) return too_large(fn);
     return from_hip(dw::launch_dwconv2d_fwd(x, w, bias, lengths, y, B, g, dtype == DW_BF16, vec,
                                             (hipStream_t)stream), fn);
 }
@@ -248,7 +268,10 @@ size_t dwconv2d_bwd_workspace_bytes_ex(int64_t B, int64_t T, int64_t F, int64_t 
                                        int64_t stride, int64_t pad_t0, int64_t pad_t1, int64_t pad_f0,
                                        int64_t pad_f1) {
     if (B < 0 || T < 0 || F < 0 || C < 0 || !geometry_ok_2d(KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1)) return 0;
-    return dw::dwconv2d_bwd_workspace(B, dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1));
+    if (!extents_ok(B, T, F, C)) return 0;
+    const dw::Conv2dGeom g = dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1);
+    if (!dw::dwconv2d_fits(B, g, 2)) return 0;
+    return dw::dwconv2d_bwd_workspace(B, g);
 }
 
 size_t dwconv2d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH, int64_t KW,
@@ -265,11 +288,14 @@ dw_status dwconv2d_bwd_ex(const void* x, const void* w, const int32_t* lengths, 
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const dw_status gs = check_geometry_2d(fn, KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1);
     if (gs != DW_OK) return gs;
+    if (!extents_ok(B, T, F, C)) return too_large(fn);
     const dw::Conv2dGeom g = dw::conv2d_geom(T, F, C, pad_t0, pad_t1, pad_f0, pad_f1);
-    if ((!x && B * T * F * C > 0) || (!dy && B * g.To * g.Fo * C > 0) || (!w && C > 0))
+    if ((!x && nonempty(B, T, F, C)) || (!dy && nonempty(B, g.To, g.Fo, C)) || (!w && C > 0))
         return fail(DW_ERR_INVALID_ARG, "%s: x, w and dy must not be NULL (unless empty)", fn);
     if (dx && (dx == x || dx == dy)) return fail(DW_ERR_INVALID_ARG, "%s: dx must not alias x or dy", fn);
     const bool want_wb = dw_ || db;
+    const int es = dtype == DW_BF16 ? 2 : 4;
+    if (!dw::dwconv2d_fits(B, g, es)) return too_large(fn);
     if (want_wb) {
         const size_t need = dw::dwconv2d_bwd_workspace(B, g);
         if (!workspace || workspace_bytes < need)
@@ -279,10 +305,8 @@ dw_status dwconv2d_bwd_ex(const void* x, const void* w, const int32_t* lengths, 
     if (C == 0) return ok();
     // An empty batch or item still defines dw = 0 and db = 0; the launcher
     // writes those zeros when there is nothing to reduce.
-    const int es = dtype == DW_BF16 ? 2 : 4;
     const void* ptrs[4] = {x, w, dy, dx};
     const int vec = dw::pick_vec(C, es, ptrs, 4, 4);
-    if (!dw::dwconv2d_fits(B, g, es)) return fail(DW_ERR_UNSUPPORTED, "%s: sizes too large for one launch", fn);
     return from_hip(dw::launch_dwconv2d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, g, dtype == DW_BF16, vec,
                                             (hipStream_t)stream), fn);
 }

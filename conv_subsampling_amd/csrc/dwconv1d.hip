@@ -261,7 +261,7 @@ static bool lds_form_1d(int64_t K, int64_t CG) { return (K == 9 || K == 15) && C
 bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec) {
     // Per-item byte offsets, including the left padding as a negative
     // offset, must stay within a signed 32-bit range.
-    if ((T + K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    if (!product_below((int64_t)1 << 31, {T + K + 32, C, elem_bytes})) return false;
     const int64_t tt = tile_for(K, elem_bytes == 2);
     const int64_t per_item = ((T + tt - 1) / tt) * (C / vec);
     int64_t blocks = B * ((per_item + kBlock1d - 1) / kBlock1d);
@@ -482,7 +482,7 @@ static int stream_tile(int64_t K, bool bf16, int64_t Tc) {
 }
 
 bool dwconv1d_stream_fits(int64_t B, int64_t Tc, int64_t C, int64_t K, int elem_bytes, int vec) {
-    if ((Tc + 2 * K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    if (!product_below((int64_t)1 << 31, {Tc + 2 * K + 32, C, elem_bytes})) return false;
     const int64_t tt = stream_tile(K, elem_bytes == 2, Tc);
     const int64_t per_item = ((Tc + tt - 1) / tt + 1) * (C / vec);
     return B * ((per_item + kBlock1d - 1) / kBlock1d) < ((int64_t)1 << 31);
@@ -725,7 +725,7 @@ bool dwconv1d_bwd_supported(int64_t K) {
 int dwconv1d_bwd_max_vec(int64_t K) { return bwd1d_vmax((int)K); }
 
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
-    if ((T + K + 32) * C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    if (!product_below((int64_t)1 << 31, {T + K + 32, C, elem_bytes})) return false;
     return (uint64_t)B * ((T + kBwdTile1d - 1) / kBwdTile1d) < ((uint64_t)1 << 31);
 }
 

@@ -566,9 +566,10 @@ static Geo2d device_geo(const Conv2dGeom& c, int tq) {
 bool dwconv2d_fits(int64_t B, const Conv2dGeom& g, int elem_bytes) {
     // Per-item byte offsets (with two rows of slack on each side) must stay
     // within a signed 32-bit range, and the row groups within 32 bits.
-    if ((g.T + 4) * g.F * g.C * elem_bytes >= ((int64_t)1 << 31)) return false;
-    if ((g.To + 4) * (g.Fo + 2) * g.C * elem_bytes >= ((int64_t)1 << 31)) return false;
-    if ((g.F + 4) * g.C * elem_bytes >= ((int64_t)1 << 31)) return false;
+    constexpr int64_t lim = (int64_t)1 << 31;
+    if (!product_below(lim, {g.T + 4, g.F, g.C, elem_bytes})) return false;
+    if (!product_below(lim, {g.To + 4, g.Fo + 2, g.C, elem_bytes})) return false;
+    if (!product_below(lim, {g.F + 4, g.C, elem_bytes})) return false;
     return (uint64_t)B * (uint64_t)(g.T / 2 + 2) * (uint64_t)(g.F / 2 + 2) < ((uint64_t)1 << 31);
 }
 

@@ -190,8 +190,8 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
 bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes) {
     const FrontDims fd = front_dims(T, F, causal ? 1 : 0);
     const int64_t T2 = fd.T2, F2 = fd.F2;
-    if ((T2 + kSubRows) * F2 * C * elem_bytes >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28)) return false;
+    if (!product_below((int64_t)1 << 31, {T2 + kSubRows, F2, C, elem_bytes})) return false;
     const int64_t blocks = B * ((T2 + kSubRows - 1) / kSubRows) * ((F2 + kSubCols - 1) / kSubCols) *
                            ((C + kSubBlock - 1) / kSubBlock);
     return blocks < ((int64_t)1 << 31);
@@ -458,8 +458,8 @@ static FrontBwdGrid front_bwd_grid(int64_t B, int64_t T, int64_t F, int d) {
 bool dwsub_fused_bwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes) {
     const FrontDims fd = front_dims(T, F, causal ? 1 : 0);
     const int64_t T2 = fd.T2, F2 = fd.F2;
-    if ((T2 + kBQR + 1) * F2 * C * elem_bytes >= ((int64_t)1 << 31)) return false;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28) || C >= ((int64_t)1 << 24)) return false;
+    if (!product_below((int64_t)1 << 31, {T2 + kBQR + 1, F2, C, elem_bytes})) return false;
     const int qc = front_bwd_qcols(F2);
     return (uint64_t)B * ((T2 + kBQR - 1) / kBQR) * ((F2 + qc - 1) / qc) < ((uint64_t)1 << 31);
 }

@@ -7,7 +7,27 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 namespace dw {
+
+// Every extent the C ABI passes to these launchers (B, T, F, C, K) is below
+// this; the *_fits checks rely on it to add extents without overflow.
+constexpr int64_t kMaxExtent = (int64_t)1 << 31;
+
+// Whether the product of the non-negative factors is below limit, formed
+// without overflow: the running product stays below limit <= 2^63 before
+// each multiplication, so it never exceeds 2^126 in 128 bits.
+inline bool product_below(int64_t limit, std::initializer_list<int64_t> factors) {
+    for (int64_t f : factors)
+        if (f == 0) return 0 < limit;
+    __int128 p = 1;
+    for (int64_t f : factors) {
+        p *= f;
+        if (p >= limit) return false;
+    }
+    return true;
+}
 
 // Outputs of a partial reduction: output s receives rows
 // [first[s], first[s] + count[s]) of the K rows, as [count[s]][C] floats.

@@ -45,8 +45,12 @@
  *     with no elements may be NULL.
  *   - The kernels address each batch item with 32-bit byte offsets: an item
  *     whose tensors (with a few frames of padding) would reach 2^31 bytes is
- *     refused with DW_ERR_UNSUPPORTED ("sizes too large for one launch").
- *     The batch as a whole may be larger.
+ *     refused with DW_ERR_UNSUPPORTED ("sizes too large for one launch"),
+ *     and so is any extent (B, T, F, C, K) of 2^31 or more.  These limits
+ *     are computed without integer overflow for any int64_t input.  The
+ *     batch as a whole may be larger than 2^31 bytes.
+ *   - The workspace queries return 0 for sizes their call would refuse
+ *     (invalid, unsupported, or too large for one launch).
  *   - Errors: every argument is validated on the host before anything is
  *     enqueued.  A failing call returns a negative dw_status, enqueues
  *     nothing (except DW_ERR_HIP, raised when a launch is rejected) and sets

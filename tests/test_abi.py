@@ -262,3 +262,30 @@ def test_header_is_c99_and_the_library_links_from_c(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "c abi check: ok" in r.stdout, r.stdout + r.stderr
+
+
+HUGE = [(1 << 31), (1 << 40), (1 << 62), (1 << 63) - 1]
+
+
+def test_huge_extents_are_rejected_before_any_launch(lib):
+    """Extents whose byte counts overflow 64-bit products are rejected as
+    too large (never wrapped into a small size that would pass), and the
+    workspace queries return 0 for them."""
+    R, W = ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000)
+    S = ctypes.c_void_p(0x5000)
+    for h in HUGE:
+        for B, T, C in ((h, 8, 4), (2, h, 4), (2, 8, h), (h, h, h), (3, (1 << 31) - 1, (1 << 31) - 1)):
+            assert lib.dwconv1d_fwd(P, P, N, N, Q, B, T, C, 3, 0, 0, N) == UNSUPPORTED, (B, T, C)
+            assert "too large" in err(lib)
+            assert lib.dwconv1d_stream_fwd(P, P, N, N, R, Q, S, B, T, C, 9, 0, N) == UNSUPPORTED
+            assert lib.dwconv1d_bwd_workspace_bytes(B, T, C, 9) == 0
+            assert lib.dwconv1d_bwd(P, P, N, Q, R, W, N, W, 1 << 40, B, T, C, 9, 0, 0, N) == UNSUPPORTED
+        assert lib.dwconv1d_fwd(P, P, N, N, Q, 2, 8, 4, h, 0, 0, N) == UNSUPPORTED
+        for B, T, F, C in ((h, 8, 8, 4), (2, h, 8, 4), (2, 8, h, 4), (2, 8, 8, h), (h, h, h, h),
+                           (2, (1 << 31) - 1, (1 << 31) - 1, 2)):
+            assert lib.dwconv2d_fwd(P, P, N, N, Q, B, T, F, C, 3, 3, 2, 1, N) == UNSUPPORTED, (B, T, F, C)
+            assert lib.dwconv2d_bwd_workspace_bytes(B, T, F, C, 3, 3, 2, 1) == 0
+            assert lib.dwconv2d_bwd(P, P, N, Q, R, W, N, W, 1 << 40, B, T, F, C, 3, 3, 2, 1, N) == UNSUPPORTED
+            assert lib.dwsub_fused_fwd(P, P, N, P, N, N, Q, B, T, F, C, N) == UNSUPPORTED
+            assert lib.dwsub_fused_bwd_workspace_bytes(B, T, F, C) == 0
+            assert lib.dwsub_fused_bwd(P, P, N, P, N, Q, W, W, W, W, R, 1 << 40, B, T, F, C, N) == UNSUPPORTED
