@@ -289,13 +289,25 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
     const int32_t c = (int32_t)cblk * kSubBlock + (int32_t)threadIdx.x;
     const bool active = c < C;
 
-    double wa[9], wb[9], ba = 0.0;
+    // Parameters of channel c (channel 0 stands in for a thread past C, which
+    // computes nothing), loaded with no condition around each load so that
+    // the 19 loads are in flight together: a select per load had made each
+    // one wait for the last (front backward 38.6 -> 36.8 us on MI355X).
+    const int32_t cp = active ? c : 0;
+    S wa_s[9], wb_s[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        wa[k] = active ? (double)to_f32(w0[(int64_t)k * C + c]) : 0.0;
-        wb[k] = active ? (double)to_f32(w1[(int64_t)k * C + c]) : 0.0;
+        wa_s[k] = w0[(int64_t)k * C + cp];
+        wb_s[k] = w1[(int64_t)k * C + cp];
     }
-    if (active && b0) ba = (double)to_f32(b0[c]);
+    const S ba_s = b0 ? b0[cp] : S(0);
+    double wa[9], wb[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        wa[k] = (double)to_f32(wa_s[k]);
+        wb[k] = (double)to_f32(wb_s[k]);
+    }
+    const double ba = (double)to_f32(ba_s);
 
     double gw0[9], gw1[9], gb0 = 0.0, gb1 = 0.0;
 #pragma unroll
