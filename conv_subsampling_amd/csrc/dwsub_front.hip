@@ -79,12 +79,39 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     const int32_t len = (int32_t)item_length(lengths, b, T);
     const int32_t L1 = len > 0 ? (len - 1 + d) / 2 + 1 : 0;
 
+    // This thread's parameters (channel 0 stands in past C), loaded first so
+    // that they arrive with the patch.
+    const int32_t cp = min((int32_t)cblk * kSubBlock + (int32_t)threadIdx.x, C - 1);
+    S wa_s[9], wb_s[9];
+#pragma unroll
+    for (int k = 0; k < 9; ++k) {
+        wa_s[k] = w0[(int64_t)k * C + cp];
+        wb_s[k] = w1[(int64_t)k * C + cp];
+    }
+    const S ba_s = b0 ? b0[cp] : S(0), bb_s = b1 ? b1[cp] : S(0);
+
     // Stage the zero-padded mel patch.  The input is not length-masked.
-    const S* xb = x + (int64_t)b * T * F;
-    for (int i = threadIdx.x; i < kPatchRows * kPatchCols; i += kSubBlock) {
+    // Every thread issues its loads before it writes any of them, through a
+    // buffer resource: a row above the input wraps to an offset past the
+    // item, a row below lies past it, and a column outside [0, F) is sent
+    // out of range, so each reads zero with no select on the loaded value.
+    constexpr int kPatchN = kPatchRows * kPatchCols;
+    constexpr int kPer = (kPatchN + kSubBlock - 1) / kSubBlock;
+    constexpr uint32_t esx = sizeof(S);
+    const rsrc_t xr = make_rsrc(x + (int64_t)b * T * F, (uint32_t)T * (uint32_t)F * esx);
+    float pv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int i = (int)threadIdx.x + u * kSubBlock;
         const int r = i / kPatchCols, q = i % kPatchCols;
         const int32_t t = 4 * t0 - 3 - 3 * d + r, f = 4 * f0 - 5 - 3 * d + q;
-        patch[r][q] = (t >= 0 && t < T && f >= 0 && f < F) ? to_f32(xb[(int64_t)t * F + f]) : 0.0f;
+        const uint32_t off = i < kPatchN && f >= 0 && f < F ? (uint32_t)((t * F + f) * (int32_t)esx) : 0x80000000u;
+        pv[u] = Buf<S, 1>::load(xr, off).v[0];
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int i = (int)threadIdx.x + u * kSubBlock;
+        if (i < kPatchN) patch[i / kPatchCols][i % kPatchCols] = pv[u];
     }
     __syncthreads();
 
@@ -94,11 +121,10 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     float wa[9], wb[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
-        wa[k] = to_f32(w0[(int64_t)k * C + c]);
-        wb[k] = to_f32(w1[(int64_t)k * C + c]);
+        wa[k] = to_f32(wa_s[k]);
+        wb[k] = to_f32(wb_s[k]);
     }
-    const float ba = b0 ? to_f32(b0[c]) : 0.0f;
-    const float bb = b1 ? to_f32(b1[c]) : 0.0f;
+    const float ba = to_f32(ba_s), bb = to_f32(bb_s);
     constexpr uint32_t es = sizeof(S);
 
     // h rows 2*t0-1-d+l, l = 0..2*TY, read mel patch rows 2l .. 2l+2.
@@ -192,6 +218,7 @@ bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causa
     const int64_t T2 = fd.T2, F2 = fd.F2;
     if (T >= ((int64_t)1 << 28) || F >= ((int64_t)1 << 28)) return false;
     if (!product_below((int64_t)1 << 31, {T2 + kSubRows, F2, C, elem_bytes})) return false;
+    if (!product_below((int64_t)1 << 31, {T, F, elem_bytes})) return false;  // one item's mel input
     const int64_t blocks = B * ((T2 + kSubRows - 1) / kSubRows) * ((F2 + kSubCols - 1) / kSubCols) *
                            ((C + kSubBlock - 1) / kSubBlock);
     return blocks < ((int64_t)1 << 31);
