@@ -155,15 +155,26 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_lds_kernel(
         return;
     }
     const rsrc_t xr = make_rsrc(x + item, (uint32_t)len * row);
-#pragma unroll
-    for (int j = 0; j < (R + W - 1) / W; ++j) {
-        const int r = (int)wv + W * j;
-        if (r < R) lds_put<V>(&tile[r][lane * V], Buf<S, V>::load(xr, (uint32_t)((t0 - pL + r) * (int32_t)row) + coff));
-    }
+    // Taps first, then every staged row's load, all in flight together: a
+    // row past the tile (only in the last round, where R is not a multiple
+    // of the wave count) is loaded out of range and not written.
     Vf<V> wk[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
     const Vf<V> bv = bias ? load_param<S, V>(bias + c0) : vzero<V>();
+    constexpr int kRounds = (R + W - 1) / W;
+    Vf<V> st[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+        const int r = (int)wv + W * j;
+        const uint32_t ro = (R % W == 0 || r < R) ? (uint32_t)((t0 - pL + r) * (int32_t)row) + coff : 0x80000000u;
+        st[j] = Buf<S, V>::load(xr, ro);
+    }
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+        const int r = (int)wv + W * j;
+        if (R % W == 0 || r < R) lds_put<V>(&tile[r][lane * V], st[j]);
+    }
     __syncthreads();
     Vf<V> win[TT + K - 1];
 #pragma unroll
