@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_kernel(
     }
 }
 
-// LDS-staged form, for the wide fp32 kernels: a workgroup owns TW output
+// LDS-staged form, for the fp32 kernels: a workgroup owns TW output
 // frames of 64 channel groups (one slab).  Its four waves stage the
 // TW + K - 1 input frames the tile needs into LDS once (each wave a quarter
 // of the rows, one vector per lane per row), then each wave computes TW / 4
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_kernel(
 // per 32 output frames instead of once per thread tile: at K = 15 a thread
 // tile of 12 frames reads 26, 2.2 times its share, against 1.4 times here
 // (measured on MI355X at [32,1500,512]: K15 40.2 -> 37.5 us, K9 37.2 -> 36.7;
-// at K <= 4 and in bf16 the register window stays ahead).
+// in bf16 the register window stays ahead).
 constexpr int kLdsTile1d = 32;
 template <int V>
 __device__ __forceinline__ void lds_put(float* p, const Vf<V>& a) {
@@ -264,10 +264,14 @@ static int tile_for(int64_t K, bool bf16) {
     }
 }
 
-// The fp32 forward takes the LDS-staged form at K = 9 and 15 when there are
-// at least 32 channel groups; a last slab of fewer than 64 groups leaves its
-// other lanes idle (C = 200: 21.5 -> 19.9 us against the register form).
-static bool lds_form_1d(int64_t K, int64_t CG) { return (K == 9 || K == 15) && CG >= 32; }
+// The fp32 forward takes the LDS-staged form at the compiled widths (3, 4, 5,
+// 9, 15) when there are at least 32 channel groups; a last slab of fewer than
+// 64 groups leaves its other lanes idle (C = 200: 21.5 -> 19.9 us against the
+// register form).  At K <= 5 it is ahead since its loads are issued together
+// (K5 36.6 -> 34.7 us, K3 35.5 -> 35.0 at [32,1500,512] on MI355X).
+static bool lds_form_1d(int64_t K, int64_t CG) {
+    return (K == 3 || K == 4 || K == 5 || K == 9 || K == 15) && CG >= 32;
+}
 
 bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec) {
     // Per-item byte offsets, including the left padding as a negative
@@ -295,7 +299,16 @@ static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int3
             constexpr int TW = kLdsTile1d;
             const uint32_t n_tt = (uint32_t)((T + TW - 1) / TW), n_sl = (CG + 63) / 64;
             const dim3 lgrid((uint32_t)(B * n_tt * n_sl));
-            if (K == 9)
+            if (K == 3)
+                hipLaunchKernelGGL((dwconv1d_fwd_lds_kernel<S, V, 3, TW>), lgrid, block, 0, st, x, w, bias,
+                                   lengths, y, T32, C32, p32, n_tt, n_sl, CG);
+            else if (K == 4)
+                hipLaunchKernelGGL((dwconv1d_fwd_lds_kernel<S, V, 4, TW>), lgrid, block, 0, st, x, w, bias,
+                                   lengths, y, T32, C32, p32, n_tt, n_sl, CG);
+            else if (K == 5)
+                hipLaunchKernelGGL((dwconv1d_fwd_lds_kernel<S, V, 5, TW>), lgrid, block, 0, st, x, w, bias,
+                                   lengths, y, T32, C32, p32, n_tt, n_sl, CG);
+            else if (K == 9)
                 hipLaunchKernelGGL((dwconv1d_fwd_lds_kernel<S, V, 9, TW>), lgrid, block, 0, st, x, w, bias,
                                    lengths, y, T32, C32, p32, n_tt, n_sl, CG);
             else

@@ -63,6 +63,10 @@ GRID = [
     (2, 97, 768, 9, True), (3, 64, 256, 15, False),
     # partial last slabs of the LDS-staged form: 50, 45 and 65 (= 64 + 1) channel groups
     (2, 70, 200, 9, True), (2, 40, 180, 15, False), (2, 70, 260, 9, True),
+    # the LDS-staged form at K = 3, 4, 5: whole and partial slabs, the minimum
+    # of 32 groups, T below the tile and a single frame
+    (3, 70, 256, 3, False), (2, 45, 200, 4, True), (2, 33, 512, 5, True), (1, 5, 256, 4, False),
+    (2, 1, 128, 3, True), (2, 65, 260, 5, False), (3, 40, 128, 4, False),
 ]
 
 
@@ -119,8 +123,8 @@ def test_guard_bands_untouched():
 @pytest.mark.parametrize("C,K", [(16, 9), (256, 9), (512, 15), (128, 5)])
 def test_unaligned_pointers_take_the_narrow_path(C, K):
     """A pointer off 16-byte alignment gets one-channel lanes; at C = 256 and
-    512 those still fill whole 64-lane slabs, so K = 9 and 15 run the
-    LDS-staged form with one channel per lane."""
+    512 those still fill whole 64-lane slabs, so the LDS-staged form runs with
+    one channel per lane (at C = 16 the register form does)."""
     B, T = 2, 40
     x, w, b, lengths = make(B, T, C, K)
     xs = torch.empty(x.numel() + 1, device=DEV)[1:].view(B, T, C)
