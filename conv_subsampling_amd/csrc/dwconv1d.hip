@@ -18,9 +18,9 @@
 // independent loads, the K taps slide over it with fp32 FMAs (the bias seeds
 // each sum), and frames at or past the length are stored as exact zeros.  A
 // tile that lies wholly past the length stores zeros without loading.
-// Output uses non-temporal stores: nothing here reads it back.  fp32 at
-// K = 9 and 15 stages the window through LDS instead (the LDS-staged form
-// below).
+// Output uses non-temporal stores: nothing here reads it back.  fp32 at the
+// compiled widths (3, 4, 5, 9, 15) with at least 32 channel groups stages the
+// window through LDS instead (the LDS-staged form below).
 #include "common.h"
 #include "launch.h"
 
