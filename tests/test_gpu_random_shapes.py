@@ -7,6 +7,8 @@ chunk, channel counts that do or do not fill whole lanes and slabs, lengths
 from 0 past T).  Sizes stay small so that the oracle finishes in well under
 a second per case.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,8 @@ from gpu_util import TOL_BF16, TOL_F32, assert_exact_zero, assert_parity, say, t
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda", 0)
-N_CASES = 64
+# Cases per family; DW_RANDOM_CASES raises it for a longer sweep.
+N_CASES = int(os.environ.get("DW_RANDOM_CASES", "64"))
 
 
 def lib():
