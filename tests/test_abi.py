@@ -289,3 +289,12 @@ def test_huge_extents_are_rejected_before_any_launch(lib):
             assert lib.dwsub_fused_fwd(P, P, N, P, N, N, Q, B, T, F, C, N) == UNSUPPORTED
             assert lib.dwsub_fused_bwd_workspace_bytes(B, T, F, C) == 0
             assert lib.dwsub_fused_bwd(P, P, N, P, N, Q, W, W, W, W, R, 1 << 40, B, T, F, C, N) == UNSUPPORTED
+
+
+def test_front_forward_refuses_a_mel_item_past_2gb(lib):
+    """The forward stages the mel input through a per-item buffer resource,
+    so one item's mel input must stay below 2^31 bytes even when its output
+    is small (one channel)."""
+    T, F = 1 << 27, 8          # 2^32 bytes of fp32 mel per item; output [2^25, 2, 1]
+    assert lib.dwsub_fused_fwd(P, P, N, P, N, N, Q, 1, T, F, 1, N) == UNSUPPORTED
+    assert "too large" in err(lib)
