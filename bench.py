@@ -412,12 +412,21 @@ def cpu_baseline(data, target_s: float):
             frames += 2 * m * st["T"]
         return secs, frames
 
-    s1, _ = one_pass(1)
-    n = int(max(1, min(g["B"], math.floor(target_s / max(s1, 1e-3)))))
-    secs, frames, reps = 0.0, 0, 0
-    while reps == 0 or secs < target_s:
-        ds, df = one_pass(n)
-        secs, frames, reps = secs + ds, frames + df, reps + 1
+    # The oracle is single-threaded C; the process is held to one core while
+    # it runs, so that nothing else (numpy's own threads) lends it another.
+    saved = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
+    if saved:
+        os.sched_setaffinity(0, {min(saved)})
+    try:
+        s1, _ = one_pass(1)
+        n = int(max(1, min(g["B"], math.floor(target_s / max(s1, 1e-3)))))
+        secs, frames, reps = 0.0, 0, 0
+        while reps == 0 or secs < target_s:
+            ds, df = one_pass(n)
+            secs, frames, reps = secs + ds, frames + df, reps + 1
+    finally:
+        if saved:
+            os.sched_setaffinity(0, saved)
     model = None
     try:
         with open("/proc/cpuinfo") as fh:
@@ -428,7 +437,7 @@ def cpu_baseline(data, target_s: float):
                 cpu_model=model, host_cpus=os.cpu_count(),
                 sample=(f"every operation of the step on the first {n} items of its batch (at most its batch "
                         f"size), same shapes and lengths, {reps} pass(es): {frames} frames in {secs:.2f} s; "
-                        f"the oracle is single-threaded C with fp64 accumulation"))
+                        f"the oracle is single-threaded C with fp64 accumulation, run on one pinned core"))
 
 
 def read_traffic():
