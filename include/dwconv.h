@@ -49,8 +49,12 @@
  *     and so is any extent (B, T, F, C, K) of 2^31 or more.  These limits
  *     are computed without integer overflow for any int64_t input.  The
  *     batch as a whole may be larger than 2^31 bytes.
- *   - The workspace queries return 0 for sizes their call would refuse
- *     (invalid, unsupported, or too large for one launch).
+ *   - The workspace queries take no storage type.  They return 0 for sizes
+ *     that their call refuses in both storage types (invalid, unsupported,
+ *     or too large for one launch).  An item within the bf16 call's size
+ *     limit but past the float32 call's (which is half as large in bytes
+ *     per element) gets its workspace size, and the float32 call then
+ *     refuses it.
  *   - Errors: every argument is validated on the host before anything is
  *     enqueued.  A failing call returns a negative dw_status, enqueues
  *     nothing (except DW_ERR_HIP, raised when a launch is rejected) and sets
@@ -80,9 +84,23 @@ typedef enum {
     DW_ERR_HIP = -4           /* the HIP runtime rejected a launch */
 } dw_status;
 
-typedef enum { DW_F32 = 0, DW_BF16 = 1 } dw_dtype;
+/* The *_INT32_LO_ and *_INT32_HI_ members are not values to pass: they give
+ * each enum the full int32 range, so that an out-of-range value from a
+ * caller is a defined value of the type (and refused with
+ * DW_ERR_INVALID_ARG) rather than undefined behaviour in the library. */
+typedef enum {
+    DW_F32 = 0,
+    DW_BF16 = 1,
+    DW_DTYPE_INT32_LO_ = -2147483647 - 1,
+    DW_DTYPE_INT32_HI_ = 2147483647
+} dw_dtype;
 
-typedef enum { DW_PAD_SYMMETRIC = 0, DW_PAD_CAUSAL = 1 } dw_pad;
+typedef enum {
+    DW_PAD_SYMMETRIC = 0,
+    DW_PAD_CAUSAL = 1,
+    DW_PAD_INT32_LO_ = -2147483647 - 1,
+    DW_PAD_INT32_HI_ = 2147483647
+} dw_pad;
 
 /* DW_ABI_VERSION of the built library. */
 int dw_abi_version(void);

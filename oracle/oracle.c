@@ -246,7 +246,7 @@ int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
                                 acc += (double)x[(b * T + t) * F + f] * (double)w0[(i * 3 + j) * C + c];
                             }
                         }
-                        acc += (double)b0[c];
+                        acc += b0 ? (double)b0[c] : 0.0;
                         v = acc > 0.0 ? acc : 0.0;
                     }
                     h[(t1 * F1 + f1) * C + c] = v;
@@ -265,7 +265,7 @@ int oracle_dwsub_front_fwd(const float *x, const float *w0, const float *b0,
                             acc += h[(t1 * F1 + f1) * C + c] * (double)w1[(i * 3 + j) * C + c];
                         }
                     }
-                    acc += (double)b1[c];
+                    acc += b1 ? (double)b1[c] : 0.0;
                     y[((b * T2 + t2) * F2 + f2) * C + c] = acc;
                 }
     }

@@ -54,6 +54,26 @@ int main(void) {
     expect(dwconv2d_bwd(p, p, NULL, q, NULL, NULL, NULL, NULL, 0, 32, 1500, 64, 256, 3, 3, 2, 1, NULL) == DW_OK,
            "2-D bwd nothing requested");
 
+    /* extents and size products that would overflow int64 are refused, not wrapped */
+    const int64_t big = INT64_MAX;
+    expect(dwconv1d_fwd(p, p, NULL, NULL, q, big, big, big, 9, DW_PAD_CAUSAL, DW_F32, NULL) == DW_ERR_UNSUPPORTED,
+           "1-D huge extents");
+    expect(dwconv1d_fwd(p, p, NULL, NULL, q, 2, (int64_t)1 << 30, (int64_t)1 << 30, 9, DW_PAD_CAUSAL, DW_F32,
+                        NULL) == DW_ERR_UNSUPPORTED, "1-D item past 2^31 bytes");
+    expect(dwconv2d_fwd(p, p, NULL, NULL, q, 1, (int64_t)1 << 30, (int64_t)1 << 30, 1 << 30, 3, 3, 2, 1, NULL)
+               == DW_ERR_UNSUPPORTED, "2-D huge product");
+    expect(dwconv2d_bwd_workspace_bytes(big, big, big, big, 3, 3, 2, 1) == 0, "2-D workspace of huge sizes");
+    expect(dwconv1d_bwd_workspace_bytes(big, 1, 1, 9) == 0, "1-D workspace of huge B");
+    expect(dwsub_fused_bwd_workspace_bytes(4, big, 80, 256) == 0, "front workspace of huge T");
+    expect(dwsub_fused_fwd_ex(p, p, NULL, p, NULL, NULL, q, big, big, big, big, DW_PAD_SYMMETRIC, DW_F32, NULL)
+               == DW_ERR_UNSUPPORTED, "front huge extents");
+    /* enum values outside the named ones are refused */
+    expect(dwconv1d_fwd(p, p, NULL, NULL, q, 2, 8, 4, 3, (dw_pad)-5, DW_F32, NULL) == DW_ERR_INVALID_ARG,
+           "1-D negative pad");
+    expect(dwconv1d_fwd(p, p, NULL, NULL, q, 2, 8, 4, 3, DW_PAD_CAUSAL, (dw_dtype)2, NULL) == DW_ERR_INVALID_ARG,
+           "1-D dtype 2");
+    expect(dwsub_fused_bwd_workspace_bytes_ex(4, 1000, 80, 256, (dw_pad)2) == 0, "front ws bad pad");
+
     if (failures == 0) printf("c abi check: ok\n");
     return failures == 0 ? 0 : 1;
 }

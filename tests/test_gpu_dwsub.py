@@ -32,9 +32,7 @@ def run(f, x=None, b0="b0", b1="b1", L="L"):
 
 
 def ref(f, b0=True, b1=True, L=True):
-    C = f["w0"].shape[2]
-    z = torch.zeros(C)
-    return oracle.dwsub_front_fwd(f["x"], f["w0"], f["b0"] if b0 else z, f["w1"], f["b1"] if b1 else z,
+    return oracle.dwsub_front_fwd(f["x"], f["w0"], f["b0"] if b0 else None, f["w1"], f["b1"] if b1 else None,
                                   f["lengths"] if L else None)
 
 
@@ -106,8 +104,7 @@ def run_bwd(f, x=None, need=("dw0", "db0", "dw1", "db1"), b0="b0", L="L", worksp
 
 
 def ref_bwd(f, b0=True, L=True):
-    C = f["w0"].shape[2]
-    return oracle.dwsub_front_bwd(f["x"], f["w0"], f["b0"] if b0 else torch.zeros(C), f["w1"],
+    return oracle.dwsub_front_bwd(f["x"], f["w0"], f["b0"] if b0 else None, f["w1"],
                                   f["lengths"] if L else None, f["dy"])
 
 

@@ -906,3 +906,52 @@ def test_1d_stream_empty_chunk_keeps_the_cache_and_nan_past_length_never_read():
     xn[1, 4:] = np.nan
     y2, c3 = oracle.dwconv1d_stream_fwd(xn, w, b, L, cache)
     assert np.array_equal(y, y2) and np.array_equal(c2, c3)
+
+
+# ------------------------------------------------------- null biases -----
+
+def _bits(a):
+    return np.ascontiguousarray(a, dtype=np.float64).view(np.uint64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_null_bias_is_zero_bias_in_every_function(causal):
+    """A NULL bias means zero for every operation that takes one: the result
+    is bit for bit the zero-bias result (sign of zero included), and matches
+    torch's chain run with zero biases."""
+    r = rng(90 + causal)
+    B, T, F, C = 2, 19, 11, 3
+    lengths = np.array([19, 8], np.int32)
+    zc = np.zeros(C, np.float32)
+    # fused front, forward: either bias NULL, and both
+    x = f32(r.standard_normal((B, T, F)))
+    w0, w1 = f32(r.standard_normal((3, 3, C))), f32(r.standard_normal((3, 3, C)))
+    b0, b1 = f32(r.standard_normal(C)), f32(r.standard_normal(C))
+    tf = torch_front_causal if causal else torch_front
+    for nb0, nb1 in ((True, False), (False, True), (True, True)):
+        got = oracle.dwsub_front_fwd(x, w0, None if nb0 else b0, w1, None if nb1 else b1, lengths, causal=causal)
+        zero = oracle.dwsub_front_fwd(x, w0, zc if nb0 else b0, w1, zc if nb1 else b1, lengths, causal=causal)
+        assert np.array_equal(_bits(got), _bits(zero))
+        close(got, tf(x, w0, zc if nb0 else b0, w1, zc if nb1 else b1, lengths))
+    # fused front, backward: NULL b0
+    T2, F2 = got.shape[1], got.shape[2]
+    dy = f32(r.standard_normal((B, T2, F2, C)))
+    for g, z in zip(oracle.dwsub_front_bwd(x, w0, None, w1, lengths, dy, causal=causal),
+                    oracle.dwsub_front_bwd(x, w0, zc, w1, lengths, dy, causal=causal)):
+        assert np.array_equal(_bits(g), _bits(z))
+    # 1-D conv and the streaming conv
+    x1 = f32(r.standard_normal((B, T, C)))
+    w9 = f32(r.standard_normal((9, C)))
+    got = oracle.dwconv1d_fwd(x1, w9, None, lengths, causal)
+    assert np.array_equal(_bits(got), _bits(oracle.dwconv1d_fwd(x1, w9, zc, lengths, causal)))
+    close(got, torch_dwconv1d(x1, w9, zc, lengths, causal))
+    cache = f32(r.standard_normal((B, 8, C)))
+    for a, z in zip(oracle.dwconv1d_stream_fwd(x1, w9, None, lengths, cache),
+                    oracle.dwconv1d_stream_fwd(x1, w9, zc, lengths, cache)):
+        assert np.array_equal(_bits(a), _bits(z))
+    # conv2d
+    x2 = f32(r.standard_normal((B, T, F, C)))
+    pads = (2, 1, 2, 1) if causal else (1, 1, 1, 1)
+    got = oracle.dwconv2d_fwd(x2, w0, None, lengths, pads=pads)
+    assert np.array_equal(_bits(got), _bits(oracle.dwconv2d_fwd(x2, w0, zc, lengths, pads=pads)))
+    close(got, torch_dwconv2d_pads(x2, w0, zc, lengths, 2, pads))
