@@ -4,6 +4,7 @@
 One step runs every operation of the path once, each at its workload's full
 size, on synthetic inputs resident in HBM:
 
+  small   dwconv1d_fwd      [2,64,8] K=9 symmetric                      fp32 (µs per launch)
   front   dwsub_fused_fwd   mel [4,1000,80] -> [4,250,20,256]           fp32
           dwsub_fused_bwd   dw0, db0, dw1, db1 of the same, dy given     fp64 sums
           dwsub_fused_*_ex  the same two in causal mode -> [4,251,21,256]
@@ -32,8 +33,17 @@ Prints one JSON line on stdout (progress goes to stderr):
   hbm          algorithmic bytes per step / step time, and its fraction of
                the 8 TB/s HBM peak
   roofline     the dominant kernel's achieved algorithmic GB/s against 8 TB/s
-  rows         the same figures for every operation (mean time per call, and
-               its median, minimum and 90th percentile over the steps)
+  forward_target  the lowest fraction of 8 TB/s among the forward depthwise
+               rows, the row that sets it, and whether every one reaches 70%
+  rows         the same figures for every operation: mean time per call from
+               HIP events (and its median, minimum and 90th percentile over
+               the steps); kernel_us, the kernel-only mean from the committed
+               rocprofv3 summary (null when the kernels changed since it was
+               taken); for HBM-bound rows, probe_us, the time of a plain
+               streaming kernel moving the row's own read and write bytes,
+               timed the same way, and of_probe = probe_us / us; max_err,
+               max |gpu - oracle| / (1 + |oracle|) on the items the CPU
+               baseline runs, and its ratio to the row's tolerance
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
 `python bench.py --summarize-profile DIR` turns rocprofv3 output under DIR
@@ -59,6 +69,10 @@ VALU_F32_PEAK_TFLOPS = 78.6       # 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 
 DOMINANT_ROW = "stage_bwd"         # the row with the largest share of the step
 DOMINANT_KERNEL = "dwconv2d_bwd_kernel"
 DOMINANT_SOURCES = ["conv_subsampling_amd/csrc/dwconv2d.hip", "conv_subsampling_amd/csrc/common.h"]
+# every source the per-row kernel-only times depend on
+KERNEL_SOURCES = ["conv_subsampling_amd/csrc/" + f for f in
+                  ("capi.hip", "common.h", "launch.h", "dwconv1d.hip", "dwconv2d.hip", "dwsub_front.hip",
+                   "reduce.hip", "probe.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dwconv2d_bwd_stage_traffic.txt")
 
 
@@ -85,6 +99,7 @@ def sources_sha(paths) -> str:
 # name within a step belongs to the k-th row listing it; the profile
 # summaries attribute dispatches to rows that way.
 ROW_KERNELS = [
+    ("conv1d_small", "dw::dwconv1d_fwd_kernel<float, 4, 9, 8>("),
     ("front", "dw::dwsub_fused_fwd_kernel<float>("),
     ("front_bwd", "dw::dwsub_fused_bwd_kernel<float, 4>("),
     ("front_causal", "dw::dwsub_fused_fwd_kernel<float>("),
@@ -203,67 +218,132 @@ def work_stage_bwd(c, pads=(1, 1, 1, 1), es=4):
 # --------------------------------------------------------------------------
 
 def build_rows(dev):
+    """Every row of the step: its work, the call the step times, and, for the
+    accuracy check and the CPU baseline, the same operation on the first n
+    items of its batch through the GPU path (`gpu`) and through the oracle
+    (`ref`: copies those items to the host and returns a call that runs the
+    oracle on them, so that only the oracle is timed)."""
     import torch
 
     import conv_subsampling_amd as dw
     import datagen
 
     rows = []
+    T32, TBF = 1e-5, 2e-2     # |gpu - ref| <= tol * (1 + |ref|): fp32 storage, bf16 storage
 
-    def add(name, op, cfg, frames, rd, wr, flops, rd_dense, fn, bound="hbm"):
+    def add(name, op, cfg, frames, rd, wr, flops, rd_dense, fn, bound="hbm", *, items, item_frames, gpu, ref, tol):
         rows.append(dict(name=name, op=op, cfg=cfg, frames=frames, read=rd, write=wr, flops=flops,
-                         read_dense=rd_dense, fn=fn, bound=bound))
+                         read_dense=rd_dense, fn=fn, bound=bound, items=items, item_frames=item_frames,
+                         gpu=gpu, ref=ref, tol=tol))
 
+    def host(t, n=None):
+        return (t if n is None else t[:n]).detach().float().cpu()
+
+    def oracle_mod():
+        import oracle
+        return oracle
+
+    # small 1-D conv: [2,64,8] K9 symmetric fp32, lengths {64, 41}
+    c1 = datagen.conv1d_small(device=dev)
+    c1L = c1["lengths"].to(dev)
+    c1y = torch.empty_like(c1["x"])
+
+    def c1_ref(n):
+        o, xs, w, b, L = oracle_mod(), host(c1["x"], n), host(c1["w"]), host(c1["b"]), c1["lengths"][:n]
+        return lambda: [o.dwconv1d_fwd(xs, w, b, L, False)]
+
+    add("conv1d_small", "dwconv1d_fwd", "[2,64,8] K9 symmetric fp32 (launch-latency bound)", c1["B"] * c1["T"],
+        *work_conv1d(c1, 4), lambda: dw.dwconv1d_fwd(c1["x"], c1["w"], c1["b"], c1L, y=c1y, causal=False),
+        bound="latency", items=c1["B"], item_frames=c1["T"],
+        gpu=lambda n: [dw.dwconv1d_fwd(c1["x"][:n], c1["w"], c1["b"], c1L[:n], causal=False)],
+        ref=c1_ref, tol=[T32])
+
+    # fused front, symmetric and causal, forward and backward
     f = datagen.fused_front(device=dev)
     fL = f["lengths"].to(dev)
     fy = torch.empty((f["B"], 250, 20, f["C"]), device=dev)
-    add("front", "dwsub_fused_fwd", "mel [4,1000,80] -> [4,250,20,256] fp32", f["B"] * f["T"], *work_front(f),
-        lambda: dw.dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], fL, y=fy), bound="alu")
-
     fdy = datagen.normal((f["B"], 250, 20, f["C"]), 1.0, "c2/dy", device=dev)
+    fcdy = datagen.normal((f["B"], 251, 21, f["C"]), 1.0, "c2/dy", device=dev)
     fg = [torch.empty(sh, device=dev) for sh in ((3, 3, f["C"]), (f["C"],), (3, 3, f["C"]), (f["C"],))]
     fws = torch.empty((dw.dwsub_fused_bwd_workspace_bytes(f["B"], f["T"], f["F"], f["C"]),), dtype=torch.uint8,
                       device=dev)
-    add("front_bwd", "dwsub_fused_bwd", "dw0,db0,dw1,db1 of the front, dy [4,250,20,256] fp64 accumulation",
-        f["B"] * f["T"], *work_front_bwd(f),
-        lambda: dw.dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], fL, fdy, *fg, workspace=fws), bound="alu")
-    f["dy"] = fdy
     fcy = torch.empty((f["B"], 251, 21, f["C"]), device=dev)
-    fcdy = datagen.normal((f["B"], 251, 21, f["C"]), 1.0, "c2/dy", device=dev)
     fcws = torch.empty((dw.dwsub_fused_bwd_workspace_bytes(f["B"], f["T"], f["F"], f["C"], causal=True),),
                        dtype=torch.uint8, device=dev)
-    add("front_causal", "dwsub_fused_fwd_ex", "mel [4,1000,80] -> [4,251,21,256] causal fp32", f["B"] * f["T"],
-        *work_front(f, 1),
-        lambda: dw.dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], fL, y=fcy, causal=True), bound="alu")
-    add("front_bwd_causal", "dwsub_fused_bwd_ex", "dw0,db0,dw1,db1 of the causal front, dy [4,251,21,256]",
-        f["B"] * f["T"], *work_front_bwd(f, 1),
-        lambda: dw.dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], fL, fcdy, *fg, workspace=fcws, causal=True),
-        bound="alu")
-    f["dy_causal"] = fcdy
+    fp = {k: host(f[k]) for k in ("w0", "b0", "w1", "b1")}
+
+    def front_ref(causal):
+        def make(n):
+            o, xs, L = oracle_mod(), host(f["x"], n), f["lengths"][:n]
+            return lambda: [o.dwsub_front_fwd(xs, fp["w0"], fp["b0"], fp["w1"], fp["b1"], L, causal=causal)]
+        return make
+
+    def front_bwd_ref(causal):
+        def make(n):
+            o, xs, L = oracle_mod(), host(f["x"], n), f["lengths"][:n]
+            dys = host(fcdy if causal else fdy, n)
+            return lambda: list(o.dwsub_front_bwd(xs, fp["w0"], fp["b0"], fp["w1"], L, dys, causal=causal))
+        return make
+
+    for causal in (False, True):
+        sfx = "_causal" if causal else ""
+        shape = "[4,251,21,256] causal" if causal else "[4,250,20,256]"
+        add("front" + sfx, "dwsub_fused_fwd" + ("_ex" if causal else ""), f"mel [4,1000,80] -> {shape} fp32",
+            f["B"] * f["T"], *work_front(f, int(causal)),
+            (lambda c=causal: dw.dwsub_fused_fwd(f["x"], f["w0"], f["b0"], f["w1"], f["b1"], fL,
+                                                 y=fcy if c else fy, causal=c)),
+            bound="alu", items=f["B"], item_frames=f["T"],
+            gpu=(lambda n, c=causal: [dw.dwsub_fused_fwd(f["x"][:n], f["w0"], f["b0"], f["w1"], f["b1"], fL[:n],
+                                                         causal=c)]),
+            ref=front_ref(causal), tol=[T32])
+        add("front_bwd" + sfx, "dwsub_fused_bwd" + ("_ex" if causal else ""),
+            f"dw0,db0,dw1,db1 of the front, dy {shape}, fp64 accumulation", f["B"] * f["T"],
+            *work_front_bwd(f, int(causal)),
+            (lambda c=causal: dw.dwsub_fused_bwd(f["x"], f["w0"], f["b0"], f["w1"], fL, fcdy if c else fdy, *fg,
+                                                 workspace=fcws if c else fws, causal=c)),
+            bound="alu", items=f["B"], item_frames=f["T"],
+            gpu=(lambda n, c=causal: list(dw.dwsub_fused_bwd(f["x"][:n], f["w0"], f["b0"], f["w1"], fL[:n],
+                                                             (fcdy if c else fdy)[:n], causal=c))),
+            ref=front_bwd_ref(causal), tol=[T32] * 4)
+
+    def conv1d_rows(name, cfg, d, es, tol, causal):
+        L = d["lengths"].to(dev)
+        y = torch.empty_like(d["x"])
+        w, b = host(d["w"]), host(d["b"])
+
+        def make(n):
+            o, xs, Ls = oracle_mod(), host(d["x"], n), d["lengths"][:n]
+            return lambda: [o.dwconv1d_fwd(xs, w, b, Ls, causal)]
+        add(name, "dwconv1d_fwd", cfg, d["B"] * d["T"], *work_conv1d(d, es),
+            lambda: dw.dwconv1d_fwd(d["x"], d["w"], d["b"], L, y=y, causal=causal),
+            items=d["B"], item_frames=d["T"],
+            gpu=lambda n: [dw.dwconv1d_fwd(d["x"][:n], d["w"], d["b"], L[:n], causal=causal)], ref=make, tol=[tol])
 
     e = datagen.conv1d_encoder_bf16(device=dev)
-    eL = e["lengths"].to(dev)
-    ey = torch.empty_like(e["x"])
-    add("conv1d_bf16", "dwconv1d_fwd", "[16,750,1024] K9 symmetric bf16", e["B"] * e["T"], *work_conv1d(e, 2),
-        lambda: dw.dwconv1d_fwd(e["x"], e["w"], e["b"], eL, y=ey, causal=False))
+    conv1d_rows("conv1d_bf16", "[16,750,1024] K9 symmetric bf16", e, 2, TBF, False)
 
     sweep = []
     for K, C in [(3, 512), (4, 512), (5, 512), (9, 512), (15, 512), (9, 200)]:
-        s = datagen.conv1d_causal_sweep(K, device=dev, C=C)
-        sweep.append(s)
-        sL = s["lengths"].to(dev)
-        sy = torch.empty_like(s["x"])
-        add(f"conv1d_causal_K{K}_C{C}", "dwconv1d_fwd", f"[32,1500,{C}] K{K} causal fp32", s["B"] * s["T"],
-            *work_conv1d(s, 4),
-            (lambda s=s, sL=sL, sy=sy: dw.dwconv1d_fwd(s["x"], s["w"], s["b"], sL, y=sy, causal=True)))
+        sd = datagen.conv1d_causal_sweep(K, device=dev, C=C)
+        sweep.append(sd)
+        conv1d_rows(f"conv1d_causal_K{K}_C{C}", f"[32,1500,{C}] K{K} causal fp32", sd, 4, T32, True)
 
     st = datagen.conv1d_stream(device=dev)
     stL = st["lengths"].to(dev)
     sty = torch.empty_like(st["x"])
     stc = torch.empty_like(st["cache"])
+    stw, stb = host(st["w"]), host(st["b"])
+
+    def stream_ref(n):
+        o, xs, cs, Ls = oracle_mod(), host(st["x"], n), host(st["cache"], n), st["lengths"][:n]
+        return lambda: list(o.dwconv1d_stream_fwd(xs, stw, stb, Ls, cs))
+
     add("conv1d_stream_bf16", "dwconv1d_stream_fwd", "1024 streams x 8-frame chunks, C1024 K9, K-1 frame cache, bf16",
         st["B"] * st["Tc"], *work_conv1d_stream(st, 2),
-        lambda: dw.dwconv1d_stream_fwd(st["x"], st["w"], st["b"], stL, st["cache"], cache_out=stc, y=sty))
+        lambda: dw.dwconv1d_stream_fwd(st["x"], st["w"], st["b"], stL, st["cache"], cache_out=stc, y=sty),
+        items=st["B"], item_frames=st["Tc"],
+        gpu=lambda n: list(dw.dwconv1d_stream_fwd(st["x"][:n], st["w"], st["b"], stL[:n], st["cache"][:n])),
+        ref=stream_ref, tol=[TBF, TBF])
 
     s9 = sweep[3]
     assert s9["K"] == 9 and s9["C"] == 512
@@ -274,142 +354,91 @@ def build_rows(dev):
     bdb = torch.empty((s9["C"],), device=dev)
     bws = torch.empty((dw.dwconv1d_bwd_workspace_bytes(s9["B"], s9["T"], s9["C"], 9),), dtype=torch.uint8,
                       device=dev)
+    s9w = host(s9["w"])
+
+    def bwd1d_ref(n):
+        o, xs, dys, Ls = oracle_mod(), host(s9["x"], n), host(s9["dy"], n), s9["lengths"][:n]
+        return lambda: list(o.dwconv1d_bwd(xs, s9w, Ls, dys, True))
+
     add("conv1d_bwd_K9_C512", "dwconv1d_bwd", "dx,dw,db of [32,1500,512] K9 causal fp32, fp64 sums",
         s9["B"] * s9["T"], *work_conv1d_bwd(s9),
         lambda: dw.dwconv1d_bwd(s9["x"], s9["w"], s9L, s9["dy"], dx=bdx, dw=bdw, db=bdb, workspace=bws,
-                                causal=True))
+                                causal=True),
+        items=s9["B"], item_frames=s9["T"],
+        gpu=lambda n: list(dw.dwconv1d_bwd(s9["x"][:n], s9["w"], s9L[:n], s9["dy"][:n], causal=True)),
+        ref=bwd1d_ref, tol=[T32] * 3)
 
+    # the conv2d stage: symmetric fp32, causal fp32, symmetric bf16; then the third stage
     g = datagen.conv2d_stage(device=dev)
     gL = g["lengths"].to(dev)
-    gy = torch.empty((g["B"], 750, 32, g["C"]), device=dev)
-    gdx = torch.empty_like(g["x"])
-    gdw = torch.empty((3, 3, g["C"]), device=dev)
-    gdb = torch.empty((g["C"],), device=dev)
-    ws = torch.empty((dw.dwconv2d_bwd_workspace_bytes(g["B"], g["T"], g["F"], g["C"]),), dtype=torch.uint8,
-                     device=dev)
-    add("stage_fwd", "dwconv2d_fwd", "[32,1500,64,256] -> [32,750,32,256] fp32", g["B"] * g["T"],
-        *work_stage_fwd(g), lambda: dw.dwconv2d_fwd(g["x"], g["w"], g["b"], gL, y=gy))
-    add("stage_bwd", "dwconv2d_bwd", "dx,dw,db of [32,1500,64,256] fp32", g["B"] * g["T"], *work_stage_bwd(g),
-        lambda: dw.dwconv2d_bwd(g["x"], g["w"], gL, g["dy"], dx=gdx, dw=gdw, db=gdb, workspace=ws))
-
-    # the same stage with causal padding (fp32), and with bf16 storage (symmetric)
     causal = dw.CAUSAL_PADS_2D
     To_c, Fo_c = dw.conv2d_out_shape(g["T"], g["F"], pads=causal)
     gc = dict(g, dy=datagen.normal((g["B"], To_c, Fo_c, g["C"]), 1.0, "c5/dy", device=dev))
-    gcy = torch.empty((g["B"], To_c, Fo_c, g["C"]), device=dev)
-    wsc = torch.empty((dw.dwconv2d_bwd_workspace_bytes(g["B"], g["T"], g["F"], g["C"], pads=causal),),
-                      dtype=torch.uint8, device=dev)
-    add("stage_fwd_causal", "dwconv2d_fwd_ex", "[32,1500,64,256] -> [32,751,33,256] causal pads fp32",
-        g["B"] * g["T"], *work_stage_fwd(g, causal),
-        lambda: dw.dwconv2d_fwd(g["x"], g["w"], g["b"], gL, y=gcy, pads=causal))
-    add("stage_bwd_causal", "dwconv2d_bwd_ex", "dx,dw,db of [32,1500,64,256] causal pads fp32", g["B"] * g["T"],
-        *work_stage_bwd(g, causal),
-        lambda: dw.dwconv2d_bwd(g["x"], g["w"], gL, gc["dy"], dx=gdx, dw=gdw, db=gdb, workspace=wsc, pads=causal))
     h = {k: (v.to(torch.bfloat16) if k in ("x", "w", "b", "dy") else v) for k, v in g.items()}
-    hy = torch.empty((g["B"], 750, 32, g["C"]), dtype=torch.bfloat16, device=dev)
-    hdx = torch.empty_like(h["x"])
-    add("stage_fwd_bf16", "dwconv2d_fwd_ex", "[32,1500,64,256] -> [32,750,32,256] bf16 storage", g["B"] * g["T"],
-        *work_stage_fwd(g, es=2), lambda: dw.dwconv2d_fwd(h["x"], h["w"], h["b"], gL, y=hy))
-    add("stage_bwd_bf16", "dwconv2d_bwd_ex", "dx,dw,db of [32,1500,64,256] bf16 storage, fp32 dw/db",
-        g["B"] * g["T"], *work_stage_bwd(g, es=2),
-        lambda: dw.dwconv2d_bwd(h["x"], h["w"], gL, h["dy"], dx=hdx, dw=gdw, db=gdb, workspace=ws))
-    # 8x subsampling's third stride-2 stage, on the 4x front output of a 15 s batch
     g3 = datagen.conv2d_stage(device=dev, B=32, T=375, F=20, C=256)
-    g3L = g3["lengths"].to(dev)
-    g3y = torch.empty((32, 188, 10, 256), device=dev)
-    g3dx = torch.empty_like(g3["x"])
-    ws3 = torch.empty((dw.dwconv2d_bwd_workspace_bytes(32, 375, 20, 256),), dtype=torch.uint8, device=dev)
-    add("stage3_fwd", "dwconv2d_fwd", "[32,375,20,256] -> [32,188,10,256] fp32 (8x third stage)", g3["B"] * g3["T"],
-        *work_stage_fwd(g3), lambda: dw.dwconv2d_fwd(g3["x"], g3["w"], g3["b"], g3L, y=g3y))
-    add("stage3_bwd", "dwconv2d_bwd", "dx,dw,db of [32,375,20,256] fp32 (8x third stage)", g3["B"] * g3["T"],
-        *work_stage_bwd(g3),
-        lambda: dw.dwconv2d_bwd(g3["x"], g3["w"], g3L, g3["dy"], dx=g3dx, dw=gdw, db=gdb, workspace=ws3))
-    data = dict(front=f, conv1d_bf16=e, sweep=sweep, stage=g, stage_causal=gc, stage_bf16=h, stream=st, stage3=g3)
+    gdw = torch.empty((3, 3, g["C"]), device=dev)
+    gdb = torch.empty((g["C"],), device=dev)
+    gdx = torch.empty_like(g["x"])
+
+    def stage_rows(name, cfg, d, pads, es, tol):
+        L = d["lengths"].to(dev)
+        To, Fo = dw.conv2d_out_shape(d["T"], d["F"], pads=pads)
+        y = torch.empty((d["B"], To, Fo, d["C"]), dtype=d["x"].dtype, device=dev)
+        dx = gdx if d["x"].shape == gdx.shape and d["x"].dtype == gdx.dtype else torch.empty_like(d["x"])
+        ws = torch.empty((dw.dwconv2d_bwd_workspace_bytes(d["B"], d["T"], d["F"], d["C"], pads=pads),),
+                         dtype=torch.uint8, device=dev)
+        w, b = host(d["w"]), host(d["b"])
+        pd = "" if pads is None and es == 4 else "_ex"
+
+        def fref(n):
+            o, xs, Ls = oracle_mod(), host(d["x"], n), d["lengths"][:n]
+            return lambda: [o.dwconv2d_fwd(xs, w, b, Ls, pads=pads)]
+
+        def bref(n):
+            o, xs, dys, Ls = oracle_mod(), host(d["x"], n), host(d["dy"], n), d["lengths"][:n]
+            return lambda: list(o.dwconv2d_bwd(xs, w, Ls, dys, pads=pads))
+
+        add(f"{name}_fwd" + cfg[0], "dwconv2d_fwd" + pd, cfg[1], d["B"] * d["T"], *work_stage_fwd(d, pads or (1, 1, 1, 1), es),
+            lambda: dw.dwconv2d_fwd(d["x"], d["w"], d["b"], L, y=y, pads=pads),
+            items=d["B"], item_frames=d["T"],
+            gpu=lambda n: [dw.dwconv2d_fwd(d["x"][:n], d["w"], d["b"], L[:n], pads=pads)], ref=fref, tol=[tol])
+        add(f"{name}_bwd" + cfg[0], "dwconv2d_bwd" + pd, cfg[2], d["B"] * d["T"], *work_stage_bwd(d, pads or (1, 1, 1, 1), es),
+            lambda: dw.dwconv2d_bwd(d["x"], d["w"], L, d["dy"], dx=dx, dw=gdw, db=gdb, workspace=ws, pads=pads),
+            items=d["B"], item_frames=d["T"],
+            gpu=lambda n: list(dw.dwconv2d_bwd(d["x"][:n], d["w"], L[:n], d["dy"][:n], pads=pads)), ref=bref,
+            tol=[tol, T32, T32])
+
+    stage_rows("stage", ("", "[32,1500,64,256] -> [32,750,32,256] fp32", "dx,dw,db of [32,1500,64,256] fp32"),
+               g, None, 4, T32)
+    stage_rows("stage", ("_causal", "[32,1500,64,256] -> [32,751,33,256] causal pads fp32",
+                         "dx,dw,db of [32,1500,64,256] causal pads fp32"), gc, causal, 4, T32)
+    stage_rows("stage", ("_bf16", "[32,1500,64,256] -> [32,750,32,256] bf16 storage",
+                         "dx,dw,db of [32,1500,64,256] bf16 storage, fp32 dw/db"), h, None, 2, TBF)
+    stage_rows("stage3", ("", "[32,375,20,256] -> [32,188,10,256] fp32 (8x third stage)",
+                          "dx,dw,db of [32,375,20,256] fp32 (8x third stage)"), g3, None, 4, T32)
     assert [r["name"] for r in rows] == [n for n, _ in ROW_KERNELS], "ROW_KERNELS is out of date"
-    return rows, data
+    return rows
 
 
-def cpu_baseline(data, target_s: float):
-    """Time the CPU oracle on whole items of each workload (same shapes and
-    lengths), single-threaded, and scale to frames per second."""
-    import oracle
+def oracle_check(rows, target_s: float, time_it: bool = True):
+    """Run the oracle on the first n items of every row's batch (n chosen so
+    that one pass over the rows takes about target_s of CPU time), timed on
+    one pinned core, and compare the GPU path on the same items with it.
 
-    host = lambda t, n: t[:n].detach().float().cpu()
-    # parameters copied to the host once, outside the timed calls
-    hp = lambda d: {k: (v.detach().float().cpu() if hasattr(v, "detach") and k != "x" and k != "dy" else v)
-                    for k, v in d.items()}
-    f, e, g = hp(data["front"]), hp(data["conv1d_bf16"]), hp(data["stage"])
-    f["x"], f["dy"], f["dy_causal"] = data["front"]["x"], data["front"]["dy"], data["front"]["dy_causal"]
-    e["x"], g["x"], g["dy"] = data["conv1d_bf16"]["x"], data["stage"]["x"], data["stage"]["dy"]
-    gc = dict(g, dy=data["stage_causal"]["dy"])
-    gh = hp(data["stage_bf16"])                    # bf16 values, widened exactly on the host
-    gh["x"], gh["dy"] = data["stage_bf16"]["x"], data["stage_bf16"]["dy"]
-    g3 = hp(data["stage3"])
-    g3["x"], g3["dy"] = data["stage3"]["x"], data["stage3"]["dy"]
-    sm = hp(data["stream"])
-    sm["x"], sm["cache"] = data["stream"]["x"], data["stream"]["cache"]
-    sweep = []
-    for s in data["sweep"]:
-        hs = hp(s)
-        hs["x"] = s["x"]
-        if "dy" in s:
-            hs["dy"] = s["dy"]
-        sweep.append(hs)
+    Returns (cpu_baseline dict or None, {row: max |gpu - ref| / (1 + |ref|)})."""
+    import torch
 
-    def one_pass(n):
-        """The oracle on the first min(n, B) items of every operation's batch."""
+    def one_pass(n, keep):
         secs, frames = 0.0, 0
-        m = min(n, f["B"])
-        xs = host(f["x"], m)
-        t = time.perf_counter()
-        oracle.dwsub_front_fwd(xs, f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"][:m])
-        secs += time.perf_counter() - t
-        frames += m * f["T"]
-        m = min(n, f["B"])
-        xs, dys = host(f["x"], m), host(f["dy"], m)
-        t = time.perf_counter()
-        oracle.dwsub_front_bwd(xs, f["w0"], f["b0"], f["w1"], f["lengths"][:m], dys)
-        secs += time.perf_counter() - t
-        frames += m * f["T"]
-        dys = host(f["dy_causal"], m)
-        t = time.perf_counter()
-        oracle.dwsub_front_fwd(xs, f["w0"], f["b0"], f["w1"], f["b1"], f["lengths"][:m], causal=True)
-        oracle.dwsub_front_bwd(xs, f["w0"], f["b0"], f["w1"], f["lengths"][:m], dys, causal=True)
-        secs += time.perf_counter() - t
-        frames += 2 * m * f["T"]
-        m = min(n, e["B"])
-        xs = host(e["x"], m)
-        t = time.perf_counter()
-        oracle.dwconv1d_fwd(xs, e["w"], e["b"], e["lengths"][:m], False)
-        secs += time.perf_counter() - t
-        frames += m * e["T"]
-        for s in sweep:
-            m = min(n, s["B"])
-            xs = host(s["x"], m)
+        for r in rows:
+            m = min(n, r["items"])
+            call = r["ref"](m)
             t = time.perf_counter()
-            oracle.dwconv1d_fwd(xs, s["w"], s["b"], s["lengths"][:m], True)
+            out = call()
             secs += time.perf_counter() - t
-            frames += m * s["T"]
-            if "dy" in s:
-                dys = host(s["dy"], m)
-                t = time.perf_counter()
-                oracle.dwconv1d_bwd(xs, s["w"], s["lengths"][:m], dys, True)
-                secs += time.perf_counter() - t
-                frames += m * s["T"]
-        m = min(n, sm["B"])
-        xs, cs = host(sm["x"], m), host(sm["cache"], m)
-        t = time.perf_counter()
-        oracle.dwconv1d_stream_fwd(xs, sm["w"], sm["b"], sm["lengths"][:m], cs)
-        secs += time.perf_counter() - t
-        frames += m * sm["Tc"]
-        m = min(n, g["B"])
-        for st, pads in ((g, None), (gc, (2, 1, 2, 1)), (gh, None), (g3, None)):
-            xs, dys = host(st["x"], m), host(st["dy"], m)
-            t = time.perf_counter()
-            oracle.dwconv2d_fwd(xs, st["w"], st["b"], st["lengths"][:m], pads=pads)
-            oracle.dwconv2d_bwd(xs, st["w"], st["lengths"][:m], dys, pads=pads)
-            secs += time.perf_counter() - t
-            frames += 2 * m * st["T"]
+            frames += m * r["item_frames"]
+            if keep is not None:
+                keep[r["name"]] = (m, out)
         return secs, frames
 
     # The oracle is single-threaded C; the process is held to one core while
@@ -417,27 +446,46 @@ def cpu_baseline(data, target_s: float):
     saved = os.sched_getaffinity(0) if hasattr(os, "sched_getaffinity") else None
     if saved:
         os.sched_setaffinity(0, {min(saved)})
+    refs = {}
     try:
-        s1, _ = one_pass(1)
-        n = int(max(1, min(g["B"], math.floor(target_s / max(s1, 1e-3)))))
-        secs, frames, reps = 0.0, 0, 0
-        while reps == 0 or secs < target_s:
-            ds, df = one_pass(n)
-            secs, frames, reps = secs + ds, frames + df, reps + 1
+        s1, _ = one_pass(1, refs if not time_it else None)
+        n, secs, frames, reps = 1, 0.0, 0, 0
+        if time_it:
+            n = int(max(1, min(32, math.floor(target_s / max(s1, 1e-3)))))
+            while reps == 0 or secs < target_s:
+                ds, df = one_pass(n, refs)
+                secs, frames, reps = secs + ds, frames + df, reps + 1
     finally:
         if saved:
             os.sched_setaffinity(0, saved)
+
+    errs = {}
+    for r in rows:
+        m, ref = refs[r["name"]]
+        got = r["gpu"](m)
+        torch.cuda.synchronize()
+        worst, worst_rel = 0.0, 0.0
+        for gt, rf, tol in zip(got, ref, r["tol"]):
+            gv = gt.detach().double().cpu().numpy()
+            assert gv.shape == rf.shape, (r["name"], gv.shape, rf.shape)
+            e = float((abs(gv - rf) / (1.0 + abs(rf))).max()) if gv.size else 0.0
+            e = e if math.isfinite(e) else float("inf")
+            worst, worst_rel = max(worst, e), max(worst_rel, e / tol)
+        errs[r["name"]] = dict(items=m, max_err=worst, max_err_over_tol=worst_rel)
+    if not time_it:
+        return None, errs
     model = None
     try:
         with open("/proc/cpuinfo") as fh:
             model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
     except OSError:
         pass
-    return dict(value=round(frames / secs, 1), unit="frames/s", cores=1, kind="oracle",
-                cpu_model=model, host_cpus=os.cpu_count(),
-                sample=(f"every operation of the step on the first {n} items of its batch (at most its batch "
-                        f"size), same shapes and lengths, {reps} pass(es): {frames} frames in {secs:.2f} s; "
-                        f"the oracle is single-threaded C with fp64 accumulation, run on one pinned core"))
+    cpu = dict(value=round(frames / secs, 1), unit="frames/s", cores=1, kind="oracle",
+               cpu_model=model, host_cpus=os.cpu_count(),
+               sample=(f"every row of the step on the first {n} items of its batch (at most its batch size), "
+                       f"same shapes and lengths, {reps} pass(es): {frames} frames in {secs:.2f} s; the oracle "
+                       f"is single-threaded C with fp64 accumulation, run on one pinned core"))
+    return cpu, errs
 
 
 def read_traffic():
@@ -458,6 +506,47 @@ def read_traffic():
         return None
 
 
+def load_probe():
+    """The HBM streaming probe library (include/dwprobe.h), or None if it is
+    not built."""
+    import ctypes
+    path = os.path.join(ROOT, "conv_subsampling_amd", "libdwprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.dw_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                    ctypes.c_void_p]
+    lib.dw_probe_stream.restype = ctypes.c_int
+    return lib
+
+
+def read_kernel_stats(path=None):
+    """Per-row kernel-only mean durations (us) from the committed rocprofv3
+    summary, if it was taken on the current kernel sources; else {}."""
+    path = path or os.path.join(ROOT, "profiles", "kernel_stats_bench_step.txt")
+    if not os.path.exists(path):
+        return {}
+    text = open(path).read().splitlines()
+    sha = next((ln.split("=", 1)[1].strip() for ln in text if ln.startswith("# src_sha256=")), None)
+    if sha != sources_sha(KERNEL_SOURCES):
+        return {}
+    names = {n for n, _ in ROW_KERNELS}
+    out = {}
+    for ln in text:
+        parts = ln.split()  # row, kernel (may hold spaces), n, avg_us, min_us, max_us
+        if len(parts) >= 6 and parts[0] in names and parts[-4].isdigit():
+            try:
+                out[parts[0]] = float(parts[-3])
+            except ValueError:
+                pass
+    return out
+
+
+FORWARD_BAR = 0.70   # forward depthwise kernels: at least 70% of peak HBM bandwidth
+FORWARD_ROWS = [n for n, _ in ROW_KERNELS if ("conv1d_" in n and "bwd" not in n and n != "conv1d_small")
+                or n.startswith("stage") and "_fwd" in n]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -465,6 +554,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM streaming probe pass")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 output under DIR and exit")
@@ -482,7 +572,7 @@ def main():
 
     dev = torch.device("cuda", 0)
     log("building workloads ...")
-    rows, data = build_rows(dev)
+    rows = build_rows(dev)
     torch.cuda.synchronize()
     if args.calib_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -529,6 +619,45 @@ def main():
     torch.cuda.synchronize()
     log(f"per-row pass of {args.steps} steps done")
 
+    # The probe pass: for every HBM-bound row, the streaming probe moves the
+    # row's algorithmic read and write bytes, timed with the same events.
+    # Successive probes use successive regions of two 4 GiB buffers, so every
+    # probe reads and writes memory no other call touched for at least 4 GiB
+    # of traffic: cold, like the rows inside the step.
+    probe_us = {}
+    plib = None if args.no_probe else load_probe()
+    if plib is not None:
+        span = 4 << 30
+        psrc = torch.empty(span, dtype=torch.uint8, device=dev)
+        pdst = torch.empty(span, dtype=torch.uint8, device=dev)
+        psrc.fill_(1)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        prow = [r for r in rows if r["bound"] == "hbm" and r["read"] <= span and r["write"] <= span]
+        pev = {r["name"]: [] for r in prow}
+        off = 0
+        for s in range(args.steps + 1):
+            for r in prow:
+                need = max(r["read"], r["write"])
+                if off + need > span:
+                    off = 0
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                rc = plib.dw_probe_stream(psrc.data_ptr() + off, pdst.data_ptr() + off, r["read"], r["write"], 2,
+                                          stream)
+                b.record()
+                if rc != 0:
+                    raise RuntimeError(f"dw_probe_stream failed ({rc}) for {r['name']}")
+                if s > 0:  # the first round warms the probe up
+                    pev[r["name"]].append((a, b))
+                off += (need + 4095) // 4096 * 4096
+        torch.cuda.synchronize()
+        for name, evs in pev.items():
+            ts = [a.elapsed_time(b) * 1e3 for a, b in evs]
+            probe_us[name] = sum(ts) / len(ts)
+        del psrc, pdst
+        log(f"probe pass of {args.steps} steps done")
+
+    kstats = read_kernel_stats()
     ms_step = wall * 1e3 / args.steps
     frames = sum(r["frames"] for r in rows)
     alg = sum(r["read"] + r["write"] for r in rows)
@@ -539,18 +668,23 @@ def main():
         b = r["read"] + r["write"]
         row = dict(row=r["name"], op=r["op"], config=r["cfg"], us=round(us, 2), us_median=round(ts[len(ts) // 2], 2),
                    us_min=round(ts[0], 2), us_p90=round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 2),
+                   kernel_us=kstats.get(r["name"]),
                    frames_per_s=round(r["frames"] / (us * 1e-6)), alg_bytes=b,
                    gbps=round(b / (us * 1e-6) / 1e9, 1), hbm_frac=round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                    dense_bytes=r["read_dense"] + r["write"],
                    dense_gbps=round((r["read_dense"] + r["write"]) / (us * 1e-6) / 1e9, 1))
+        if r["name"] in probe_us:
+            pu = probe_us[r["name"]]
+            row.update(probe_us=round(pu, 2), probe_gbps=round(b / (pu * 1e-6) / 1e9, 1),
+                       of_probe=round(pu / us, 4))
+        row["bound"] = r["bound"]
         if r["bound"] == "alu":
             tf = r["flops"] / (us * 1e-6) / 1e12
-            row.update(bound="alu", alg_flops=r["flops"], tflops=round(tf, 2),
-                       alu_frac=round(tf / VALU_F32_PEAK_TFLOPS, 4))
-        else:
-            row.update(bound="hbm")
+            row.update(alg_flops=r["flops"], tflops=round(tf, 2), alu_frac=round(tf / VALU_F32_PEAK_TFLOPS, 4))
         out_rows.append(row)
-        log(f"  {r['name']:<22} {us:9.2f} us  {row['gbps']:8.1f} GB/s  ({100 * row['hbm_frac']:.1f}% of 8 TB/s)")
+        extra = f"  probe {row['probe_us']:7.2f} us ({100 * row['of_probe']:.0f}%)" if "probe_us" in row else ""
+        log(f"  {r['name']:<24} {us:9.2f} us  {row['gbps']:8.1f} GB/s  ({100 * row['hbm_frac']:.1f}% of 8 TB/s)"
+            + extra)
 
     dom = next(r for r in out_rows if r["row"] == DOMINANT_ROW)
     dom_mean = sum(dom_us) / len(dom_us)
@@ -558,12 +692,23 @@ def main():
     roofline = dict(kernel=DOMINANT_KERNEL, bound="hbm", achieved=dom_gbps, peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(dom_gbps / HBM_PEAK_GBPS, 4), traffic=read_traffic(),
                     launch_us=round(dom_mean, 2), alg_bytes_per_launch=dom["alg_bytes"])
+    fwd = [r for r in out_rows if r["row"] in FORWARD_ROWS]
+    low = min(fwd, key=lambda r: r["hbm_frac"])
+    forward_target = dict(bar=FORWARD_BAR, min_hbm_frac=low["hbm_frac"], row=low["row"],
+                          rows_below=[r["row"] for r in fwd if r["hbm_frac"] < FORWARD_BAR],
+                          met=all(r["hbm_frac"] >= FORWARD_BAR for r in fwd))
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample ...")
-        cpu = cpu_baseline(data, args.cpu_seconds)
+    log("running the oracle on a sample of every row, and the GPU path on the same items ...")
+    cpu, errs = oracle_check(rows, args.cpu_seconds, time_it=not args.no_cpu_baseline)
+    for row in out_rows:
+        e = errs[row["row"]]
+        row.update(max_err=float(f"{e['max_err']:.3e}"), max_err_over_tol=round(e["max_err_over_tol"], 4),
+                   err_items=e["items"])
+    if cpu:
         log(f"  oracle: {cpu['value']:.0f} frames/s ({cpu['sample']})")
+    worst = max(out_rows, key=lambda r: r["max_err_over_tol"])
+    log(f"  worst error against the oracle: {worst['row']} {worst['max_err']:.2e} "
+        f"({worst['max_err_over_tol']:.3f} of its tolerance)")
 
     line = {
         "metric": "depthwise conv frames/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
@@ -576,13 +721,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "mixed: f32 arithmetic on f32 or bf16 storage (bf16 rows say so); f64 weight-gradient sums",
         "data": "synthetic (seeded; log-mel-shaped inputs, lengths ~U[T/2,T])",
         "config": {
-            "workload": "encoder depthwise path: fused front [4,1000,80] fwd+bwd (symmetric and causal); conv-module dwconv1d [16,750,1024] K9 "
-                        "bf16; causal dwconv1d [32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; streaming dwconv1d 1024x8x1024 K9 bf16 with cache; depthwise conv2d "
-                        "stage [32,1500,64,256] fwd+bwd (symmetric fp32, causal fp32, symmetric bf16); third stage "
-                        "[32,375,20,256] fwd+bwd",
+            "workload": "encoder depthwise path: small dwconv1d [2,64,8] K9; fused front [4,1000,80] fwd+bwd "
+                        "(symmetric and causal); conv-module dwconv1d [16,750,1024] K9 bf16; causal dwconv1d "
+                        "[32,1500,512] K3/4/5/9/15 (K9 fwd+bwd) and [32,1500,200] K9; streaming dwconv1d "
+                        "1024x8x1024 K9 bf16 with cache; depthwise conv2d stage [32,1500,64,256] fwd+bwd "
+                        "(symmetric fp32, causal fp32, symmetric bf16); third stage [32,375,20,256] fwd+bwd",
             "frames_per_step": frames,
             "alg_bytes_per_step": alg,
             "parallelism": "single GPU",
@@ -590,6 +736,8 @@ def main():
         "hbm": {"achieved_gbps": round(alg / (ms_step * 1e-3) / 1e9, 1), "peak_gbps": HBM_PEAK_GBPS,
                 "frac": round(alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
+        "forward_target": forward_target,
+        "max_err_over_tol": worst["max_err_over_tol"],
         "rows": out_rows,
         "cpu_baseline": cpu,
     }
@@ -635,6 +783,7 @@ def summarize_profile(d):
     if stats:
         lines = ["# rocprofv3 --kernel-trace --stats, one bench.py run on one MI355X",
                  "# command: " + cmd("stats"),
+                 f"# src_sha256={sources_sha(KERNEL_SOURCES)}",
                  "# per kernel name (every dispatch of the run: warm-up, timed and per-row steps):",
                  f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
         for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):

@@ -49,3 +49,41 @@ def time_mask(lengths, B, T, clamp=True):
     L = np.asarray(lengths.cpu() if isinstance(lengths, torch.Tensor) else lengths, dtype=np.int64)
     L = np.clip(L, 0, T) if clamp else L
     return np.arange(T)[None, :] >= L[:, None]
+
+
+# Canary bit patterns: quiet NaNs with a payload no kernel produces.
+_CANARY = {torch.float32: (torch.int32, 0x7FC0BEEF), torch.bfloat16: (torch.int16, 0x7FDE),
+           torch.uint8: (torch.uint8, 0xA5)}
+
+
+class Guarded:
+    """An output (or workspace) tensor with G canary elements on each side.
+
+    The canaries and the tensor itself start as the canary pattern (a NaN for
+    float storage), so after a call `check()` proves that nothing was written
+    outside the tensor, and a finite-output check proves that every element
+    inside was written.  G keeps the tensor 16-byte aligned, so the kernels'
+    widest lanes still run."""
+
+    def __init__(self, shape, dtype, device, G=1024):
+        self.shape, self.dtype, self.G = tuple(shape), dtype, G
+        n = 1
+        for s in self.shape:
+            n *= s
+        self.n = n
+        idt, pat = _CANARY[dtype]
+        self.buf = torch.empty(n + 2 * G, dtype=dtype, device=device)
+        self.buf.view(idt).fill_(pat)
+        self.t = self.buf[G:G + n].view(self.shape)
+        self._pat = pat
+        self._idt = idt
+
+    def check(self, what=""):
+        raw = self.buf.view(self._idt)
+        lo, hi = raw[:self.G], raw[self.G + self.n:]
+        bad = int((lo != self._pat).sum()) + int((hi != self._pat).sum())
+        assert bad == 0, f"{what}: {bad} guard elements overwritten"
+
+    def untouched_inside(self):
+        """Number of elements inside the tensor still holding the canary."""
+        return int((self.t.reshape(-1).view(self._idt) == self._pat).sum())

@@ -49,8 +49,8 @@ def lib():
     return lib
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined"})
 
@@ -298,3 +298,30 @@ def test_front_forward_refuses_a_mel_item_past_2gb(lib):
     T, F = 1 << 27, 8          # 2^32 bytes of fp32 mel per item; output [2^25, 2, 1]
     assert lib.dwsub_fused_fwd(P, P, N, P, N, N, Q, 1, T, F, 1, N) == UNSUPPORTED
     assert "too large" in err(lib)
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "dwprobe.h")
+PROBE_LIB = os.path.join(ROOT, "conv_subsampling_amd", "libdwprobe.so")
+
+
+def test_probe_library_exports_its_header_and_validates():
+    """The HBM streaming probe (measurement only) is its own library; its
+    argument checks answer without a GPU."""
+    assert os.path.exists(PROBE_LIB), "libdwprobe.so is not built"
+    plib = ctypes.CDLL(PROBE_LIB)
+    names = declared_functions(PROBE_HEADER)
+    assert names == ["dw_probe_stream"]
+    for name in names:
+        assert hasattr(plib, name)
+    f = plib.dw_probe_stream
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(P, Q, 0, 0, 2, N) == 0                  # nothing to move
+    assert f(P, Q, 15, 15, 2, N) == 0                # rounds down to nothing
+    assert f(N, Q, 64, 64, 2, N) == -1               # NULL source with bytes to read
+    assert f(P, Q, -16, 16, 2, N) == -1
+    assert f(P, Q, 16, 16, 3, N) == -1               # unknown policy
+    assert f(ctypes.c_void_p(0x1004), Q, 16, 16, 0, N) == -1   # misaligned
+    assert f(P, Q, (1 << 42) + 16, 0, 0, N) == -1
+    # every header in include/ belongs to a built library that exports it
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["dwconv.h", "dwprobe.h"]

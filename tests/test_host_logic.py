@@ -74,3 +74,26 @@ def test_import_without_the_library_fails_loudly(tmp_path):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libdwconv.so is missing" in r.stderr
+
+
+def test_bench_reads_kernel_only_times_of_current_sources(tmp_path):
+    """Per-row kernel-only times come from the rocprofv3 summary only when it
+    was taken on the current kernel sources."""
+    import bench
+    name, prefix = bench.ROW_KERNELS[3]
+    body = [f"# src_sha256={bench.sources_sha(bench.KERNEL_SOURCES)}",
+            f"{'row':<24} {'kernel':<52} {'n':>4} {'avg_us':>9} {'min_us':>9} {'max_us':>9}",
+            f"{name:<24} {prefix.replace('dw::', '').rstrip('('):<52} {12:>4} {36.25:>9.2f} {35.0:>9.2f} {38.0:>9.2f}"]
+    p = tmp_path / "stats.txt"
+    p.write_text("\n".join(body) + "\n")
+    assert bench.read_kernel_stats(str(p)) == {name: 36.25}
+    p.write_text("\n".join(["# src_sha256=0000"] + body[1:]) + "\n")
+    assert bench.read_kernel_stats(str(p)) == {}
+
+
+def test_bench_forward_rows_are_the_forward_depthwise_kernels():
+    import bench
+    assert set(bench.FORWARD_ROWS) == {
+        "conv1d_bf16", "conv1d_causal_K3_C512", "conv1d_causal_K4_C512", "conv1d_causal_K5_C512",
+        "conv1d_causal_K9_C512", "conv1d_causal_K15_C512", "conv1d_causal_K9_C200", "conv1d_stream_bf16",
+        "stage_fwd", "stage_fwd_causal", "stage_fwd_bf16", "stage3_fwd"}
