@@ -66,9 +66,9 @@ MUTANTS = [
     ("front mask dropped", "if (t1 < L1) {", "if (1) {"),
     ("front input length-masked", "                            if (t < 0 || t >= T) continue;\n                            for (long j = 0; j < 3; ++j) {\n                                long f = 2 * f1 + j - pl;",
      "                            if (t < 0 || t >= len) continue;\n                            for (long j = 0; j < 3; ++j) {\n                                long f = 2 * f1 + j - pl;"),
-    ("front output bias dropped", "                    acc += (double)b1[c];\n", "\n"),
-    ("front conv0 bias after ReLU", "                        acc += (double)b0[c];\n                        v = acc > 0.0 ? acc : 0.0;",
-     "                        v = acc > 0.0 ? acc : 0.0;\n                        v += (double)b0[c];"),
+    ("front output bias dropped", "                    acc += b1 ? (double)b1[c] : 0.0;\n", "\n"),
+    ("front conv0 bias after ReLU", "                        acc += b0 ? (double)b0[c] : 0.0;\n                        v = acc > 0.0 ? acc : 0.0;",
+     "                        v = acc > 0.0 ? acc : 0.0;\n                        v += b0 ? (double)b0[c] : 0.0;"),
     ("front stage-2 stride 1", "long t1 = 2 * t2 + i - pl;", "long t1 = t2 + i - pl;"),
     ("front bwd ReLU derivative ignored", "double dz = z[q] > 0.0 ? dh[q] : 0.0;", "double dz = dh[q];"),
     ("front bwd time mask ignored", "if (t1 >= L1) continue; /* masked", "if (0) continue; /* masked"),
