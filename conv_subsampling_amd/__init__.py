@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "LIB_PATH", "DwconvError", "abi_version",
     "dwconv1d_fwd", "dwconv1d_stream_fwd", "dwconv1d_bwd", "dwconv1d_bwd_workspace_bytes", "dwsub_fused_fwd", "dwsub_fused_bwd", "dwsub_fused_bwd_workspace_bytes",
-    "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes",
+    "dwconv2d_fwd", "dwconv2d_bwd", "dwconv2d_bwd_workspace_bytes", "dwconv2d_bwd_noalloc",
     "conv2d_out_shape", "CAUSAL_PADS_2D", "front_out_shape", "out_len",
 ]
 
@@ -87,6 +87,8 @@ def _bind(path: str) -> ctypes.CDLL:
     lib.dwconv2d_bwd_workspace_bytes_ex.argtypes = [_i64] * 11
     lib.dwconv2d_bwd_ex.restype = _int
     lib.dwconv2d_bwd_ex.argtypes = [_vp] * 8 + [_sz] + [_i64] * 11 + [_int, _vp]
+    lib.dwconv2d_bwd_noalloc.restype = _int
+    lib.dwconv2d_bwd_noalloc.argtypes = [_vp] * 7 + [_i64] * 11 + [_int, _vp]
     return lib
 
 
@@ -398,4 +400,26 @@ def dwconv2d_bwd(x, w, lengths, dy, dx=None, dw=None, db=None, workspace=None,
     _check(_lib.dwconv2d_bwd_ex(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
                                 _ptr(workspace), ws_bytes, B, T, F, C, KH, KW, stride, pt0, pt1, pf0, pf1, code,
                                 _stream(dev)))
+    return dx, dw, db
+
+
+def dwconv2d_bwd_noalloc(x, w, lengths, dy, dx=None, dw=None, db=None, stride: int = 2, pad: int = 1, pads=None):
+    """dwconv2d_bwd through the allocation-free entry point: the caller gives
+    every output it wants (None skips it) and no workspace; the library keeps
+    the partial sums in its own per-device scratch array.  Nothing here
+    allocates device memory.  Calls that overlap in time on one GPU race."""
+    dev, f32 = x.device, torch.float32
+    st, code = _storage(x)
+    B, T, F, C, KH, KW = _conv2d_dims(x, w)
+    _dev_tensor("x", x, st, dev)
+    _dev_tensor("w", w, st, dev)
+    _dev_tensor("lengths", lengths, torch.int32, dev, (B,), allow_none=True)
+    pt0, pt1, pf0, pf1 = _pads(pad, pads)
+    To, Fo = conv2d_out_shape(T, F, KH, KW, stride, pads=(pt0, pt1, pf0, pf1))
+    _dev_tensor("dy", dy, st, dev, (B, To, Fo, C))
+    _dev_tensor("dx", dx, st, dev, (B, T, F, C), allow_none=True)
+    _dev_tensor("dw", dw, f32, dev, (KH, KW, C), allow_none=True)
+    _dev_tensor("db", db, f32, dev, (C,), allow_none=True)
+    _check(_lib.dwconv2d_bwd_noalloc(_ptr(x), _ptr(w), _ptr(lengths), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
+                                     B, T, F, C, KH, KW, stride, pt0, pt1, pf0, pf1, code, _stream(dev)))
     return dx, dw, db

@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdwconv.so")
-SOURCES = ["capi.hip", "dwconv1d.hip", "dwsub_front.hip", "dwconv2d.hip", "reduce.hip"]
+SOURCES = ["capi.hip", "dwconv1d.hip", "dwsub_front.hip", "dwconv2d.hip", "reduce.hip", "scratch.hip"]
 # The HBM streaming probe (include/dwprobe.h) is a library of its own: it is
 # measurement infrastructure for the benchmark, not part of the path.
 PROBE_LIB = os.path.join(PKG, "libdwprobe.so")

@@ -7,6 +7,7 @@
 
 #include "../../include/dwconv.h"
 #include "launch.h"
+#include "scratch.h"
 
 #ifndef DW1D_BF16_VEC
 #define DW1D_BF16_VEC 4  // bf16 channels per lane access in the 1-D kernel
@@ -279,11 +280,14 @@ size_t dwconv2d_bwd_workspace_bytes(int64_t B, int64_t T, int64_t F, int64_t C, 
     return dwconv2d_bwd_workspace_bytes_ex(B, T, F, C, KH, KW, stride, pad, pad, pad, pad);
 }
 
-dw_status dwconv2d_bwd_ex(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
-                          float* dw_, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
-                          int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad_t0,
-                          int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype, void* stream) {
-    const char* fn = "dwconv2d_bwd";
+// The conv2d backward's checks and launch.  With use_scratch, the fp64
+// partials go to the library's own per-device scratch array (allocation-free
+// entry point) instead of the caller's workspace.
+static dw_status dwconv2d_bwd_impl(const char* fn, const void* x, const void* w, const int32_t* lengths,
+                                   const void* dy, void* dx, float* dw_, float* db, void* workspace,
+                                   size_t workspace_bytes, bool use_scratch, int64_t B, int64_t T, int64_t F,
+                                   int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad_t0,
+                                   int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype, void* stream) {
     if (B < 0 || T < 0 || F < 0 || C < 0) return fail(DW_ERR_INVALID_ARG, "%s: negative size", fn);
     if (dtype != DW_F32 && dtype != DW_BF16) return fail(DW_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
     const dw_status gs = check_geometry_2d(fn, KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1);
@@ -298,17 +302,46 @@ dw_status dwconv2d_bwd_ex(const void* x, const void* w, const int32_t* lengths, 
     if (!dw::dwconv2d_fits(B, g, es)) return too_large(fn);
     if (want_wb) {
         const size_t need = dw::dwconv2d_bwd_workspace(B, g);
-        if (!workspace || workspace_bytes < need)
-            return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
+        if (use_scratch) {
+            if (need > dw::kScratchBytes)
+                return fail(DW_ERR_UNSUPPORTED, "%s: dw and db need %zu bytes of scratch, more than the %zu bytes "
+                            "this allocation-free entry point holds (C = %lld; at most about 800 channels fit)", fn,
+                            need, dw::kScratchBytes, (long long)C);
+        } else if (!workspace || workspace_bytes < need) {
+            return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn,
+                        workspace ? workspace_bytes : (size_t)0, need);
+        }
     }
     if (!dx && !want_wb) return ok();
     if (C == 0) return ok();
+    if (use_scratch && want_wb) {
+        const hipError_t e = dw::scratch_on_current_device(&workspace);
+        if (e != hipSuccess)
+            return fail(DW_ERR_HIP, "%s: the device address of the library's scratch array: %s", fn,
+                        hipGetErrorString(e));
+    }
     // An empty batch or item still defines dw = 0 and db = 0; the launcher
     // writes those zeros when there is nothing to reduce.
     const void* ptrs[4] = {x, w, dy, dx};
     const int vec = dw::pick_vec(C, es, ptrs, 4, 4);
     return from_hip(dw::launch_dwconv2d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, g, dtype == DW_BF16, vec,
                                             (hipStream_t)stream), fn);
+}
+
+dw_status dwconv2d_bwd_ex(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
+                          float* dw_, float* db, void* workspace, size_t workspace_bytes, int64_t B, int64_t T,
+                          int64_t F, int64_t C, int64_t KH, int64_t KW, int64_t stride, int64_t pad_t0,
+                          int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype, void* stream) {
+    return dwconv2d_bwd_impl("dwconv2d_bwd", x, w, lengths, dy, dx, dw_, db, workspace, workspace_bytes, false, B, T,
+                             F, C, KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1, dtype, stream);
+}
+
+dw_status dwconv2d_bwd_noalloc(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,
+                               float* dw_, float* db, int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH,
+                               int64_t KW, int64_t stride, int64_t pad_t0, int64_t pad_t1, int64_t pad_f0,
+                               int64_t pad_f1, dw_dtype dtype, void* stream) {
+    return dwconv2d_bwd_impl("dwconv2d_bwd_noalloc", x, w, lengths, dy, dx, dw_, db, nullptr, 0, true, B, T, F, C,
+                             KH, KW, stride, pad_t0, pad_t1, pad_f0, pad_f1, dtype, stream);
 }
 
 dw_status dwconv2d_bwd(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,

@@ -389,6 +389,31 @@ dw_status dwconv2d_bwd_ex(const void *x, const void *w, const int32_t *lengths, 
                           int64_t pad_t0, int64_t pad_t1, int64_t pad_f0, int64_t pad_f1, dw_dtype dtype,
                           void *stream);
 
+/*
+ * dwconv2d_bwd_noalloc -- dwconv2d_bwd_ex with no workspace argument, for
+ * callers that cannot allocate device memory around a call: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The same gradients, bit for bit, as dwconv2d_bwd_ex with the same
+ * arguments (the same kernels run).  The fp64 partial sums of dw and db go to
+ * a 16 MiB array that the library holds on each GPU it runs on, for the life
+ * of the process; the call itself allocates nothing and frees nothing
+ * (callers still pass every input and output).  Every call on one GPU shares
+ * that GPU's array, so two calls that overlap in time on the same GPU (on
+ * different streams, or from different host threads without ordering) race
+ * and may return wrong dw and db; calls ordered on one stream do not.
+ * Arguments, layouts, ownership and the other errors are those of
+ * dwconv2d_bwd_ex.  Errors: DW_ERR_UNSUPPORTED when dw or db is requested
+ * and the partials would not fit the array: they take (P + 4) * 10 * C * 8
+ * bytes for P <= 256 workgroup partials (fewer for a small batch), so at
+ * most 806 channels fit at any batch size; DW_ERR_HIP if the array's device
+ * address cannot be looked up.
+ */
+dw_status dwconv2d_bwd_noalloc(const void *x, const void *w, const int32_t *lengths, const void *dy, void *dx,
+                               float *dw, float *db, int64_t B, int64_t T, int64_t F, int64_t C, int64_t KH,
+                               int64_t KW, int64_t stride, int64_t pad_t0, int64_t pad_t1, int64_t pad_f0,
+                               int64_t pad_f1, dw_dtype dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,7 @@ def lib():
     lib.dwsub_fused_bwd_workspace_bytes_ex.argtypes = [i64] * 4 + [i]
     lib.dwsub_fused_bwd_workspace_bytes_ex.restype = sz
     lib.dwsub_fused_bwd_ex.argtypes = [vp] * 11 + [sz] + [i64] * 4 + [i, i, vp]
+    lib.dwconv2d_bwd_noalloc.argtypes = [vp] * 7 + [i64] * 11 + [i, vp]
     return lib
 
 
@@ -325,3 +326,18 @@ def test_probe_library_exports_its_header_and_validates():
     assert f(P, Q, (1 << 42) + 16, 0, 0, N) == -1
     # every header in include/ belongs to a built library that exports it
     assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["dwconv.h", "dwprobe.h"]
+
+
+def test_noalloc_conv2d_bwd_validation(lib):
+    """The allocation-free conv2d backward refuses, before touching a device,
+    what the workspace entry point refuses, and channel counts whose partial
+    sums would not fit its scratch array."""
+    f = lib.dwconv2d_bwd_noalloc
+    geo = [3, 3, 2, 1, 1, 1, 1]
+    assert f(N, P, N, P, Q, N, N, 2, 8, 8, 4, *geo, 0, N) == INVALID                 # NULL x
+    assert f(P, P, N, P, P, N, N, 2, 8, 8, 4, *geo, 0, N) == INVALID                 # dx aliases x
+    assert f(P, P, N, P, Q, N, N, 2, 8, 8, 4, 3, 3, 1, 1, 1, 1, 1, 0, N) == UNSUPPORTED   # stride 1
+    assert f(P, P, N, P, N, Q, N, 32, 1500, 64, 1024, *geo, 0, N) == UNSUPPORTED   # dw of 1024 channels
+    assert b"scratch" in lib.dw_last_error()
+    assert f(P, P, N, P, N, N, N, 32, 1500, 64, 1024, *geo, 0, N) == OK            # nothing requested
+    assert f(P, P, N, P, Q, N, N, 0, 8, 8, 4, *geo, 7, N) == INVALID                 # unknown dtype
