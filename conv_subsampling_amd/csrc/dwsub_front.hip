@@ -128,14 +128,17 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
     constexpr uint32_t es = sizeof(S);
 
     // h rows 2*t0-1-d+l, l = 0..2*TY, read mel patch rows 2l .. 2l+2.
-    // h row validity: inside [0, T1) and before the time mask.
-    bool hrow_ok[2 * kSubRows + 1];
+    // h row validity: inside [0, T1) and before the time mask.  hlim is the
+    // upper clamp of the row's ReLU: +inf for a valid row, 0 for a masked
+    // one, so that one median-of-three gives max(z, 0) or 0.
+    float hlim[2 * kSubRows + 1];
     bool any_ok = false;
 #pragma unroll
     for (int l = 0; l < 2 * kSubRows + 1; ++l) {
         const int32_t r = 2 * t0 - 1 - d + l;
-        hrow_ok[l] = r >= 0 && r < T1 && r < L1;
-        any_ok |= hrow_ok[l];
+        const bool ok = r >= 0 && r < T1 && r < L1;
+        hlim[l] = ok ? __builtin_inff() : 0.0f;
+        any_ok |= ok;
     }
 
     const int32_t ncols = min(kSubCols, F2 - f0);
@@ -157,60 +160,73 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_fwd_kernel(
 
     // conv0 + bias + ReLU at h row l, for the h column whose three mel
     // columns start at patch column q; zero where the row is masked.  The
-    // sum is computed for every row and then selected, so the loads and FMAs
-    // of all rows can be scheduled together.
+    // sum is computed for every row and then clamped, so the loads and FMAs
+    // of all rows can be scheduled together.  med3(z, 0, hlim) is max(z, 0)
+    // for a valid row and 0 for a masked one; a NaN z (from a NaN input)
+    // gives 0 either way, as max(NaN, 0) does.
     auto conv0 = [&](int l, int q) -> float {
         float a = ba;
 #pragma unroll
         for (int i = 0; i < 3; ++i)
 #pragma unroll
             for (int j = 0; j < 3; ++j) a = __builtin_fmaf(patch[2 * l + i][q + j], wa[3 * i + j], a);
-        return hrow_ok[l] ? fmaxf(a, 0.0f) : 0.0f;
+        return __builtin_amdgcn_fmed3f(a, 0.0f, hlim[l]);
     };
 
-    // Carried h column 2*f0-1-d (zero left of the first h column).
-    float hc[2 * kSubRows + 1];
+    // Carried h column 2*f0-1-d (zero left of the first h column).  Two
+    // carry arrays take turns, so the walk moves no registers between steps.
+    float hc[2 * kSubRows + 1], hn[2 * kSubRows + 1];
 #pragma unroll
     for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = 2 * f0 - 1 - d >= 0 ? conv0(l, 2) : 0.0f;
 
-    // One output column: h columns 2f2-d and 2f2+1-d for every h row, then
-    // the depthwise taps.  The first lies in the padding only at output
-    // column 0 of the causal mode, the second only at the last output column
-    // when it passes F1; those steps are peeled off the loop so that the loop
-    // body has no condition around its LDS reads.
-    auto step = [&](int s, auto odd_valid, auto even_valid) {
+    // One output column: h columns 2f2-d and 2f2+1-d for every h row (the
+    // odd one lands in `out`, the carry of the next column), then the
+    // depthwise taps.  The first lies in the padding only at output column 0
+    // of the causal mode, the second only at the last output column when it
+    // passes F1; those steps are peeled off the loop so that the loop body
+    // has no condition around its LDS reads.
+    auto step = [&](int s, const float* in, float* out, auto odd_valid, auto even_valid) {
         const int32_t f2 = f0 + s;
-        float he[2 * kSubRows + 1], ho[2 * kSubRows + 1];
+        float he[2 * kSubRows + 1];
 #pragma unroll
         for (int l = 0; l < 2 * kSubRows + 1; ++l) {
             he[l] = decltype(even_valid)::value ? conv0(l, 4 * s + 4) : 0.0f;
-            ho[l] = decltype(odd_valid)::value ? conv0(l, 4 * s + 6) : 0.0f;
+            out[l] = decltype(odd_valid)::value ? conv0(l, 4 * s + 6) : 0.0f;
         }
 #pragma unroll
         for (int i = 0; i < kSubRows; ++i) {
             float a = bb;
 #pragma unroll
             for (int r = 0; r < 3; ++r) {
-                a = __builtin_fmaf(hc[2 * i + r], wb[3 * r + 0], a);
+                a = __builtin_fmaf(in[2 * i + r], wb[3 * r + 0], a);
                 a = __builtin_fmaf(he[2 * i + r], wb[3 * r + 1], a);
-                a = __builtin_fmaf(ho[2 * i + r], wb[3 * r + 2], a);
+                a = __builtin_fmaf(out[2 * i + r], wb[3 * r + 2], a);
             }
             store((uint32_t)(t0 + i) * yrow + ((uint32_t)f2 * C + c) * es, a);
         }
-#pragma unroll
-        for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = ho[l];
     };
     const bool first_even_pad = 2 * f0 - d < 0;
     const bool last_odd_pad = 2 * (f0 + ncols - 1) + 1 - d >= F1;
     int s = 0;
     if (first_even_pad) {
-        if (ncols == 1 && last_odd_pad) step(0, std::false_type{}, std::false_type{});
-        else step(0, std::true_type{}, std::false_type{});
+        if (ncols == 1 && last_odd_pad) step(0, hc, hn, std::false_type{}, std::false_type{});
+        else step(0, hc, hn, std::true_type{}, std::false_type{});
+#pragma unroll
+        for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = hn[l];
         s = 1;
     }
     const int full = last_odd_pad ? ncols - 1 : ncols;
-    for (; s < full; ++s) step(s, std::true_type{}, std::true_type{});
-    if (last_odd_pad && s < ncols) step(s, std::false_type{}, std::true_type{});
+    for (; s + 1 < full; s += 2) {
+        step(s, hc, hn, std::true_type{}, std::true_type{});
+        step(s + 1, hn, hc, std::true_type{}, std::true_type{});
+    }
+    if (s < full) {
+        step(s, hc, hn, std::true_type{}, std::true_type{});
+#pragma unroll
+        for (int l = 0; l < 2 * kSubRows + 1; ++l) hc[l] = hn[l];
+        ++s;
+    }
+    if (last_odd_pad && s < ncols) step(s, hc, hn, std::false_type{}, std::true_type{});
 }
 
 bool dwsub_fused_fwd_fits(int64_t B, int64_t T, int64_t F, int64_t C, bool causal, int elem_bytes) {
@@ -396,12 +412,14 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
                 // are zeros: its terms are then formed and add exact zeros.
                 const bool v0 = r0 >= 0 && r0 < hvalid, v1 = r0 + 1 >= 0 && r0 + 1 < hvalid;
                 if (r0 >= hvalid) continue;  // both rows masked: no other term
-                double P[5][5];
+                // The quad's top h row (mel patch rows 4q .. 4q+2), then its
+                // bottom row (4q+2 .. 4q+4): three patch rows live at a time.
+                double P[3][5];
 #pragma unroll
-                for (int a = 0; a < 5; ++a)
+                for (int a = 0; a < 3; ++a)
 #pragma unroll
                     for (int e = 0; e < 5; ++e) P[a][e] = patch[4 * q + a][4 * s + e];
-                double z00 = ba, z01 = ba, z10 = 0.0, z11 = 0.0;
+                double z00 = ba, z01 = ba;
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
@@ -409,31 +427,12 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
                         z00 = __builtin_fma(P[i][k], wa[3 * i + k], z00);
                         z01 = __builtin_fma(P[i][2 + k], wa[3 * i + k], z01);
                     }
-                if (v1) {
-                    z10 = ba;
-                    z11 = ba;
-#pragma unroll
-                    for (int i = 0; i < 3; ++i)
-#pragma unroll
-                        for (int k = 0; k < 3; ++k) {
-                            z10 = __builtin_fma(P[2 + i][k], wa[3 * i + k], z10);
-                            z11 = __builtin_fma(P[2 + i][2 + k], wa[3 * i + k], z11);
-                        }
-                }
                 const bool m00 = v0 && eok && z00 > 0.0, m01 = v0 && cok && z01 > 0.0;
-                const bool m10 = v1 && eok && z10 > 0.0, m11 = v1 && cok && z11 > 0.0;
                 const double h00 = m00 ? z00 : 0.0, h01 = m01 ? z01 : 0.0;
-                const double h10 = m10 ? z10 : 0.0, h11 = m11 ? z11 : 0.0;
                 // depthwise stage: weight gradient from the (h, dy) pairs of this quad
                 gw1[4] = __builtin_fma(g00, h00, gw1[4]);
                 gw1[5] = __builtin_fma(g00, h01, gw1[5]);
                 gw1[3] = __builtin_fma(g01, h01, gw1[3]);
-                gw1[7] = __builtin_fma(g00, h10, gw1[7]);
-                gw1[1] = __builtin_fma(g10, h10, gw1[1]);
-                gw1[8] = __builtin_fma(g00, h11, gw1[8]);
-                gw1[6] = __builtin_fma(g01, h11, gw1[6]);
-                gw1[2] = __builtin_fma(g10, h11, gw1[2]);
-                gw1[0] = __builtin_fma(g11, h11, gw1[0]);
                 // gradient at h, then through the ReLU and the mask
                 const double dh00 = g00 * wb[4];
                 const double dh01 = __builtin_fma(g01, wb[3], g00 * wb[5]);
@@ -446,6 +445,26 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
                         gw0[3 * i + k] =
                             __builtin_fma(dz01, P[i][2 + k], __builtin_fma(dz00, P[i][k], gw0[3 * i + k]));
                 if (v1) {
+#pragma unroll
+                    for (int a = 0; a < 3; ++a)
+#pragma unroll
+                        for (int e = 0; e < 5; ++e) P[a][e] = patch[4 * q + 2 + a][4 * s + e];
+                    double z10 = ba, z11 = ba;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int k = 0; k < 3; ++k) {
+                            z10 = __builtin_fma(P[i][k], wa[3 * i + k], z10);
+                            z11 = __builtin_fma(P[i][2 + k], wa[3 * i + k], z11);
+                        }
+                    const bool m10 = eok && z10 > 0.0, m11 = cok && z11 > 0.0;
+                    const double h10 = m10 ? z10 : 0.0, h11 = m11 ? z11 : 0.0;
+                    gw1[7] = __builtin_fma(g00, h10, gw1[7]);
+                    gw1[1] = __builtin_fma(g10, h10, gw1[1]);
+                    gw1[8] = __builtin_fma(g00, h11, gw1[8]);
+                    gw1[6] = __builtin_fma(g01, h11, gw1[6]);
+                    gw1[2] = __builtin_fma(g10, h11, gw1[2]);
+                    gw1[0] = __builtin_fma(g11, h11, gw1[0]);
                     const double dh10 = __builtin_fma(g10, wb[1], g00 * wb[7]);
                     const double dh11 =
                         __builtin_fma(g11, wb[0], __builtin_fma(g10, wb[2], __builtin_fma(g01, wb[6], g00 * wb[8])));
@@ -455,8 +474,8 @@ __global__ __launch_bounds__(kSubBlock) void dwsub_fused_bwd_kernel(
                     for (int i = 0; i < 3; ++i)
 #pragma unroll
                         for (int k = 0; k < 3; ++k)
-                            gw0[3 * i + k] = __builtin_fma(dz11, P[2 + i][2 + k],
-                                                           __builtin_fma(dz10, P[2 + i][k], gw0[3 * i + k]));
+                            gw0[3 * i + k] =
+                                __builtin_fma(dz11, P[i][2 + k], __builtin_fma(dz10, P[i][k], gw0[3 * i + k]));
                 }
             }
 #pragma unroll
