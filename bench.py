@@ -530,7 +530,7 @@ def read_kernel_stats(path=None):
     sha = next((ln.split("=", 1)[1].strip() for ln in text if ln.startswith("# src_sha256=")), None)
     if sha != sources_sha(KERNEL_SOURCES):
         return {}
-    names = {n for n, _ in ROW_KERNELS}
+    names = {n for n, _ in ROW_KERNELS} | {"probe:" + n for n in PROBE_ROWS}
     out = {}
     for ln in text:
         parts = ln.split()  # row, kernel (may hold spaces), n, avg_us, min_us, max_us
@@ -541,6 +541,11 @@ def read_kernel_stats(path=None):
                 pass
     return out
 
+
+# The rows the probe pass copies for, in the order it launches them: every
+# HBM-bound row (all but the launch-bound small conv and the ALU-bound front).
+PROBE_ROWS = [n for n, _ in ROW_KERNELS if n != "conv1d_small" and not n.startswith("front")]
+PROBE_KERNEL = "stream_probe_kernel<2, 18>"
 
 FORWARD_BAR = 0.70   # forward depthwise kernels: at least 70% of peak HBM bandwidth
 FORWARD_ROWS = [n for n, _ in ROW_KERNELS if ("conv1d_" in n and "bwd" not in n and n != "conv1d_small")
@@ -555,6 +560,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM streaming probe pass")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle comparison and the CPU baseline (profiling runs: only the timed, "
+                         "per-row and probe passes dispatch kernels)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--summarize-profile", metavar="DIR", help="summarise rocprofv3 output under DIR and exit")
@@ -633,6 +641,7 @@ def main():
         psrc.fill_(1)
         stream = torch.cuda.current_stream(dev).cuda_stream
         prow = [r for r in rows if r["bound"] == "hbm" and r["read"] <= span and r["write"] <= span]
+        assert [r["name"] for r in prow] == PROBE_ROWS, "PROBE_ROWS is out of date"
         pev = {r["name"]: [] for r in prow}
         off = 0
         for s in range(args.steps + 1):
@@ -668,7 +677,7 @@ def main():
         b = r["read"] + r["write"]
         row = dict(row=r["name"], op=r["op"], config=r["cfg"], us=round(us, 2), us_median=round(ts[len(ts) // 2], 2),
                    us_min=round(ts[0], 2), us_p90=round(ts[min(len(ts) - 1, (9 * len(ts)) // 10)], 2),
-                   kernel_us=kstats.get(r["name"]),
+                   kernel_us=kstats.get(r["name"]), probe_kernel_us=kstats.get("probe:" + r["name"]),
                    frames_per_s=round(r["frames"] / (us * 1e-6)), alg_bytes=b,
                    gbps=round(b / (us * 1e-6) / 1e9, 1), hbm_frac=round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                    dense_bytes=r["read_dense"] + r["write"],
@@ -698,17 +707,19 @@ def main():
                           rows_below=[r["row"] for r in fwd if r["hbm_frac"] < FORWARD_BAR],
                           met=all(r["hbm_frac"] >= FORWARD_BAR for r in fwd))
 
-    log("running the oracle on a sample of every row, and the GPU path on the same items ...")
-    cpu, errs = oracle_check(rows, args.cpu_seconds, time_it=not args.no_cpu_baseline)
-    for row in out_rows:
-        e = errs[row["row"]]
-        row.update(max_err=float(f"{e['max_err']:.3e}"), max_err_over_tol=round(e["max_err_over_tol"], 4),
-                   err_items=e["items"])
-    if cpu:
-        log(f"  oracle: {cpu['value']:.0f} frames/s ({cpu['sample']})")
-    worst = max(out_rows, key=lambda r: r["max_err_over_tol"])
-    log(f"  worst error against the oracle: {worst['row']} {worst['max_err']:.2e} "
-        f"({worst['max_err_over_tol']:.3f} of its tolerance)")
+    cpu, worst = None, None
+    if not args.no_check:
+        log("running the oracle on a sample of every row, and the GPU path on the same items ...")
+        cpu, errs = oracle_check(rows, args.cpu_seconds, time_it=not args.no_cpu_baseline)
+        for row in out_rows:
+            e = errs[row["row"]]
+            row.update(max_err=float(f"{e['max_err']:.3e}"), max_err_over_tol=round(e["max_err_over_tol"], 4),
+                       err_items=e["items"])
+        if cpu:
+            log(f"  oracle: {cpu['value']:.0f} frames/s ({cpu['sample']})")
+        worst = max(out_rows, key=lambda r: r["max_err_over_tol"])
+        log(f"  worst error against the oracle: {worst['row']} {worst['max_err']:.2e} "
+            f"({worst['max_err_over_tol']:.3f} of its tolerance)")
 
     line = {
         "metric": "depthwise conv frames/s and achieved HBM GB/s (% of MI355X peak), 1 GPU",
@@ -737,7 +748,7 @@ def main():
                 "frac": round(alg / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "roofline": roofline,
         "forward_target": forward_target,
-        "max_err_over_tol": worst["max_err_over_tol"],
+        "max_err_over_tol": worst["max_err_over_tol"] if worst else None,
         "rows": out_rows,
         "cpu_baseline": cpu,
     }
@@ -748,6 +759,13 @@ def main():
 # --------------------------------------------------------------------------
 # rocprofv3 summaries
 # --------------------------------------------------------------------------
+
+def kernel_short_name(name):
+    """A kernel's name without 'void ', namespaces that hide it, or its argument list."""
+    name = name[5:] if name.startswith("void ") else name
+    name = name.replace("(anonymous namespace)::", "")
+    return name.split("(")[0]
+
 
 def _csv_rows(pattern):
     out = []
@@ -770,6 +788,58 @@ def attribute_dispatches(disp):
     return out
 
 
+FRONT_SQ_PASSES = {
+    "sq1": ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+            "SQ_WAIT_INST_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CYCLES"],
+    "sq2": ["SQ_INSTS_VALU_FMA_F32", "SQ_INSTS_VALU_FMA_F64", "SQ_INSTS_VALU_CVT", "SQ_INSTS_SALU",
+            "SQ_WAVE_CYCLES", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VALU_MUL_F64", "SQ_INSTS_VALU_ADD_F64"],
+}
+
+
+def front_sq_summary(d, cmd):
+    """Text summary of the front kernels' SQ counters (d/sq1, d/sq2), with the
+    VALU-busy fraction against their kernel-only durations in d/stats; None if
+    the counter runs are missing."""
+    if not all(_csv_rows(os.path.join(d, k, "**", "*counter_collection.csv")) for k in FRONT_SQ_PASSES):
+        return None
+    per = {}
+    for k in FRONT_SQ_PASSES:
+        for r in _csv_rows(os.path.join(d, k, "**", "*counter_collection.csv")):
+            name = r.get("Kernel_Name", "")
+            if "dwsub_fused" not in name:
+                continue
+            short = kernel_short_name(name)
+            per.setdefault(short, {}).setdefault((k, r["Dispatch_Id"]), {})
+            dct = per[short][(k, r["Dispatch_Id"])]
+            dct[r["Counter_Name"]] = dct.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    stats = {}
+    for r in _csv_rows(os.path.join(d, "stats", "**", "*kernel_stats.csv")):
+        name = r.get("Name", r.get("KernelName", "?"))
+        stats[kernel_short_name(name)] = float(r.get("AverageNs", 0)) / 1e3
+    lines = ["# SQ counters of the fused front's kernels on one MI355X, two counter passes over a short bench.py run",
+             "# sq1: " + cmd("sq1"), "# sq2: " + cmd("sq2"),
+             "# Values are means per dispatch (the symmetric and causal forward share one kernel name).",
+             "# VALU-busy = SQ_INSTS_VALU x 4 cycles (a wave64 vector instruction on a 16-lane SIMD) / 1024",
+             "# SIMDs / 2.4 GHz, against the kernel-only mean duration of the kernel-trace run (stats).", ""]
+    for short in sorted(per):
+        byp = {}
+        for (k, did), vals in per[short].items():
+            for cn, v in vals.items():
+                byp.setdefault(cn, []).append(v)
+        mean = {cn: sum(v) / len(v) for cn, v in byp.items()}
+        ndisp = max(len(v) for v in byp.values())
+        lines.append(f"kernel: {short.replace('dw::', '')}   dispatches per pass: {ndisp}")
+        for cn in FRONT_SQ_PASSES["sq1"] + FRONT_SQ_PASSES["sq2"]:
+            if cn in mean:
+                lines.append(f"  {cn:<28} {mean[cn]:>12.4g}")
+        dur = stats.get(short)
+        if dur and "SQ_INSTS_VALU" in mean:
+            busy = mean["SQ_INSTS_VALU"] * 4 / 1024 / 2.4e3
+            lines.append(f"  VALU issue time {busy:6.2f} us of a {dur:.2f} us kernel: {100 * busy / dur:.0f}% VALU-busy")
+        lines.append("")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_profile(d):
     """Write profiles/ summaries from rocprofv3 output under d:
     d/stats/**/*kernel_stats.csv and *kernel_trace.csv (durations),
@@ -788,7 +858,7 @@ def summarize_profile(d):
                  f"{'kernel':<60} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}"]
         for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0) or 0)):
             name = r.get("Name", r.get("KernelName", "?"))
-            short = (name[5:] if name.startswith("void ") else name).split("(")[0][:60]
+            short = kernel_short_name(name)[:60]
             lines.append(f"{short:<60} {int(r.get('Calls', 0)):>6} {float(r.get('AverageNs', 0)) / 1e3:>10.2f} "
                          f"{float(r.get('MinNs', 0)) / 1e3:>10.2f} {float(r.get('MaxNs', 0)) / 1e3:>10.2f} "
                          f"{float(r.get('Percentage', 0)):>6.2f}")
@@ -808,6 +878,19 @@ def summarize_profile(d):
                                  f"{max(v):>9.2f}")
                 else:
                     lines.append(f"{name:<24} {kshort:<52}    - (no dispatches attributed)")
+            # the probe pass: one probe per HBM-bound row per round, in PROBE_ROWS order; the
+            # first round warms up
+            probes = [du for _, kn, du in sorted(disp, key=lambda t: int(t[0]))
+                      if kernel_short_name(kn) == PROBE_KERNEL]
+            if probes and len(probes) % len(PROBE_ROWS) == 0:
+                lines += ["", "# the probe pass: a plain copy of each HBM-bound row's read and write bytes (rounds",
+                          "# after the first), kernel-only durations",
+                          f"{'row':<24} {'kernel':<52} {'n':>4} {'avg_us':>9} {'min_us':>9} {'max_us':>9}"]
+                for k, name in enumerate(PROBE_ROWS):
+                    v = probes[len(PROBE_ROWS) + k::len(PROBE_ROWS)]
+                    if v:
+                        lines.append(f"probe:{name:<18} {PROBE_KERNEL:<52} {len(v):>4} {sum(v) / len(v):>9.2f} "
+                                     f"{min(v):>9.2f} {max(v):>9.2f}")
         with open(os.path.join(ROOT, "profiles", "kernel_stats_bench_step.txt"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
         print("\n".join(lines))
@@ -822,6 +905,12 @@ def summarize_profile(d):
             name, v = r.get("Kernel_Name", ""), float(r.get("Counter_Value", 0))
             per[key] = (name, per.get(key, (name, 0.0))[1] + v)
         return [(k, n, v) for k, (n, v) in per.items()]
+
+    sq = front_sq_summary(d, cmd)
+    if sq:
+        with open(os.path.join(ROOT, "profiles", "dwsub_front_sq_counters.txt"), "w") as fh:
+            fh.write(sq)
+        print(sq)
 
     fetch = counter("fetch", "FETCH_SIZE")
     write = counter("write", "WRITE_SIZE")
