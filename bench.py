@@ -105,10 +105,10 @@ ROW_KERNELS = [
     ("front_causal", "dw::dwsub_fused_fwd_kernel<float>("),
     ("front_bwd_causal", "dw::dwsub_fused_bwd_kernel<float, 5>("),
     ("conv1d_bf16", "dw::dwconv1d_fwd_kernel<unsigned short, 4, 9, 12>("),
-    ("conv1d_causal_K3_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 3, 32>("),
-    ("conv1d_causal_K4_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 4, 32>("),
-    ("conv1d_causal_K5_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 5, 32>("),
-    ("conv1d_causal_K9_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 9, 32>("),
+    ("conv1d_causal_K3_C512", "dw::dwconv1d_fwd_pipe_kernel<3>("),
+    ("conv1d_causal_K4_C512", "dw::dwconv1d_fwd_pipe_kernel<4>("),
+    ("conv1d_causal_K5_C512", "dw::dwconv1d_fwd_pipe_kernel<5>("),
+    ("conv1d_causal_K9_C512", "dw::dwconv1d_fwd_pipe_kernel<9>("),
     ("conv1d_causal_K15_C512", "dw::dwconv1d_fwd_lds_kernel<float, 4, 15, 32>("),
     ("conv1d_causal_K9_C200", "dw::dwconv1d_fwd_lds_kernel<float, 4, 9, 32>("),
     ("conv1d_stream_bf16", "dw::dwconv1d_stream_kernel<unsigned short, 8, 9, 8>("),

@@ -20,7 +20,9 @@
 // tile that lies wholly past the length stores zeros without loading.
 // Output uses non-temporal stores: nothing here reads it back.  fp32 at the
 // compiled widths (3, 4, 5, 9, 15) with at least 32 channel groups stages the
-// window through LDS instead (the LDS-staged form below).
+// window through LDS instead (the LDS-staged form below), and at widths 3, 4,
+// 5 and 9 with 64 or more groups a persistent workgroup streams its tiles
+// through two LDS buffers (the persistent form below).
 #include "common.h"
 #include "launch.h"
 
@@ -193,6 +195,156 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_lds_kernel(
     }
 }
 
+// Persistent, double-buffered form (fp32 at widths 3, 4, 5 and 9 with at
+// least one full slab of 64 channel groups).  The one-shot form above loads
+// its tile, waits, computes and exits, so within a workgroup the loads never
+// overlap the FMAs and stores, and tens of thousands of short workgroups
+// leave gaps between them.  Here a fixed grid of about 256 workgroups walks
+// the 16-frame time tiles of its channel slab (tile g, g + G, g + 2G, ...),
+// and while it computes one tile the rows of its next tile are already on
+// their way into a second LDS buffer, by buffer-to-LDS loads
+// (buffer_load_dwordx4 ... lds) that hold no registers: lane i of a wave
+// writes its 16 bytes at byte 16 i of the LDS row named by M0, so a wave's
+// load of one frame fills one 1 KiB row.  Out-of-range frames arrive as zeros,
+// as everywhere here.
+//
+// The two buffers are separate arrays, and the loop body is written out once
+// per buffer, so that waits for one buffer's loads do not cover the other's.
+// The workgroup syncs with a bare s_barrier after an explicit wait: vmcnt(kR)
+// leaves this wave's kR just-issued loads of the next tile in flight and
+// retires everything older, which includes this tile's loads, since loads
+// return in issue order; a __syncthreads fence would wait for all of them.
+// Before a buffer is refilled, each wave waits for its own LDS reads
+// (lgkmcnt(0)) and the workgroup meets at a barrier.
+//
+// Measured in the full step on MI355X at [32,1500,512] causal: K3 35.5 ->
+// 33.4 us, K4 35.5 -> 32.0, K5 35.0 -> 32.2, K9 36.2 -> 34.9.  At K15 (30
+// staged rows per 16 frames) and at C = 200 (one partial slab) the one-shot
+// form stays ahead, and those keep it.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+#define DW_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)  // vmcnt(n) alone (gfx9 s_waitcnt layout)
+constexpr int kWaitLds = 0xC07F;                                 // lgkmcnt(0) alone
+constexpr int kPipeTile1d = 16;
+// Stores of the persistent form: non-temporal with the sc1 scope bit (18);
+// measured ahead of non-temporal alone (2) in the full step.
+constexpr int kPipeStorePolicy = 18;
+
+template <int K>
+struct Pipe1d {
+    static constexpr int TW = kPipeTile1d, R = TW + K - 1, W = kBlock1d / 64, TT = TW / W;
+    static constexpr int kR = (R + W - 1) / W;  // rows each wave loads; rows past R land in spare rows
+    static constexpr int kRows = kR * W;
+};
+
+// Issue the buffer-to-LDS loads of tile j (item b, frames t0 - pL ...) into
+// `tile`; false (and nothing issued) when the tile lies wholly past the length.
+template <int K>
+__device__ __forceinline__ bool pipe1d_issue(float (*tile)[256], uint32_t j, uint32_t n_tt, const float* x,
+                                             const int32_t* lengths, int32_t T, int32_t C, int32_t pL,
+                                             uint32_t row, uint32_t coff, uint32_t wv) {
+    using P = Pipe1d<K>;
+    const uint32_t b = j / n_tt, tt = j - b * n_tt;
+    const int32_t len = (int32_t)item_length(lengths, b, T);
+    const int32_t t0 = (int32_t)tt * P::TW;
+    if (t0 >= len) return false;
+    const rsrc_t xr = make_rsrc(x + (int64_t)b * T * C, (uint32_t)len * row);
+#pragma unroll
+    for (int q = 0; q < P::kR; ++q) {
+        const int r = (int)wv + P::W * q;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)&tile[r][0], 16,
+                                                 (uint32_t)((t0 - pL + r) * (int32_t)row) + coff, 0, 0, 0);
+    }
+    return true;
+}
+
+// This wave's TT output frames of tile j from the staged rows.
+template <int K>
+__device__ __forceinline__ void pipe1d_compute(const float (*tile)[256], uint32_t j, uint32_t n_tt, float* y,
+                                               const int32_t* lengths, int32_t T, int32_t C, uint32_t row,
+                                               uint32_t coff, uint32_t lane, uint32_t wv, const Vf<4>* wk,
+                                               const Vf<4>& bv) {
+    using P = Pipe1d<K>;
+    constexpr int V = 4, TT = P::TT;
+    const uint32_t b = j / n_tt, tt = j - b * n_tt;
+    const int32_t len = (int32_t)item_length(lengths, b, T);
+    const int32_t t0 = (int32_t)tt * P::TW, tw = t0 + (int32_t)wv * TT;
+    const rsrc_t yr = make_rsrc(y + (int64_t)b * T * C, (uint32_t)T * row);
+    if (t0 >= len) {  // uniform: the whole tile is past the length
+        const Vf<V> z = vzero<V>();
+#pragma unroll
+        for (int i = 0; i < TT; ++i)
+            Buf<float, V>::template store<kPipeStorePolicy>(yr, (uint32_t)(tw + i) * row + coff, z);
+        return;
+    }
+    Vf<V> win[TT + K - 1];
+#pragma unroll
+    for (int r = 0; r < TT + K - 1; ++r) win[r] = lds_get<V>(&tile[(int)wv * TT + r][lane * V]);
+#pragma unroll
+    for (int i = 0; i < TT; ++i) {
+        Vf<V> acc = bv;
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int e = 0; e < V; ++e) acc.v[e] = __builtin_fmaf(win[i + k].v[e], wk[k].v[e], acc.v[e]);
+        const bool keep = tw + i < len;
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc.v[e] = keep ? acc.v[e] : 0.0f;
+        Buf<float, V>::template store<kPipeStorePolicy>(yr, (uint32_t)(tw + i) * row + coff, acc);
+    }
+}
+
+// grid: G workgroups per slab of 64 channel groups (block = slab + n_slabs * g)
+template <int K>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_pipe_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const float* __restrict__ bias,
+    const int32_t* __restrict__ lengths, float* __restrict__ y, int32_t T, int32_t C, int32_t pL,
+    uint32_t n_ttiles, uint32_t n_slabs, uint32_t CG, uint32_t ntiles) {
+    using P = Pipe1d<K>;
+    constexpr int V = 4;
+    __shared__ __align__(16) float ta[P::kRows][64 * V];
+    __shared__ __align__(16) float tb[P::kRows][64 * V];
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t slab = blk % n_slabs, g = blk / n_slabs;
+    const uint32_t G = gridDim.x / n_slabs;
+    const uint32_t row = (uint32_t)C * sizeof(float);
+    const uint32_t lane = threadIdx.x % 64, wv = threadIdx.x / 64;
+    const bool active = slab * 64 + lane < CG;
+    const int32_t c0 = active ? (int32_t)(slab * 64 + lane) * V : 0;
+    const uint32_t coff = active ? (uint32_t)c0 * sizeof(float) : 0x80000000u;
+    Vf<V> wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
+    const Vf<V> bv = bias ? load_param<float, V>(bias + c0) : vzero<V>();
+    uint32_t j = g;  // uniform over the workgroup, as is every branch below
+    if (j >= ntiles) return;
+    pipe1d_issue<K>(ta, j, n_ttiles, x, lengths, T, C, pL, row, coff, wv);
+    for (;;) {
+        // tile j is in ta (or needs no rows); stage tile j + G into tb
+        uint32_t jn = j + G;
+        bool more = jn < ntiles && pipe1d_issue<K>(tb, jn, n_ttiles, x, lengths, T, C, pL, row, coff, wv);
+        if (more) __builtin_amdgcn_s_waitcnt(DW_VMCNT(P::kR));
+        else __builtin_amdgcn_s_waitcnt(DW_VMCNT(0));
+        __builtin_amdgcn_s_barrier();
+        pipe1d_compute<K>(ta, j, n_ttiles, y, lengths, T, C, row, coff, lane, wv, wk, bv);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        __builtin_amdgcn_s_barrier();
+        j = jn;
+        if (j >= ntiles) break;
+        // tile j is in tb; stage tile j + G into ta
+        jn = j + G;
+        more = jn < ntiles && pipe1d_issue<K>(ta, jn, n_ttiles, x, lengths, T, C, pL, row, coff, wv);
+        if (more) __builtin_amdgcn_s_waitcnt(DW_VMCNT(P::kR));
+        else __builtin_amdgcn_s_waitcnt(DW_VMCNT(0));
+        __builtin_amdgcn_s_barrier();
+        pipe1d_compute<K>(tb, j, n_ttiles, y, lengths, T, C, row, coff, lane, wv, wk, bv);
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        __builtin_amdgcn_s_barrier();
+        j = jn;
+        if (j >= ntiles) break;
+    }
+}
+#undef DW_VMCNT
+
 // Any K: the same tiling, with the taps read through the cache instead of a
 // register window whose size would have to be known at compile time.
 template <typename S, int V, int TT>
@@ -273,6 +425,11 @@ static bool lds_form_1d(int64_t K, int64_t CG) {
     return (K == 3 || K == 4 || K == 5 || K == 9 || K == 15) && CG >= 32;
 }
 
+// Of those, widths 3, 4, 5 and 9 with at least one full slab of 64 channel
+// groups take the persistent, double-buffered form, on about 256 workgroups.
+static bool pipe_form_1d(int64_t K, int64_t CG) { return (K == 3 || K == 4 || K == 5 || K == 9) && CG >= 64; }
+constexpr uint32_t kPipeWorkgroups1d = 256;
+
 bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec) {
     // Per-item byte offsets, including the left padding as a negative
     // offset, must stay within a signed 32-bit range.
@@ -282,6 +439,8 @@ bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
     int64_t blocks = B * ((per_item + kBlock1d - 1) / kBlock1d);
     if (elem_bytes == 4 && lds_form_1d(K, C / vec))
         blocks = B * ((T + kLdsTile1d - 1) / kLdsTile1d) * ((C / vec + 63) / 64);
+    // the persistent form counts its tiles, B * ceil(T / 16), in 32 bits
+    if (elem_bytes == 4 && pipe_form_1d(K, C / vec)) blocks = B * ((T + kPipeTile1d - 1) / kPipeTile1d);
     return blocks < ((int64_t)1 << 31);
 }
 
@@ -294,6 +453,29 @@ static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int3
     const uint32_t bpi = (uint32_t)(((uint64_t)n_tiles * CG + kBlock1d - 1) / kBlock1d);
     const dim3 grid((uint32_t)(B * bpi)), block(kBlock1d);
     const int32_t T32 = (int32_t)T, C32 = (int32_t)C, p32 = (int32_t)pL;
+    if constexpr (sizeof(S) == 4 && V == 4) {
+        if (pipe_form_1d(K, (int64_t)CG)) {
+            const uint32_t n_tt = (uint32_t)((T + kPipeTile1d - 1) / kPipeTile1d), n_sl = (CG + 63) / 64;
+            const uint32_t ntiles = (uint32_t)B * n_tt;
+            if (ntiles == 0) return hipSuccess;
+            uint32_t G = kPipeWorkgroups1d / n_sl;
+            G = G < 1 ? 1 : (G > ntiles ? ntiles : G);
+            const dim3 pgrid(G * n_sl);
+            if (K == 3)
+                hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<3>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
+                                   C32, p32, n_tt, n_sl, CG, ntiles);
+            else if (K == 4)
+                hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<4>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
+                                   C32, p32, n_tt, n_sl, CG, ntiles);
+            else if (K == 5)
+                hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<5>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
+                                   C32, p32, n_tt, n_sl, CG, ntiles);
+            else
+                hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<9>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
+                                   C32, p32, n_tt, n_sl, CG, ntiles);
+            return hipGetLastError();
+        }
+    }
     if constexpr (sizeof(S) == 4) {
         if (lds_form_1d(K, (int64_t)CG)) {
             constexpr int TW = kLdsTile1d;

@@ -67,6 +67,11 @@ GRID = [
     # of 32 groups, T below the tile and a single frame
     (3, 70, 256, 3, False), (2, 45, 200, 4, True), (2, 33, 512, 5, True), (1, 5, 256, 4, False),
     (2, 1, 128, 3, True), (2, 65, 260, 5, False), (3, 40, 128, 4, False),
+    # the persistent form (K = 3, 4, 5, 9 with 64 or more groups): more 16-frame
+    # tiles than workgroups, so each workgroup walks two to four tiles through
+    # both LDS buffers; one to four slabs, a partial last slab, ragged tiles
+    (6, 700, 512, 9, True), (5, 900, 256, 4, False), (9, 500, 320, 3, True),
+    (4, 1000, 1024, 5, False), (17, 260, 256, 9, False), (3, 999, 516, 5, True),
 ]
 
 
@@ -95,10 +100,12 @@ def test_null_bias_equals_zero_bias_bitwise():
     assert torch.equal(run(x, w, None, lengths, True), run(x, w, z, lengths, True))
 
 
-def test_masked_input_is_never_read():
-    """NaN beyond each item's length must not reach any output."""
+@pytest.mark.parametrize("C", [32, 512])
+def test_masked_input_is_never_read(C):
+    """NaN beyond each item's length must not reach any output (C = 512 at
+    fp32: the persistent form, whose tiles past a length issue no loads)."""
     for dtype in (torch.float32, torch.bfloat16):
-        B, T, C, K = 3, 80, 32, 9
+        B, T, K = 3, 80, 9
         x, w, b, _ = make(B, T, C, K, dtype)
         lengths = torch.tensor([80, 33, 0], dtype=torch.int32, device=DEV)
         y = run(x, w, b, lengths, False)

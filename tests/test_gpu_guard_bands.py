@@ -41,13 +41,15 @@ def guarded_ws(nbytes):
 
 
 CASES_1D = [
-    # (B, T, C, K, causal, dtype): register window, LDS-staged slab, partial slab, any-K loop, bf16
+    # (B, T, C, K, causal, dtype): register window, persistent slab, partial slab, any-K loop, bf16,
+    # LDS-staged slab, persistent form over several tiles
     (3, 45, 20, 5, True, torch.float32),
     (2, 77, 256, 9, True, torch.float32),
     (3, 41, 200, 9, False, torch.float32),
     (2, 30, 24, 7, False, torch.float32),
     (3, 53, 96, 9, False, torch.bfloat16),
     (2, 19, 1024, 15, True, torch.float32),
+    (5, 900, 320, 4, False, torch.float32),  # persistent form, several tiles per workgroup
 ]
 
 
@@ -57,7 +59,7 @@ def test_dwconv1d_fwd_and_bwd_guards(B, T, C, K, causal, dt):
     w = datagen.normal((K, C), 1.0 / K, f"gb1/w/{C}/{K}", device=DEV).to(dt)
     b = datagen.normal((C,), 0.1, f"gb1/b/{C}", device=DEV).to(dt)
     dy = datagen.normal((B, T, C), 1.0, f"gb1/dy/{B}/{T}/{C}", device=DEV).to(dt)
-    lens = torch.tensor([T, T // 2 + 1, 0][:B], dtype=torch.int32)
+    lens = torch.tensor([T, T // 2 + 1, 0, max(T - 17, 0), min(7, T)][:B], dtype=torch.int32)
     L = lens.to(DEV)
     tol = TOL_BF16 if dt == torch.bfloat16 else TOL_F32
     say(f"guards dwconv1d B={B} T={T} C={C} K={K} causal={causal} {dt}")
