@@ -20,9 +20,10 @@
 // tile that lies wholly past the length stores zeros without loading.
 // Output uses non-temporal stores: nothing here reads it back.  fp32 at the
 // compiled widths (3, 4, 5, 9, 15) with at least 32 channel groups stages the
-// window through LDS instead (the LDS-staged form below), and at widths 3, 4,
-// 5 and 9 with 64 or more groups a persistent workgroup streams its tiles
-// through two LDS buffers (the persistent form below).
+// window through LDS instead: with 16-byte lanes a persistent workgroup
+// streams its tiles through two LDS buffers (the persistent form below), with
+// narrower lanes (a pointer off 16-byte alignment) each workgroup stages one
+// tile (the LDS-staged form below).
 #include "common.h"
 #include "launch.h"
 
@@ -195,12 +196,12 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_lds_kernel(
     }
 }
 
-// Persistent, double-buffered form (fp32 at widths 3, 4, 5 and 9 with at
-// least one full slab of 64 channel groups).  The one-shot form above loads
-// its tile, waits, computes and exits, so within a workgroup the loads never
+// Persistent, double-buffered form (fp32 at the compiled widths with 16-byte
+// lanes and at least 32 channel groups).  The one-shot form above loads its
+// tile, waits, computes and exits, so within a workgroup the loads never
 // overlap the FMAs and stores, and tens of thousands of short workgroups
-// leave gaps between them.  Here a fixed grid of about 256 workgroups walks
-// the 16-frame time tiles of its channel slab (tile g, g + G, g + 2G, ...),
+// leave gaps between them.  Here a fixed grid of workgroups walks the time
+// tiles (16 frames; 32 at K = 15) of its channel slab (tile g, g + G, ...),
 // and while it computes one tile the rows of its next tile are already on
 // their way into a second LDS buffer, by buffer-to-LDS loads
 // (buffer_load_dwordx4 ... lds) that hold no registers: lane i of a wave
@@ -218,20 +219,23 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_fwd_lds_kernel(
 // (lgkmcnt(0)) and the workgroup meets at a barrier.
 //
 // Measured in the full step on MI355X at [32,1500,512] causal: K3 35.5 ->
-// 33.4 us, K4 35.5 -> 32.0, K5 35.0 -> 32.2, K9 36.2 -> 34.9.  At K15 (30
-// staged rows per 16 frames) and at C = 200 (one partial slab) the one-shot
-// form stays ahead, and those keep it.
+// 33.4 us, K4 35.5 -> 32.0, K5 35.0 -> 32.2, K9 36.2 -> 34.9; K15 with
+// 32-frame tiles 37.0 -> 35.5 (with 16-frame tiles, 30 staged rows per 16
+// frames, it lost); [32,1500,200] K9 19.8 -> 19.2 on 512 workgroups (it lost
+// on 256, and on 1024).
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 #define DW_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)  // vmcnt(n) alone (gfx9 s_waitcnt layout)
 constexpr int kWaitLds = 0xC07F;                                 // lgkmcnt(0) alone
-constexpr int kPipeTile1d = 16;
+// Frames per tile: 16, and 32 at K = 15, where a 16-frame tile would stage
+// 30 rows for 16 outputs.
+constexpr int pipe_tile_1d(int K) { return K >= 15 ? 32 : 16; }
 // Stores of the persistent form: non-temporal with the sc1 scope bit (18);
 // measured ahead of non-temporal alone (2) in the full step.
 constexpr int kPipeStorePolicy = 18;
 
 template <int K>
 struct Pipe1d {
-    static constexpr int TW = kPipeTile1d, R = TW + K - 1, W = kBlock1d / 64, TT = TW / W;
+    static constexpr int TW = pipe_tile_1d(K), R = TW + K - 1, W = kBlock1d / 64, TT = TW / W;
     static constexpr int kR = (R + W - 1) / W;  // rows each wave loads; rows past R land in spare rows
     static constexpr int kRows = kR * W;
 };
@@ -416,19 +420,24 @@ static int tile_for(int64_t K, bool bf16) {
     }
 }
 
-// The fp32 forward takes the LDS-staged form at the compiled widths (3, 4, 5,
-// 9, 15) when there are at least 32 channel groups; a last slab of fewer than
+// The fp32 forward stages through LDS at the compiled widths (3, 4, 5, 9, 15)
+// when there are at least 32 channel groups; a last slab of fewer than
 // 64 groups leaves its other lanes idle (C = 200: 21.5 -> 19.9 us against the
 // register form).  At K <= 5 it is ahead since its loads are issued together
-// (K5 36.6 -> 34.7 us, K3 35.5 -> 35.0 at [32,1500,512] on MI355X).
+// (K5 36.6 -> 34.7 us, K3 35.5 -> 35.0 at [32,1500,512] on MI355X; figures
+// of the one-shot form).
 static bool lds_form_1d(int64_t K, int64_t CG) {
     return (K == 3 || K == 4 || K == 5 || K == 9 || K == 15) && CG >= 32;
 }
 
-// Of those, widths 3, 4, 5 and 9 with at least one full slab of 64 channel
-// groups take the persistent, double-buffered form, on about 256 workgroups.
-static bool pipe_form_1d(int64_t K, int64_t CG) { return (K == 3 || K == 4 || K == 5 || K == 9) && CG >= 64; }
-constexpr uint32_t kPipeWorkgroups1d = 256;
+// With 16-byte lanes those take the persistent, double-buffered form instead.
+// Its grid: 256 workgroups (one per CU) when the channels span two or more
+// slabs, 512 when they fit one and K < 15 (two per CU; a K = 15 workgroup's
+// 96 KiB of LDS leaves room for one).  Measured: [32,1500,512] 33.1 us on 256
+// against 35.0 on 512 (K3; K9 34.2 against 35.1); [32,1500,200] K9 19.2 on
+// 512 against 23.2 on 256 and 21.5 on 1024.
+static bool pipe_form_1d(int64_t K, int64_t CG) { return lds_form_1d(K, CG); }
+static uint32_t pipe_workgroups_1d(int64_t K, uint32_t n_slabs) { return n_slabs == 1 && K < 15 ? 512 : 256; }
 
 bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes, int vec) {
     // Per-item byte offsets, including the left padding as a negative
@@ -440,7 +449,7 @@ bool dwconv1d_fwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
     if (elem_bytes == 4 && lds_form_1d(K, C / vec))
         blocks = B * ((T + kLdsTile1d - 1) / kLdsTile1d) * ((C / vec + 63) / 64);
     // the persistent form counts its tiles, B * ceil(T / 16), in 32 bits
-    if (elem_bytes == 4 && pipe_form_1d(K, C / vec)) blocks = B * ((T + kPipeTile1d - 1) / kPipeTile1d);
+    if (elem_bytes == 4 && vec == 4 && pipe_form_1d(K, C / vec)) blocks = B * ((T + 15) / 16);
     return blocks < ((int64_t)1 << 31);
 }
 
@@ -455,10 +464,11 @@ static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int3
     const int32_t T32 = (int32_t)T, C32 = (int32_t)C, p32 = (int32_t)pL;
     if constexpr (sizeof(S) == 4 && V == 4) {
         if (pipe_form_1d(K, (int64_t)CG)) {
-            const uint32_t n_tt = (uint32_t)((T + kPipeTile1d - 1) / kPipeTile1d), n_sl = (CG + 63) / 64;
+            const int64_t TW = pipe_tile_1d((int)K);
+            const uint32_t n_tt = (uint32_t)((T + TW - 1) / TW), n_sl = (CG + 63) / 64;
             const uint32_t ntiles = (uint32_t)B * n_tt;
             if (ntiles == 0) return hipSuccess;
-            uint32_t G = kPipeWorkgroups1d / n_sl;
+            uint32_t G = pipe_workgroups_1d(K, n_sl) / n_sl;
             G = G < 1 ? 1 : (G > ntiles ? ntiles : G);
             const dim3 pgrid(G * n_sl);
             if (K == 3)
@@ -470,8 +480,11 @@ static hipError_t launch_typed(const S* x, const S* w, const S* bias, const int3
             else if (K == 5)
                 hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<5>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
                                    C32, p32, n_tt, n_sl, CG, ntiles);
-            else
+            else if (K == 9)
                 hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<9>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
+                                   C32, p32, n_tt, n_sl, CG, ntiles);
+            else
+                hipLaunchKernelGGL((dwconv1d_fwd_pipe_kernel<15>), pgrid, block, 0, st, x, w, bias, lengths, y, T32,
                                    C32, p32, n_tt, n_sl, CG, ntiles);
             return hipGetLastError();
         }

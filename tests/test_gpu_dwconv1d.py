@@ -57,7 +57,7 @@ GRID = [
     (2, 13, 4, 2, False), (2, 13, 4, 2, True), (1, 33, 100, 9, False), (3, 45, 200, 9, True),
     (2, 17, 256, 3, True), (2, 40, 12, 7, False), (2, 40, 12, 16, True), (1, 100, 1, 9, False),
     (2, 64, 128, 31, False), (3, 49, 6, 9, False), (1, 300, 64, 5, False),
-    # whole 64-lane slabs of 4-channel groups at K = 9, 15 (the LDS-staged fp32 form):
+    # whole 64-lane slabs of 4-channel groups at K = 9, 15 (the LDS-staged fp32 forms):
     # ragged 32-frame tiles, T below the tile and below K, several slabs
     (3, 70, 256, 9, False), (4, 31, 256, 9, True), (2, 33, 512, 15, True), (1, 5, 256, 15, False),
     (2, 97, 768, 9, True), (3, 64, 256, 15, False),
@@ -67,11 +67,13 @@ GRID = [
     # of 32 groups, T below the tile and a single frame
     (3, 70, 256, 3, False), (2, 45, 200, 4, True), (2, 33, 512, 5, True), (1, 5, 256, 4, False),
     (2, 1, 128, 3, True), (2, 65, 260, 5, False), (3, 40, 128, 4, False),
-    # the persistent form (K = 3, 4, 5, 9 with 64 or more groups): more 16-frame
-    # tiles than workgroups, so each workgroup walks two to four tiles through
-    # both LDS buffers; one to four slabs, a partial last slab, ragged tiles
+    # the persistent form (16-byte lanes, 32 or more groups): more tiles than
+    # workgroups, so each workgroup walks two to four tiles through both LDS
+    # buffers; one to four slabs, a partial last slab, a lone partial slab
+    # (512 workgroups), 32-frame tiles at K = 15, ragged tiles
     (6, 700, 512, 9, True), (5, 900, 256, 4, False), (9, 500, 320, 3, True),
     (4, 1000, 1024, 5, False), (17, 260, 256, 9, False), (3, 999, 516, 5, True),
+    (8, 900, 512, 15, True), (12, 1000, 200, 5, True), (9, 1300, 180, 15, False),
 ]
 
 
