@@ -34,7 +34,9 @@ Prints one JSON line on stdout (progress goes to stderr):
                the 8 TB/s HBM peak
   roofline     the dominant kernel's achieved algorithmic GB/s against 8 TB/s
   forward_target  the lowest fraction of 8 TB/s among the forward depthwise
-               rows, the row that sets it, and whether every one reaches 70%
+               rows, the row that sets it, and whether every one reaches 70%;
+               kernel_only: the same from the kernels' own durations in the
+               committed rocprofv3 summary (absent when that is out of date)
   rows         the same figures for every operation: mean time per call from
                HIP events (and its median, minimum and 90th percentile over
                the steps); kernel_us, the kernel-only mean from the committed
@@ -706,6 +708,15 @@ def main():
     forward_target = dict(bar=FORWARD_BAR, min_hbm_frac=low["hbm_frac"], row=low["row"],
                           rows_below=[r["row"] for r in fwd if r["hbm_frac"] < FORWARD_BAR],
                           met=all(r["hbm_frac"] >= FORWARD_BAR for r in fwd))
+    # the same from the kernels' own durations (the committed rocprofv3 summary),
+    # which leave out the dispatch latency that an event pair around a call adds
+    kfrac = {r["row"]: round(r["alg_bytes"] / (r["kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+             for r in fwd if r.get("kernel_us")}
+    if len(kfrac) == len(fwd):
+        klow = min(kfrac, key=kfrac.get)
+        forward_target["kernel_only"] = dict(min_hbm_frac=kfrac[klow], row=klow,
+                                             rows_below=[n for n, v in kfrac.items() if v < FORWARD_BAR],
+                                             met=all(v >= FORWARD_BAR for v in kfrac.values()))
 
     cpu, worst = None, None
     if not args.no_check:
