@@ -45,6 +45,9 @@ GRID = [
     # (B, Tc, C, K)
     (1, 1, 4, 3), (3, 1, 8, 9), (2, 2, 4, 5), (3, 7, 3, 4), (2, 50, 8, 15), (3, 5, 200, 9), (2, 17, 256, 3),
     (2, 13, 6, 1), (2, 9, 12, 2), (2, 20, 64, 7), (2, 40, 130, 31), (1, 100, 1, 9), (4, 8, 1024, 9),
+    # the persistent form (16-byte lanes, chunks of at most 8 frames, 32 or more channel
+    # groups): more streams than workgroups, a partial second slab, K = 15, one-frame chunks
+    (1200, 8, 256, 9), (700, 3, 384, 4), (2100, 1, 512, 5), (600, 8, 256, 15), (5, 6, 1024, 3),
 ]
 
 
@@ -55,14 +58,16 @@ def test_grid(B, Tc, C, K, dtype):
     check(x, w, b, cache, L, "grid")
 
 
+@pytest.mark.parametrize("C", [64, 256])
 @pytest.mark.parametrize("K", [3, 9, 15, 31])
-def test_chunks_equal_the_whole_causal_conv_bitwise(K):
+def test_chunks_equal_the_whole_causal_conv_bitwise(K, C):
     """Streaming a sequence chunk by chunk (ping-pong caches, ragged chunks)
     gives, bit for bit, the GPU's causal conv of the whole sequence, and the
-    final cache is its last K-1 frames."""
-    B, C, Tc, n = 3, 64, 6, 9
+    final cache is its last K-1 frames (C = 256: the persistent form at the
+    compiled widths)."""
+    B, Tc, n = 3, 6, 9
     r = np.random.default_rng(K)
-    chunks = [datagen.normal((B, Tc, C), 1.0, f"t1s/chunk/{K}/{i}", device=DEV) for i in range(n)]
+    chunks = [datagen.normal((B, Tc, C), 1.0, f"t1s/chunk/{K}/{C}/{i}", device=DEV) for i in range(n)]
     lens = [torch.as_tensor(r.integers(0, Tc + 1, B), dtype=torch.int32) for _ in range(n)]
     w = datagen.normal((K, C), 1.0 / K, f"t1s/w/{K}", device=DEV)
     b = datagen.normal((C,), 0.1, f"t1s/b/{K}", device=DEV)
@@ -84,10 +89,11 @@ def test_chunks_equal_the_whole_causal_conv_bitwise(K):
         assert_parity(whole, oracle.dwconv1d_fwd(seq[None], w, b, None, True)[0], TOL_F32, "whole sequence")
 
 
-def test_empty_chunks_keep_the_cache_and_masked_frames_are_never_read():
-    B, Tc, C, K = 3, 12, 32, 9
+@pytest.mark.parametrize("Tc,C", [(12, 32), (8, 512)])
+def test_empty_chunks_keep_the_cache_and_masked_frames_are_never_read(Tc, C):
+    B, K = 3, 9
     x, w, b, cache, _ = make(B, Tc, C, K, lens=[0, 0, 0])
-    L = torch.tensor([0, 5, 12], dtype=torch.int32, device=DEV)
+    L = torch.tensor([0, 5, Tc], dtype=torch.int32, device=DEV)
     y, c2 = check(x, w, b, cache, L, "empty and partial chunks")
     assert torch.equal(c2[0], cache[0]) and torch.all(y[0] == 0)
     xp = x.clone()
@@ -98,8 +104,9 @@ def test_empty_chunks_keep_the_cache_and_masked_frames_are_never_read():
     assert torch.equal(y, y2) and torch.equal(c2, c3)
 
 
-def test_zero_frame_chunk_copies_the_cache():
-    B, C, K = 2, 16, 5
+@pytest.mark.parametrize("C", [16, 256])
+def test_zero_frame_chunk_copies_the_cache(C):
+    B, K = 2, 5
     x, w, b, cache, _ = make(B, 1, C, K, lens=[1, 1])
     x0 = x[:, :0].contiguous()
     y, c2 = lib().dwconv1d_stream_fwd(x0, w, b, torch.zeros(B, dtype=torch.int32, device=DEV), cache)
