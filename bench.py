@@ -927,6 +927,13 @@ def summarize_profile(d):
     write = counter("write", "WRITE_SIZE")
     if not (fetch and write):
         return
+    # Rows are matched to dispatches by their order, so the counter runs must
+    # not include the oracle check, whose sub-batch calls dispatch the same
+    # kernels on fewer items and would be averaged into the rows' bytes.
+    for k in ("fetch", "write"):
+        if "--no-check" not in cmd(k):
+            raise SystemExit(f"{k} counter run was taken without --no-check: its per-row bytes would mix in "
+                             "the oracle check's dispatches; take it again with --no-check")
     copy_bytes = float(1 << 30)
 
     def calib(tab):

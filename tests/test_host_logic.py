@@ -97,3 +97,17 @@ def test_bench_forward_rows_are_the_forward_depthwise_kernels():
         "conv1d_bf16", "conv1d_causal_K3_C512", "conv1d_causal_K4_C512", "conv1d_causal_K5_C512",
         "conv1d_causal_K9_C512", "conv1d_causal_K15_C512", "conv1d_causal_K9_C200", "conv1d_stream_bf16",
         "stage_fwd", "stage_fwd_causal", "stage_fwd_bf16", "stage3_fwd"}
+
+
+def test_traffic_summary_refuses_counter_runs_taken_with_the_oracle_check(tmp_path):
+    """Rows are matched to counter dispatches by their order; a run that also
+    ran the oracle check has extra sub-batch dispatches, so it is refused."""
+    import bench
+    for kind, cname in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        d = tmp_path / kind
+        d.mkdir()
+        (d / "command.txt").write_text("rocprofv3 --pmc " + cname + " -- python3 bench.py --steps 1 --calib-copy\n")
+        (d / "run_counter_collection.csv").write_text(
+            "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n1,copyBuffer,%s,1048576\n" % cname)
+    with pytest.raises(SystemExit, match="--no-check"):
+        bench.summarize_profile(str(tmp_path))
