@@ -84,8 +84,11 @@ def test_grid(B, T, C, K, causal, dtype):
     check(x, w, b, lengths, causal, "grid")
 
 
-def test_lengths_clamped_and_null():
-    B, T, C, K = 4, 30, 8, 9
+@pytest.mark.parametrize("C", [8, 512])
+def test_lengths_clamped_and_null(C):
+    """Out-of-range lengths clamp to [0, T], NULL means T (C = 512: the
+    persistent form)."""
+    B, T, K = 4, 30, 9
     x, w, b, _ = make(B, T, C, K)
     lengths = torch.tensor([-5, 0, 31, 1000], dtype=torch.int32, device=DEV)
     y, _ = check(x, w, b, lengths, False, "out-of-range lengths")

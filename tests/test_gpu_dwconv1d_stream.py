@@ -114,6 +114,23 @@ def test_zero_frame_chunk_copies_the_cache(C):
     assert y.shape == (B, 0, C) and torch.equal(c2, cache)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_null_lengths_mean_full_chunks(dtype):
+    """lengths = NULL: every chunk is full, the same as lengths of Tc (C = 512,
+    the persistent form; C = 24, the tiled form, in fp32)."""
+    for C in ((512, 24) if dtype == torch.float32 else (512,)):
+        B, Tc, K = 40, 8, 9
+        x, w, b, cache, _ = make(B, Tc, C, K, dtype, lens=[Tc] * B)
+        full = torch.full((B,), Tc, dtype=torch.int32, device=DEV)
+        y0, c0 = lib().dwconv1d_stream_fwd(x, w, b, None, cache)
+        y1, c1 = lib().dwconv1d_stream_fwd(x, w, b, full, cache)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1) and torch.equal(c0, c1)
+        ry, rc = oracle.dwconv1d_stream_fwd(x, w, b, None, cache)
+        assert_parity(y0, ry, TOL_BF16 if dtype == torch.bfloat16 else TOL_F32, "null lengths")
+        assert np.array_equal(c0.float().cpu().numpy().astype(np.float64), rc)
+
+
 def test_same_cache_buffer_is_rejected():
     x, w, b, cache, L = make(2, 8, 16, 9)
     with pytest.raises(lib().DwconvError, match="different"):
