@@ -861,6 +861,10 @@ def summarize_profile(d):
                      if os.path.exists(os.path.join(d, k, "command.txt")) else "?")
     stats = _csv_rows(os.path.join(d, "stats", "**", "*kernel_stats.csv"))
     trace = _csv_rows(os.path.join(d, "stats", "**", "*kernel_trace.csv"))
+    if stats and "--no-check" not in cmd("stats"):
+        # rows are matched to dispatches by their order: the oracle check's
+        # sub-batch calls would be averaged into the rows' kernel-only times
+        raise SystemExit("the kernel-trace run was taken without --no-check; take it again with --no-check")
     if stats:
         lines = ["# rocprofv3 --kernel-trace --stats, one bench.py run on one MI355X",
                  "# command: " + cmd("stats"),
