@@ -108,3 +108,47 @@ def test_conv2d_forward_and_backward_captured():
         torch.cuda.synchronize()
         for name, got, r in zip(("y", "dx", "dw", "db"), (y, dx, dwt, db), ref):
             assert torch.equal(got, r), f"replay {rep}: {name}"
+
+
+def test_conv1d_forward_and_backward_captured():
+    """The 1-D forward's persistent form (C = 512, K = 9 and K = 15) and the
+    1-D backward, replayed from a graph, bit for bit against eager calls."""
+    dw = lib()
+    B, T, C = 6, 700, 512
+    x = datagen.normal((B, T, C), 1.0, "graph1d/x", device=DEV)
+    dy = datagen.normal((B, T, C), 1.0, "graph1d/dy", device=DEV)
+    L = torch.as_tensor(datagen.int_uniform(B, 0, T, "graph1d/len"), dtype=torch.int32).to(DEV)
+    w9 = datagen.normal((9, C), 1.0 / 9, "graph1d/w9", device=DEV)
+    w15 = datagen.normal((15, C), 1.0 / 15, "graph1d/w15", device=DEV)
+    b = datagen.normal((C,), 0.1, "graph1d/b", device=DEV)
+    y9, y15, dx = torch.empty_like(x), torch.empty_like(x), torch.empty_like(x)
+    gw, gb = torch.empty((9, C), device=DEV), torch.empty((C,), device=DEV)
+    ws = torch.empty((dw.dwconv1d_bwd_workspace_bytes(B, T, C, 9),), dtype=torch.uint8, device=DEV)
+
+    def step():
+        dw.dwconv1d_fwd(x, w9, b, L, y=y9, causal=True)
+        dw.dwconv1d_fwd(x, w15, b, L, y=y15, causal=False)
+        dw.dwconv1d_bwd(x, w9, L, dy, dx=dx, dw=gw, db=gb, workspace=ws, causal=True)
+
+    step()
+    torch.cuda.synchronize()
+    outs = (y9, y15, dx, gw, gb)
+    ref = [t.clone() for t in outs]
+    assert_parity(y9, oracle.dwconv1d_fwd(x, w9, b, L, True), 1e-5, "eager y (K9)")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for t in outs:
+            t.fill_(float("nan"))
+        ws.fill_(255)
+        torch.cuda.synchronize()
+        say(f"conv1d graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for name, got, r in zip(("y K9", "y K15", "dx", "dw", "db"), outs, ref):
+            assert torch.equal(got, r), f"replay {rep}: {name}"
