@@ -323,7 +323,7 @@ static dw_status dwconv2d_bwd_impl(const char* fn, const void* x, const void* w,
     // An empty batch or item still defines dw = 0 and db = 0; the launcher
     // writes those zeros when there is nothing to reduce.
     const void* ptrs[4] = {x, w, dy, dx};
-    const int vec = dw::pick_vec(C, es, ptrs, 4, 4);
+    const int vec = dw::pick_vec(C, es, ptrs, 4, dtype == DW_BF16 ? 8 : 4);
     return from_hip(dw::launch_dwconv2d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, g, dtype == DW_BF16, vec,
                                             (hipStream_t)stream), fn);
 }

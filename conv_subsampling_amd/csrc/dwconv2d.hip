@@ -285,7 +285,37 @@ struct AxisTerms {
     }
 };
 
-template <typename S, int V, int TQ, int PR, int PC>
+// Paired lanes: lane i < 32 holds 8 bf16 channels of column 2n and lane i + 32
+// the same 8 channels of column 2n + 1.  Two cross-half swaps give lane i the
+// first four channels of both columns (dwords x, y: column 2n; z, w: 2n + 1)
+// and lane i + 32 the last four; applied to that layout, the same two swaps
+// give back one column's 8 channels per lane.
+__device__ __forceinline__ void pair_swap(u32x4& t) {
+    const auto a = __builtin_amdgcn_permlane32_swap(t.x, t.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(t.y, t.w, false, false);
+    t.x = a[0]; t.z = a[1];
+    t.y = b[0]; t.w = b[1];
+}
+
+__device__ __forceinline__ Vf<4> widen_bf16x4(uint32_t lo, uint32_t hi) {
+    Vf<4> a;
+    a.v[0] = bf16_lo(lo); a.v[1] = bf16_hi(lo); a.v[2] = bf16_lo(hi); a.v[3] = bf16_hi(hi);
+    return a;
+}
+
+// PAIR (bf16 storage, V = 4): the x loads and dx stores move 16 bytes per
+// lane instead of 8.  Lanes i and i + 32 of a wave share channels
+// 8i .. 8i+7 of the channel block; for x columns 2n, 2n+1, lane i loads them
+// at column 2n and lane i + 32 at column 2n+1, and pair_swap leaves lane i
+// with channels 8i .. 8i+3 and lane i + 32 with 8i+4 .. 8i+7, of both
+// columns: the four-channel layout the arithmetic takes.  Between its load
+// and its use a lane's raw 16-byte piece rides in the xe registers of its row,
+// bit for bit (xo is not loaded), and the swap is made where it is used.  The
+// dx pair is swapped back before its 16-byte store.  A lane whose channels are past C
+// runs every load, swap and store (at out-of-range offsets), so that every
+// swap sees whole waves.  The host takes this form when C is a multiple of 8
+// and x and dx are 16-byte aligned.
+template <typename S, int V, int TQ, int PR, int PC, bool PAIR = false>
 __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     const S* __restrict__ x, const S* __restrict__ w, const int32_t* __restrict__ lengths,
     const S* __restrict__ dy, S* __restrict__ dx, double* __restrict__ partial, Geo2d geo,
@@ -303,8 +333,11 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
     const uint32_t G = gridDim.x / n_cblk;
     const uint32_t g = blk / n_cblk, cblk = blk - g * n_cblk;
-    const uint32_t cg = cblk * kLanes2d + threadIdx.x % kLanes2d;
+    const uint32_t lane = threadIdx.x % kLanes2d;
+    static_assert(!PAIR || (sizeof(S) == 2 && V == 4 && kLanes2d == 64), "paired lanes: bf16, 4 channels, waves of 64");
+    const uint32_t cg = PAIR ? cblk * kLanes2d + 2 * (lane % 32) + lane / 32 : cblk * kLanes2d + lane;
     const int32_t c0 = (int32_t)cg * V;
+    const bool chan_ok = cg < CG;  // with PAIR, lanes i and i + 32 are both in or both out (C % 8 == 0)
 
     double gw[9][V], gb[V];
 #pragma unroll
@@ -318,15 +351,15 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     Vf<V> wk[9];
 #pragma unroll
     for (int k = 0; k < 9; ++k) wk[k] = vzero<V>();
-    if (cg < CG) {
+    if (chan_ok) {
 #pragma unroll
         for (int k = 0; k < 9; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
     }
 
     for (uint32_t j = g; j < n_groups; j += G) {
         const uint32_t b = j / groups_per_item;
-        const uint32_t rb = (j - b * groups_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;
-        if (rb >= n_rb || cg >= CG) continue;
+        const uint32_t rb = (j - b * groups_per_item) * kRowsPerBlock + threadIdx.x / kLanes2d;  // one per wave
+        if (rb >= n_rb || (!PAIR && !chan_ok)) continue;
         const int32_t len = (int32_t)item_length(lengths, b, T);
         const int32_t leno = out_rows(len, geo);
         const uint32_t xrow = (uint32_t)(F * C * es), grow = (uint32_t)(Fo * C * es);
@@ -340,17 +373,34 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
         const int32_t xr0 = 2 * t0;                        // its first x row
         const int32_t na = (int32_t)(rb % geo.nqc) * geo.qcols;  // quad columns na .. nb-1
         const int32_t nb = min(geo.NQf, na + geo.qcols);
+        // PAIR: the offset of this lane's 16-byte piece of x (and dx) columns
+        // ce, ce + 1 within a row, out of range where that column or these
+        // channels do not exist.
+        const uint32_t pair_off = (lane / 32) * (uint32_t)pix + (cblk * kLanes2d + 2 * (lane % 32)) * V * es;
+        auto pair_col = [&](int32_t ce) -> uint32_t {
+            return chan_ok && ce + (int32_t)(lane / 32) < F ? (uint32_t)(ce * pix) + pair_off : kOutOfRange;
+        };
 
         if (xr0 >= len && t0 >= leno) {
             // Every x row of this block is masked, and so is every g row it
             // adds to db: dx is zero and nothing adds to dw or db.
             if (dx) {
-                const Vf<V> z = vzero<V>();
                 const int32_t fa = 2 * na, fb = min(F, 2 * nb);
-                for (int32_t f = fa; f < fb; ++f)
+                if constexpr (PAIR) {
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    for (int32_t f = fa; f < fb; f += 2) {
+                        const uint32_t po = pair_col(f);
 #pragma unroll
-                    for (int r = 0; r < 2 * TQ; ++r)
-                        Buf<S, V>::template store<kStorePolicy2d>(dxr, (uint32_t)(xr0 + r) * xrow + (uint32_t)(f * pix) + coff, z);
+                        for (int r = 0; r < 2 * TQ; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b128(z, dxr, (uint32_t)(xr0 + r) * xrow + po, 0, kStorePolicy2d);
+                    }
+                } else {
+                    const Vf<V> z = vzero<V>();
+                    for (int32_t f = fa; f < fb; ++f)
+#pragma unroll
+                        for (int r = 0; r < 2 * TQ; ++r)
+                            Buf<S, V>::template store<kStorePolicy2d>(dxr, (uint32_t)(xr0 + r) * xrow + (uint32_t)(f * pix) + coff, z);
+                }
             }
             continue;
         }
@@ -371,25 +421,49 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
             for (int q = 0; q <= TQ; ++q)
                 gn[q] = select_v<V>(n + 1 < Fo,
                                     Buf<S, V>::load(gr, (uint32_t)((t0 + q) * (int32_t)grow + (n + 1) * pix) + coff));
-            const uint32_t eo = ce < F ? (uint32_t)(ce * pix) : kOutOfRange;
-            const uint32_t oo = ce + 1 < F ? (uint32_t)((ce + 1) * pix) : kOutOfRange;
+            if constexpr (PAIR) {
+                const uint32_t po = pair_col(ce);
 #pragma unroll
-            for (int r = 0; r < 2 * TQ; ++r) {
-                const uint32_t ro = (uint32_t)((xr0 + r) * (int32_t)xrow) + coff;
-                xe[r] = Buf<S, V>::template load<kBwdXPolicy>(xr, ro + eo);
-                xo[r] = Buf<S, V>::template load<kBwdXPolicy>(xr, ro + oo);
+                for (int r = 0; r < 2 * TQ; ++r) {
+                    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)((xr0 + r) * (int32_t)xrow) + po, 0,
+                                                                          kBwdXPolicy);
+                    xe[r].v[0] = __uint_as_float(t.x); xe[r].v[1] = __uint_as_float(t.y);
+                    xe[r].v[2] = __uint_as_float(t.z); xe[r].v[3] = __uint_as_float(t.w);
+                }
+            } else {
+                const uint32_t eo = ce < F ? (uint32_t)(ce * pix) : kOutOfRange;
+                const uint32_t oo = ce + 1 < F ? (uint32_t)((ce + 1) * pix) : kOutOfRange;
+#pragma unroll
+                for (int r = 0; r < 2 * TQ; ++r) {
+                    const uint32_t ro = (uint32_t)((xr0 + r) * (int32_t)xrow) + coff;
+                    xe[r] = Buf<S, V>::template load<kBwdXPolicy>(xr, ro + eo);
+                    xo[r] = Buf<S, V>::template load<kBwdXPolicy>(xr, ro + oo);
+                }
             }
         };
         // The quads of column n, given its loads; g column n+1 becomes the
         // current column afterwards.  Each pair of x rows and each pair of x
         // columns takes its terms from AxisTerms; db adds g[m][n] once per
         // quad (and the g column past the last quad after the walk).
-        auto quads = [&](int32_t n, const Vf<V>(&gnext)[TQ + 1], const Vf<V>(&xe)[2 * TQ],
-                         const Vf<V>(&xo)[2 * TQ]) {
+        auto quads = [&](int32_t n, const Vf<V>(&gnext)[TQ + 1], const Vf<V>(&xe_in)[2 * TQ],
+                         const Vf<V>(&xo_in)[2 * TQ]) {
             using R = AxisTerms<PR>;
             using Cc = AxisTerms<PC>;
             const int32_t ce = 2 * n;
-            const bool col_ok[2] = {ce < F, ce + 1 < F};
+            Vf<V> xe[2 * TQ], xo[2 * TQ];
+#pragma unroll
+            for (int r = 0; r < 2 * TQ; ++r) {
+                if constexpr (PAIR) {
+                    u32x4 t = {__float_as_uint(xe_in[r].v[0]), __float_as_uint(xe_in[r].v[1]),
+                               __float_as_uint(xe_in[r].v[2]), __float_as_uint(xe_in[r].v[3])};
+                    pair_swap(t);
+                    xe[r] = widen_bf16x4(t.x, t.y);
+                    xo[r] = widen_bf16x4(t.z, t.w);
+                } else {
+                    xe[r] = xe_in[r];
+                    xo[r] = xo_in[r];
+                }
+            }
 #pragma unroll
             for (int q = 0; q < TQ; ++q) {
                 const Vf<V> G[2][2] = {{gcur[q], gnext[q]}, {gcur[q + 1], gnext[q + 1]}};  // g[m+i][n+j]
@@ -427,13 +501,29 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
                     // those stores are skipped; rows at or past T are past the
                     // resource and dropped.
                     const int32_t te = xr0 + 2 * q;
+                    if constexpr (PAIR) {
+                        const uint32_t po = pair_col(ce);
 #pragma unroll
-                    for (int ec = 0; ec < 2; ++ec)
+                        for (int er = 0; er < 2; ++er) {
+                            const Vf<V> de = select_v<V>(te + er < len, D[er][0]);
+                            const Vf<V> dd = select_v<V>(te + er < len, D[er][1]);
+                            u32x4 t = {pack_bf16x2(de.v[0], de.v[1]), pack_bf16x2(de.v[2], de.v[3]),
+                                       pack_bf16x2(dd.v[0], dd.v[1]), pack_bf16x2(dd.v[2], dd.v[3])};
+                            pair_swap(t);
+                            __builtin_amdgcn_raw_buffer_store_b128(t, dxr, (uint32_t)((te + er) * (int32_t)xrow) + po, 0,
+                                                                   kStorePolicy2d);
+                        }
+                    } else {
+                        const bool col_ok[2] = {ce < F, ce + 1 < F};
 #pragma unroll
-                        for (int er = 0; er < 2; ++er)
-                            if (col_ok[ec])
-                                Buf<S, V>::template store<kStorePolicy2d>(dxr, (uint32_t)((te + er) * (int32_t)xrow + (ce + ec) * pix) + coff,
-                                                 select_v<V>(te + er < len, D[er][ec]));
+                        for (int ec = 0; ec < 2; ++ec)
+#pragma unroll
+                            for (int er = 0; er < 2; ++er)
+                                if (col_ok[ec])
+                                    Buf<S, V>::template store<kStorePolicy2d>(
+                                        dxr, (uint32_t)((te + er) * (int32_t)xrow + (ce + ec) * pix) + coff,
+                                        select_v<V>(te + er < len, D[er][ec]));
+                    }
                 }
             }
 #pragma unroll
@@ -473,7 +563,7 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     // Sum the row blocks of this workgroup in a fixed order (row block 0
     // first), then write one partial per workgroup: partial[p][k][c], k = 0..8
     // the taps, 9 the bias.
-    const uint32_t lane = threadIdx.x % kLanes2d, rsub = threadIdx.x / kLanes2d;
+    const uint32_t rsub = threadIdx.x / kLanes2d;
     if (rsub > 0) {
 #pragma unroll
         for (int e = 0; e < V; ++e) {
@@ -487,7 +577,7 @@ __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     const uint32_t p = g;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-        const int32_t c = ((int32_t)cblk * kLanes2d + (int32_t)lane) * V + e;
+        const int32_t c = PAIR ? c0 + e : ((int32_t)cblk * kLanes2d + (int32_t)lane) * V + e;
         if (c >= C) continue;
 #pragma unroll
         for (int k = 0; k < 10; ++k) {
@@ -668,7 +758,7 @@ size_t dwconv2d_bwd_workspace(int64_t B, const Conv2dGeom& c) {
     return (size_t)(rows * 10 * c.C * (int64_t)sizeof(double));
 }
 
-template <typename S, int V>
+template <typename S, int V, bool PAIR = false>
 static hipError_t launch_bwd_typed(const S* x, const S* w, const int32_t* lengths, const S* dy, S* dx, float* dw,
                                    float* db, double* partial, int64_t B, const Conv2dGeom& c, hipStream_t st) {
     constexpr int TQ = bwd_rows<S>();
@@ -680,16 +770,16 @@ static hipError_t launch_bwd_typed(const S* x, const S* w, const int32_t* length
     if (blocks > 0 && (dx || partial)) {
         const dim3 grid((uint32_t)blocks), block(kBlock2d);
         if (geo.dt == 0 && geo.df == 0)
-            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 0, 0>), grid, block, 0, st, x, w, lengths, dy, dx,
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 0, 0, PAIR>), grid, block, 0, st, x, w, lengths, dy, dx,
                                partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         else if (geo.dt == 1 && geo.df == 1)
-            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 1, 1>), grid, block, 0, st, x, w, lengths, dy, dx,
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 1, 1, PAIR>), grid, block, 0, st, x, w, lengths, dy, dx,
                                partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         else if (geo.dt == 1)
-            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 1, 0>), grid, block, 0, st, x, w, lengths, dy, dx,
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 1, 0, PAIR>), grid, block, 0, st, x, w, lengths, dy, dx,
                                partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         else
-            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 0, 1>), grid, block, 0, st, x, w, lengths, dy, dx,
+            hipLaunchKernelGGL((dwconv2d_bwd_kernel<S, V, TQ, 0, 1, PAIR>), grid, block, 0, st, x, w, lengths, dy, dx,
                                partial, geo, g.n_rb, CG, n_cblk, g.groups_per_item, g.n_groups);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -705,7 +795,7 @@ static hipError_t launch_bwd_typed(const S* x, const S* w, const int32_t* length
 }
 
 #ifndef DW2D_BWD_VEC
-#define DW2D_BWD_VEC 4
+#define DW2D_BWD_VEC 8
 #endif
 
 template <typename S>
@@ -718,6 +808,10 @@ static hipError_t launch_bwd_s(const void* x, const void* w, const int32_t* leng
     S* dxs = (S*)dx;
     if (vec > DW2D_BWD_VEC) vec = DW2D_BWD_VEC;
     switch (vec) {
+        case 8:  // bf16 only: 16-byte x and dx accesses through paired lanes
+            if constexpr (sizeof(S) == 2)
+                return launch_bwd_typed<S, 4, true>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
+            return launch_bwd_typed<S, 4>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
         case 4: return launch_bwd_typed<S, 4>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
         case 2: return launch_bwd_typed<S, 2>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);
         default: return launch_bwd_typed<S, 1>(xs, ws, lengths, gs, dxs, dw, db, partial, B, c, st);

@@ -210,3 +210,37 @@ def test_unaligned_pointers_take_the_narrow_path(pads, bf16):
     assert_parity(y, oracle.dwconv2d_fwd(s["x"], s["w"], s["b"], s["L"], pads=pads), tol, "unaligned fwd")
     rdx, _, _ = oracle.dwconv2d_bwd(s["x"], s["w"], s["L"], s["dy"], pads=pads)
     assert_parity(dx, rdx, tol, "unaligned dx")
+
+
+def _offset8(t):
+    """A copy of t whose storage starts 8 bytes past a 16-byte-aligned address."""
+    k = 8 // t.element_size()
+    buf = torch.empty(t.numel() + k, dtype=t.dtype, device=t.device)
+    out = buf[k:].view(t.shape)
+    out.copy_(t)
+    return out
+
+
+@pytest.mark.parametrize("pads", [(1, 1, 1, 1), CAUSAL, (2, 1, 1, 1), (1, 1, 2, 1)],
+                         ids=["symmetric", "causal", "causal-time", "causal-freq"])
+@pytest.mark.parametrize("B,T,F,C", [(3, 30, 21, 64), (2, 25, 64, 256), (2, 19, 9, 40), (2, 14, 33, 520)])
+def test_bf16_backward_paired_lanes_match_eight_byte_lanes(B, T, F, C, pads):
+    """With C a multiple of 8 and 16-byte-aligned x and dx, the bf16 backward
+    moves 16 bytes per lane, two lanes sharing 8 channels of two columns.  x
+    and dx 8 bytes off that alignment take 8-byte lanes instead; both forms
+    run the same arithmetic in the same order, so dx, dw and db agree bit for
+    bit.  Shapes: partial channel blocks (C = 40, 520), odd F (the last
+    column pair has one column), masked rows."""
+    s = make(B, T, F, C, pads, bf16=True, lens=[T, T // 2 + 1, 0][:B])
+    say(f"dwconv2d bf16 paired against 8-byte lanes B={B} T={T} F={F} C={C} pads={pads}")
+    wide = lib().dwconv2d_bwd(s["x"], s["w"], s["L"], s["dy"], pads=pads)
+    x8 = _offset8(s["x"])
+    dx8 = _offset8(torch.full_like(s["x"], float("nan")))
+    dw8, db8 = lib().dwconv2d_bwd(x8, s["w"], s["L"], s["dy"], dx=dx8, pads=pads)[1:]
+    sync()
+    assert torch.equal(wide[0], dx8), "dx"
+    assert torch.equal(wide[1], dw8) and torch.equal(wide[2], db8), "dw, db"
+    rdx, rdw, rdb = oracle.dwconv2d_bwd(s["x"], s["w"], s["L"], s["dy"], pads=pads)
+    assert_parity(wide[0], rdx, TOL_BF16, "paired dx")
+    assert_parity(wide[1], rdw, TOL_F32, "paired dw")
+    assert_parity(wide[2], rdb, TOL_F32, "paired db")
