@@ -1080,6 +1080,160 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
     }
 }
 
+// Paired lanes (fp32, 16-byte-aligned tensors, K = 9 or 15): two channels per
+// lane, so the fp64 sums take half the registers of the four-channel form and
+// three waves fit per SIMD, while every x and dy load and every dx store still
+// moves 16 bytes.  Lanes i and i + 32 of a wave share four channels
+// (4(cblk*32 + i) .. +3): of each pair of consecutive frames, lane i loads the
+// even one and lane i + 32 the odd one, and two cross-half swaps
+// (v_permlane32_swap) leave lane i with channels 0-1 and lane i + 32 with
+// channels 2-3 of the four, at both frames.  dx goes back through the same
+// swaps before lane i stores the even frame and lane i + 32 the odd one.  The
+// arithmetic is the two-channel form's, term for term.  A lane whose channels
+// are past C runs every load, swap and store at out-of-range offsets, so that
+// the swaps see whole waves.
+__device__ __forceinline__ void pair_swap_1d(u32x4& t) {
+    const auto a = __builtin_amdgcn_permlane32_swap(t.x, t.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(t.y, t.w, false, false);
+    t.x = a[0]; t.z = a[1];
+    t.y = b[0]; t.w = b[1];
+}
+
+template <int K, bool CAUSAL, int TT>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_pair_kernel(
+    const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
+    const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
+    uint32_t n_tb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
+    constexpr int V = 2, NW = TT + K - 1;
+    static_assert(TT % 2 == 0 && NW % 2 == 0, "frames are loaded in pairs");
+    constexpr int pL = CAUSAL ? K - 1 : (K - 1) / 2;
+    __shared__ double red[kSubs1b - 1][K + 1][kLanes1b * V];
+    const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
+    const uint32_t G = gridDim.x / n_cblk;
+    const uint32_t g = blk / n_cblk, cblk = blk - g * n_cblk;
+    const uint32_t lane = threadIdx.x % kLanes1b, sub = threadIdx.x / kLanes1b;
+    const uint32_t half = lane / 32;
+    // CG counts two-channel groups; lanes i and i + 32 hold groups 2i and 2i + 1
+    // of the block (both valid or both not, since C % 4 == 0)
+    const uint32_t cg = cblk * kLanes1b + 2 * (lane % 32) + half;
+    const bool cvalid = cg < CG;
+    const int32_t c0 = (int32_t)(cvalid ? cg : 0) * V;
+    const uint32_t row = (uint32_t)C * sizeof(float);
+    // this lane's 16-byte piece of a frame: the pair's four channels
+    const uint32_t qoff = cvalid ? (uint32_t)(c0 - 2 * (int32_t)half) * (uint32_t)sizeof(float) : 0x80000000u;
+
+    Vf<V> wk[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
+    double gw[K][V], gb[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        gb[e] = 0.0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) gw[k][e] = 0.0;
+    }
+
+    for (uint32_t j = g; j < n_groups; j += G) {
+        const uint32_t b = j / groups_per_item;
+        const uint32_t tb = (j - b * groups_per_item) * kSubs1b + sub;  // one per wave
+        if (tb >= n_tb) continue;
+        const int32_t len = (int32_t)item_length(lengths, b, T);
+        const int32_t u0 = (int32_t)tb * TT;
+        const int64_t item = (int64_t)b * T * C;
+        const rsrc_t dxr = make_rsrc(dx ? dx + item : x, dx ? (uint32_t)T * row : 0u);
+        if (u0 >= len) {
+            // masked input frames: dx is zero, and there is nothing to add
+            if (dx) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int p = 0; p < TT / 2; ++p)
+                    __builtin_amdgcn_raw_buffer_store_b128(z, dxr, (uint32_t)(u0 + 2 * p + (int32_t)half) * row + qoff, 0,
+                                                           kNonTemporal);
+            }
+            continue;
+        }
+        const rsrc_t gr = make_rsrc(dy + item, (uint32_t)len * row);
+        const rsrc_t xr = make_rsrc(x + item, (uint32_t)len * row);
+        const int32_t gs = u0 + pL - (K - 1);  // first gradient frame of the window
+        u32x4 graw[NW / 2], xraw[TT / 2];
+#pragma unroll
+        for (int p = 0; p < NW / 2; ++p)
+            graw[p] = __builtin_amdgcn_raw_buffer_load_b128(gr, (uint32_t)((gs + 2 * p + (int32_t)half) * (int32_t)row) + qoff,
+                                                            0, kLoadPolicy);
+#pragma unroll
+        for (int p = 0; p < TT / 2; ++p)
+            xraw[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(u0 + 2 * p + (int32_t)half) * row + qoff, 0,
+                                                            kBwdXPolicy1d);
+        Vf<V> gwin[NW], xv[TT];
+#pragma unroll
+        for (int p = 0; p < NW / 2; ++p) {
+            u32x4 t = graw[p];
+            pair_swap_1d(t);
+            gwin[2 * p].v[0] = __uint_as_float(t.x); gwin[2 * p].v[1] = __uint_as_float(t.y);
+            gwin[2 * p + 1].v[0] = __uint_as_float(t.z); gwin[2 * p + 1].v[1] = __uint_as_float(t.w);
+        }
+#pragma unroll
+        for (int p = 0; p < TT / 2; ++p) {
+            u32x4 t = xraw[p];
+            pair_swap_1d(t);
+            xv[2 * p].v[0] = __uint_as_float(t.x); xv[2 * p].v[1] = __uint_as_float(t.y);
+            xv[2 * p + 1].v[0] = __uint_as_float(t.z); xv[2 * p + 1].v[1] = __uint_as_float(t.w);
+        }
+#pragma unroll
+        for (int p = 0; p < TT / 2; ++p) {
+            Vf<V> d[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int i = 2 * p + h;
+                d[h] = vzero<V>();
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int e = 0; e < V; ++e) {
+                        const float gv = gwin[i + K - 1 - k].v[e];
+                        d[h].v[e] = __builtin_fmaf(gv, wk[k].v[e], d[h].v[e]);
+                        gw[k][e] = __builtin_fma((double)gv, (double)xv[i].v[e], gw[k][e]);
+                    }
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    gb[e] += (double)gwin[i + K - 1 - pL].v[e];
+                    d[h].v[e] = u0 + i < len ? d[h].v[e] : 0.0f;
+                }
+            }
+            if (dx) {
+                u32x4 t = {__float_as_uint(d[0].v[0]), __float_as_uint(d[0].v[1]), __float_as_uint(d[1].v[0]),
+                           __float_as_uint(d[1].v[1])};
+                pair_swap_1d(t);
+                __builtin_amdgcn_raw_buffer_store_b128(t, dxr, (uint32_t)(u0 + 2 * p + (int32_t)half) * row + qoff, 0,
+                                                       kNonTemporal);
+            }
+        }
+    }
+
+    if (!partial) return;  // uniform: dw and db not requested
+    if (sub > 0) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) red[sub - 1][k][lane * V + e] = gw[k][e];
+            red[sub - 1][K][lane * V + e] = gb[e];
+        }
+    }
+    __syncthreads();
+    if (sub > 0 || !cvalid) return;
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const int32_t c = c0 + e;
+#pragma unroll
+        for (int k = 0; k <= K; ++k) {
+            double s = k < K ? gw[k][e] : gb[e];
+#pragma unroll
+            for (int q = 0; q < kSubs1b - 1; ++q) s += red[q][k][lane * V + e];
+            partial[((int64_t)g * (K + 1) + k) * C + c] = s;
+        }
+    }
+}
+
 struct Bwd1dGrid {
     uint32_t n_tb, groups_per_item, n_groups, G;
 };
@@ -1090,19 +1244,34 @@ static int bwd1d_vec(int vec, int64_t K) {
     return vec >= 4 && vm >= 4 ? 4 : (vec >= 2 && vm >= 2 ? 2 : 1);
 }
 
+#ifndef DW1B_PAIR
+#define DW1B_PAIR 1
+#endif
+#ifndef DW1B_PAIR_WGS
+#define DW1B_PAIR_WGS 512
+#endif
+// Whether an fp32 call with 16-byte-aligned tensors takes the paired-lane form.
+static bool bwd1d_pair(int vec, int64_t K, bool bf16) {
+    return DW1B_PAIR && !bf16 && vec >= 4 && (K == 9 || K == 15);
+}
+
 // Persistent grid: G workgroups per channel block.  With 16-byte lanes
 // about DW1D_BWD_WGS workgroups in all (one per CU), with narrower lanes
 // DW1D_BWD_WGS per channel block (measured on MI355X at [32..128,1500,512]:
 // K9 and K5 on 16-byte lanes 2-6% faster with 256 in all than with 512;
 // K15 on 8-byte lanes 3% slower with 512 in all than with 1024).
-static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V) {
+// The paired-lane form (two channels per lane, 16-byte accesses) takes about
+// DW1B_PAIR_WGS workgroups in all.
+static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V, bool pair = false) {
     Bwd1dGrid g;
     g.n_tb = (uint32_t)((T + kBwdTile1d - 1) / kBwdTile1d);
     g.groups_per_item = (g.n_tb + kSubs1b - 1) / kSubs1b;
     const uint64_t n = (uint64_t)B * g.groups_per_item;
     g.n_groups = (uint32_t)n;
+    if (pair) V = 2;
     const int64_t n_cblk = ((C + V - 1) / V + kLanes1b - 1) / kLanes1b;
-    const int64_t per = V >= 4 ? (n_cblk > 0 ? (DW1D_BWD_WGS + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
+    const int64_t wide = pair ? DW1B_PAIR_WGS : DW1D_BWD_WGS;
+    const int64_t per = V >= 4 || pair ? (n_cblk > 0 ? (wide + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
     g.G = (uint32_t)(n < (uint64_t)per ? n : (uint64_t)per);
     return g;
 }
@@ -1111,7 +1280,8 @@ bool dwconv1d_bwd_supported(int64_t K) {
     return K == 3 || K == 4 || K == 5 || K == 7 || K == 9 || K == 15 || K == 31;
 }
 
-int dwconv1d_bwd_max_vec(int64_t K) { return bwd1d_vmax((int)K); }
+// The paired-lane form takes 16-byte accesses at K = 9 and 15 whatever its lane width.
+int dwconv1d_bwd_max_vec(int64_t K) { return DW1B_PAIR && (K == 9 || K == 15) ? 4 : bwd1d_vmax((int)K); }
 
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
     if (!product_below((int64_t)1 << 31, {T + K + 32, C, elem_bytes})) return false;
@@ -1120,7 +1290,7 @@ bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
 
 size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
     // enough for whichever lane width the pointers' alignment allows
-    int64_t P = 0;
+    int64_t P = bwd1d_grid(B, T, C, 2, true).G;
     for (int v : {1, 2, 4}) {
         const int64_t p = bwd1d_grid(B, T, C, v).G;
         P = p > P ? p : P;
@@ -1142,6 +1312,19 @@ static hipError_t launch_bwd1d_typed(const S* x, const S* w, const int32_t* leng
     return hipGetLastError();
 }
 
+template <int K, bool CAUSAL>
+static hipError_t launch_bwd1d_pair(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
+                                    double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+    const Bwd1dGrid g = bwd1d_grid(B, T, C, 2, true);
+    const uint32_t CG = (uint32_t)(C / 2);
+    const uint32_t n_cblk = (CG + kLanes1b - 1) / kLanes1b;
+    if (g.G == 0 || (!dx && !partial)) return hipSuccess;
+    hipLaunchKernelGGL((dwconv1d_bwd_pair_kernel<K, CAUSAL, kBwdTile1d>), dim3(g.G * n_cblk), dim3(kBlock1d), 0, st,
+                       x, w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk, g.groups_per_item,
+                       g.n_groups);
+    return hipGetLastError();
+}
+
 template <typename S, int K, bool CAUSAL>
 static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const int32_t* lengths, const void* dyv,
                                  void* dxv, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
@@ -1150,6 +1333,9 @@ static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const 
     const S* w = (const S*)wv;
     const S* dy = (const S*)dyv;
     S* dx = (S*)dxv;
+    if constexpr (sizeof(S) == 4 && (K == 9 || K == 15)) {
+        if (bwd1d_pair(vec, K, false)) return launch_bwd1d_pair<K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    }
     if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<S, (VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
     if (vec >= 2 && VMAX >= 2) return launch_bwd1d_typed<S, (VMAX >= 2 ? 2 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
     return launch_bwd1d_typed<S, 1, K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
@@ -1181,7 +1367,7 @@ hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* leng
     }
 #undef DW1B_CASE
     if (e != hipSuccess || !partial) return e;
-    const int64_t P = bwd1d_grid(B, T, C, bwd1d_vec(vec, K)).G;
+    const int64_t P = bwd1d_grid(B, T, C, bwd1d_vec(vec, K), bwd1d_pair(vec, K, bf16)).G;
     RowOutputs out = {};
     out.n = 2;
     out.p[0] = dw; out.first[0] = 0; out.count[0] = (int32_t)K;

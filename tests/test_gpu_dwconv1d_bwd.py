@@ -173,3 +173,38 @@ def test_bf16_conv_module_full_size():
     assert_parity(gx, rx, TOL_BF16, "full bf16 dx")
     assert_parity(gw, rw, TOL_F32, "full bf16 dw")
     assert_parity(gb, rb, TOL_F32, "full bf16 db")
+
+
+def _offset8(t):
+    """A copy of t whose storage starts 8 bytes past a 16-byte-aligned address."""
+    k = 8 // t.element_size()
+    buf = torch.empty(t.numel() + k, dtype=t.dtype, device=t.device)
+    out = buf[k:].view(t.shape)
+    out.copy_(t)
+    return out
+
+
+@pytest.mark.parametrize("B,T,C,K,causal", [(3, 75, 512, 9, True), (2, 61, 100, 9, False), (4, 40, 20, 15, True),
+                                            (2, 33, 260, 15, False), (3, 130, 8, 9, False)])
+def test_paired_lanes_match_eight_byte_lanes(B, T, C, K, causal):
+    """fp32 at K = 9 and 15 with 16-byte-aligned tensors takes the paired-lane
+    form (two channels per lane, 16-byte loads and stores through cross-half
+    swaps).  The same call 8 bytes off that alignment takes two-channel lanes
+    with 8-byte accesses.  Both run the same per-element arithmetic: dx is
+    equal bit for bit; dw and db are the same fp64 sums over another split of
+    the tiles across workgroups, so they agree to within one float32 ulp."""
+    x, w, dy, L = make(B, T, C, K, lens=[T, T // 2 + 1, 0, max(T - 9, 0)][:B])
+    say(f"dwconv1d_bwd paired against 8-byte lanes B={B} T={T} C={C} K={K} causal={causal}")
+    wide = run(x, w, L, dy, causal)
+    x8, dy8 = _offset8(x), _offset8(dy)
+    dx8 = _offset8(torch.full_like(x, float("nan")))
+    _, dw8, db8 = lib().dwconv1d_bwd(x8, w, L, dy8, dx=dx8, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[0], dx8), "dx"
+    for a, b in ((wide[1], dw8), (wide[2], db8)):
+        mag = torch.maximum(a.abs(), b.abs())
+        ulp = torch.nextafter(mag, torch.full_like(mag, float("inf"))) - mag
+        assert torch.all((a - b).abs() <= ulp)
+    ref = oracle.dwconv1d_bwd(x, w, L, dy, causal)
+    for name, g, r in zip(("dx", "dw", "db"), wide, ref):
+        assert_parity(g, r, TOL_F32, f"paired {name}")
