@@ -223,7 +223,8 @@ def _offset8(t):
 
 @pytest.mark.parametrize("pads", [(1, 1, 1, 1), CAUSAL, (2, 1, 1, 1), (1, 1, 2, 1)],
                          ids=["symmetric", "causal", "causal-time", "causal-freq"])
-@pytest.mark.parametrize("B,T,F,C", [(3, 30, 21, 64), (2, 25, 64, 256), (2, 19, 9, 40), (2, 14, 33, 520)])
+@pytest.mark.parametrize("B,T,F,C", [(3, 30, 21, 64), (2, 25, 64, 256), (2, 19, 9, 40), (2, 14, 33, 520),
+                                     (1, 1, 1, 8), (3, 3, 2, 16), (2, 2, 3, 8)])
 def test_bf16_backward_paired_lanes_match_eight_byte_lanes(B, T, F, C, pads):
     """With C a multiple of 8 and 16-byte-aligned x and dx, the bf16 backward
     moves 16 bytes per lane, two lanes sharing 8 channels of two columns.  x
