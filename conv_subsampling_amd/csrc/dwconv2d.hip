@@ -311,10 +311,10 @@ __device__ __forceinline__ Vf<4> widen_bf16x4(uint32_t lo, uint32_t hi) {
 // columns: the four-channel layout the arithmetic takes.  Between its load
 // and its use a lane's raw 16-byte piece rides in the xe registers of its row,
 // bit for bit (xo is not loaded), and the swap is made where it is used.  The
-// dx pair is swapped back before its 16-byte store.  A lane whose channels are past C
-// runs every load, swap and store (at out-of-range offsets), so that every
-// swap sees whole waves.  The host takes this form when C is a multiple of 8
-// and x and dx are 16-byte aligned.
+// dx pair is swapped back before its 16-byte store.  A lane whose channels
+// are past C runs every load, swap and store (at out-of-range offsets), so
+// that every swap sees whole waves.  The host takes this form when C is a
+// multiple of 8 and x and dx are 16-byte aligned.
 template <typename S, int V, int TQ, int PR, int PC, bool PAIR = false>
 __global__ __launch_bounds__(kBlock2d) void dwconv2d_bwd_kernel(
     const S* __restrict__ x, const S* __restrict__ w, const int32_t* __restrict__ lengths,
