@@ -1080,7 +1080,7 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
     }
 }
 
-// Paired lanes (fp32, 16-byte-aligned tensors, K = 9 or 15): two channels per
+// Paired lanes (fp32, 16-byte-aligned tensors, K = 7, 9 or 15): two channels per
 // lane, so the fp64 sums take half the registers of the four-channel form and
 // three waves fit per SIMD, while every x and dy load and every dx store still
 // moves 16 bytes.  Lanes i and i + 32 of a wave share four channels
@@ -1250,9 +1250,16 @@ static int bwd1d_vec(int vec, int64_t K) {
 #ifndef DW1B_PAIR_WGS
 #define DW1B_PAIR_WGS 512
 #endif
+// The widths that take the paired-lane kernel: odd, so that the frame window
+// splits into pairs, and wide enough that the four-channel form runs short of
+// registers or lanes (measured on MI355X at [32,1500,512], causal, cold caches:
+// K7 67.7 -> 63.9 us against two-channel 8-byte lanes, while K3 and K5 stay
+// faster with four channels and 16-byte lanes, 59.6 and 60.5 against 62.0
+// and 62.9).
+constexpr bool bwd1d_pair_width(int64_t K) { return K == 7 || K == 9 || K == 15; }
 // Whether an fp32 call with 16-byte-aligned tensors takes the paired-lane form.
 static bool bwd1d_pair(int vec, int64_t K, bool bf16) {
-    return DW1B_PAIR && !bf16 && vec >= 4 && (K == 9 || K == 15);
+    return DW1B_PAIR && !bf16 && vec >= 4 && bwd1d_pair_width(K);
 }
 
 // Persistent grid: G workgroups per channel block.  With 16-byte lanes
@@ -1280,8 +1287,8 @@ bool dwconv1d_bwd_supported(int64_t K) {
     return K == 3 || K == 4 || K == 5 || K == 7 || K == 9 || K == 15 || K == 31;
 }
 
-// The paired-lane form takes 16-byte accesses at K = 9 and 15 whatever its lane width.
-int dwconv1d_bwd_max_vec(int64_t K) { return DW1B_PAIR && (K == 9 || K == 15) ? 4 : bwd1d_vmax((int)K); }
+// The paired-lane form takes 16-byte accesses at K = 7, 9 and 15 whatever its lane width.
+int dwconv1d_bwd_max_vec(int64_t K) { return DW1B_PAIR && bwd1d_pair_width(K) ? 4 : bwd1d_vmax((int)K); }
 
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
     if (!product_below((int64_t)1 << 31, {T + K + 32, C, elem_bytes})) return false;
@@ -1333,7 +1340,7 @@ static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const 
     const S* w = (const S*)wv;
     const S* dy = (const S*)dyv;
     S* dx = (S*)dxv;
-    if constexpr (sizeof(S) == 4 && (K == 9 || K == 15)) {
+    if constexpr (sizeof(S) == 4 && bwd1d_pair_width(K)) {
         if (bwd1d_pair(vec, K, false)) return launch_bwd1d_pair<K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
     }
     if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<S, (VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);

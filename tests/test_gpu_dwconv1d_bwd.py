@@ -186,9 +186,10 @@ def _offset8(t):
 
 @pytest.mark.parametrize("B,T,C,K,causal", [(3, 75, 512, 9, True), (2, 61, 100, 9, False), (4, 40, 20, 15, True),
                                             (2, 33, 260, 15, False), (3, 130, 8, 9, False), (1, 1, 4, 9, True),
-                                            (3, 2, 4, 15, False), (2, 9, 12, 9, False)])
+                                            (3, 2, 4, 15, False), (2, 9, 12, 9, False), (3, 90, 64, 7, True),
+                                            (2, 31, 36, 7, False)])
 def test_paired_lanes_match_eight_byte_lanes(B, T, C, K, causal):
-    """fp32 at K = 9 and 15 with 16-byte-aligned tensors takes the paired-lane
+    """fp32 at K = 7, 9 and 15 with 16-byte-aligned tensors takes the paired-lane
     form (two channels per lane, 16-byte loads and stores through cross-half
     swaps).  The same call 8 bytes off that alignment takes two-channel lanes
     with 8-byte accesses.  Both run the same per-element arithmetic: dx is
