@@ -1080,47 +1080,90 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
     }
 }
 
-// Paired lanes (fp32, 16-byte-aligned tensors, K = 7, 9 or 15): two channels per
-// lane, so the fp64 sums take half the registers of the four-channel form and
-// three waves fit per SIMD, while every x and dy load and every dx store still
-// moves 16 bytes.  Lanes i and i + 32 of a wave share four channels
-// (4(cblk*32 + i) .. +3): of each pair of consecutive frames, lane i loads the
-// even one and lane i + 32 the odd one, and two cross-half swaps
-// (v_permlane32_swap) leave lane i with channels 0-1 and lane i + 32 with
-// channels 2-3 of the four, at both frames.  dx goes back through the same
-// swaps before lane i stores the even frame and lane i + 32 the odd one.  The
-// arithmetic is the two-channel form's, term for term.  A lane whose channels
-// are past C runs every load, swap and store at out-of-range offsets, so that
-// the swaps see whole waves.
-__device__ __forceinline__ void pair_swap_1d(u32x4& t) {
+// Lane groups (fp32, 16-byte-aligned tensors, the widths below): Q = 2 or 4
+// lanes share one 16-byte piece of four channels, so each lane computes
+// V = 4 / Q channels and keeps that many channels' fp64 sums, while every x
+// and dy load and every dx store still moves 16 bytes.  The Q lanes of a
+// group sit 64 / Q apart (lane l + r * 64 / Q, r = 0 .. Q-1, holds the
+// piece 4 (cblk * 64 / Q + l) .. +3).  Of each run of Q consecutive frames,
+// lane r of the group loads frame r, and a transpose of the group's Q x 4
+// dwords by cross-lane swaps leaves lane r with its V channels at all Q
+// frames: for Q = 2 one swap of the wave's halves (v_permlane32_swap) per
+// dword pair; for Q = 4 the same, then a swap of neighbouring 16-lane rows
+// (v_permlane16_swap).  dx goes back through the same swaps in reverse order
+// before lane r stores frame r of the run.  The arithmetic is the V-channel
+// form's, term for term.  A lane whose channels are past C runs every load,
+// swap and store at out-of-range offsets, so that the swaps see whole waves.
+template <int Q>
+__device__ __forceinline__ void group_transpose(u32x4& t) {
+    // halves: lanes l and l + 32 exchange dwords z, w of the low half with x, y of the high half
+    const auto a = __builtin_amdgcn_permlane32_swap(t.x, t.z, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(t.y, t.w, false, false);
+    t.x = a[0]; t.z = a[1];
+    t.y = b[0]; t.w = b[1];
+    if constexpr (Q == 4) {
+        // rows: lanes l and l + 16 (within each half) exchange dword y of the
+        // even row with x of the odd row, and w with z
+        const auto c = __builtin_amdgcn_permlane16_swap(t.x, t.y, false, false);
+        const auto d = __builtin_amdgcn_permlane16_swap(t.z, t.w, false, false);
+        t.x = c[0]; t.y = c[1];
+        t.z = d[0]; t.w = d[1];
+    }
+}
+
+// The inverse of group_transpose: each stage is its own inverse, taken in
+// reverse order.
+template <int Q>
+__device__ __forceinline__ void group_untranspose(u32x4& t) {
+    if constexpr (Q == 4) {
+        const auto c = __builtin_amdgcn_permlane16_swap(t.x, t.y, false, false);
+        const auto d = __builtin_amdgcn_permlane16_swap(t.z, t.w, false, false);
+        t.x = c[0]; t.y = c[1];
+        t.z = d[0]; t.w = d[1];
+    }
     const auto a = __builtin_amdgcn_permlane32_swap(t.x, t.z, false, false);
     const auto b = __builtin_amdgcn_permlane32_swap(t.y, t.w, false, false);
     t.x = a[0]; t.z = a[1];
     t.y = b[0]; t.w = b[1];
 }
 
-template <int K, bool CAUSAL, int TT>
-__global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_pair_kernel(
+// The V = 4 / Q channels of frame i of a transposed run: dwords (x, y) or
+// (z, w) for Q = 2, one dword for Q = 4.
+template <int Q>
+__device__ __forceinline__ Vf<4 / Q> group_frame(const u32x4& t, int i) {
+    Vf<4 / Q> a;
+    if constexpr (Q == 2) {
+        a.v[0] = __uint_as_float(i == 0 ? t.x : t.z);
+        a.v[1] = __uint_as_float(i == 0 ? t.y : t.w);
+    } else {
+        a.v[0] = __uint_as_float(i == 0 ? t.x : (i == 1 ? t.y : (i == 2 ? t.z : t.w)));
+    }
+    return a;
+}
+
+template <int K, bool CAUSAL, int TT, int Q>
+__global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_group_kernel(
     const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
     const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
     uint32_t n_tb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
-    constexpr int V = 2, NW = TT + K - 1;
-    static_assert(TT % 2 == 0 && NW % 2 == 0, "frames are loaded in pairs");
+    constexpr int V = 4 / Q, NW = TT + K - 1, NR = (NW + Q - 1) / Q;  // window frames, runs of Q loaded
+    static_assert((Q == 2 || Q == 4) && TT % Q == 0, "frames are loaded in runs of Q");
     constexpr int pL = CAUSAL ? K - 1 : (K - 1) / 2;
+    constexpr uint32_t span = 64 / Q;  // lanes between the members of a group
     __shared__ double red[kSubs1b - 1][K + 1][kLanes1b * V];
     const uint32_t blk = xcd_contiguous_block(blockIdx.x, gridDim.x);
     const uint32_t G = gridDim.x / n_cblk;
     const uint32_t g = blk / n_cblk, cblk = blk - g * n_cblk;
     const uint32_t lane = threadIdx.x % kLanes1b, sub = threadIdx.x / kLanes1b;
-    const uint32_t half = lane / 32;
-    // CG counts two-channel groups; lanes i and i + 32 hold groups 2i and 2i + 1
-    // of the block (both valid or both not, since C % 4 == 0)
-    const uint32_t cg = cblk * kLanes1b + 2 * (lane % 32) + half;
+    const uint32_t r = lane / span;  // this lane's member index in its group
+    // CG counts V-channel groups; the members of a piece hold Q consecutive
+    // ones (all valid or none, since C % 4 == 0)
+    const uint32_t cg = (cblk * span + lane % span) * Q + r;
     const bool cvalid = cg < CG;
     const int32_t c0 = (int32_t)(cvalid ? cg : 0) * V;
     const uint32_t row = (uint32_t)C * sizeof(float);
-    // this lane's 16-byte piece of a frame: the pair's four channels
-    const uint32_t qoff = cvalid ? (uint32_t)(c0 - 2 * (int32_t)half) * (uint32_t)sizeof(float) : 0x80000000u;
+    // this lane's 16-byte piece of a frame: its group's four channels
+    const uint32_t qoff = cvalid ? (uint32_t)(c0 - (int32_t)r * V) * (uint32_t)sizeof(float) : 0x80000000u;
 
     Vf<V> wk[K];
 #pragma unroll
@@ -1146,8 +1189,8 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_pair_kernel(
             if (dx) {
                 const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-                for (int p = 0; p < TT / 2; ++p)
-                    __builtin_amdgcn_raw_buffer_store_b128(z, dxr, (uint32_t)(u0 + 2 * p + (int32_t)half) * row + qoff, 0,
+                for (int p = 0; p < TT / Q; ++p)
+                    __builtin_amdgcn_raw_buffer_store_b128(z, dxr, (uint32_t)(u0 + Q * p + (int32_t)r) * row + qoff, 0,
                                                            kNonTemporal);
             }
             continue;
@@ -1155,36 +1198,36 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_pair_kernel(
         const rsrc_t gr = make_rsrc(dy + item, (uint32_t)len * row);
         const rsrc_t xr = make_rsrc(x + item, (uint32_t)len * row);
         const int32_t gs = u0 + pL - (K - 1);  // first gradient frame of the window
-        u32x4 graw[NW / 2], xraw[TT / 2];
+        u32x4 graw[NR], xraw[TT / Q];
 #pragma unroll
-        for (int p = 0; p < NW / 2; ++p)
-            graw[p] = __builtin_amdgcn_raw_buffer_load_b128(gr, (uint32_t)((gs + 2 * p + (int32_t)half) * (int32_t)row) + qoff,
+        for (int p = 0; p < NR; ++p)
+            graw[p] = __builtin_amdgcn_raw_buffer_load_b128(gr, (uint32_t)((gs + Q * p + (int32_t)r) * (int32_t)row) + qoff,
                                                             0, kLoadPolicy);
 #pragma unroll
-        for (int p = 0; p < TT / 2; ++p)
-            xraw[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(u0 + 2 * p + (int32_t)half) * row + qoff, 0,
+        for (int p = 0; p < TT / Q; ++p)
+            xraw[p] = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(u0 + Q * p + (int32_t)r) * row + qoff, 0,
                                                             kBwdXPolicy1d);
-        Vf<V> gwin[NW], xv[TT];
+        Vf<V> gwin[NR * Q], xv[TT];
 #pragma unroll
-        for (int p = 0; p < NW / 2; ++p) {
+        for (int p = 0; p < NR; ++p) {
             u32x4 t = graw[p];
-            pair_swap_1d(t);
-            gwin[2 * p].v[0] = __uint_as_float(t.x); gwin[2 * p].v[1] = __uint_as_float(t.y);
-            gwin[2 * p + 1].v[0] = __uint_as_float(t.z); gwin[2 * p + 1].v[1] = __uint_as_float(t.w);
+            group_transpose<Q>(t);
+#pragma unroll
+            for (int i = 0; i < Q; ++i) gwin[Q * p + i] = group_frame<Q>(t, i);
         }
 #pragma unroll
-        for (int p = 0; p < TT / 2; ++p) {
+        for (int p = 0; p < TT / Q; ++p) {
             u32x4 t = xraw[p];
-            pair_swap_1d(t);
-            xv[2 * p].v[0] = __uint_as_float(t.x); xv[2 * p].v[1] = __uint_as_float(t.y);
-            xv[2 * p + 1].v[0] = __uint_as_float(t.z); xv[2 * p + 1].v[1] = __uint_as_float(t.w);
+            group_transpose<Q>(t);
+#pragma unroll
+            for (int i = 0; i < Q; ++i) xv[Q * p + i] = group_frame<Q>(t, i);
         }
 #pragma unroll
-        for (int p = 0; p < TT / 2; ++p) {
-            Vf<V> d[2];
+        for (int p = 0; p < TT / Q; ++p) {
+            Vf<V> d[Q];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int i = 2 * p + h;
+            for (int h = 0; h < Q; ++h) {
+                const int i = Q * p + h;
                 d[h] = vzero<V>();
 #pragma unroll
                 for (int k = 0; k < K; ++k)
@@ -1201,10 +1244,16 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_pair_kernel(
                 }
             }
             if (dx) {
-                u32x4 t = {__float_as_uint(d[0].v[0]), __float_as_uint(d[0].v[1]), __float_as_uint(d[1].v[0]),
-                           __float_as_uint(d[1].v[1])};
-                pair_swap_1d(t);
-                __builtin_amdgcn_raw_buffer_store_b128(t, dxr, (uint32_t)(u0 + 2 * p + (int32_t)half) * row + qoff, 0,
+                u32x4 t;
+                if constexpr (Q == 2) {
+                    t = u32x4{__float_as_uint(d[0].v[0]), __float_as_uint(d[0].v[1]), __float_as_uint(d[1].v[0]),
+                              __float_as_uint(d[1].v[1])};
+                } else {
+                    t = u32x4{__float_as_uint(d[0].v[0]), __float_as_uint(d[1].v[0]), __float_as_uint(d[2].v[0]),
+                              __float_as_uint(d[3].v[0])};
+                }
+                group_untranspose<Q>(t);
+                __builtin_amdgcn_raw_buffer_store_b128(t, dxr, (uint32_t)(u0 + Q * p + (int32_t)r) * row + qoff, 0,
                                                        kNonTemporal);
             }
         }
@@ -1250,16 +1299,27 @@ static int bwd1d_vec(int vec, int64_t K) {
 #ifndef DW1B_PAIR_WGS
 #define DW1B_PAIR_WGS 512
 #endif
-// The widths that take the paired-lane kernel: odd, so that the frame window
-// splits into pairs, and wide enough that the four-channel form runs short of
-// registers or lanes (measured on MI355X at [32,1500,512], causal, cold caches:
-// K7 67.7 -> 63.9 us against two-channel 8-byte lanes, while K3 and K5 stay
-// faster with four channels and 16-byte lanes, 59.6 and 60.5 against 62.0
-// and 62.9).
-constexpr bool bwd1d_pair_width(int64_t K) { return K == 7 || K == 9 || K == 15; }
-// Whether an fp32 call with 16-byte-aligned tensors takes the paired-lane form.
-static bool bwd1d_pair(int vec, int64_t K, bool bf16) {
-    return DW1B_PAIR && !bf16 && vec >= 4 && bwd1d_pair_width(K);
+#ifndef DW1B_Q9
+#define DW1B_Q9 2
+#endif
+#ifndef DW1B_Q15
+#define DW1B_Q15 2
+#endif
+#ifndef DW1B_Q31
+#define DW1B_Q31 4
+#endif
+// Lanes per 16-byte piece (2 or 4) for the widths that take the lane-group
+// kernel, 0 for the others.  Those widths are wide enough that the
+// four-channel form runs short of registers or lanes (measured on MI355X at
+// [32,1500,512], causal, cold caches: K7 67.7 -> 63.9 us with pairs against
+// two-channel 8-byte lanes, while K3 and K5 stay faster with four channels
+// and 16-byte lanes, 59.6 and 60.5 against 62.0 and 62.9).
+constexpr int bwd1d_group_q(int64_t K) {
+    return K == 7 ? 2 : (K == 9 ? DW1B_Q9 : (K == 15 ? DW1B_Q15 : (K == 31 ? DW1B_Q31 : 0)));
+}
+// The lane-group size an fp32 call with 16-byte-aligned tensors takes, or 0.
+static int bwd1d_group(int vec, int64_t K, bool bf16) {
+    return DW1B_PAIR && !bf16 && vec >= 4 ? bwd1d_group_q(K) : 0;
 }
 
 // Persistent grid: G workgroups per channel block.  With 16-byte lanes
@@ -1267,18 +1327,18 @@ static bool bwd1d_pair(int vec, int64_t K, bool bf16) {
 // DW1D_BWD_WGS per channel block (measured on MI355X at [32..128,1500,512]:
 // K9 and K5 on 16-byte lanes 2-6% faster with 256 in all than with 512;
 // K15 on 8-byte lanes 3% slower with 512 in all than with 1024).
-// The paired-lane form (two channels per lane, 16-byte accesses) takes about
-// DW1B_PAIR_WGS workgroups in all.
-static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V, bool pair = false) {
+// The lane-group form (q lanes per 16-byte piece, 4 / q channels per lane)
+// takes about DW1B_PAIR_WGS workgroups in all.
+static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V, int q = 0) {
     Bwd1dGrid g;
     g.n_tb = (uint32_t)((T + kBwdTile1d - 1) / kBwdTile1d);
     g.groups_per_item = (g.n_tb + kSubs1b - 1) / kSubs1b;
     const uint64_t n = (uint64_t)B * g.groups_per_item;
     g.n_groups = (uint32_t)n;
-    if (pair) V = 2;
+    if (q) V = 4 / q;
     const int64_t n_cblk = ((C + V - 1) / V + kLanes1b - 1) / kLanes1b;
-    const int64_t wide = pair ? DW1B_PAIR_WGS : DW1D_BWD_WGS;
-    const int64_t per = V >= 4 || pair ? (n_cblk > 0 ? (wide + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
+    const int64_t wide = q ? DW1B_PAIR_WGS : DW1D_BWD_WGS;
+    const int64_t per = V >= 4 || q ? (n_cblk > 0 ? (wide + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
     g.G = (uint32_t)(n < (uint64_t)per ? n : (uint64_t)per);
     return g;
 }
@@ -1287,8 +1347,8 @@ bool dwconv1d_bwd_supported(int64_t K) {
     return K == 3 || K == 4 || K == 5 || K == 7 || K == 9 || K == 15 || K == 31;
 }
 
-// The paired-lane form takes 16-byte accesses at K = 7, 9 and 15 whatever its lane width.
-int dwconv1d_bwd_max_vec(int64_t K) { return DW1B_PAIR && bwd1d_pair_width(K) ? 4 : bwd1d_vmax((int)K); }
+// The lane-group form takes 16-byte accesses whatever its lane width.
+int dwconv1d_bwd_max_vec(int64_t K) { return DW1B_PAIR && bwd1d_group_q(K) > 0 ? 4 : bwd1d_vmax((int)K); }
 
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
     if (!product_below((int64_t)1 << 31, {T + K + 32, C, elem_bytes})) return false;
@@ -1297,7 +1357,9 @@ bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
 
 size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
     // enough for whichever lane width the pointers' alignment allows
-    int64_t P = bwd1d_grid(B, T, C, 2, true).G;
+    int64_t P = bwd1d_grid(B, T, C, 2, 2).G;
+    const int64_t P4 = bwd1d_grid(B, T, C, 1, 4).G;
+    P = P4 > P ? P4 : P;
     for (int v : {1, 2, 4}) {
         const int64_t p = bwd1d_grid(B, T, C, v).G;
         P = p > P ? p : P;
@@ -1319,16 +1381,16 @@ static hipError_t launch_bwd1d_typed(const S* x, const S* w, const int32_t* leng
     return hipGetLastError();
 }
 
-template <int K, bool CAUSAL>
-static hipError_t launch_bwd1d_pair(const float* x, const float* w, const int32_t* lengths, const float* dy, float* dx,
-                                    double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
-    const Bwd1dGrid g = bwd1d_grid(B, T, C, 2, true);
-    const uint32_t CG = (uint32_t)(C / 2);
+template <int K, bool CAUSAL, int Q>
+static hipError_t launch_bwd1d_group(const float* x, const float* w, const int32_t* lengths, const float* dy,
+                                     float* dx, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+    const Bwd1dGrid g = bwd1d_grid(B, T, C, 4 / Q, Q);
+    const uint32_t CG = (uint32_t)(C / (4 / Q));
     const uint32_t n_cblk = (CG + kLanes1b - 1) / kLanes1b;
     if (g.G == 0 || (!dx && !partial)) return hipSuccess;
-    hipLaunchKernelGGL((dwconv1d_bwd_pair_kernel<K, CAUSAL, kBwdTile1d>), dim3(g.G * n_cblk), dim3(kBlock1d), 0, st,
-                       x, w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk, g.groups_per_item,
-                       g.n_groups);
+    hipLaunchKernelGGL((dwconv1d_bwd_group_kernel<K, CAUSAL, kBwdTile1d, Q>), dim3(g.G * n_cblk), dim3(kBlock1d), 0,
+                       st, x, w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk,
+                       g.groups_per_item, g.n_groups);
     return hipGetLastError();
 }
 
@@ -1340,8 +1402,9 @@ static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const 
     const S* w = (const S*)wv;
     const S* dy = (const S*)dyv;
     S* dx = (S*)dxv;
-    if constexpr (sizeof(S) == 4 && bwd1d_pair_width(K)) {
-        if (bwd1d_pair(vec, K, false)) return launch_bwd1d_pair<K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    if constexpr (sizeof(S) == 4 && bwd1d_group_q(K) > 0) {
+        if (bwd1d_group(vec, K, false))
+            return launch_bwd1d_group<K, CAUSAL, bwd1d_group_q(K)>(x, w, lengths, dy, dx, partial, B, T, C, st);
     }
     if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<S, (VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
     if (vec >= 2 && VMAX >= 2) return launch_bwd1d_typed<S, (VMAX >= 2 ? 2 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
@@ -1374,7 +1437,7 @@ hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* leng
     }
 #undef DW1B_CASE
     if (e != hipSuccess || !partial) return e;
-    const int64_t P = bwd1d_grid(B, T, C, bwd1d_vec(vec, K), bwd1d_pair(vec, K, bf16)).G;
+    const int64_t P = bwd1d_grid(B, T, C, bwd1d_vec(vec, K), bwd1d_group(vec, K, bf16)).G;
     RowOutputs out = {};
     out.n = 2;
     out.p[0] = dw; out.first[0] = 0; out.count[0] = (int32_t)K;

@@ -187,14 +187,17 @@ def _offset8(t):
 @pytest.mark.parametrize("B,T,C,K,causal", [(3, 75, 512, 9, True), (2, 61, 100, 9, False), (4, 40, 20, 15, True),
                                             (2, 33, 260, 15, False), (3, 130, 8, 9, False), (1, 1, 4, 9, True),
                                             (3, 2, 4, 15, False), (2, 9, 12, 9, False), (3, 90, 64, 7, True),
-                                            (2, 31, 36, 7, False)])
+                                            (2, 31, 36, 7, False), (2, 40, 128, 31, True), (3, 37, 36, 31, False),
+                                            (1, 3, 4, 31, True)])
 def test_paired_lanes_match_eight_byte_lanes(B, T, C, K, causal):
-    """fp32 at K = 7, 9 and 15 with 16-byte-aligned tensors takes the paired-lane
-    form (two channels per lane, 16-byte loads and stores through cross-half
-    swaps).  The same call 8 bytes off that alignment takes two-channel lanes
-    with 8-byte accesses.  Both run the same per-element arithmetic: dx is
-    equal bit for bit; dw and db are the same fp64 sums over another split of
-    the tiles across workgroups, so they agree to within one float32 ulp."""
+    """fp32 with 16-byte-aligned tensors takes the lane-group form at K = 7, 9
+    and 15 (pairs of lanes, two channels each) and at K = 31 (four lanes, one
+    channel each): 16-byte loads and stores, transposed through cross-lane
+    swaps.  The same call 8 bytes off that alignment takes two-channel lanes
+    with 8-byte accesses (one channel, 4-byte accesses at K = 31).  Both run
+    the same per-element arithmetic: dx is equal bit for bit; dw and db are
+    the same fp64 sums over another split of the tiles across workgroups, so
+    they agree to within one float32 ulp."""
     x, w, dy, L = make(B, T, C, K, lens=[T, T // 2 + 1, 0, max(T - 9, 0)][:B])
     say(f"dwconv1d_bwd paired against 8-byte lanes B={B} T={T} C={C} K={K} causal={causal}")
     wide = run(x, w, L, dy, causal)
