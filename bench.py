@@ -114,7 +114,7 @@ ROW_KERNELS = [
     ("conv1d_causal_K15_C512", "dw::dwconv1d_fwd_pipe_kernel<15>("),
     ("conv1d_causal_K9_C200", "dw::dwconv1d_fwd_pipe_kernel<9>("),
     ("conv1d_stream_bf16", "dw::dwconv1d_stream_pipe_kernel<unsigned short, 9>("),
-    ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_group_kernel<9, true, 8, 2>("),
+    ("conv1d_bwd_K9_C512", "dw::dwconv1d_bwd_group_kernel<float, 9, true, 8, 2>("),
     ("stage_fwd", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),
     ("stage_bwd", "dw::dwconv2d_bwd_kernel<float, 4, 1, 0, 0, false>("),
     ("stage_fwd_causal", "dw::dwconv2d_fwd_kernel<float, 4, 1, 64>("),

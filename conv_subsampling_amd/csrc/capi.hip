@@ -161,7 +161,7 @@ dw_status dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, con
             return fail(DW_ERR_WORKSPACE, "%s: workspace of %zu bytes given, %zu needed", fn, workspace ? workspace_bytes : (size_t)0, need);
     }
     const void* ptrs[4] = {x, w, dy, dx};
-    const int vec = dw::pick_vec(C, es, ptrs, 4, dw::dwconv1d_bwd_max_vec(K));
+    const int vec = dw::pick_vec(C, es, ptrs, 4, dw::dwconv1d_bwd_max_vec(K, dtype == DW_BF16));
     return from_hip(dw::launch_dwconv1d_bwd(x, w, lengths, dy, dx, dw_, db, workspace, B, T, C, K,
                                             pad == DW_PAD_CAUSAL, dtype == DW_BF16, vec, (hipStream_t)stream), fn);
 }

@@ -1080,20 +1080,21 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_kernel(
     }
 }
 
-// Lane groups (fp32, 16-byte-aligned tensors, the widths below): Q = 2 or 4
-// lanes share one 16-byte piece of four channels, so each lane computes
-// V = 4 / Q channels and keeps that many channels' fp64 sums, while every x
-// and dy load and every dx store still moves 16 bytes.  The Q lanes of a
-// group sit 64 / Q apart (lane l + r * 64 / Q, r = 0 .. Q-1, holds the
-// piece 4 (cblk * 64 / Q + l) .. +3).  Of each run of Q consecutive frames,
-// lane r of the group loads frame r, and a transpose of the group's Q x 4
-// dwords by cross-lane swaps leaves lane r with its V channels at all Q
-// frames: for Q = 2 one swap of the wave's halves (v_permlane32_swap) per
-// dword pair; for Q = 4 the same, then a swap of neighbouring 16-lane rows
-// (v_permlane16_swap).  dx goes back through the same swaps in reverse order
-// before lane r stores frame r of the run.  The arithmetic is the V-channel
-// form's, term for term.  A lane whose channels are past C runs every load,
-// swap and store at out-of-range offsets, so that the swaps see whole waves.
+// Lane groups (16-byte-aligned tensors, the widths below): Q = 2 or 4 lanes
+// share one 16-byte piece of P channels (4 fp32 or 8 bf16), so each lane
+// computes V = P / Q channels and keeps that many channels' fp64 sums, while
+// every x and dy load and every dx store still moves 16 bytes.  The Q lanes
+// of a group sit 64 / Q apart (lane l + r * 64 / Q, r = 0 .. Q-1, holds the
+// piece P (cblk * 64 / Q + l) .. +P-1).  Of each run of Q consecutive
+// frames, lane r of the group loads frame r, and a transpose of the group's
+// Q x 4 dwords by cross-lane swaps leaves lane r with its 4 / Q dwords (its
+// V channels) at all Q frames: for Q = 2 one swap of the wave's halves
+// (v_permlane32_swap) per dword pair; for Q = 4 the same, then a swap of
+// neighbouring 16-lane rows (v_permlane16_swap).  dx goes back through the
+// same swaps in reverse order before lane r stores frame r of the run.  The
+// arithmetic is the V-channel form's, term for term.  A lane whose channels
+// are past C runs every load, swap and store at out-of-range offsets, so
+// that the swaps see whole waves.
 template <int Q>
 __device__ __forceinline__ void group_transpose(u32x4& t) {
     // halves: lanes l and l + 32 exchange dwords z, w of the low half with x, y of the high half
@@ -1127,26 +1128,46 @@ __device__ __forceinline__ void group_untranspose(u32x4& t) {
     t.y = b[0]; t.w = b[1];
 }
 
-// The V = 4 / Q channels of frame i of a transposed run: dwords (x, y) or
-// (z, w) for Q = 2, one dword for Q = 4.
-template <int Q>
-__device__ __forceinline__ Vf<4 / Q> group_frame(const u32x4& t, int i) {
-    Vf<4 / Q> a;
+// The V channels of frame i of a transposed run, widened to float: dwords
+// (x, y) or (z, w) for Q = 2, one dword for Q = 4; a dword holds one fp32 or
+// two bf16 channels.
+template <typename S, int Q>
+__device__ __forceinline__ Vf<16 / (int)sizeof(S) / Q> group_frame(const u32x4& t, int i) {
+    constexpr int V = 16 / (int)sizeof(S) / Q;
+    uint32_t u[4 / Q];
     if constexpr (Q == 2) {
-        a.v[0] = __uint_as_float(i == 0 ? t.x : t.z);
-        a.v[1] = __uint_as_float(i == 0 ? t.y : t.w);
+        u[0] = i == 0 ? t.x : t.z;
+        u[1] = i == 0 ? t.y : t.w;
     } else {
-        a.v[0] = __uint_as_float(i == 0 ? t.x : (i == 1 ? t.y : (i == 2 ? t.z : t.w)));
+        u[0] = i == 0 ? t.x : (i == 1 ? t.y : (i == 2 ? t.z : t.w));
+    }
+    Vf<V> a;
+#pragma unroll
+    for (int k = 0; k < 4 / Q; ++k) {
+        if constexpr (sizeof(S) == 2) {
+            a.v[2 * k] = bf16_lo(u[k]);
+            a.v[2 * k + 1] = bf16_hi(u[k]);
+        } else {
+            a.v[k] = __uint_as_float(u[k]);
+        }
     }
     return a;
 }
 
-template <int K, bool CAUSAL, int TT, int Q>
+// Dword k of a V-channel value in storage form (bf16 rounded to nearest even).
+template <typename S, int V>
+__device__ __forceinline__ uint32_t group_dword(const Vf<V>& a, int k) {
+    if constexpr (sizeof(S) == 2) return pack_bf16x2(a.v[2 * k], a.v[2 * k + 1]);
+    else return __float_as_uint(a.v[k]);
+}
+
+template <typename S, int K, bool CAUSAL, int TT, int Q>
 __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_group_kernel(
-    const float* __restrict__ x, const float* __restrict__ w, const int32_t* __restrict__ lengths,
-    const float* __restrict__ dy, float* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
+    const S* __restrict__ x, const S* __restrict__ w, const int32_t* __restrict__ lengths,
+    const S* __restrict__ dy, S* __restrict__ dx, double* __restrict__ partial, int32_t T, int32_t C,
     uint32_t n_tb, uint32_t CG, uint32_t n_cblk, uint32_t groups_per_item, uint32_t n_groups) {
-    constexpr int V = 4 / Q, NW = TT + K - 1, NR = (NW + Q - 1) / Q;  // window frames, runs of Q loaded
+    constexpr int P = 16 / (int)sizeof(S);                                 // channels per piece
+    constexpr int V = P / Q, NW = TT + K - 1, NR = (NW + Q - 1) / Q;  // window frames, runs of Q loaded
     static_assert((Q == 2 || Q == 4) && TT % Q == 0, "frames are loaded in runs of Q");
     constexpr int pL = CAUSAL ? K - 1 : (K - 1) / 2;
     constexpr uint32_t span = 64 / Q;  // lanes between the members of a group
@@ -1157,17 +1178,17 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_group_kernel(
     const uint32_t lane = threadIdx.x % kLanes1b, sub = threadIdx.x / kLanes1b;
     const uint32_t r = lane / span;  // this lane's member index in its group
     // CG counts V-channel groups; the members of a piece hold Q consecutive
-    // ones (all valid or none, since C % 4 == 0)
+    // ones (all valid or none, since C % P == 0)
     const uint32_t cg = (cblk * span + lane % span) * Q + r;
     const bool cvalid = cg < CG;
     const int32_t c0 = (int32_t)(cvalid ? cg : 0) * V;
-    const uint32_t row = (uint32_t)C * sizeof(float);
-    // this lane's 16-byte piece of a frame: its group's four channels
-    const uint32_t qoff = cvalid ? (uint32_t)(c0 - (int32_t)r * V) * (uint32_t)sizeof(float) : 0x80000000u;
+    const uint32_t row = (uint32_t)C * sizeof(S);
+    // this lane's 16-byte piece of a frame: its group's P channels
+    const uint32_t qoff = cvalid ? (uint32_t)(c0 - (int32_t)r * V) * (uint32_t)sizeof(S) : 0x80000000u;
 
     Vf<V> wk[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) wk[k] = load_param<float, V>(w + (int64_t)k * C + c0);
+    for (int k = 0; k < K; ++k) wk[k] = load_param<S, V>(w + (int64_t)k * C + c0);
     double gw[K][V], gb[V];
 #pragma unroll
     for (int e = 0; e < V; ++e) {
@@ -1213,14 +1234,14 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_group_kernel(
             u32x4 t = graw[p];
             group_transpose<Q>(t);
 #pragma unroll
-            for (int i = 0; i < Q; ++i) gwin[Q * p + i] = group_frame<Q>(t, i);
+            for (int i = 0; i < Q; ++i) gwin[Q * p + i] = group_frame<S, Q>(t, i);
         }
 #pragma unroll
         for (int p = 0; p < TT / Q; ++p) {
             u32x4 t = xraw[p];
             group_transpose<Q>(t);
 #pragma unroll
-            for (int i = 0; i < Q; ++i) xv[Q * p + i] = group_frame<Q>(t, i);
+            for (int i = 0; i < Q; ++i) xv[Q * p + i] = group_frame<S, Q>(t, i);
         }
 #pragma unroll
         for (int p = 0; p < TT / Q; ++p) {
@@ -1246,11 +1267,11 @@ __global__ __launch_bounds__(kBlock1d) void dwconv1d_bwd_group_kernel(
             if (dx) {
                 u32x4 t;
                 if constexpr (Q == 2) {
-                    t = u32x4{__float_as_uint(d[0].v[0]), __float_as_uint(d[0].v[1]), __float_as_uint(d[1].v[0]),
-                              __float_as_uint(d[1].v[1])};
+                    t = u32x4{group_dword<S, V>(d[0], 0), group_dword<S, V>(d[0], 1), group_dword<S, V>(d[1], 0),
+                              group_dword<S, V>(d[1], 1)};
                 } else {
-                    t = u32x4{__float_as_uint(d[0].v[0]), __float_as_uint(d[1].v[0]), __float_as_uint(d[2].v[0]),
-                              __float_as_uint(d[3].v[0])};
+                    t = u32x4{group_dword<S, V>(d[0], 0), group_dword<S, V>(d[1], 0), group_dword<S, V>(d[2], 0),
+                              group_dword<S, V>(d[3], 0)};
                 }
                 group_untranspose<Q>(t);
                 __builtin_amdgcn_raw_buffer_store_b128(t, dxr, (uint32_t)(u0 + Q * p + (int32_t)r) * row + qoff, 0,
@@ -1317,28 +1338,36 @@ static int bwd1d_vec(int vec, int64_t K) {
 constexpr int bwd1d_group_q(int64_t K) {
     return K == 7 ? 2 : (K == 9 ? DW1B_Q9 : (K == 15 ? DW1B_Q15 : (K == 31 ? DW1B_Q31 : 0)));
 }
-// The lane-group size an fp32 call with 16-byte-aligned tensors takes, or 0.
+#ifndef DW1B_QB
+#define DW1B_QB 4
+#endif
+// The same for bf16 storage (8 channels per piece): groups of DW1B_QB lanes at
+// K = 7, 9 and 15; at K = 31 even two channels per lane would not fit.
+constexpr int bwd1d_group_q_bf16(int64_t K) { return K == 7 || K == 9 || K == 15 ? DW1B_QB : 0; }
+// The lane-group size a call with 16-byte-aligned tensors takes, or 0.
 static int bwd1d_group(int vec, int64_t K, bool bf16) {
-    return DW1B_PAIR && !bf16 && vec >= 4 ? bwd1d_group_q(K) : 0;
+    if (!DW1B_PAIR) return 0;
+    return bf16 ? (vec >= 8 ? bwd1d_group_q_bf16(K) : 0) : (vec >= 4 ? bwd1d_group_q(K) : 0);
 }
+// Channels per lane of the lane-group form.
+static int bwd1d_group_v(int q, bool bf16) { return (bf16 ? 8 : 4) / q; }
 
 // Persistent grid: G workgroups per channel block.  With 16-byte lanes
 // about DW1D_BWD_WGS workgroups in all (one per CU), with narrower lanes
 // DW1D_BWD_WGS per channel block (measured on MI355X at [32..128,1500,512]:
 // K9 and K5 on 16-byte lanes 2-6% faster with 256 in all than with 512;
 // K15 on 8-byte lanes 3% slower with 512 in all than with 1024).
-// The lane-group form (q lanes per 16-byte piece, 4 / q channels per lane)
-// takes about DW1B_PAIR_WGS workgroups in all.
-static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V, int q = 0) {
+// The lane-group form (V channels per lane, 16-byte accesses) takes about
+// DW1B_PAIR_WGS workgroups in all.
+static Bwd1dGrid bwd1d_grid(int64_t B, int64_t T, int64_t C, int V, bool group = false) {
     Bwd1dGrid g;
     g.n_tb = (uint32_t)((T + kBwdTile1d - 1) / kBwdTile1d);
     g.groups_per_item = (g.n_tb + kSubs1b - 1) / kSubs1b;
     const uint64_t n = (uint64_t)B * g.groups_per_item;
     g.n_groups = (uint32_t)n;
-    if (q) V = 4 / q;
     const int64_t n_cblk = ((C + V - 1) / V + kLanes1b - 1) / kLanes1b;
-    const int64_t wide = q ? DW1B_PAIR_WGS : DW1D_BWD_WGS;
-    const int64_t per = V >= 4 || q ? (n_cblk > 0 ? (wide + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
+    const int64_t wide = group ? DW1B_PAIR_WGS : DW1D_BWD_WGS;
+    const int64_t per = V >= 4 || group ? (n_cblk > 0 ? (wide + n_cblk - 1) / n_cblk : 1) : DW1D_BWD_WGS;
     g.G = (uint32_t)(n < (uint64_t)per ? n : (uint64_t)per);
     return g;
 }
@@ -1347,8 +1376,12 @@ bool dwconv1d_bwd_supported(int64_t K) {
     return K == 3 || K == 4 || K == 5 || K == 7 || K == 9 || K == 15 || K == 31;
 }
 
-// The lane-group form takes 16-byte accesses whatever its lane width.
-int dwconv1d_bwd_max_vec(int64_t K) { return DW1B_PAIR && bwd1d_group_q(K) > 0 ? 4 : bwd1d_vmax((int)K); }
+// The lane-group form takes 16-byte accesses whatever its lane width: 4 fp32
+// or 8 bf16 channels.
+int dwconv1d_bwd_max_vec(int64_t K, bool bf16) {
+    if (DW1B_PAIR && (bf16 ? bwd1d_group_q_bf16(K) : bwd1d_group_q(K)) > 0) return bf16 ? 8 : 4;
+    return bwd1d_vmax((int)K);
+}
 
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes) {
     if (!product_below((int64_t)1 << 31, {T + K + 32, C, elem_bytes})) return false;
@@ -1357,13 +1390,12 @@ bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_byte
 
 size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K) {
     // enough for whichever lane width the pointers' alignment allows
-    int64_t P = bwd1d_grid(B, T, C, 2, 2).G;
-    const int64_t P4 = bwd1d_grid(B, T, C, 1, 4).G;
-    P = P4 > P ? P4 : P;
-    for (int v : {1, 2, 4}) {
-        const int64_t p = bwd1d_grid(B, T, C, v).G;
-        P = p > P ? p : P;
-    }
+    int64_t P = 0;
+    for (int v : {1, 2, 4})
+        for (bool group : {false, true}) {
+            const int64_t p = bwd1d_grid(B, T, C, v, group).G;
+            P = p > P ? p : P;
+        }
     const int64_t ch = partial_reduce_chunks(P);
     return (size_t)((P + (ch > 0 ? ch : 1)) * (K + 1) * C * (int64_t)sizeof(double));
 }
@@ -1381,15 +1413,16 @@ static hipError_t launch_bwd1d_typed(const S* x, const S* w, const int32_t* leng
     return hipGetLastError();
 }
 
-template <int K, bool CAUSAL, int Q>
-static hipError_t launch_bwd1d_group(const float* x, const float* w, const int32_t* lengths, const float* dy,
-                                     float* dx, double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
-    const Bwd1dGrid g = bwd1d_grid(B, T, C, 4 / Q, Q);
-    const uint32_t CG = (uint32_t)(C / (4 / Q));
+template <typename S, int K, bool CAUSAL, int Q>
+static hipError_t launch_bwd1d_group(const S* x, const S* w, const int32_t* lengths, const S* dy, S* dx,
+                                     double* partial, int64_t B, int64_t T, int64_t C, hipStream_t st) {
+    constexpr int V = 16 / (int)sizeof(S) / Q;
+    const Bwd1dGrid g = bwd1d_grid(B, T, C, V, true);
+    const uint32_t CG = (uint32_t)(C / V);
     const uint32_t n_cblk = (CG + kLanes1b - 1) / kLanes1b;
     if (g.G == 0 || (!dx && !partial)) return hipSuccess;
-    hipLaunchKernelGGL((dwconv1d_bwd_group_kernel<K, CAUSAL, kBwdTile1d, Q>), dim3(g.G * n_cblk), dim3(kBlock1d), 0,
-                       st, x, w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk,
+    hipLaunchKernelGGL((dwconv1d_bwd_group_kernel<S, K, CAUSAL, kBwdTile1d, Q>), dim3(g.G * n_cblk), dim3(kBlock1d),
+                       0, st, x, w, lengths, dy, dx, partial, (int32_t)T, (int32_t)C, g.n_tb, CG, n_cblk,
                        g.groups_per_item, g.n_groups);
     return hipGetLastError();
 }
@@ -1402,9 +1435,10 @@ static hipError_t launch_bwd1d_k(int vec, const void* xv, const void* wv, const 
     const S* w = (const S*)wv;
     const S* dy = (const S*)dyv;
     S* dx = (S*)dxv;
-    if constexpr (sizeof(S) == 4 && bwd1d_group_q(K) > 0) {
-        if (bwd1d_group(vec, K, false))
-            return launch_bwd1d_group<K, CAUSAL, bwd1d_group_q(K)>(x, w, lengths, dy, dx, partial, B, T, C, st);
+    constexpr int Q = sizeof(S) == 2 ? bwd1d_group_q_bf16(K) : bwd1d_group_q(K);
+    if constexpr (Q > 0) {
+        if (bwd1d_group(vec, K, sizeof(S) == 2))
+            return launch_bwd1d_group<S, K, CAUSAL, Q>(x, w, lengths, dy, dx, partial, B, T, C, st);
     }
     if (vec >= 4 && VMAX >= 4) return launch_bwd1d_typed<S, (VMAX >= 4 ? 4 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
     if (vec >= 2 && VMAX >= 2) return launch_bwd1d_typed<S, (VMAX >= 2 ? 2 : 1), K, CAUSAL>(x, w, lengths, dy, dx, partial, B, T, C, st);
@@ -1437,7 +1471,8 @@ hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* leng
     }
 #undef DW1B_CASE
     if (e != hipSuccess || !partial) return e;
-    const int64_t P = bwd1d_grid(B, T, C, bwd1d_vec(vec, K), bwd1d_group(vec, K, bf16)).G;
+    const int q = bwd1d_group(vec, K, bf16);
+    const int64_t P = (q ? bwd1d_grid(B, T, C, bwd1d_group_v(q, bf16), true) : bwd1d_grid(B, T, C, bwd1d_vec(vec, K))).G;
     RowOutputs out = {};
     out.n = 2;
     out.p[0] = dw; out.first[0] = 0; out.count[0] = (int32_t)K;

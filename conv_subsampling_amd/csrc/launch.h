@@ -62,7 +62,7 @@ hipError_t launch_dwconv1d_stream(const void* x, const void* w, const void* bias
 // 1-D backward: the widths with a kernel, the widest vector each takes, and
 // the workspace (fp64 partials) it needs.
 bool dwconv1d_bwd_supported(int64_t K);
-int dwconv1d_bwd_max_vec(int64_t K);
+int dwconv1d_bwd_max_vec(int64_t K, bool bf16);
 bool dwconv1d_bwd_fits(int64_t B, int64_t T, int64_t C, int64_t K, int elem_bytes);
 size_t dwconv1d_bwd_workspace(int64_t B, int64_t T, int64_t C, int64_t K);
 hipError_t launch_dwconv1d_bwd(const void* x, const void* w, const int32_t* lengths, const void* dy, void* dx,

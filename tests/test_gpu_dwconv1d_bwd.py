@@ -213,3 +213,31 @@ def test_paired_lanes_match_eight_byte_lanes(B, T, C, K, causal):
     ref = oracle.dwconv1d_bwd(x, w, L, dy, causal)
     for name, g, r in zip(("dx", "dw", "db"), wide, ref):
         assert_parity(g, r, TOL_F32, f"paired {name}")
+
+
+@pytest.mark.parametrize("B,T,C,K,causal", [(3, 75, 512, 9, True), (2, 61, 104, 9, False), (4, 40, 24, 15, True),
+                                            (2, 33, 264, 15, False), (3, 90, 64, 7, True), (1, 3, 8, 9, True),
+                                            (2, 9, 16, 7, False)])
+def test_bf16_lane_groups_match_narrow_lanes(B, T, C, K, causal):
+    """bf16 at K = 7, 9 and 15 with 16-byte-aligned tensors (C a multiple of
+    8) takes groups of four lanes, two channels each, sharing a 16-byte piece
+    of eight channels.  The same call 8 bytes off that alignment takes
+    four-channel 8-byte lanes (two-channel 4-byte lanes at K = 7 and 15).  The
+    arithmetic per element is the same: dx is equal bit for bit, and dw and
+    db, summed over another split of the tiles, agree to one float32 ulp."""
+    x, w, dy, L = make(B, T, C, K, lens=[T, T // 2 + 1, 0, max(T - 9, 0)][:B])
+    x, w, dy = x.to(torch.bfloat16), w.to(torch.bfloat16), dy.to(torch.bfloat16)
+    say(f"dwconv1d_bwd bf16 lane groups against narrow lanes B={B} T={T} C={C} K={K} causal={causal}")
+    wide = run(x, w, L, dy, causal)
+    x8, dy8 = _offset8(x), _offset8(dy)
+    dx8 = _offset8(torch.full_like(x, float("nan")))
+    _, dw8, db8 = lib().dwconv1d_bwd(x8, w, L, dy8, dx=dx8, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[0], dx8), "dx"
+    for a, b in ((wide[1], dw8), (wide[2], db8)):
+        mag = torch.maximum(a.abs(), b.abs())
+        ulp = torch.nextafter(mag, torch.full_like(mag, float("inf"))) - mag
+        assert torch.all((a - b).abs() <= ulp)
+    ref = oracle.dwconv1d_bwd(x, w, L, dy, causal)
+    for name, g, r, tol in zip(("dx", "dw", "db"), wide, ref, (TOL_BF16, TOL_F32, TOL_F32)):
+        assert_parity(g, r, tol, f"bf16 lane groups {name}")
