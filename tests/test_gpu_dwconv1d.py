@@ -74,6 +74,9 @@ GRID = [
     (6, 700, 512, 9, True), (5, 900, 256, 4, False), (9, 500, 320, 3, True),
     (4, 1000, 1024, 5, False), (17, 260, 256, 9, False), (3, 999, 516, 5, True),
     (8, 900, 512, 15, True), (12, 1000, 200, 5, True), (9, 1300, 180, 15, False),
+    # the fp32 register window (fewer than 32 channel groups) over longer
+    # items: many tiles per item, masked tiles past each length
+    (4, 1000, 64, 9, True), (3, 700, 100, 5, False), (2, 2100, 16, 15, False),
 ]
 
 
@@ -105,14 +108,15 @@ def test_null_bias_equals_zero_bias_bitwise():
     assert torch.equal(run(x, w, None, lengths, True), run(x, w, z, lengths, True))
 
 
-@pytest.mark.parametrize("C", [32, 512])
-def test_masked_input_is_never_read(C):
+@pytest.mark.parametrize("C,T", [(32, 80), (512, 80), (64, 600)])
+def test_masked_input_is_never_read(C, T):
     """NaN beyond each item's length must not reach any output (C = 512 at
-    fp32: the persistent form, whose tiles past a length issue no loads)."""
+    fp32: the persistent form, whose tiles past a length issue no loads;
+    C = 32 and 64: the register window, short and long items)."""
     for dtype in (torch.float32, torch.bfloat16):
-        B, T, K = 3, 80, 9
+        B, K = 3, 9
         x, w, b, _ = make(B, T, C, K, dtype)
-        lengths = torch.tensor([80, 33, 0], dtype=torch.int32, device=DEV)
+        lengths = torch.tensor([T, 33, 0], dtype=torch.int32, device=DEV)
         y = run(x, w, b, lengths, False)
         xp = x.clone()
         xp[1, 33:] = float("nan")
