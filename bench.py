@@ -851,6 +851,71 @@ def front_sq_summary(d, cmd):
     return "\n".join(lines) + "\n"
 
 
+# Memory-side counters of every row's main kernel and of its probe copy,
+# one rocprofv3 --pmc run per pass (derived counters are computed by rocprofv3).
+MEM_PASSES = {
+    "memA": ["VmemLatency", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"],
+    "memB": ["MeanOccupancyPerCU", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_ANY"],
+    "memC": ["TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum"],
+    "memD": ["TCC_EA0_WRREQ_LEVEL_sum", "TCC_EA0_WRREQ_sum"],
+}
+
+
+def mem_counter_summary(d, cmd):
+    """Text summary of the MEM_PASSES counters per bench row (its main
+    kernel's dispatches) and per probe copy; None if a pass is missing."""
+    per_pass = {}
+    for k in MEM_PASSES:
+        rows = _csv_rows(os.path.join(d, k, "**", "*counter_collection.csv"))
+        if not rows:
+            return None
+        disp = {}
+        for r in rows:
+            did = r.get("Dispatch_Id")
+            name, vals = disp.get(did, (r.get("Kernel_Name", ""), {}))
+            cn = r.get("Counter_Name")
+            vals[cn] = vals.get(cn, 0.0) + float(r.get("Counter_Value", 0))
+            disp[did] = (name, vals)
+        per_pass[k] = [(did, name, vals) for did, (name, vals) in disp.items()]
+    table = {}
+    for k, disp in per_pass.items():
+        for name, v in attribute_dispatches(disp).items():
+            for vals in v:
+                for cn, x in vals.items():
+                    table.setdefault(name, {}).setdefault(cn, []).append(x)
+        probes = [vals for _, kn, vals in sorted(disp, key=lambda t: int(t[0]))
+                  if kernel_short_name(kn) == PROBE_KERNEL]
+        if probes and len(probes) % len(PROBE_ROWS) == 0:
+            for j, name in enumerate(PROBE_ROWS):
+                for vals in probes[len(PROBE_ROWS) + j::len(PROBE_ROWS)]:
+                    for cn, x in vals.items():
+                        table.setdefault("probe:" + name, {}).setdefault(cn, []).append(x)
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    lines = ["# Memory-side counters per bench row's main kernel and per probe copy, on one MI355X",
+             *[f"# {k}: " + cmd(k) for k in MEM_PASSES],
+             f"# src_sha256={sources_sha(KERNEL_SOURCES)}",
+             "# Means per dispatch.  occ: MeanOccupancyPerCU (waves resident per CU); vmem_lat:",
+             "# VmemLatency (cycles a vector memory instruction is in flight); wait: SQ_WAIT_ANY /",
+             "# SQ_WAVE_CYCLES (both in quad-cycles: the share of wave time spent waiting);",
+             "# rd_lat, wr_lat: TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum and the same for writes",
+             "# (cycles an L2-to-memory request is in flight).",
+             f"{'row':<30} {'occ':>6} {'vmem_lat':>9} {'wait':>6} {'rd_lat':>8} {'wr_lat':>8}"]
+    order = [n for n, _ in ROW_KERNELS]
+    names = [n for n in order if n in table]
+    names += ["probe:" + n for n in PROBE_ROWS if "probe:" + n in table]
+    for name in names:
+        t = {cn: mean(v) for cn, v in table[name].items()}
+        occ = t.get("MeanOccupancyPerCU", float("nan"))
+        vl = t.get("VmemLatency", float("nan"))
+        wc = t.get("SQ_WAVE_CYCLES", 0.0)
+        wait = t.get("SQ_WAIT_ANY", float("nan")) / wc if wc else float("nan")
+        rq, wq = t.get("TCC_EA0_RDREQ_sum", 0.0), t.get("TCC_EA0_WRREQ_sum", 0.0)
+        rl = t.get("TCC_EA0_RDREQ_LEVEL_sum", float("nan")) / rq if rq else float("nan")
+        wl = t.get("TCC_EA0_WRREQ_LEVEL_sum", float("nan")) / wq if wq else float("nan")
+        lines.append(f"{name:<30} {occ:>6.1f} {vl:>9.0f} {wait:>6.2f} {rl:>8.0f} {wl:>8.0f}")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_profile(d):
     """Write profiles/ summaries from rocprofv3 output under d:
     d/stats/**/*kernel_stats.csv and *kernel_trace.csv (durations),
@@ -920,6 +985,12 @@ def summarize_profile(d):
             name, v = r.get("Kernel_Name", ""), float(r.get("Counter_Value", 0))
             per[key] = (name, per.get(key, (name, 0.0))[1] + v)
         return [(k, n, v) for k, (n, v) in per.items()]
+
+    mem = mem_counter_summary(d, cmd)
+    if mem:
+        with open(os.path.join(ROOT, "profiles", "row_memory_counters.txt"), "w") as fh:
+            fh.write(mem)
+        print(mem)
 
     sq = front_sq_summary(d, cmd)
     if sq:
