@@ -877,6 +877,9 @@ def mem_counter_summary(d, cmd):
             vals[cn] = vals.get(cn, 0.0) + float(r.get("Counter_Value", 0))
             disp[did] = (name, vals)
         per_pass[k] = [(did, name, vals) for did, (name, vals) in disp.items()]
+        if "--no-check" not in cmd(k):
+            # rows are matched to dispatches by their order (see the traffic summary)
+            raise SystemExit(f"{k} counter run was taken without --no-check; take it again with --no-check")
     table = {}
     for k, disp in per_pass.items():
         for name, v in attribute_dispatches(disp).items():

@@ -111,3 +111,51 @@ def test_traffic_summary_refuses_counter_runs_taken_with_the_oracle_check(tmp_pa
             "Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n1,copyBuffer,%s,1048576\n" % cname)
     with pytest.raises(SystemExit, match="--no-check"):
         bench.summarize_profile(str(tmp_path))
+
+
+def _write_mem_passes(d, with_check=False):
+    """Counter CSVs for every memory-side pass: one step of row dispatches
+    (dispatch i of the step carries value i + 1) and two probe rounds."""
+    import bench
+    rows = bench.ROW_KERNELS
+    for k, counters in bench.MEM_PASSES.items():
+        p = d / k
+        p.mkdir()
+        flags = "--steps 1" + ("" if with_check else " --no-check")
+        (p / "command.txt").write_text(f"rocprofv3 --pmc {' '.join(counters)} -- python3 bench.py {flags}\n")
+        lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value"]
+        did = 0
+        for i, (_, prefix) in enumerate(rows):
+            did += 1
+            for cn in counters:
+                lines.append(f'{did},"void {prefix}float const*)",{cn},{(i + 1) * (2 if "LEVEL" in cn else 1)}')
+        for _ in range(2):
+            for _ in bench.PROBE_ROWS:
+                did += 1
+                for cn in counters:
+                    lines.append(f'{did},"void {bench.PROBE_KERNEL}(uint4 const*)",{cn},{3 if "LEVEL" in cn else 1}')
+        (p / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+
+def test_memory_counter_summary_attributes_rows_and_probes(tmp_path):
+    import bench
+    _write_mem_passes(tmp_path)
+    cmd = lambda k: (tmp_path / k / "command.txt").read_text().strip()
+    text = bench.mem_counter_summary(str(tmp_path), cmd)
+    got = {ln.split()[0]: ln.split()[1:] for ln in text.splitlines() if ln and not ln.startswith("#")}
+    # a row's read latency is its LEVEL sum over its request count: 2 (i + 1) / (i + 1)
+    for i, (name, prefix) in enumerate(bench.ROW_KERNELS):
+        same = [n for n, p in bench.ROW_KERNELS if p == prefix]
+        if len(same) == 1:
+            occ, vl, wait, rd, wr = map(float, got[name])
+            assert occ == i + 1 and vl == i + 1 and wait == 1.0 and rd == 2.0 and wr == 2.0, name
+    for name in bench.PROBE_ROWS:
+        assert list(map(float, got["probe:" + name]))[3:] == [3.0, 3.0]
+
+
+def test_memory_counter_summary_refuses_runs_with_the_oracle_check(tmp_path):
+    import bench
+    _write_mem_passes(tmp_path, with_check=True)
+    cmd = lambda k: (tmp_path / k / "command.txt").read_text().strip()
+    with pytest.raises(SystemExit, match="--no-check"):
+        bench.mem_counter_summary(str(tmp_path), cmd)
