@@ -2,6 +2,7 @@
 against the oracle's definitions, and the profile summaries' attribution of
 kernel dispatches to bench rows."""
 import itertools
+import os
 
 import pytest
 
@@ -159,3 +160,20 @@ def test_memory_counter_summary_refuses_runs_with_the_oracle_check(tmp_path):
     cmd = lambda k: (tmp_path / k / "command.txt").read_text().strip()
     with pytest.raises(SystemExit, match="--no-check"):
         bench.mem_counter_summary(str(tmp_path), cmd)
+
+
+def test_row_kernel_names_exist_in_the_library():
+    """Every bench row's kernel name (which the profile summaries match
+    against rocprofv3's demangled names) names a kernel the library holds."""
+    import shutil
+    import subprocess
+    import bench
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    lib = os.path.join(root, "conv_subsampling_amd", "libdwconv.so")
+    plib = os.path.join(root, "conv_subsampling_amd", "libdwprobe.so")
+    if not (shutil.which("nm") and os.path.exists(lib) and os.path.exists(plib)):
+        pytest.skip("nm or the built libraries are missing")
+    syms = subprocess.run(["nm", "-C", lib, plib], capture_output=True, text=True, check=True).stdout
+    for name, prefix in bench.ROW_KERNELS:
+        assert "void " + prefix in syms, (name, prefix)
+    assert bench.PROBE_KERNEL + "(" in syms
